@@ -1,0 +1,358 @@
+"""Pins of the CPU fp64 oracle against facts that do not come from the oracle
+itself: a library Transformer (torch.nn, float64 on the CPU), brute-force
+Jacobians with numpy.linalg.slogdet, the triangular structure of the affine AF
+block, exact round trips, the Jacobi prefix-exactness invariant and closed-form
+special cases.
+
+Sources: STARFlow-V notes (papernotes.org), 关键设计 1 (affine AF equation,
+self-exclusive causal mask, alternating directions), 关键设计 3 (Jacobi
+fixed-point equation, residual stop, worst case of B iterations from the
+triangular system), 损失函数 (log|det J| in L_NF), 一个完整示例 (I2V: forward
+encoding into the KV cache).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from autoregressive_normalizing_flow_amd import synth
+from oracle import af_oracle as O
+
+
+def tiny(C=3, d=16, H=2, layers=2, max_len=12, seed=0, aux=True, n_blocks=1,
+         dtype="f32"):
+    cfg = synth.BlockCfg(C=C, d=d, n_heads=H, n_layers=layers, max_len=max_len,
+                         dtype=dtype)
+    ps = [O.to64(p) for p in synth.make_params(cfg, seed, randomize_aux=aux,
+                                               n_blocks=n_blocks)]
+    return cfg, ps
+
+
+def scaled(ps, s):
+    """Scale all weight matrices by s to strengthen the token coupling, so the
+    structural checks are not passed by a near-constant network."""
+    out = []
+    for p in ps:
+        q = {k: (v * s if k.startswith("w_") else v) for k, v in p.items()
+             if k != "layers"}
+        q["layers"] = [{k: (v * s if k.startswith("w_") else v)
+                        for k, v in l.items()} for l in p["layers"]]
+        out.append(q)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 1. the network against torch.nn's Transformer layer (a library routine)
+# ---------------------------------------------------------------------------
+def torch_net(p, inp, n_heads):
+    torch = pytest.importorskip("torch")
+    nn = torch.nn
+    d = p["w_in"].shape[0]
+    x = torch.from_numpy(inp)
+    h = x @ torch.from_numpy(p["w_in"]).T + torch.from_numpy(p["b_in"]) \
+        + torch.from_numpy(p["pos"][: inp.shape[1]])
+    R = inp.shape[1]
+    mask = nn.Transformer.generate_square_subsequent_mask(R, dtype=torch.float64)
+    for L in p["layers"]:
+        layer = nn.TransformerEncoderLayer(
+            d, n_heads, dim_feedforward=L["w_1"].shape[0], dropout=0.0,
+            activation="gelu", layer_norm_eps=1e-5, batch_first=True,
+            norm_first=True, dtype=torch.float64)
+        with torch.no_grad():
+            layer.self_attn.in_proj_weight.copy_(torch.from_numpy(L["w_qkv"]))
+            layer.self_attn.in_proj_bias.copy_(torch.from_numpy(L["b_qkv"]))
+            layer.self_attn.out_proj.weight.copy_(torch.from_numpy(L["w_o"]))
+            layer.self_attn.out_proj.bias.copy_(torch.from_numpy(L["b_o"]))
+            layer.linear1.weight.copy_(torch.from_numpy(L["w_1"]))
+            layer.linear1.bias.copy_(torch.from_numpy(L["b_1"]))
+            layer.linear2.weight.copy_(torch.from_numpy(L["w_2"]))
+            layer.linear2.bias.copy_(torch.from_numpy(L["b_2"]))
+            layer.norm1.weight.copy_(torch.from_numpy(L["ln1_g"]))
+            layer.norm1.bias.copy_(torch.from_numpy(L["ln1_b"]))
+            layer.norm2.weight.copy_(torch.from_numpy(L["ln2_g"]))
+            layer.norm2.bias.copy_(torch.from_numpy(L["ln2_b"]))
+        layer.train(False)
+        with torch.no_grad():
+            h = layer(h, src_mask=mask, is_causal=True)
+    hf = nn.functional.layer_norm(h, (d,), torch.from_numpy(p["ln_f_g"]),
+                                  torch.from_numpy(p["ln_f_b"]), eps=1e-5)
+    out = (hf @ torch.from_numpy(p["w_head"]).T + torch.from_numpy(p["b_head"]))
+    return out.detach().numpy()
+
+
+@pytest.mark.parametrize("d,H,layers,R", [(16, 2, 2, 9), (32, 4, 1, 13), (24, 3, 3, 5)])
+def test_net_matches_torch_transformer_layer(d, H, layers, R):
+    cfg, (p,) = tiny(C=5, d=d, H=H, layers=layers, max_len=R, seed=d + R)
+    p = scaled([p], 8.0)[0]
+    inp = np.random.default_rng(1).standard_normal((2, R, 5))
+    mu, raw, _ = O.net_rows(p, inp, np.arange(R), H)
+    ref = torch_net(p, inp, H)
+    np.testing.assert_allclose(np.concatenate([mu, raw], -1), ref, rtol=0, atol=1e-12)
+    assert np.abs(ref).max() > 0.1  # a non-trivial output
+
+
+def test_gelu_and_layernorm_textbook_values():
+    # GELU(x) = x * Phi(x); Phi(1) = 0.8413447460685429 (normal CDF table value)
+    np.testing.assert_allclose(O.gelu(np.array([1.0, -1.0, 0.0])),
+                               [0.8413447460685429, -0.15865525393145707, 0.0],
+                               rtol=1e-15, atol=1e-16)
+    h = np.array([[1.0, 2.0, 3.0, 4.0]])
+    out = O.layernorm(h, np.ones(4), np.zeros(4))
+    np.testing.assert_allclose(out, (h - 2.5) / math.sqrt(1.25 + 1e-5), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# 2. brute-force Jacobians: triangularity, diagonal 1/sigma, slogdet = logdet
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("direction", ["l2r", "r2l"])
+def test_jacobian_triangular_and_slogdet(direction):
+    L, C = 6, 3
+    cfg, ps = tiny(C=C, d=16, H=2, layers=2, max_len=L, seed=3)
+    p = scaled(ps, 6.0)[0]
+    x = np.random.default_rng(5).standard_normal((1, L, C))
+    f = lambda xx: O.forward_block(p, xx, 2, direction)[0]
+    J = O.jacobian_bruteforce(f, x)                      # [(L*C), (L*C)]
+    z, logdet = O.forward_block(p, x, 2, direction)
+    Jb = J.reshape(L, C, L, C)
+    # logsigma per token in storage order
+    xs = x if direction == "l2r" else x[:, ::-1]
+    _, raw, _ = O.net_rows(p, O.shift(xs), np.arange(L), 2)
+    ls = O.log_sigma(raw)[0]
+    if direction == "r2l":
+        ls = ls[::-1]
+    for t in range(L):
+        for j in range(L):
+            blk = Jb[t, :, j, :]
+            later = j > t if direction == "l2r" else j < t
+            if later:
+                assert np.abs(blk).max() < 1e-9, (t, j)
+            elif j == t:
+                np.testing.assert_allclose(blk, np.diag(np.exp(-ls[t])), atol=1e-8)
+    # exactly one-token shift: z_t depends on its neighbour x_{t-1} (processing order)
+    for t in range(1, L):
+        j = t - 1 if direction == "l2r" else L - t
+        tt = t if direction == "l2r" else L - 1 - t
+        assert np.abs(Jb[tt, :, j, :]).max() > 1e-4
+    sign, lad = np.linalg.slogdet(J)
+    assert sign > 0
+    np.testing.assert_allclose(lad, logdet[0], rtol=0, atol=1e-8)
+
+
+def test_stack_jacobian_logdet():
+    L, C, T = 5, 2, 3
+    cfg, ps = tiny(C=C, d=16, H=2, layers=1, max_len=L, seed=11, n_blocks=T)
+    ps = scaled(ps, 5.0)
+    x = np.random.default_rng(2).standard_normal((1, L, C))
+    J = O.jacobian_bruteforce(lambda xx: O.forward_stack(ps, xx, 2)[0], x)
+    _, logdet = O.forward_stack(ps, x, 2)
+    sign, lad = np.linalg.slogdet(J)
+    np.testing.assert_allclose(lad, logdet[0], rtol=0, atol=1e-8)
+    # the block log-dets add
+    z = x.copy()
+    tot = 0.0
+    for t, p in enumerate(ps):
+        z, l = O.forward_block(p, z, 2, O.direction_of(t))
+        tot += l[0]
+    np.testing.assert_allclose(tot, logdet[0], rtol=1e-14)
+    # a stack of alternating blocks is dense, not triangular
+    assert np.abs(J.reshape(L, C, L, C)[0, :, L - 1, :]).max() > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# 3. exact inverse
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("direction", ["l2r", "r2l"])
+def test_sequential_inverse_roundtrip(direction):
+    L, C = 10, 4
+    cfg, (p,) = tiny(C=C, d=16, H=2, layers=2, max_len=L, seed=7)
+    p = scaled([p], 4.0)[0]
+    x = np.random.default_rng(3).standard_normal((2, L, C))
+    z, _ = O.forward_block(p, x, 2, direction)
+    x2 = O.inverse_sequential_block(p, z, 2, direction)
+    np.testing.assert_allclose(x2, x, rtol=0, atol=1e-12)
+    zz = np.random.default_rng(4).standard_normal((2, L, C))
+    xx = O.inverse_sequential_block(p, zz, 2, direction)
+    np.testing.assert_allclose(O.forward_block(p, xx, 2, direction)[0], zz,
+                               rtol=0, atol=1e-12)
+
+
+def test_stack_roundtrip():
+    cfg, ps = tiny(C=3, d=16, H=2, layers=1, max_len=8, seed=9, n_blocks=4)
+    ps = scaled(ps, 4.0)
+    x = np.random.default_rng(6).standard_normal((3, 8, 3))
+    z, _ = O.forward_stack(ps, x, 2)
+    np.testing.assert_allclose(O.inverse_sequential_stack(ps, z, 2), x, atol=1e-12)
+    xj, it = O.inverse_jacobi_stack(ps, z, 2, B=4, tau=0.0)
+    np.testing.assert_allclose(xj, x, atol=1e-11)
+    assert it.shape == (4, 2) and np.all(it == 4)
+
+
+# ---------------------------------------------------------------------------
+# 4. KV cache and prefix
+# ---------------------------------------------------------------------------
+def test_cache_equivalence():
+    L, C = 12, 3
+    cfg, (p,) = tiny(C=C, max_len=L, seed=12)
+    inp = np.random.default_rng(8).standard_normal((2, L, C))
+    mu, raw, kv = O.net_rows(p, inp, np.arange(L), 2)
+    cache = O._empty_cache(p, 2, 2)
+    outs = []
+    for s, e in ((0, 5), (5, 7), (7, 12)):
+        m, r, kvb = O.net_rows(p, inp[:, s:e], np.arange(s, e), 2, cache)
+        outs.append(np.concatenate([m, r], -1))
+        cache = O._append(cache, kvb)
+    np.testing.assert_allclose(np.concatenate(outs, 1),
+                               np.concatenate([mu, raw], -1), atol=1e-13)
+    for (kc, vc), (k, v) in zip(cache, kv):
+        np.testing.assert_allclose(kc, k, atol=1e-14)
+        np.testing.assert_allclose(vc, v, atol=1e-14)
+
+
+def test_prefill_then_continue_equals_full_sequence():
+    P, L, C = 6, 5, 3
+    cfg, (p,) = tiny(C=C, max_len=P + L, seed=13)
+    p = scaled([p], 4.0)[0]
+    xall = np.random.default_rng(9).standard_normal((2, P + L, C))
+    z_full, _ = O.forward_block(p, xall, 2)
+    cache, x_last = O.prefill(p, xall[:, :P], 2)
+    z_tail, _ = O.forward_block(p, xall[:, P:], 2, pos0=P, cache=cache, x_last=x_last)
+    np.testing.assert_allclose(z_tail, z_full[:, P:], atol=1e-13)
+    xs = O.inverse_sequential_block(p, z_full[:, P:], 2, pos0=P, cache=cache,
+                                    x_last=x_last)
+    np.testing.assert_allclose(xs, xall[:, P:], atol=1e-12)
+    xj, it = O.inverse_jacobi_block(p, z_full[:, P:], 2, B=3, tau=0.0, pos0=P,
+                                    cache=cache, x_last=x_last, init="given",
+                                    x_init=np.zeros((2, L, C)))
+    np.testing.assert_allclose(xj, xall[:, P:], atol=1e-11)
+    assert list(it) == [3, 2]
+
+
+# ---------------------------------------------------------------------------
+# 5. Jacobi: prefix exactness, cap, closed forms, stop rule
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("init", ["zero", "given"])
+def test_jacobi_prefix_exactness(init):
+    L, C, B = 12, 3, 6
+    cfg, (p,) = tiny(C=C, max_len=L, seed=21)
+    p = scaled([p], 6.0)[0]
+    z = np.random.default_rng(10).standard_normal((2, L, C))
+    x_seq = O.inverse_sequential_block(p, z, 2)
+    x_init = np.random.default_rng(11).standard_normal((2, L, C))
+    for k in range(1, B + 1):
+        x, it = O.inverse_jacobi_block(p, z, 2, B, tau=0.0, init=init,
+                                       x_init=x_init, forced_iters=[B, k])
+        # block 0 exact after B updates; block 1's first k tokens exact
+        np.testing.assert_allclose(x[:, :B + k], x_seq[:, :B + k], atol=1e-11)
+        if k < B:
+            assert np.abs(x[:, B + k:] - x_seq[:, B + k:]).max() > 1e-6
+        assert list(it) == [B, k]
+
+
+def test_jacobi_caps_at_block_length_and_reaches_sequential():
+    L, C, B = 10, 3, 4
+    cfg, (p,) = tiny(C=C, max_len=L, seed=22)
+    p = scaled([p], 6.0)[0]
+    z = np.random.default_rng(12).standard_normal((1, L, C))
+    x_seq = O.inverse_sequential_block(p, z, 2)
+    trace = []
+    x, it = O.inverse_jacobi_block(p, z, 2, B, tau=1e-300, trace=trace)
+    assert list(it) == [4, 4, 2]     # cap Bb, last block ragged
+    np.testing.assert_allclose(x, x_seq, atol=1e-11)
+    # B = 1 is sequential decoding, one update per token
+    x1, it1 = O.inverse_jacobi_block(p, z, 2, 1, tau=1e-3)
+    assert np.all(it1 == 1)
+    np.testing.assert_allclose(x1, x_seq, atol=1e-12)
+
+
+def test_jacobi_closed_form_constant_network():
+    """All weights zero, head bias (mu0, raw0): x = mu0 + exp(0.5 tanh raw0) z,
+    reached from zero init with iters = 2 (r1 = 1, r2 = 0)."""
+    L, C = 8, 2
+    cfg, (p,) = tiny(C=C, max_len=L, seed=0, aux=False)
+    for k in list(p):
+        if k.startswith("w_") or k == "pos":
+            p[k] = np.zeros_like(p[k])
+    for l in p["layers"]:
+        for k in l:
+            if k.startswith("w_"):
+                l[k] = np.zeros_like(l[k])
+    mu0 = np.array([0.3, -1.2])
+    raw0 = np.array([0.7, -2.0])
+    p["b_head"] = np.concatenate([mu0, raw0])
+    z = np.random.default_rng(13).standard_normal((2, L, C))
+    expect = mu0 + np.exp(0.5 * np.tanh(raw0)) * z
+    trace = []
+    x, it = O.inverse_jacobi_block(p, z, 2, B=4, tau=1e-3, trace=trace)
+    np.testing.assert_allclose(x, expect, rtol=1e-15, atol=1e-15)
+    assert list(it) == [2, 2]
+    assert np.allclose(trace[0][2], 1.0) and np.allclose(trace[1][2], 0.0)
+    zf, ld = O.forward_block(p, expect, 2)
+    np.testing.assert_allclose(zf, z, atol=1e-14)
+    np.testing.assert_allclose(ld, -L * (0.5 * np.tanh(raw0)).sum(), rtol=1e-14)
+
+
+def test_jacobi_init_at_solution_stops_after_one_update():
+    L, C = 8, 3
+    cfg, (p,) = tiny(C=C, max_len=L, seed=23)
+    z = np.random.default_rng(14).standard_normal((1, L, C))
+    x_seq = O.inverse_sequential_block(p, z, 2)
+    x, it = O.inverse_jacobi_block(p, z, 2, 4, tau=1e-3, init="given", x_init=x_seq)
+    assert list(it) == [1, 1]
+    np.testing.assert_allclose(x, x_seq, atol=1e-13)
+
+
+def test_jacobi_stop_rule_and_forced_count():
+    L, C, B = 16, 3, 8
+    cfg, (p,) = tiny(C=C, max_len=L, seed=24)
+    p = scaled([p], 3.0)[0]
+    z = np.random.default_rng(15).standard_normal((2, L, C))
+    trace = []
+    x, it = O.inverse_jacobi_block(p, z, 2, B, tau=1e-3, trace=trace)
+    # every stop is the first update whose residuals are all < tau
+    by_block = {}
+    for b, k, r in trace:
+        by_block.setdefault(b, []).append(r)
+    for b, rs in by_block.items():
+        assert len(rs) == it[b]
+        assert all(np.any(r >= 1e-3) for r in rs[:-1])
+        assert np.all(rs[-1] < 1e-3) or it[b] == B
+    # tau <= 0 forces min(max_iters, Bb) updates
+    _, it2 = O.inverse_jacobi_block(p, z, 2, B, tau=0.0, max_iters=3)
+    assert list(it2) == [3, 3]
+    # the residual matches its definition on one update
+    b, k, r = trace[0]
+    assert k == 1 and np.allclose(r, 1.0)   # from zero init r_1 = 1 exactly
+
+
+def test_jacobi_prev_frame_init():
+    F, C = 4, 2
+    L = 3 * F
+    cfg, (p,) = tiny(C=C, max_len=L, seed=25)
+    p = scaled([p], 4.0)[0]
+    z = np.random.default_rng(16).standard_normal((1, L, C))
+    tr = []
+    x, it = O.inverse_jacobi_block(p, z, 2, F, tau=0.0, init="prev_frame",
+                                   frame_len=F, forced_iters=[F, 1, 1])
+    # with one update from x^(0) = previous frame, token 0 of the frame is exact
+    x_seq = O.inverse_sequential_block(p, z, 2)
+    np.testing.assert_allclose(x[:, :F + 1], x_seq[:, :F + 1], atol=1e-12)
+    # the rest of frame 1 equals one Jacobi update from the previous frame
+    inp = O.shift(x[:, :F].copy(), x[:, F - 1])
+    cache = O._empty_cache(p, 1, 2)
+    _, _, kv = O.net_rows(p, O.shift(x[:, :F]), np.arange(F), 2, cache)
+    cache = O._append(cache, kv)
+    mu, raw, _ = O.net_rows(p, inp, np.arange(F, 2 * F), 2, cache)
+    np.testing.assert_allclose(x[:, F:2 * F], mu + np.exp(O.log_sigma(raw)) * z[:, F:2 * F],
+                               atol=1e-13)
+
+
+def test_frames_are_independent_in_a_batch():
+    cfg, ps = tiny(C=3, d=16, H=2, layers=1, max_len=6, seed=30, n_blocks=2)
+    x = np.random.default_rng(17).standard_normal((4, 6, 3))
+    z, ld = O.forward_stack(ps, x, 2)
+    for n in range(4):
+        zn, ldn = O.forward_stack(ps, x[n:n + 1], 2)
+        np.testing.assert_allclose(zn[0], z[n], atol=1e-14)
+        np.testing.assert_allclose(ldn[0], ld[n], rtol=1e-14)
+    xj, _ = O.inverse_jacobi_stack(ps, z, 2, B=3, tau=0.0)
+    np.testing.assert_allclose(xj, x, atol=1e-11)
