@@ -1,0 +1,72 @@
+// Internal launchers of the AF-block kernels.  Every launcher validates
+// nothing (the runtime does) and returns the launch's hipError_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace af {
+
+// ---- token-side kernels ----------------------------------------------------
+// h[m, :] = shift(x)[m] W_in^T + b_in + pos[pos_base + t] for the chunk rows
+// m = n*R + t (processing index i = s + t); the shifted input of processing
+// index i is token i-1 of the same sample, or x_last[n] (zeros if NULL) at i=0.
+hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
+                        const float* b_in, const float* pos, float* h, int N,
+                        int R, int C, int d, int L, int s, int dir, int pos_base,
+                        hipStream_t st);
+
+// out = LayerNorm(h) * g + b over rows of width d (eps 1e-5); out is bf16 when
+// out_bf16, else fp32.
+hipError_t launch_layernorm(const float* h, const float* g, const float* b,
+                            void* out, bool out_bf16, int M, int d, hipStream_t st);
+
+// x^(0) of a Jacobi block: mode 0 zeros, 1 copy of x_init, 2 previous frame.
+hipError_t launch_init_block(float* x, const float* x_init, int mode, int N,
+                             int R, int C, int L, int s, int dir, int F,
+                             hipStream_t st);
+
+hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st);
+
+struct AffineArgs {
+  const float* head;   // [N*R, 2C]: [mu | raw] per row
+  const float* z;      // inverse: z tokens [N, L, C]
+  float* x;            // inverse: x tokens, updated in place; forward: x tokens (read)
+  float* zout;         // forward: z tokens (written)
+  int N, R, C, L, s, dir;
+  float* partials;     // [N][G][2]
+  float* res;          // [N][2]
+  unsigned* counter;   // zero before the first launch; the kernel leaves it zero
+  float* logdet;       // forward: logdet[n] += -sum log sigma (may be NULL)
+};
+// mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
+hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);
+int affine_groups(int R, int C);   // G, the partial slots per sample
+
+// ---- GEMMs: y[M, N] = A[M, K] W[N, K]^T + bias -----------------------------
+struct QKVDst {
+  void* q;        // [M, d]
+  void* kc;       // K cache of this layer  [Nb][H][Lcap][dh]
+  void* vt;       // V cache (transposed)   [Nb][H][dh][Lcap]
+  int R, d, dh, H, Lcap, pos_base;
+};
+hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* W,
+                           const float* bias, int M, int N, int K, QKVDst dst,
+                           hipStream_t st);
+hipError_t launch_gemm_resid(bool bf16, const void* A, const void* W,
+                             const float* bias, float* h, int M, int N, int K,
+                             hipStream_t st);
+hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* W,
+                            const float* bias, void* out, int M, int N, int K,
+                            hipStream_t st);
+hipError_t launch_gemm_f32out(bool bf16, const void* A, const void* W,
+                              const float* bias, float* out, int M, int N, int K,
+                              hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------
+// out[m, h*dh:(h+1)*dh] = softmax(q k^T / sqrt(dh)) v over cached keys
+// 0..pos_base+t (inclusive) for chunk row m = n*R + t.
+hipError_t launch_attention(bool bf16, const void* q, const void* kc,
+                            const void* vt, void* out, int N, int R, int H,
+                            int dh, int d, int Lcap, int pos_base, hipStream_t st);
+
+}  // namespace af

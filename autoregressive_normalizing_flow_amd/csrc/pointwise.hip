@@ -1,0 +1,306 @@
+// Token-side kernels of the AF block: the masked shift + input embedding,
+// LayerNorm, Jacobi-block initialisation and the fused affine kernel that
+// applies the affine map, reduces log sigma (forward) or the Jacobi residual
+// (inverse) per sample.
+//
+// Method: STARFlow-V notes (papernotes.org), 关键设计 1 (affine AF equation
+// z = (x - mu(x*m)) / sigma(x*m) with the self-exclusive causal mask) and
+// 关键设计 3 (Jacobi update x = mu + sigma * z and the scale-normalised
+// residual ||x^(k+1) - x^(k)||^2 / ||x^(k+1)||^2).
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace af {
+
+// ---------------------------------------------------------------------------
+// shift + embed.  Block: 256 output columns x 16 rows.  W_in is staged
+// transposed through LDS in chunks of 32 channels so that column reads are
+// conflict-free; the 16 shifted input rows are broadcast from LDS.
+// ---------------------------------------------------------------------------
+constexpr int EMB_ROWS = 16;
+constexpr int EMB_COLS = 256;
+constexpr int EMB_CCH = 32;
+constexpr int EMB_MAXC = 256;
+
+__global__ __launch_bounds__(256) void embed_kernel(
+    const float* __restrict__ x, const float* __restrict__ x_last,
+    const float* __restrict__ w_in, const float* __restrict__ b_in,
+    const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
+    int d, int L, int s, int dir, int pos_base) {
+  __shared__ float s_in[EMB_ROWS][EMB_MAXC];
+  __shared__ float s_w[EMB_CCH][EMB_COLS + 1];
+  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * EMB_COLS;
+  const int m0 = blockIdx.y * EMB_ROWS;
+  const int M = N * R;
+
+  // shifted inputs of the 16 rows
+  for (int e = tid; e < EMB_ROWS * C; e += 256) {
+    int r = e / C, c = e - r * C;
+    int m = m0 + r;
+    float v = 0.f;
+    if (m < M) {
+      int n = m / R, t = m - n * R;
+      int i = s + t;  // processing index
+      if (i > 0) {
+        v = x[((size_t)n * L + storage_index(i - 1, L, dir)) * C + c];
+      } else if (x_last) {
+        v = x_last[(size_t)n * C + c];
+      }
+    }
+    s_in[r][c] = v;
+  }
+
+  float acc[EMB_ROWS];
+#pragma unroll
+  for (int r = 0; r < EMB_ROWS; ++r) acc[r] = 0.f;
+  const int j = j0 + tid;
+  for (int c0 = 0; c0 < C; c0 += EMB_CCH) {
+    const int cc_n = min(EMB_CCH, C - c0);
+    __syncthreads();
+    for (int e = tid; e < EMB_COLS * EMB_CCH; e += 256) {
+      int jj = e / EMB_CCH, cc = e - jj * EMB_CCH;
+      float v = 0.f;
+      if (j0 + jj < d && cc < cc_n) v = w_in[(size_t)(j0 + jj) * C + c0 + cc];
+      s_w[cc][jj] = v;
+    }
+    __syncthreads();
+    for (int cc = 0; cc < cc_n; ++cc) {
+      float w = s_w[cc][tid];
+#pragma unroll
+      for (int r = 0; r < EMB_ROWS; ++r) acc[r] += s_in[r][c0 + cc] * w;
+    }
+  }
+  if (j >= d) return;
+  const float bj = b_in[j];
+#pragma unroll
+  for (int r = 0; r < EMB_ROWS; ++r) {
+    int m = m0 + r;
+    if (m >= M) break;
+    int t = m % R;
+    h[(size_t)m * d + j] = acc[r] + bj + pos[(size_t)(pos_base + t) * d + j];
+  }
+}
+
+hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
+                        const float* b_in, const float* pos, float* h, int N,
+                        int R, int C, int d, int L, int s, int dir, int pos_base,
+                        hipStream_t st) {
+  dim3 grid((d + EMB_COLS - 1) / EMB_COLS, (N * R + EMB_ROWS - 1) / EMB_ROWS);
+  hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, st, x, x_last, w_in, b_in,
+                     pos, h, N, R, C, d, L, s, dir, pos_base);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm: one wave per row, VPL = d / 64 values per lane kept in registers
+// (two-pass mean / variance).
+// ---------------------------------------------------------------------------
+template <int VPL, class OutT>
+__global__ __launch_bounds__(256) void layernorm_kernel(
+    const float* __restrict__ h, const float* __restrict__ g,
+    const float* __restrict__ b, OutT* __restrict__ out, int M) {
+  constexpr int D = VPL * AF_WAVE;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* hr = h + (size_t)row * D;
+  float v[VPL];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    v[i] = hr[lane + AF_WAVE * i];
+    sum += v[i];
+  }
+  const float mean = wave_sum(sum) * (1.0f / D);
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    float c = v[i] - mean;
+    sq += c * c;
+  }
+  const float rstd = rsqrtf(wave_sum(sq) * (1.0f / D) + 1e-5f);
+  OutT* orow = out + (size_t)row * D;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    int j = lane + AF_WAVE * i;
+    orow[j] = from_f32<OutT>((v[i] - mean) * rstd * g[j] + b[j]);
+  }
+}
+
+template <class OutT>
+static hipError_t ln_dispatch(const float* h, const float* g, const float* b,
+                              OutT* out, int M, int d, hipStream_t st) {
+  dim3 grid((M + 3) / 4), blk(256);
+  switch (d / AF_WAVE) {
+    case 1: hipLaunchKernelGGL((layernorm_kernel<1, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 2: hipLaunchKernelGGL((layernorm_kernel<2, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 4: hipLaunchKernelGGL((layernorm_kernel<4, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 8: hipLaunchKernelGGL((layernorm_kernel<8, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 16: hipLaunchKernelGGL((layernorm_kernel<16, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 32: hipLaunchKernelGGL((layernorm_kernel<32, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 64: hipLaunchKernelGGL((layernorm_kernel<64, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float* h, const float* g, const float* b,
+                            void* out, bool out_bf16, int M, int d, hipStream_t st) {
+  if (out_bf16) return ln_dispatch(h, g, b, (bf16*)out, M, d, st);
+  return ln_dispatch(h, g, b, (float*)out, M, d, st);
+}
+
+// ---------------------------------------------------------------------------
+// Jacobi-block initial iterate, in processing order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void init_block_kernel(
+    float* __restrict__ x, const float* __restrict__ x_init, int mode, int N,
+    int R, int C, int L, int s, int dir, int F) {
+  const size_t total = (size_t)N * R * C;
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * 256) {
+    int c = (int)(e % C);
+    size_t nt = e / C;
+    int t = (int)(nt % R), n = (int)(nt / R);
+    int i = s + t;
+    size_t dst = ((size_t)n * L + storage_index(i, L, dir)) * C + c;
+    float v = 0.f;
+    if (mode == 1) {
+      v = x_init[dst];
+    } else if (mode == 2 && s >= F) {
+      v = x[((size_t)n * L + storage_index(i - F, L, dir)) * C + c];
+    }
+    x[dst] = v;
+  }
+}
+
+hipError_t launch_init_block(float* x, const float* x_init, int mode, int N,
+                             int R, int C, int L, int s, int dir, int F,
+                             hipStream_t st) {
+  size_t total = (size_t)N * R * C;
+  int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(init_block_kernel, dim3(blocks), dim3(256), 0, st, x, x_init,
+                     mode, N, R, C, L, s, dir, F);
+  return hipGetLastError();
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
+    p[e] = v;
+}
+
+hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, v, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused affine kernel.
+//   mode 0 (inverse):  x <- mu + exp(ls) * z,  sums (x_new - x_old)^2, x_new^2
+//   mode 1 (forward):  z <- (x - mu) * exp(-ls), sums ls, #non-finite z
+// with ls = log sigma = 0.5 tanh(raw).  Each block reduces its range of one
+// sample into partials; the last block to finish (atomic ticket) sums the
+// partials in a fixed order, so results do not depend on block scheduling.
+// ---------------------------------------------------------------------------
+constexpr int AFF_EPT = 4;                 // elements per thread per block range
+constexpr int AFF_EB = 256 * AFF_EPT;      // elements per block
+
+int affine_groups(int R, int C) {
+  long total = (long)R * C;
+  return (int)((total + AFF_EB - 1) / AFF_EB);
+}
+
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) {
+    red[2 * wv] = a;
+    red[2 * wv + 1] = b;
+  }
+  __syncthreads();
+  a = (red[0] + red[2]) + (red[4] + red[6]);
+  b = (red[1] + red[3]) + (red[5] + red[7]);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
+  __shared__ float red[8];
+  __shared__ unsigned ticket;
+  const int n = blockIdx.y, g = blockIdx.x;
+  const int C = a.C;
+  const long total = (long)a.R * C;
+  const long e_end = min(total, (long)(g + 1) * AFF_EB);
+  float s0 = 0.f, s1 = 0.f;
+  for (long e = (long)g * AFF_EB + threadIdx.x; e < e_end; e += 256) {
+    const int t = (int)(e / C), c = (int)(e - (long)t * C);
+    const size_t row = (size_t)n * a.R + t;
+    const float mu = a.head[row * 2 * C + c];
+    const float raw = a.head[row * 2 * C + C + c];
+    const float ls = 0.5f * tanhf(raw);
+    const size_t xi = ((size_t)n * a.L + storage_index(a.s + t, a.L, a.dir)) * C + c;
+    if (MODE == 0) {
+      const float xo = a.x[xi];
+      const float xn = mu + expf(ls) * a.z[xi];
+      a.x[xi] = xn;
+      const float df = xn - xo;
+      s0 += df * df;
+      s1 += xn * xn;
+    } else {
+      const float zv = (a.x[xi] - mu) * expf(-ls);
+      a.zout[xi] = zv;
+      s0 += ls;
+      s1 += isfinite(zv) ? 0.f : 1.f;
+    }
+  }
+  block_sum2(s0, s1, red);
+  if (threadIdx.x == 0) {
+    a.partials[((size_t)n * G + g) * 2] = s0;
+    a.partials[((size_t)n * G + g) * 2 + 1] = s1;
+    __threadfence();
+    ticket = atomicAdd(a.counter, 1u);
+  }
+  __syncthreads();
+  if (ticket != (unsigned)(gridDim.x * gridDim.y) - 1) return;
+  // last block: fixed-order final sums for every sample
+  __threadfence();
+  for (int nn = 0; nn < a.N; ++nn) {
+    float p0 = 0.f, p1 = 0.f;
+    for (int gg = threadIdx.x; gg < G; gg += 256) {
+      p0 += __hip_atomic_load(&a.partials[((size_t)nn * G + gg) * 2],
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p1 += __hip_atomic_load(&a.partials[((size_t)nn * G + gg) * 2 + 1],
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_sum2(p0, p1, red);
+    if (threadIdx.x == 0) {
+      if (MODE == 0) {
+        a.res[2 * nn] = p0;
+        a.res[2 * nn + 1] = p1;
+      } else {
+        a.res[2 * nn] = -p0;
+        a.res[2 * nn + 1] = p1;
+        if (a.logdet) a.logdet[nn] += -p0;
+      }
+    }
+  }
+  if (threadIdx.x == 0) *a.counter = 0u;
+}
+
+hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st) {
+  const int G = affine_groups(a.R, a.C);
+  dim3 grid(G, a.N);
+  if (mode == 0)
+    hipLaunchKernelGGL(affine_kernel<0>, grid, dim3(256), 0, st, a, G);
+  else
+    hipLaunchKernelGGL(affine_kernel<1>, grid, dim3(256), 0, st, a, G);
+  return hipGetLastError();
+}
+
+}  // namespace af

@@ -1,0 +1,497 @@
+// Host runtime of the AF-block library: plan, workspace layout, argument
+// validation, the per-pass kernel sequence and the block-wise Jacobi schedule.
+//
+// Method (STARFlow-V notes, papernotes.org, "STARFlow-V: End-to-End Video
+// Generative Modeling with Autoregressive Normalizing Flows"):
+//   关键设计 1 - affine AF block z = (x - mu(x*m)) / sigma(x*m), alternating
+//                mask directions in a stack;
+//   关键设计 3 - Jacobi fixed point x = mu(x*m) + sigma(x*m) z solved block by
+//                block with a KV cache, warm start from the previous frame and
+//                the residual stop ||dx||^2 / ||x||^2 < tau;
+//   一个完整示例 - conditioning by forward-encoding observed tokens into the cache.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/af.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+af_status fail(af_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define AF_HIP(expr)                                                        \
+  do {                                                                      \
+    hipError_t e_ = (expr);                                                 \
+    if (e_ != hipSuccess)                                                   \
+      return fail(AF_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct LayerW {
+  const float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
+  const void *w_qkv, *w_o, *w_1, *w_2;
+};
+
+struct BlockW {
+  const float *w_in, *b_in, *pos, *ln_f_g, *ln_f_b, *w_head, *b_head;
+  std::vector<LayerW> layers;
+};
+
+// Byte offsets of the workspace regions for (batch, rows).
+struct WsLayout {
+  size_t cache_layer;  // bytes of one layer's K (or V) cache
+  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, xtmp, total;
+};
+
+enum KClass { K_EMBED, K_LN, K_QKV, K_O, K_MLP1, K_MLP2, K_HEAD, K_ATTN, K_AFFINE, K_NCLASS };
+const char* kclass_names[K_NCLASS] = {"embed", "layernorm", "gemm_qkv", "gemm_o",
+                                      "gemm_mlp1", "gemm_mlp2", "gemm_head",
+                                      "attention", "affine"};
+
+}  // namespace
+
+struct af_plan {
+  af_block_cfg cfg;
+  int T;
+  int dh, dmlp, Lcap;
+  bool bf;
+  size_t esz;  // bytes per element of the per-layer operand type
+  std::vector<BlockW> blocks;
+  float* host_res = nullptr;  // pinned [res_cap][2]
+  int res_cap = 0;
+  // profiling
+  int prof_class = -1;
+  std::vector<hipEvent_t> ev;  // pairs
+  int prof_n = 0;
+};
+
+namespace {
+
+WsLayout layout(const af_plan* p, int N, int rows) {
+  WsLayout w{};
+  const af_block_cfg& c = p->cfg;
+  const size_t M = (size_t)N * rows;
+  w.cache_layer = (size_t)N * c.n_heads * p->Lcap * p->dh * p->esz;
+  size_t off = 0;
+  w.cache = off;
+  off += align256(2 * w.cache_layer * c.n_layers);
+  w.h = off;        off += align256(M * c.d * 4);
+  w.a = off;        off += align256(M * c.d * p->esz);
+  w.q = off;        off += align256(M * c.d * p->esz);
+  w.att = off;      off += align256(M * c.d * p->esz);
+  w.u = off;        off += align256(M * p->dmlp * p->esz);
+  w.hf = off;       off += align256(M * c.d * 4);
+  w.head = off;     off += align256(M * 2 * c.C * 4);
+  w.partials = off; off += align256((size_t)N * af::affine_groups(rows, c.C) * 2 * 4);
+  w.res = off;      off += align256((size_t)N * 2 * 4);
+  w.counter = off;  off += 256;
+  w.xtmp = off;
+  if (p->T > 1) off += align256((size_t)N * c.max_len * c.C * 4);
+  w.total = off;
+  return w;
+}
+
+// Launch helper with optional per-class event timing.
+struct Launch {
+  af_plan* p;
+  hipStream_t st;
+  int cls;
+  bool on;
+  Launch(af_plan* p_, hipStream_t s, int c) : p(p_), st(s), cls(c) {
+    on = p->prof_class == cls && p->prof_n < (int)p->ev.size() / 2;
+    if (on) (void)hipEventRecord(p->ev[2 * p->prof_n], st);
+  }
+  ~Launch() {
+    if (on) {
+      (void)hipEventRecord(p->ev[2 * p->prof_n + 1], st);
+      ++p->prof_n;
+    }
+  }
+};
+
+#define LAUNCH(cls, call)                                 \
+  do {                                                    \
+    Launch l_(p, st, cls);                                \
+    hipError_t e_ = (call);                               \
+    if (e_ != hipSuccess)                                 \
+      return fail(AF_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+struct Pass {
+  const float* src;     // token tensor [N, L, C] read by the shift (x or iterate)
+  const float* x_last;  // token before processing index 0, or NULL
+  int N, L, s, R, P, dir;
+  bool kv_only;         // stop after the last layer's K/V (cache refresh)
+};
+
+// One pass of the network over chunk rows [s, s+R) of every sample:
+// shift+embed, n_layers pre-LN layers (K/V into the cache), final LN + head.
+af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
+                  const WsLayout& w, hipStream_t st) {
+  const af_block_cfg& c = p->cfg;
+  const int M = ps.N * ps.R, d = c.d;
+  float* h = (float*)(ws + w.h);
+  void* a = ws + w.a;
+  void* q = ws + w.q;
+  void* att = ws + w.att;
+  void* u = ws + w.u;
+  const int pos_base = ps.P + ps.s;
+  LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
+                                   ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
+                                   pos_base, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& lw = bw.layers[l];
+    char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
+    char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
+    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, p->bf, M, d, st));
+    af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base};
+    LAUNCH(K_QKV, af::launch_gemm_qkv(p->bf, a, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+    if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+    LAUNCH(K_ATTN, af::launch_attention(p->bf, q, kc, vt, att, ps.N, ps.R, c.n_heads,
+                                        p->dh, d, p->Lcap, pos_base, st));
+    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, lw.w_o, lw.b_o, h, M, d, d, st));
+    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, p->bf, M, d, st));
+    LAUNCH(K_MLP1, af::launch_gemm_gelu(p->bf, a, lw.w_1, lw.b_1, u, M, p->dmlp, d, st));
+    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, lw.w_2, lw.b_2, h, M, d, p->dmlp, st));
+  }
+  float* hf = (float*)(ws + w.hf);
+  float* head = (float*)(ws + w.head);
+  LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
+  LAUNCH(K_HEAD, af::launch_gemm_f32out(false, hf, bw.w_head, bw.b_head, head, M,
+                                        2 * c.C, d, st));
+  return AF_OK;
+}
+
+af_status check_ws(const af_plan* p, int N, int rows, void* ws, size_t ws_bytes,
+                   WsLayout* out) {
+  if (!ws) return fail(AF_ERR_ARG, "ws is NULL");
+  if (((uintptr_t)ws & 255) != 0) return fail(AF_ERR_ARG, "ws must be 256-byte aligned");
+  *out = layout(p, N, rows);
+  if (ws_bytes < out->total)
+    return fail(AF_ERR_WORKSPACE, "workspace too small: need " +
+                                      std::to_string(out->total) + " bytes, got " +
+                                      std::to_string(ws_bytes));
+  return AF_OK;
+}
+
+af_status ensure_host_res(af_plan* p, int N) {
+  if (p->res_cap >= N) return AF_OK;
+  if (p->host_res) (void)hipHostFree(p->host_res);
+  p->host_res = nullptr;
+  p->res_cap = 0;
+  AF_HIP(hipHostMalloc((void**)&p->host_res, (size_t)N * 2 * sizeof(float),
+                       hipHostMallocDefault));
+  p->res_cap = N;
+  return AF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* af_status_str(af_status s) {
+  switch (s) {
+    case AF_OK: return "AF_OK";
+    case AF_ERR_ARG: return "AF_ERR_ARG";
+    case AF_ERR_HIP: return "AF_ERR_HIP";
+    case AF_ERR_WORKSPACE: return "AF_ERR_WORKSPACE";
+    case AF_ERR_NONFINITE: return "AF_ERR_NONFINITE";
+    case AF_ERR_UNSUPPORTED: return "AF_ERR_UNSUPPORTED";
+  }
+  return "AF_ERR_UNKNOWN";
+}
+
+const char* af_last_error(void) { return g_err.c_str(); }
+int af_abi_version(void) { return AF_ABI_VERSION; }
+
+af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
+                         const af_block_weights* w, af_plan** out) {
+  if (!cfg || !w || !out) return fail(AF_ERR_ARG, "NULL argument");
+  *out = nullptr;
+  const af_block_cfg& c = *cfg;
+  if (n_blocks < 1 || n_blocks > 64) return fail(AF_ERR_ARG, "n_blocks must be 1..64");
+  if (c.dtype != AF_F32 && c.dtype != AF_BF16) return fail(AF_ERR_ARG, "unknown dtype");
+  if (c.C < 1 || c.C > 256) return fail(AF_ERR_ARG, "C must be 1..256");
+  if (c.n_layers < 1 || c.n_layers > 1024) return fail(AF_ERR_ARG, "n_layers must be >= 1");
+  if (c.max_len < 1 || c.max_len > (1 << 24)) return fail(AF_ERR_ARG, "max_len out of range");
+  if (c.d < 64 || c.d > 8192 || c.n_heads < 1 || c.d % c.n_heads)
+    return fail(AF_ERR_ARG, "d must be 64..8192 and divisible by n_heads");
+  const int dh = c.d / c.n_heads;
+  if (dh != 32 && dh != 64 && dh != 128)
+    return fail(AF_ERR_UNSUPPORTED, "d / n_heads must be 32, 64 or 128");
+  const int per_lane = c.d / 64;
+  if (c.d % 64 || (per_lane & (per_lane - 1)))
+    return fail(AF_ERR_UNSUPPORTED, "d must be 64 times a power of two");
+  if (c.dtype == AF_BF16 && c.d % 128)
+    return fail(AF_ERR_UNSUPPORTED, "bf16 path needs d % 128 == 0");
+  af_plan* p = new (std::nothrow) af_plan();
+  if (!p) return fail(AF_ERR_ARG, "out of host memory");
+  p->cfg = c;
+  p->T = n_blocks;
+  p->dh = dh;
+  p->dmlp = 4 * c.d;
+  p->Lcap = (c.max_len + 63) / 64 * 64;
+  p->bf = c.dtype == AF_BF16;
+  p->esz = p->bf ? 2 : 4;
+  for (int t = 0; t < n_blocks; ++t) {
+    const af_block_weights& bw = w[t];
+    BlockW b;
+    b.w_in = bw.w_in; b.b_in = bw.b_in; b.pos = bw.pos;
+    b.ln_f_g = bw.ln_f_g; b.ln_f_b = bw.ln_f_b; b.w_head = bw.w_head; b.b_head = bw.b_head;
+    if (!b.w_in || !b.b_in || !b.pos || !b.ln_f_g || !b.ln_f_b || !b.w_head || !b.b_head ||
+        !bw.ln1_g || !bw.ln1_b || !bw.w_qkv || !bw.b_qkv || !bw.w_o || !bw.b_o ||
+        !bw.ln2_g || !bw.ln2_b || !bw.w_1 || !bw.b_1 || !bw.w_2 || !bw.b_2) {
+      delete p;
+      return fail(AF_ERR_ARG, "NULL weight pointer in block " + std::to_string(t));
+    }
+    for (int l = 0; l < c.n_layers; ++l) {
+      LayerW lw{bw.ln1_g[l], bw.ln1_b[l], bw.b_qkv[l], bw.b_o[l], bw.ln2_g[l],
+                bw.ln2_b[l], bw.b_1[l], bw.b_2[l], bw.w_qkv[l], bw.w_o[l],
+                bw.w_1[l], bw.w_2[l]};
+      if (!lw.ln1_g || !lw.ln1_b || !lw.b_qkv || !lw.b_o || !lw.ln2_g || !lw.ln2_b ||
+          !lw.b_1 || !lw.b_2 || !lw.w_qkv || !lw.w_o || !lw.w_1 || !lw.w_2) {
+        delete p;
+        return fail(AF_ERR_ARG, "NULL layer weight pointer in block " +
+                                    std::to_string(t) + " layer " + std::to_string(l));
+      }
+      b.layers.push_back(lw);
+    }
+    p->blocks.push_back(std::move(b));
+  }
+  *out = p;
+  return AF_OK;
+}
+
+void af_plan_destroy(af_plan* p) {
+  if (!p) return;
+  if (p->host_res) (void)hipHostFree(p->host_res);
+  for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+  delete p;
+}
+
+size_t af_workspace_bytes(const af_plan* p, int batch, int rows) {
+  if (!p || batch < 1 || rows < 1) return 0;
+  return layout(p, batch, rows).total;
+}
+
+size_t af_cache_bytes(const af_plan* p, int batch) {
+  if (!p || batch < 1) return 0;
+  return align256(2 * layout(p, batch, 1).cache_layer * p->cfg.n_layers);
+}
+
+af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
+                     int L, void* ws_, size_t ws_bytes, void* stream) {
+  if (!p || !x || !z || !logdet) return fail(AF_ERR_ARG, "NULL argument");
+  if (N < 1 || L < 1 || L > p->cfg.max_len) return fail(AF_ERR_ARG, "need N >= 1 and 1 <= L <= max_len");
+  if (x == z) return fail(AF_ERR_ARG, "x and z may not alias");
+  WsLayout w;
+  if (af_status s = check_ws(p, N, L, ws_, ws_bytes, &w)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_;
+  const int C = p->cfg.C;
+  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 1, st));
+  AF_HIP(af::launch_fill_u32(logdet, 0u, (size_t)N, st));
+  float* xtmp = (float*)(ws + w.xtmp);
+  const float* cur = x;
+  for (int t = 0; t < p->T; ++t) {
+    float* dst = ((p->T - 1 - t) % 2 == 0) ? z : xtmp;
+    Pass ps{cur, nullptr, N, L, 0, L, 0, t & 1, false};
+    if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st)) return s;
+    af::AffineArgs aa{(const float*)(ws + w.head), nullptr, const_cast<float*>(cur), dst,
+                      N, L, C, L, 0, t & 1, (float*)(ws + w.partials),
+                      (float*)(ws + w.res), (unsigned*)(ws + w.counter), logdet};
+    LAUNCH(K_AFFINE, af::launch_affine(1, aa, st));
+    cur = dst;
+  }
+  return AF_OK;
+}
+
+af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
+                     size_t ws_bytes, void* stream) {
+  if (!p || !x_prefix) return fail(AF_ERR_ARG, "NULL argument");
+  if (p->T != 1) return fail(AF_ERR_UNSUPPORTED, "af_prefill needs a single-block plan");
+  if (N < 1 || P < 1 || P > p->cfg.max_len) return fail(AF_ERR_ARG, "need N >= 1 and 1 <= P <= max_len");
+  WsLayout w;
+  if (af_status s = check_ws(p, N, P, ws_, ws_bytes, &w)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Pass ps{x_prefix, nullptr, N, P, 0, P, 0, 0, true};
+  return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
+}
+
+af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
+                            float tau, int max_iters, af_init init,
+                            const float* x_init, int frame_len, int prefix_len,
+                            const float* x_last, float* x, int32_t* iters,
+                            void* ws_, size_t ws_bytes, void* stream) {
+  if (!p || !z || !x || !iters) return fail(AF_ERR_ARG, "NULL argument");
+  if (N < 1 || L < 1 || B < 1) return fail(AF_ERR_ARG, "need N, L, B >= 1");
+  if (std::isnan(tau)) return fail(AF_ERR_ARG, "tau is NaN");
+  if (init != AF_INIT_ZERO && init != AF_INIT_GIVEN && init != AF_INIT_PREV_FRAME)
+    return fail(AF_ERR_ARG, "unknown init");
+  if (prefix_len < 0 || (long)prefix_len + L > p->cfg.max_len)
+    return fail(AF_ERR_ARG, "need prefix_len >= 0 and prefix_len + L <= max_len");
+  if (prefix_len > 0 && !x_last) return fail(AF_ERR_ARG, "x_last is required when prefix_len > 0");
+  if (init == AF_INIT_GIVEN && !x_init) return fail(AF_ERR_ARG, "x_init is NULL");
+  const int Bc = B < L ? B : L;
+  if (init == AF_INIT_PREV_FRAME && frame_len < Bc)
+    return fail(AF_ERR_ARG, "PREV_FRAME needs frame_len >= min(B, L)");
+  if (x == z || (x_init && x_init == x)) return fail(AF_ERR_ARG, "x may not alias z or x_init");
+  if (p->T > 1 && (init != AF_INIT_ZERO || prefix_len != 0))
+    return fail(AF_ERR_UNSUPPORTED, "stacks support AF_INIT_ZERO with prefix_len 0 only");
+  WsLayout w;
+  if (af_status s = check_ws(p, N, Bc, ws_, ws_bytes, &w)) return s;
+  if (af_status s = ensure_host_res(p, N)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_;
+  const int C = p->cfg.C;
+  const int nb = (L + B - 1) / B;
+  float* xtmp = (float*)(ws + w.xtmp);
+  float* res = (float*)(ws + w.res);
+  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 1, st));
+
+  const float* zin = z;
+  for (int t = p->T - 1; t >= 0; --t) {
+    float* xo = (t % 2 == 0) ? x : xtmp;
+    const int dir = t & 1;
+    for (int b = 0; b < nb; ++b) {
+      const int s = b * B, R = (s + B < L ? s + B : L) - s;
+      const int kmax = max_iters <= 0 ? R : (max_iters < R ? max_iters : R);
+      AF_HIP(af::launch_init_block(xo, x_init, (int)init, N, R, C, L, s, dir, frame_len, st));
+      Pass ps{xo, x_last, N, L, s, R, prefix_len, dir, false};
+      af::AffineArgs aa{(const float*)(ws + w.head), zin, xo, nullptr, N, R, C, L, s,
+                        dir, (float*)(ws + w.partials), res,
+                        (unsigned*)(ws + w.counter), nullptr};
+      int k = 0;
+      bool nonfinite = false;
+      for (k = 1; k <= kmax; ++k) {
+        if (af_status e = run_net(p, p->blocks[t], ps, ws, w, st)) return e;
+        LAUNCH(K_AFFINE, af::launch_affine(0, aa, st));
+        const bool test = tau > 0.f || k == kmax;
+        if (!test) continue;
+        AF_HIP(hipMemcpyAsync(p->host_res, res, (size_t)N * 2 * sizeof(float),
+                              hipMemcpyDeviceToHost, st));
+        AF_HIP(hipStreamSynchronize(st));
+        bool all_below = true;
+        for (int n = 0; n < N; ++n) {
+          const float num = p->host_res[2 * n], den = p->host_res[2 * n + 1];
+          if (!std::isfinite(num) || !std::isfinite(den)) nonfinite = true;
+          const float r = den > 0.f ? num / den : (num == 0.f ? 0.f : INFINITY);
+          if (!(r < tau)) all_below = false;
+        }
+        if (nonfinite) break;
+        if (tau > 0.f && all_below) break;
+      }
+      if (nonfinite) {
+        iters[t * nb + b] = k;
+        return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +
+                                          ", Jacobi block " + std::to_string(b));
+      }
+      if (k > kmax) k = kmax;
+      iters[t * nb + b] = k;
+      if (k < R && b + 1 < nb) {
+        Pass pr = ps;
+        pr.kv_only = true;
+        if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) return e;
+      }
+    }
+    zin = xo;
+  }
+  AF_HIP(hipStreamSynchronize(st));
+  return AF_OK;
+}
+
+af_status af_profile_enable(af_plan* p, const char* kernel_class) {
+  if (!p || !kernel_class) return fail(AF_ERR_ARG, "NULL argument");
+  int cls = -1;
+  for (int i = 0; i < K_NCLASS; ++i)
+    if (std::strcmp(kernel_class, kclass_names[i]) == 0) cls = i;
+  if (cls < 0) return fail(AF_ERR_ARG, std::string("unknown kernel class ") + kernel_class);
+  if (p->ev.empty()) {
+    p->ev.resize(2 * 4096);
+    for (auto& e : p->ev) AF_HIP(hipEventCreate(&e));
+  }
+  p->prof_class = cls;
+  p->prof_n = 0;
+  return AF_OK;
+}
+
+af_status af_profile_disable(af_plan* p) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->prof_class = -1;
+  return AF_OK;
+}
+
+af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
+  if (!p || !launches || !total_ms) return fail(AF_ERR_ARG, "NULL argument");
+  double tot = 0.0;
+  for (int i = 0; i < p->prof_n; ++i) {
+    AF_HIP(hipEventSynchronize(p->ev[2 * i + 1]));
+    float ms = 0.f;
+    AF_HIP(hipEventElapsedTime(&ms, p->ev[2 * i], p->ev[2 * i + 1]));
+    tot += ms;
+  }
+  *launches = p->prof_n;
+  *total_ms = tot;
+  return AF_OK;
+}
+
+size_t afk_affine_partials_bytes(int N, int rows_per_sample, int C) {
+  if (N < 1 || rows_per_sample < 1 || C < 1) return 0;
+  return (size_t)N * af::affine_groups(rows_per_sample, C) * 2 * sizeof(float) + 256;
+}
+
+af_status afk_affine(int mode, const float* head, const float* src, float* dst,
+                     int N, int rows_per_sample, int C, float* res, void* partials,
+                     size_t partials_bytes, int check, void* stream) {
+  if (mode != 0 && mode != 1) return fail(AF_ERR_ARG, "mode must be 0 or 1");
+  if (!head || !src || !dst || !res || !partials) return fail(AF_ERR_ARG, "NULL argument");
+  if (src == dst) return fail(AF_ERR_ARG, "src and dst may not alias");
+  if (N < 1 || rows_per_sample < 1 || C < 1 || C > 256) return fail(AF_ERR_ARG, "bad sizes");
+  const size_t need = afk_affine_partials_bytes(N, rows_per_sample, C);
+  if (partials_bytes < need) return fail(AF_ERR_WORKSPACE, "partials too small");
+  hipStream_t st = (hipStream_t)stream;
+  char* pb = (char*)partials;
+  unsigned* counter = (unsigned*)(pb + need - 256);
+  AF_HIP(af::launch_fill_u32(counter, 0u, 1, st));
+  af::AffineArgs aa{head, mode == 0 ? src : nullptr,
+                    mode == 0 ? dst : const_cast<float*>(src),
+                    mode == 1 ? dst : nullptr, N, rows_per_sample, C,
+                    rows_per_sample, 0, 0, (float*)pb, res, counter, nullptr};
+  hipError_t e = af::launch_affine(mode, aa, st);
+  if (e != hipSuccess) return fail(AF_ERR_HIP, hipGetErrorString(e));
+  if (check) {
+    AF_HIP(hipStreamSynchronize(st));
+    std::vector<float> h((size_t)N * 2);
+    AF_HIP(hipMemcpy(h.data(), res, h.size() * sizeof(float), hipMemcpyDeviceToHost));
+    for (int n = 0; n < N; ++n) {
+      if (!std::isfinite(h[2 * n]) || !std::isfinite(h[2 * n + 1]) ||
+          (mode == 1 && h[2 * n + 1] != 0.f))
+        return fail(AF_ERR_NONFINITE, "non-finite value in sample " + std::to_string(n));
+    }
+  }
+  return AF_OK;
+}
+
+af_status afk_gemm_bf16(const void* a, const void* w, const float* bias, float* y,
+                        int M, int N, int K, void* stream) {
+  if (!a || !w || !y) return fail(AF_ERR_ARG, "NULL argument");
+  if (M < 1 || N < 64 || K < 64 || N % 64 || K % 64)
+    return fail(AF_ERR_ARG, "need M >= 1, N % 64 == 0, K % 64 == 0");
+  hipError_t e = af::launch_gemm_f32out(true, a, w, bias, y, M, N, K, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AF_ERR_HIP, hipGetErrorString(e));
+  return AF_OK;
+}
+
+}  // extern "C"

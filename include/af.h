@@ -1,0 +1,209 @@
+/*
+ * af.h - C ABI of the affine autoregressive-flow (AF) block on AMD MI355X (gfx950).
+ *
+ * The method (STARFlow-V notes, papernotes.org, "STARFlow-V: End-to-End Video
+ * Generative Modeling with Autoregressive Normalizing Flows"):
+ *   - 关键设计 1, affine AF equation: z = (x - mu(x*m)) / sigma(x*m), sigma > 0,
+ *     m the self-exclusive causal mask; blocks alternate L->R / R->L masks.
+ *   - 损失函数, L_NF: the forward map's log|det J| = -sum log sigma.
+ *   - 关键设计 3, Jacobi fixed-point equation: x^(k+1) = mu(x^(k)*m) +
+ *     sigma(x^(k)*m) * z, stopped when ||x^(k+1)-x^(k)||^2/||x^(k+1)||^2 < tau;
+ *     blocks of B tokens in sequence, tokens of a block in parallel, finished
+ *     blocks feed a KV cache, a new frame warm-starts from the previous one.
+ *   - 一个完整示例, I2V: observed tokens are forward-encoded into the KV cache.
+ *
+ * Network (one AF block): tokens are shifted by one (row t sees x[t-1], row 0
+ * sees the token before the sequence or zeros), projected by W_in (d x C) plus
+ * b_in plus a learned position row, run through n_layers pre-LN Transformer
+ * layers (LayerNorm eps 1e-5, causal attention with scale 1/sqrt(d/n_heads),
+ * exact-erf GELU MLP of width 4d), a final LayerNorm and a head W_head (2C x d)
+ * whose outputs are [mu (C) | raw (C)]; log sigma = 0.5 * tanh(raw).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous.  x, z, x_init, x_last, logdet are fp32.  Token tensors are
+ *     [N, L, C] (sample, token, channel).  The library allocates no device
+ *     memory: all scratch lives in the caller's workspace.
+ *   - Calls return a status and never abort; no exception crosses the ABI.
+ *     Arguments are validated before any device work.  af_last_error() gives
+ *     a thread-local detail string for the last failure.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  af_forward and
+ *     af_prefill are stream-ordered and return without waiting.
+ *     af_inverse_jacobi blocks: it reads each update's residual back to the
+ *     host for the stop test and returns once x and iters are final.
+ */
+#ifndef AF_H
+#define AF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AF_ABI_VERSION 1
+
+typedef enum {
+  AF_OK = 0,
+  AF_ERR_ARG = 1,          /* a bad argument: null pointer, size out of range, bad enum */
+  AF_ERR_HIP = 2,          /* a HIP runtime call failed (detail in af_last_error) */
+  AF_ERR_WORKSPACE = 3,    /* ws_bytes below what the call needs */
+  AF_ERR_NONFINITE = 4,    /* an update produced a non-finite x (output unspecified) */
+  AF_ERR_UNSUPPORTED = 5   /* a valid request this build does not implement */
+} af_status;
+
+/* Operand type of the four per-layer matrices (w_qkv, w_o, w_1, w_2) and of
+ * the activations fed to them and the KV cache.  Every other tensor is fp32. */
+typedef enum { AF_F32 = 0, AF_BF16 = 1 } af_dtype;
+
+/* Initial iterate x^(0) of each Jacobi block [s, e):
+ *   ZERO        zeros
+ *   GIVEN       x_init[:, s:e]  (x_init is [N, L, C])
+ *   PREV_FRAME  the already-solved x[:, s-F:e-F] if s >= F, else zeros */
+typedef enum { AF_INIT_ZERO = 0, AF_INIT_GIVEN = 1, AF_INIT_PREV_FRAME = 2 } af_init;
+
+typedef struct {
+  int C;          /* channels per token, 1..256 */
+  int d;          /* model width; multiple of 64 (AF_F32) or of 128 (AF_BF16) */
+  int n_heads;    /* d / n_heads in {32, 64, 128} */
+  int n_layers;   /* >= 1; MLP width is 4d */
+  int max_len;    /* positions 0..max_len-1 (rows of the position table) */
+  af_dtype dtype;
+} af_block_cfg;
+
+/* One block's parameters: borrowed device pointers that must outlive the plan.
+ * Matrices are row-major [out, in] (y = x W^T + b).  The four per-layer
+ * matrices have the element type of cfg.dtype (fp32 or bf16 bit patterns);
+ * everything else is fp32.  The per-layer fields are HOST arrays of
+ * n_layers device pointers (copied at plan creation).
+ *   w_in [d, C]  b_in [d]  pos [max_len, d]
+ *   per layer: ln1_g, ln1_b [d]; w_qkv [3d, d] rows [Q | K | V], heads
+ *   contiguous inside each; b_qkv [3d]; w_o [d, d]; b_o [d]; ln2_g, ln2_b [d];
+ *   w_1 [4d, d]; b_1 [4d]; w_2 [d, 4d]; b_2 [d]
+ *   ln_f_g, ln_f_b [d]  w_head [2C, d]  b_head [2C]  */
+typedef struct {
+  const float *w_in, *b_in, *pos;
+  const float *ln_f_g, *ln_f_b, *w_head, *b_head;
+  const float *const *ln1_g, *const *ln1_b;
+  const void *const *w_qkv;
+  const float *const *b_qkv;
+  const void *const *w_o;
+  const float *const *b_o;
+  const float *const *ln2_g, *const *ln2_b;
+  const void *const *w_1;
+  const float *const *b_1;
+  const void *const *w_2;
+  const float *const *b_2;
+} af_block_weights;
+
+typedef struct af_plan af_plan;
+
+/* Create a plan for a stack of n_blocks AF blocks sharing one shape.  Block t
+ * runs left-to-right when t is even and right-to-left when t is odd (STARFlow-V
+ * notes, 整体框架 and 关键设计 1: alternating mask directions); a deep block is
+ * a stack of one.  w points to n_blocks weight sets.  The plan keeps host
+ * metadata only.  Returns AF_ERR_ARG / AF_ERR_UNSUPPORTED for shapes outside
+ * the documented ranges. */
+af_status af_plan_create(const af_block_cfg *cfg, int n_blocks,
+                         const af_block_weights *w, af_plan **out);
+void af_plan_destroy(af_plan *p);
+
+/* Workspace bytes for `batch` samples when at most `rows` tokens per sample
+ * are processed in one pass (L for af_forward, P for af_prefill, B for
+ * af_inverse_jacobi).  The first af_cache_bytes(p, batch) bytes hold the KV
+ * cache (positions 0..max_len-1 of every layer), so a workspace keeps its
+ * cache across calls made with the same batch.  Returns 0 on bad arguments. */
+size_t af_workspace_bytes(const af_plan *p, int batch, int rows);
+size_t af_cache_bytes(const af_plan *p, int batch);
+
+/* Forward pass of the whole stack (blocks t = 0..n_blocks-1):
+ * z = f(x) and logdet[n] = log|det dz/dx| = -sum over blocks, tokens and
+ * channels of log sigma (STARFlow-V notes, 关键设计 1 and 损失函数).
+ * x, z: [N, L, C] (may not alias); logdet: [N] (overwritten).  Needs
+ * L <= max_len and ws_bytes >= af_workspace_bytes(p, N, L).  For a single
+ * block the KV cache of positions 0..L-1 is left in ws. */
+af_status af_forward(af_plan *p, const float *x, float *z, float *logdet,
+                     int N, int L, void *ws, size_t ws_bytes, void *stream);
+
+/* Encode observed tokens into the KV cache (STARFlow-V notes, 一个完整示例:
+ * I2V / V2V conditioning): runs the single block's network on the shifted
+ * x_prefix [N, P, C] at positions 0..P-1 and leaves every layer's K/V in ws.
+ * A following af_inverse_jacobi with prefix_len = P and the same ws continues
+ * at position P.  Only for n_blocks == 1.  Stream-ordered. */
+af_status af_prefill(af_plan *p, const float *x_prefix, int N, int P,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Invert the stack by video-aware block-wise Jacobi (STARFlow-V notes, 关键设计
+ * 3).  Blocks t = n_blocks-1..0 in turn; inside each, Jacobi blocks
+ * [s, e) = [b*B, min(L, (b+1)*B)) in sequence.  A Jacobi block repeats
+ *   x^(k) = mu(shift(x[:s] ++ x^(k-1))) + exp(0.5 tanh raw(...)) * z[:, s:e]
+ * from x^(0) (see af_init) and stops after the first update whose residual
+ * r_n = sum (x^(k)-x^(k-1))^2 / sum (x^(k))^2 (per sample n, over the block's
+ * tokens and channels; 0/0 = 0) is below tau for every sample, or after
+ * min(max_iters, e-s) updates (max_iters <= 0 means e-s).  tau <= 0 forces
+ * that many updates.  The finished block's K/V are then recomputed from its
+ * final x and kept in the cache (skipped when the block ran e-s updates, as
+ * its last inputs were already final).
+ *   z        [N, L, C]   input
+ *   x        [N, L, C]   output (may not alias z)
+ *   x_init   [N, L, C]   AF_INIT_GIVEN only, else may be NULL
+ *   frame_len F > 0      AF_INIT_PREV_FRAME only
+ *   prefix_len P >= 0    positions already in the cache (af_prefill); the new
+ *                        tokens take positions P..P+L-1; P + L <= max_len
+ *   x_last   [N, C]      the token at position P-1 (shifted input of position
+ *                        P); required when P > 0, NULL for zeros when P == 0
+ *   iters    HOST int32 [n_blocks][ceil(L/B)]: updates made per Jacobi block,
+ *                        row t for stack block t
+ * For n_blocks > 1 only AF_INIT_ZERO and P == 0 are supported.  Needs
+ * ws_bytes >= af_workspace_bytes(p, N, min(B, L)).  Returns AF_ERR_NONFINITE
+ * if an update produced a non-finite value. */
+af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
+                            float tau, int max_iters, af_init init,
+                            const float *x_init, int frame_len, int prefix_len,
+                            const float *x_last, float *x, int32_t *iters,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* ---- per-kernel timing (measurement only) --------------------------------
+ * While enabled, every launch of the named kernel class made by this plan is
+ * bracketed by HIP events on the launch stream; af_profile_read synchronises
+ * on those events and returns the number of launches and their summed
+ * duration in milliseconds since the last enable.  Classes: "embed",
+ * "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2", "gemm_head",
+ * "attention", "affine".  At most 4096 launches are recorded per enable. */
+af_status af_profile_enable(af_plan *p, const char *kernel_class);
+af_status af_profile_disable(af_plan *p);
+af_status af_profile_read(af_plan *p, int *launches, double *total_ms);
+
+/* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
+ * The fused affine kernel on its own, over N samples of rows_per_sample
+ * contiguous rows of C channels (token tensors [N, rows_per_sample, C]).
+ * head [N * rows_per_sample, 2C] holds [mu | raw] per row; ls = 0.5 tanh(raw).
+ * mode 0 (inverse): src = z, dst = x updated in place:
+ *   x <- mu + exp(ls) * z, res[n] = {sum (x_new - x_old)^2, sum x_new^2}.
+ * mode 1 (forward): src = x, dst = z written:
+ *   z <- (x - mu) * exp(-ls), res[n] = {-sum ls, number of non-finite z}.
+ * res is [N][2] fp32 device; partials is device scratch of at least
+ * afk_affine_partials_bytes(N, rows_per_sample, C) bytes.  Stream-ordered;
+ * with check != 0 it synchronises and returns AF_ERR_NONFINITE if a produced
+ * value is not finite. */
+size_t afk_affine_partials_bytes(int N, int rows_per_sample, int C);
+af_status afk_affine(int mode, const float *head, const float *src, float *dst,
+                     int N, int rows_per_sample, int C, float *res,
+                     void *partials, size_t partials_bytes, int check,
+                     void *stream);
+
+/* bf16 MFMA GEMM y[M, N] = a[M, K] * w[N, K]^T + bias[N] (bias may be NULL),
+ * fp32 out, for unit parity.  a, w are bf16 bit patterns, row-major;
+ * K % 64 == 0, N % 64 == 0.  Stream-ordered. */
+af_status afk_gemm_bf16(const void *a, const void *w, const float *bias,
+                        float *y, int M, int N, int K, void *stream);
+
+const char *af_status_str(af_status s);
+const char *af_last_error(void);
+int af_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AF_H */

@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/af.h declares, and rejects bad arguments with the
+documented status before any device work."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+from autoregressive_normalizing_flow_amd import binding as B  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return B.load_library()
+    except ImportError as e:  # the library is built by __graft_entry__.build()
+        pytest.skip(str(e))
+
+
+def test_exports_every_header_function(lib):
+    names = B.header_functions()
+    assert "af_forward" in names and "af_inverse_jacobi" in names and "af_prefill" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.af_abi_version() == 1
+    assert lib.af_status_str(0) == b"AF_OK"
+    assert lib.af_status_str(4) == b"AF_ERR_NONFINITE"
+
+
+# A plan over fake (never dereferenced) device pointers: af_plan_create only
+# records them.
+_FAKE = np.zeros(64, dtype=np.float32)
+
+
+def fake_weights(n_layers, n_blocks=1):
+    addr = ctypes.c_void_p(_FAKE.ctypes.data)
+    keep = []
+    ws = (B.af_block_weights * n_blocks)()
+    for w in ws:
+        for n in ("w_in", "b_in", "pos", "ln_f_g", "ln_f_b", "w_head", "b_head"):
+            setattr(w, n, addr)
+        for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g",
+                  "ln2_b", "w_1", "b_1", "w_2", "b_2"):
+            arr = (ctypes.c_void_p * n_layers)(*([addr] * n_layers))
+            keep.append(arr)
+            setattr(w, n, ctypes.cast(arr, B._PP))
+    return ws, keep
+
+
+def make_plan(lib, C=16, d=64, H=2, layers=1, max_len=64, dtype=B.AF_F32, T=1):
+    ws, keep = fake_weights(layers, T)
+    cfg = B.af_block_cfg(C, d, H, layers, max_len, dtype)
+    h = ctypes.c_void_p()
+    st = lib.af_plan_create(ctypes.byref(cfg), T, ws, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=0), B.AF_ERR_ARG),
+    (dict(C=300), B.AF_ERR_ARG),
+    (dict(d=96, H=3), B.AF_ERR_UNSUPPORTED),     # d/64 not a power of two
+    (dict(d=64, H=3), B.AF_ERR_ARG),             # d % H
+    (dict(d=256, H=16), B.AF_ERR_UNSUPPORTED),   # dh = 16
+    (dict(d=64, H=1, dtype=B.AF_BF16), B.AF_ERR_UNSUPPORTED),  # bf16 needs d % 128
+    (dict(layers=0), B.AF_ERR_ARG),
+    (dict(max_len=0), B.AF_ERR_ARG),
+    (dict(dtype=7), B.AF_ERR_ARG),
+    (dict(T=0), B.AF_ERR_ARG),
+    (dict(), B.AF_OK),
+    (dict(d=512, H=8, dtype=B.AF_BF16, T=4), B.AF_OK),
+])
+def test_plan_create_validation(lib, kw, expect):
+    st, h = make_plan(lib, **kw)
+    assert st == expect, lib.af_last_error()
+    if st == B.AF_OK:
+        lib.af_plan_destroy(h)
+    else:
+        assert lib.af_last_error()
+
+
+def test_workspace_bytes_monotone_and_cache_first(lib):
+    st, h = make_plan(lib, C=48, d=1024, H=16, layers=8, max_len=1560, dtype=B.AF_BF16)
+    assert st == B.AF_OK
+    a = lib.af_workspace_bytes(h, 1, 16)
+    b = lib.af_workspace_bytes(h, 1, 1560)
+    c = lib.af_workspace_bytes(h, 2, 1560)
+    assert 0 < a < b < c
+    cache = lib.af_cache_bytes(h, 1)
+    # 8 layers x (K + V) x 16 heads x 1600 padded positions x 64 x bf16
+    assert cache == 8 * 2 * 16 * 1600 * 64 * 2
+    assert lib.af_workspace_bytes(h, 0, 16) == 0
+    lib.af_plan_destroy(h)
+
+
+def test_entry_points_reject_bad_arguments_before_device_work(lib):
+    st, h = make_plan(lib)
+    assert st == B.AF_OK
+    buf = ctypes.c_void_p(_FAKE.ctypes.data)
+    iters = (ctypes.c_int32 * 16)()
+    big = lib.af_workspace_bytes(h, 1, 64)
+    # NULL inputs
+    assert lib.af_forward(h, None, buf, buf, 1, 64, buf, big, None) == B.AF_ERR_ARG
+    # L beyond max_len
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 65,
+                          buf, 1 << 40, None) == B.AF_ERR_ARG
+    # workspace too small (checked before any launch)
+    aligned = ctypes.c_void_p(1 << 20)
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 64,
+                          aligned, 16, None) == B.AF_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 64,
+                          ctypes.c_void_p((1 << 20) + 4), big, None) == B.AF_ERR_ARG
+
+    def inv(**kw):
+        a = dict(z=buf, N=1, L=64, B=16, tau=1e-3, max_iters=0, init=0, x_init=None,
+                 F=0, P=0, x_last=None, x=ctypes.c_void_p(_FAKE.ctypes.data + 8),
+                 ws=aligned, wsb=big)
+        a.update(kw)
+        return lib.af_inverse_jacobi(h, a["z"], a["N"], a["L"], a["B"],
+                                     ctypes.c_float(a["tau"]), a["max_iters"], a["init"],
+                                     a["x_init"], a["F"], a["P"], a["x_last"], a["x"],
+                                     iters, a["ws"], a["wsb"], None)
+
+    assert inv(tau=math.nan) == B.AF_ERR_ARG
+    assert inv(B=0) == B.AF_ERR_ARG
+    assert inv(init=9) == B.AF_ERR_ARG
+    assert inv(init=1) == B.AF_ERR_ARG                 # GIVEN without x_init
+    assert inv(init=2, F=8) == B.AF_ERR_ARG            # frame shorter than block
+    assert inv(P=1) == B.AF_ERR_ARG                    # prefix needs x_last
+    assert inv(P=10, x_last=buf) == B.AF_ERR_ARG       # P + L > max_len
+    assert inv(x=buf) == B.AF_ERR_ARG                  # x aliases z
+    assert inv(wsb=8) == B.AF_ERR_WORKSPACE
+    assert lib.af_prefill(h, None, 1, 8, aligned, big, None) == B.AF_ERR_ARG
+    lib.af_plan_destroy(h)
+
+
+def test_stack_restrictions(lib):
+    st, h = make_plan(lib, T=2)
+    assert st == B.AF_OK
+    buf = ctypes.c_void_p(_FAKE.ctypes.data)
+    iters = (ctypes.c_int32 * 16)()
+    big = lib.af_workspace_bytes(h, 1, 16)
+    x = ctypes.c_void_p(_FAKE.ctypes.data + 8)
+    assert lib.af_inverse_jacobi(h, buf, 1, 64, 16, ctypes.c_float(1e-3), 0, 2, None, 16,
+                                 0, None, x, iters, ctypes.c_void_p(1 << 20), big,
+                                 None) == B.AF_ERR_UNSUPPORTED
+    assert lib.af_prefill(h, buf, 1, 8, ctypes.c_void_p(1 << 20), big, None) == B.AF_ERR_UNSUPPORTED
+    lib.af_plan_destroy(h)
+
+
+def test_profile_class_names(lib):
+    st, h = make_plan(lib)
+    assert lib.af_profile_enable(h, b"nope") == B.AF_ERR_ARG
+    assert lib.af_profile_disable(h) == B.AF_OK
+    lib.af_plan_destroy(h)

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle on
+the same seeded inputs.  Bars: relative L2 <= 1e-4 on the fp32 path and
+<= 2e-2 on the bf16 path, log-det relative error <= 1e-3; Jacobi iteration
+counts reported side by side (equal on the fp32 path; on the bf16 path the
+oracle is re-run forced to the GPU's counts when they differ).
+
+Method: STARFlow-V notes (papernotes.org), 关键设计 1 (affine AF block,
+alternating directions), 关键设计 3 (block-wise Jacobi with KV cache, warm
+start, residual stop), 一个完整示例 (prefix encoding into the KV cache)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from autoregressive_normalizing_flow_amd import synth  # noqa: E402
+from oracle import af_oracle as O  # noqa: E402
+from parity_util import (TOL_BF16, TOL_F32, TOL_LOGDET, oracle_jacobi_like,  # noqa: E402
+                         problem, rel_err, rel_l2, say, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from autoregressive_normalizing_flow_amd import binding
+    binding.load_library()
+    return binding
+
+
+# ---------------------------------------------------------------------------
+# kernel units
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(200, 192, 128), (1560, 384, 256), (1, 128, 64),
+                                   (333, 1024, 512)])
+def test_gemm_bf16_unit(B, M, N, K):
+    say("gemm_bf16", M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    a = synth.bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_round(rng.standard_normal((N, K)).astype(np.float32))
+    bias = rng.standard_normal(N).astype(np.float32)
+    y = B.afk_gemm_bf16(to_dev(a).to(torch.bfloat16), to_dev(w).to(torch.bfloat16),
+                        to_dev(bias))
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.astype(np.float64).T + bias
+    assert rel_l2(to_np(y), ref) < 1e-6
+
+
+@pytest.mark.parametrize("N,rows,C", [(3, 77, 48), (1, 1560, 48), (2, 5, 16)])
+def test_affine_unit_both_modes(B, N, rows, C):
+    say("affine", N, rows, C)
+    rng = np.random.default_rng(rows)
+    head = rng.standard_normal((N * rows, 2 * C)).astype(np.float32)
+    z = rng.standard_normal((N, rows, C)).astype(np.float32)
+    x_old = rng.standard_normal((N, rows, C)).astype(np.float32)
+    mu = head[:, :C].reshape(N, rows, C).astype(np.float64)
+    ls = 0.5 * np.tanh(head[:, C:].reshape(N, rows, C).astype(np.float64))
+    part = torch.empty(B.afk_affine_partials_bytes(N, rows, C), dtype=torch.uint8,
+                       device="cuda")
+    res = torch.empty(N, 2, device="cuda")
+    # inverse mode: x <- mu + sigma z in place, residual sums
+    x = to_dev(x_old)
+    B.afk_affine(0, to_dev(head), to_dev(z), x, N, rows, C, res, part, check=True)
+    x_ref = mu + np.exp(ls) * z
+    assert rel_l2(to_np(x), x_ref) < 1e-6
+    num = ((x_ref - x_old) ** 2).sum(axis=(1, 2))
+    den = (x_ref ** 2).sum(axis=(1, 2))
+    r = to_np(res)
+    assert np.all(rel_err(r[:, 0], num) < 1e-5) and np.all(rel_err(r[:, 1], den) < 1e-5)
+    # forward mode: z = (x - mu) / sigma and -sum log sigma
+    zo = torch.empty_like(x)
+    B.afk_affine(1, to_dev(head), to_dev(x_old), zo, N, rows, C, res, part, check=True)
+    assert rel_l2(to_np(zo), (x_old - mu) * np.exp(-ls)) < 1e-6
+    r = to_np(res)
+    assert np.all(rel_err(r[:, 0], -ls.sum(axis=(1, 2))) < 1e-4)
+    assert np.all(r[:, 1] == 0)
+
+
+def test_affine_flags_nonfinite(B):
+    say("affine nonfinite")
+    N, rows, C = 2, 33, 8
+    head = torch.zeros(N * rows, 2 * C, device="cuda")
+    z = torch.ones(N, rows, C, device="cuda")
+    z[1, 7, 3] = float("nan")
+    x = torch.zeros_like(z)
+    part = torch.empty(B.afk_affine_partials_bytes(N, rows, C), dtype=torch.uint8,
+                       device="cuda")
+    res = torch.empty(N, 2, device="cuda")
+    with pytest.raises(B.AFError) as ei:
+        B.afk_affine(0, head, z, x, N, rows, C, res, part, check=True)
+    assert ei.value.status == B.AF_ERR_NONFINITE
+
+
+# ---------------------------------------------------------------------------
+# fp32 path, end to end
+# ---------------------------------------------------------------------------
+def test_tiny_f32_forward_and_inverse(B):
+    """One 8x8 latent frame, C=16, 1 layer d=64, 2 heads, fp32, B=16, tau=1e-3."""
+    w = synth.WORKLOADS["tiny_f32"]
+    say("tiny_f32")
+    params = synth.make_params(w.block, 0)
+    p64 = O.to64(params[0])
+    plan = B.AFPlan(w.block, params)
+    z = synth.normal((1, 64, 16), 1)
+    x_in = synth.normal((1, 64, 16), 2)
+    # forward of x
+    zg, ldg = plan.forward(to_dev(x_in))
+    zo, ldo = O.forward_block(p64, x_in, 2)
+    assert rel_l2(to_np(zg), zo) < TOL_F32
+    assert np.all(rel_err(to_np(ldg), ldo) < TOL_LOGDET)
+    # Jacobi inverse of z ~ N(0, 1)
+    xg, itg = plan.inverse_jacobi(to_dev(z), 16, 1e-3)
+    xo, ito = O.inverse_jacobi_block(p64, z, 2, 16, 1e-3)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert np.array_equal(itg[0], ito)
+    assert rel_l2(to_np(xg), xo) < TOL_F32
+    # forward then inverse recovers x up to the stop threshold, and the GPU's
+    # round trip equals the oracle's
+    xr, itr = plan.inverse_jacobi(zg, 16, 1e-3)
+    xor_, itor = O.inverse_jacobi_block(p64, zo, 2, 16, 1e-3)
+    assert np.array_equal(itr[0], itor)
+    assert rel_l2(to_np(xr), xor_) < TOL_F32
+    assert rel_l2(to_np(xr), x_in) < 0.05
+
+
+def test_f32_stack_ragged_r2l(B):
+    """T=2 (L->R, R->L), ragged last Jacobi block, batch 3, dh=32."""
+    say("f32 stack ragged")
+    cfg, params, p64 = problem(C=5, d=64, H=2, layers=2, max_len=60, dtype="f32",
+                               seed=3, n_blocks=2)
+    plan = B.AFPlan(cfg, params)
+    x_in = synth.normal((3, 60, 5), 4)
+    zg, ldg = plan.forward(to_dev(x_in))
+    zo, ldo = O.forward_stack(p64, x_in, 2)
+    assert rel_l2(to_np(zg), zo) < TOL_F32
+    assert np.all(rel_err(to_np(ldg), ldo) < TOL_LOGDET)
+    xg, itg = plan.inverse_jacobi(zg, 16, 1e-3)
+    xo, ito = O.inverse_jacobi_stack(p64, zo, 2, 16, 1e-3)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert np.array_equal(itg, ito)
+    assert rel_l2(to_np(xg), xo) < TOL_F32
+
+
+def test_f32_forced_count_and_sequential(B):
+    say("f32 forced + B=1")
+    cfg, params, p64 = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((2, 20, 4), 6)
+    xg, itg = plan.inverse_jacobi(to_dev(z), 8, 0.0, max_iters=3)
+    assert np.all(itg == 3)
+    xo, _ = O.inverse_jacobi_block(p64, z, 1, 8, 0.0, max_iters=3)
+    assert rel_l2(to_np(xg), xo) < TOL_F32
+    # B = 1: one update per token is sequential decoding
+    x1, it1 = plan.inverse_jacobi(to_dev(z), 1, 1e-3)
+    assert np.all(it1 == 1)
+    assert rel_l2(to_np(x1), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
+    # tau <= 0 with no cap runs Bb updates and reaches the sequential solution
+    xf, itf = plan.inverse_jacobi(to_dev(z), 8, 0.0)
+    assert itf.tolist() == [[8, 8, 4]]
+    assert rel_l2(to_np(xf), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
+
+
+def test_f32_prefill_given_prevframe(B):
+    say("f32 prefill/given/prev_frame")
+    cfg, params, p64 = problem(C=6, d=128, H=2, layers=2, max_len=96, dtype="f32", seed=7)
+    plan = B.AFPlan(cfg, params)
+    xp = synth.normal((2, 32, 6), 8)
+    z = synth.normal((2, 64, 6), 9)
+    xinit = synth.normal((2, 64, 6), 10)
+    plan.prefill(to_dev(xp), rows=64)
+    xg, itg = plan.inverse_jacobi(to_dev(z), 32, 1e-3, init="given", x_init=to_dev(xinit),
+                                  prefix_len=32, x_last=to_dev(xp[:, -1]))
+    cache, x_last = O.prefill(p64, xp, 2)
+    xo, ito = O.inverse_jacobi_block(p64, z, 2, 32, 1e-3, init="given", x_init=xinit,
+                                     pos0=32, cache=cache, x_last=x_last)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert np.array_equal(itg[0], ito)
+    assert rel_l2(to_np(xg), xo) < TOL_F32
+    # previous-frame warm start, frames of 16 tokens = one block each
+    z2 = synth.normal((1, 48, 6), 11)
+    xg2, itg2 = plan.inverse_jacobi(to_dev(z2), 16, 1e-3, init="prev_frame", frame_len=16)
+    xo2, ito2 = O.inverse_jacobi_block(p64, z2, 2, 16, 1e-3, init="prev_frame", frame_len=16)
+    print("iters gpu", itg2.tolist(), "oracle", ito2.tolist())
+    assert np.array_equal(itg2[0], ito2)
+    assert rel_l2(to_np(xg2), xo2) < TOL_F32
+
+
+def test_f32_run_twice_bitwise(B):
+    say("f32 determinism")
+    cfg, params, _ = problem(C=8, d=64, H=2, layers=2, max_len=80, dtype="f32", seed=12)
+    plan = B.AFPlan(cfg, params)
+    z = to_dev(synth.normal((2, 80, 8), 13))
+    a, ia = plan.inverse_jacobi(z, 32, 1e-3)
+    b, ib = plan.inverse_jacobi(z, 32, 1e-3)
+    assert np.array_equal(ia, ib) and torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# bf16 path, end to end at reduced sizes (several tiles, ragged tails)
+# ---------------------------------------------------------------------------
+def _bf16_block_case(B, d, H, layers, L, Bj, N, seed, C=48):
+    cfg, params, p64 = problem(C=C, d=d, H=H, layers=layers, max_len=L, dtype="bf16",
+                               seed=seed)
+    p = p64[0]
+    plan = B.AFPlan(cfg, params)
+    x_in = synth.normal((N, L, C), seed + 2)
+    zg, ldg = plan.forward(to_dev(x_in))
+    zo, ldo = O.forward_block(p, x_in, H)
+    e_z, e_ld = rel_l2(to_np(zg), zo), rel_err(to_np(ldg), ldo)
+    print(f"forward rel_l2 {e_z:.2e} logdet rel {e_ld.max():.2e}")
+    assert e_z < TOL_BF16
+    assert np.all(e_ld < TOL_LOGDET)
+    z = synth.normal((N, L, C), seed + 1)
+    xg, itg = plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+    xo, ito = oracle_jacobi_like(p, z, H, Bj, 1e-3, itg[0])
+    e_x = rel_l2(to_np(xg), xo)
+    print("iters gpu", itg.tolist(), "oracle(tau)", ito.tolist(), f"x rel_l2 {e_x:.2e}")
+    assert np.all(np.abs(itg[0] - ito) <= 2)
+    assert e_x < TOL_BF16
+
+
+def test_bf16_block_dh64(B):
+    say("bf16 d=256 H=4 L=300 B=128")
+    _bf16_block_case(B, d=256, H=4, layers=2, L=300, Bj=128, N=2, seed=20)
+
+
+def test_bf16_block_dh128(B):
+    say("bf16 d=256 H=2 L=200 B=100")
+    _bf16_block_case(B, d=256, H=2, layers=1, L=200, Bj=100, N=1, seed=21)
+
+
+def test_bf16_stack_alternating(B):
+    """Shallow-stack structure: T=4 alternating blocks, frames batched."""
+    say("bf16 stack T=4")
+    cfg, params, p64 = problem(C=48, d=256, H=4, layers=1, max_len=130, dtype="bf16",
+                               seed=22, n_blocks=4)
+    plan = B.AFPlan(cfg, params)
+    x_in = synth.noisy_latents((3, 130, 48), 24, 0.3)
+    zg, ldg = plan.forward(to_dev(x_in))
+    zo, ldo = O.forward_stack(p64, x_in, 4)
+    print("forward", rel_l2(to_np(zg), zo), rel_err(to_np(ldg), ldo))
+    assert rel_l2(to_np(zg), zo) < TOL_BF16
+    assert np.all(rel_err(to_np(ldg), ldo) < TOL_LOGDET)
+    xg, itg = plan.inverse_jacobi(zg, 130, 1e-3)
+    xo, ito = O.inverse_jacobi_stack(p64, to_np(zg), 4, 130, 1e-3, forced_iters=itg)
+    print("iters gpu", itg.tolist())
+    assert rel_l2(to_np(xg), xo) < TOL_BF16
+    assert rel_l2(to_np(xg), x_in) < 0.1
+
+
+def test_bf16_prefill_given(B):
+    """Prefix-conditioning structure: 2-frame prefix, then one frame warm-started
+    from the last prefix frame, batch 2, dh=128."""
+    say("bf16 prefill")
+    F = 64
+    cfg, params, p64 = problem(C=48, d=256, H=2, layers=2, max_len=3 * F, dtype="bf16",
+                               seed=25)
+    plan = B.AFPlan(cfg, params)
+    xp = synth.normal((2, 2 * F, 48), 27)
+    z = synth.normal((2, F, 48), 26)
+    plan.prefill(to_dev(xp), rows=F)
+    x_init = np.ascontiguousarray(xp[:, F:])
+    xg, itg = plan.inverse_jacobi(to_dev(z), F, 1e-3, init="given", x_init=to_dev(x_init),
+                                  prefix_len=2 * F, x_last=to_dev(xp[:, -1]))
+    cache, x_last = O.prefill(p64[0], xp, 2)
+    xo, ito = oracle_jacobi_like(p64[0], z, 2, F, 1e-3, itg[0], init="given",
+                                 x_init=x_init, pos0=2 * F, cache=cache, x_last=x_last)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert rel_l2(to_np(xg), xo) < TOL_BF16
+
+
+def test_bf16_video_prev_frame(B):
+    """Multi-frame structure: 3 frames of 96 tokens, block = frame, warm start."""
+    say("bf16 video prev_frame")
+    F = 96
+    cfg, params, p64 = problem(C=48, d=256, H=4, layers=2, max_len=3 * F, dtype="bf16",
+                               seed=28)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((1, 3 * F, 48), 29)
+    xg, itg = plan.inverse_jacobi(to_dev(z), F, 1e-3, init="prev_frame", frame_len=F)
+    xo, ito = oracle_jacobi_like(p64[0], z, 4, F, 1e-3, itg[0], init="prev_frame",
+                                 frame_len=F)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert rel_l2(to_np(xg), xo) < TOL_BF16
+
+
+def test_bf16_run_twice_bitwise(B):
+    say("bf16 determinism")
+    cfg, params, _ = problem(C=48, d=256, H=4, layers=2, max_len=200, dtype="bf16", seed=30)
+    plan = B.AFPlan(cfg, params)
+    z = to_dev(synth.normal((2, 200, 48), 31))
+    a, ia = plan.inverse_jacobi(z, 128, 1e-3)
+    b, ib = plan.inverse_jacobi(z, 128, 1e-3)
+    assert np.array_equal(ia, ib) and torch.equal(a, b)
