@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark: latent tokens/s inverted by video-aware block-wise Jacobi on one
+MI355X, with the roofline of the dominant kernel and the CPU oracle beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload frame480p]
+
+A step is one af_inverse_jacobi call over one batch of synthetic latents
+(every kernel of the hot path: shift+embed, LayerNorm, QKV/O/MLP GEMMs,
+attention over the KV cache, head, fused affine/residual kernel, host stop
+test).  Inputs are resident in HBM before timing.  Prints ONE JSON line.
+
+Workloads (autoregressive_normalizing_flow_amd.synth.WORKLOADS):
+  frame480p      one 1560-token frame, 8 layers d=1024, B=1560   (default)
+  video21        21 frames, block = frame, previous-frame warm start
+  shallow_stack  T=4 alternating blocks, 2 layers d=512, 21 frames batched
+  wide_prefix    4 layers d=4096, 2-frame prefix, batch 2
+  tiny_f32       one 8x8 frame, fp32
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 (vector / matrix)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "latent tokens/s inverted via block Jacobi (1 GPU); % MFMA/HBM peak; iters/blk"
+GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2", "gemm_head")
+ALL_CLASSES = GEMM_CLASSES + ("attention", "layernorm", "embed", "affine")
+
+
+def gemm_flops_per_launch(cls, M, cfg):
+    d, C = cfg.d, cfg.C
+    return {"gemm_qkv": 2 * M * 3 * d * d, "gemm_o": 2 * M * d * d,
+            "gemm_mlp1": 2 * M * 4 * d * d, "gemm_mlp2": 2 * M * d * 4 * d,
+            "gemm_head": 2 * M * 2 * C * d}[cls]
+
+
+class Runner:
+    """Sets up one workload on cuda:0 and exposes step()."""
+
+    def __init__(self, name, torch, binding, synth):
+        self.torch = torch
+        w = synth.WORKLOADS[name]
+        self.w = w
+        cfg = w.block
+        self.cfg = cfg
+        self.params = synth.make_params(cfg, 0, n_blocks=w.n_blocks)
+        self.plan = binding.AFPlan(cfg, self.params)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+        N, L, C = w.batch, w.length, cfg.C
+        self.rows = min(w.jacobi_block, L)
+        self.M = N * self.rows
+        self.kw = {}
+        if w.x_noise is not None:
+            # forward first: the inverse inverts the forward's z
+            x = synth.noisy_latents((N, L, C), 2, w.x_noise)
+            self.x_fwd = dev(x)
+            self.z, _ = self.plan.forward(self.x_fwd)
+        else:
+            self.x_fwd = dev(synth.normal((N, L, C), 2))
+            self.z = dev(synth.normal((N, L, C), 1))
+        if w.prefix:
+            xp = synth.normal((N, w.prefix, C), 2)
+            self.plan.prefill(dev(xp), rows=self.rows)
+            self.kw = dict(init="given", x_init=dev(xp[:, -L:]), prefix_len=w.prefix,
+                           x_last=dev(xp[:, -1]))
+        elif w.init == "prev_frame":
+            self.kw = dict(init="prev_frame", frame_len=w.frame_len)
+        torch.cuda.synchronize()
+        self.tokens_per_step = N * L
+        self.iters = None
+
+    def step(self):
+        x, it = self.plan.inverse_jacobi(self.z, self.w.jacobi_block, self.w.tau, **self.kw)
+        self.iters = it
+        self.x = x
+        return x
+
+
+def cpu_baseline(runner, synth, budget_tokens):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: block-wise Jacobi on the first `budget_tokens` tokens of sample 0
+    with the same tau (for the stack, the last block of the stack only)."""
+    from threadpoolctl import threadpool_info
+    from oracle import af_oracle as O
+    w, cfg = runner.w, runner.cfg
+    S = min(budget_tokens, w.length)
+    z = runner.z[:1, :S].detach().cpu().numpy().astype(np.float64)
+    t_idx = w.n_blocks - 1
+    p64 = O.to64(runner.params[t_idx])
+    kw = {}
+    if w.prefix:  # keep the sample small: encode a prefix of equal length
+        xp = synth.normal((1, w.prefix, cfg.C), 2)[:, -S:].astype(np.float64)
+        cache, x_last = O.prefill(p64, xp, cfg.n_heads)
+        kw = dict(pos0=S, cache=cache, x_last=x_last)
+    t0 = time.perf_counter()
+    _, it = O.inverse_jacobi_block(p64, z, cfg.n_heads, S, w.tau,
+                                   direction=O.direction_of(t_idx), **kw)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2), "iters": it.tolist(),
+            "sample": f"oracle fp64 block-Jacobi of the first {S} tokens of sample 0 "
+                      f"(one Jacobi block of {S}, tau={w.tau}"
+                      + (", after a prefix of equal length" if w.prefix else "")
+                      + (f", stack block {t_idx} only" if w.n_blocks > 1 else "") + ")"}
+
+
+def affine_sweep(torch, binding, tokens, reps=5):
+    """The fused affine kernel alone (inverse mode), HBM-cold: `tokens` rows of
+    C=48, buffers far larger than the 256 MB Infinity Cache.  Algorithmic
+    bytes: read mu, raw, z, x_old and write x = 20*C bytes per token."""
+    C = 48
+    head = torch.randn(tokens, 2 * C, device="cuda")
+    z = torch.randn(tokens, C, device="cuda")
+    x = torch.randn(tokens, C, device="cuda")
+    part = torch.empty(binding.afk_affine_partials_bytes(1, tokens, C), dtype=torch.uint8,
+                       device="cuda")
+    res = torch.empty(1, 2, device="cuda")
+    binding.afk_affine(0, head, z, x, 1, tokens, C, res, part)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        binding.afk_affine(0, head, z, x, 1, tokens, C, res, part)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    nbytes = 20 * C * tokens
+    del head, z, x, part
+    return {"tokens": tokens, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+            "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="frame480p")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="oracle sample size for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the per-GPU kernel is measured at its real shape; see the sharding "
+              "design in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from autoregressive_normalizing_flow_amd import binding, synth
+    binding.load_library()
+    assert torch.cuda.is_available(), "no GPU"
+
+    r = Runner(args.workload, torch, binding, synth)
+    cfg, w = r.cfg, r.w
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+
+    # per-class breakdown: one untimed profiled step per class
+    breakdown = {}
+    for cls in ALL_CLASSES:
+        r.plan.profile_enable(cls)
+        r.step()
+        n, ms = r.plan.profile_read()
+        r.plan.profile_disable()
+        breakdown[cls] = {"launches": n, "ms": round(ms, 4)}
+    dominant = max(GEMM_CLASSES, key=lambda c: breakdown[c]["ms"])
+
+    # timed region, with the dominant kernel timed live by HIP events on the
+    # stream it is launched on
+    r.plan.profile_enable(dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_launch, dom_ms = r.plan.profile_read()
+    r.plan.profile_disable()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = r.tokens_per_step / ((t1 - t0) / args.steps)
+
+    flops = gemm_flops_per_launch(dominant, r.M, cfg)
+    avg_ms = dom_ms / max(n_launch, 1)
+    peak = PEAK_BF16_TFLOPS if (cfg.dtype == "bf16" and dominant != "gemm_head") else PEAK_F32_TFLOPS
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "flops_per_launch": flops, "avg_ms": round(avg_ms, 5),
+                "launches": n_launch}
+
+    # all GEMMs together (algorithmic flops / summed kernel time, one step)
+    g_flops = sum(gemm_flops_per_launch(c, r.M, cfg) * breakdown[c]["launches"]
+                  for c in GEMM_CLASSES)
+    g_ms = sum(breakdown[c]["ms"] for c in GEMM_CLASSES)
+    # fused affine kernel in the path: 20*C bytes per token per launch
+    aff = breakdown["affine"]
+    aff_bytes = 20 * cfg.C * r.M
+    aff_gbs = aff_bytes * aff["launches"] / (aff["ms"] * 1e-3) / 1e9 if aff["ms"] else 0.0
+
+    # forward pass (af_forward) time, untimed by the metric
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    r.plan.forward(r.x_fwd)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - f0) * 1e3
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "tokens": w.length,
+                   "jacobi_block": w.jacobi_block, "tau": w.tau, "init": w.init,
+                   "stack_blocks": w.n_blocks, "layers": cfg.n_layers, "d": cfg.d,
+                   "heads": cfg.n_heads, "C": cfg.C, "prefix": w.prefix},
+        "iters_per_block": r.iters.tolist(),
+        "roofline": roofline,
+        "gemm_all": {"TFLOP/s": round(g_flops / (g_ms * 1e-3) / 1e12, 2) if g_ms else None,
+                     "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / peak, 4) if g_ms else None},
+        "affine_in_path": {"bound": "hbm", "GB/s": round(aff_gbs, 1),
+                           "frac": round(aff_gbs / PEAK_HBM_GBS, 4),
+                           "bytes_per_launch": aff_bytes},
+        "kernel_ms_per_step": breakdown,
+        "forward_ms": round(fwd_ms, 3),
+    }
+    if not args.no_sweep:
+        out["affine_hbm_sweep"] = [affine_sweep(torch, binding, t) for t in (1 << 20, 1 << 22)]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r, synth, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

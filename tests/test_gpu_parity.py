@@ -144,7 +144,7 @@ def test_f32_stack_ragged_r2l(B):
 
 def test_f32_forced_count_and_sequential(B):
     say("f32 forced + B=1")
-    cfg, params, p64 = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
+    cfg, params, (p64,) = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
     plan = B.AFPlan(cfg, params)
     z = synth.normal((2, 20, 4), 6)
     xg, itg = plan.inverse_jacobi(to_dev(z), 8, 0.0, max_iters=3)
@@ -163,7 +163,7 @@ def test_f32_forced_count_and_sequential(B):
 
 def test_f32_prefill_given_prevframe(B):
     say("f32 prefill/given/prev_frame")
-    cfg, params, p64 = problem(C=6, d=128, H=2, layers=2, max_len=96, dtype="f32", seed=7)
+    cfg, params, (p64,) = problem(C=6, d=128, H=2, layers=2, max_len=96, dtype="f32", seed=7)
     plan = B.AFPlan(cfg, params)
     xp = synth.normal((2, 32, 6), 8)
     z = synth.normal((2, 64, 6), 9)
