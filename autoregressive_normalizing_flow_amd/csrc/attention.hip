@@ -12,39 +12,79 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace af {
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA flash attention.  A workgroup owns 128 queries of one (sample,
-// head); each of its 4 waves owns 32 queries (two 16-query blocks).  Per
-// 64-key tile:  S^T = K Q^T  (A = K rows from LDS, B = Q held in registers),
-// online softmax in fp32 along the key axis (the 4 lanes sharing a query
-// combine with two xor-shuffles), then  O^T += Vt P^T  where P^T is already in
-// the B-operand layout of the lanes that hold the scores: the 8 k-slots of
-// lane l are keys {4(l/16)+j, 16+4(l/16)+j}, j < 4, of each 32-key step, and
-// the Vt fragment reads the same keys (two 8-byte LDS reads).
+// bf16 MFMA flash attention with key-range splitting.
+//
+// Work unit = (sample, head, 128-query tile, key chunk of KC keys).  Long key
+// ranges (a long KV-cache prefix, or the last query tiles of a frame) are cut
+// into chunks processed by separate workgroups, so the grid fills the chip
+// and no workgroup walks the whole prefix; a query tile with one chunk writes
+// its normalised output directly, otherwise each chunk writes its unnormalised
+// output and running (max, sum) to a partial slot and attn_combine merges the
+// chunks.  Units are numbered sample-head major, then query tile, then chunk.
+//
+// Inside a unit each of the 4 waves owns 32 queries (two 16-query blocks).
+// Per 64-key tile:  S^T = K Q^T  (A = K rows from LDS, B = Q held in
+// registers), online softmax in fp32 along the key axis (the 4 lanes sharing
+// a query combine with two xor-shuffles), then  O^T += Vt P^T  where P^T is
+// already in the B-operand layout of the lanes that hold the scores: the 8
+// k-slots of lane l are keys {4(l/16)+j, 16+4(l/16)+j}, j < 4, of each
+// 32-key step, and the Vt fragment reads the same keys (two 8-byte reads).
 // ---------------------------------------------------------------------------
+constexpr int ATT_QT = 128;   // queries per unit
+constexpr int ATT_KT = 64;    // keys per tile
+
+struct AttnArgs {
+  const bf16* q;
+  const bf16* kc;
+  const bf16* vt;
+  bf16* out;
+  float* part;     // partial slots: [unit][ATT_QT][DH] O, then [ATT_QT] m, [ATT_QT] l
+  int R, H, d, Lcap, pos_base, KC, U_nh;
+  float scale_log2;
+};
+
+__device__ __forceinline__ int att_chunks(int qt, int R, int pos_base, int KC) {
+  const int nk = pos_base + min(R, (qt + 1) * ATT_QT);
+  return (nk + KC - 1) / KC;
+}
+
 template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ kc,
-    const bf16* __restrict__ vt, bf16* __restrict__ out, int R, int H, int d,
-    int Lcap, int pos_base, float scale_log2) {
-  constexpr int QWAVE = 32, QB = QWAVE / 16, QTILE = 4 * QWAVE;
-  constexpr int KT = 64, KB = KT / 16, KS = DH / 32, DB = DH / 16;
-  constexpr int KLDS = DH + 8, VLDS = KT + 8;
-  constexpr int CK = KT * DH / 8 / 256;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][KT * KLDS];
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int QWAVE = 32, QB = QWAVE / 16;
+  constexpr int KB = ATT_KT / 16, KS = DH / 32, DB = DH / 16;
+  constexpr int KLDS = DH + 8, VLDS = ATT_KT + 8;
+  constexpr int CK = ATT_KT * DH / 8 / 256;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][ATT_KT * KLDS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][DH * VLDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.y, n = blockIdx.z;
-  const int q_lo = blockIdx.x * QTILE;
-  const int q_hi = min(R, q_lo + QTILE);
-  const int nk = pos_base + q_hi;  // keys 0..nk-1 can be attended
-  const int n_tiles = (nk + KT - 1) / KT;
-  const size_t hb = (size_t)n * H + head;
-  const bf16* kbase = kc + hb * Lcap * DH;
-  const bf16* vbase = vt + hb * DH * Lcap;
+  // unit -> (sample, head, query tile, chunk)
+  const int u = blockIdx.x;
+  const int nh = u / a.U_nh;
+  int rem = u - nh * a.U_nh;
+  const int n = nh / a.H, head = nh - n * a.H;
+  int qt = 0, n_chunks = att_chunks(0, a.R, a.pos_base, a.KC);
+  while (rem >= n_chunks) {
+    rem -= n_chunks;
+    ++qt;
+    n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
+  }
+  const int chunk = rem;
+  const int R = a.R, d = a.d, Lcap = a.Lcap, pos_base = a.pos_base;
+  const int q_lo = qt * ATT_QT;
+  const int nk = pos_base + min(R, q_lo + ATT_QT);   // keys of the tile: 0..nk-1
+  const int k_begin = chunk * a.KC;
+  const int k_end = min(nk, k_begin + a.KC);
+  const int t_begin = k_begin / ATT_KT;
+  const int n_tiles = (k_end - k_begin + ATT_KT - 1) / ATT_KT;
+  const size_t hb = (size_t)n * a.H + head;
+  const bf16* kbase = a.kc + hb * Lcap * DH;
+  const bf16* vbase = a.vt + hb * DH * Lcap;
   const int l16 = lane & 15, lg = lane >> 4;
 
   bf16x8 qf[QB][KS];
@@ -53,7 +93,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   for (int qb = 0; qb < QB; ++qb) {
     const int t = q_lo + wave * QWAVE + qb * 16 + l16;
     qpos[qb] = pos_base + t;
-    const bf16* qrow = q + ((size_t)n * R + min(t, R - 1)) * d + head * DH;
+    const bf16* qrow = a.q + ((size_t)n * R + min(t, R - 1)) * d + head * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[qb][ks] = *(const bf16x8*)(qrow + ks * 32 + lg * 8);
@@ -69,26 +109,27 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int db = 0; db < DB; ++db) acc_o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint4 rk[CK], rv[CK];
+  u32x4 rk[CK], rv[CK];
+  // keys outside [k_begin, k_end) are loaded as zeros (masked below)
   auto gload = [&](int kt) {
-    const int k0 = kt * KT;
+    const int k0 = (t_begin + kt) * ATT_KT;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * 256;
       const int key = c / (DH / 8), dc = c - key * (DH / 8);
       const int kk = k0 + key;
-      rk[i] = kk < nk ? *(const uint4*)(kbase + (size_t)kk * DH + dc * 8)
-                      : uint4{0u, 0u, 0u, 0u};
-      const int drow = c / (KT / 8), kc8 = c - drow * (KT / 8);
+      rk[i] = kk < k_end ? *(const u32x4*)(kbase + (size_t)kk * DH + dc * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
+      const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
       const int kk0 = k0 + kc8 * 8;  // k0 + 64 <= Lcap: always in bounds
-      uint4 v = *(const uint4*)(vbase + (size_t)drow * Lcap + kk0);
-      if (kk0 + 8 > nk) {
-        union { uint4 u; unsigned short s[8]; } tmp;
-        tmp.u = v;
+      u32x4 v = *(const u32x4*)(vbase + (size_t)drow * Lcap + kk0);
+      if (kk0 + 8 > k_end) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (kk0 + e >= nk) tmp.s[e] = 0;
-        v = tmp.u;
+        for (int e = 0; e < 4; ++e) {
+          const unsigned lo_ok = (kk0 + 2 * e) < k_end ? 0xFFFFu : 0u;
+          const unsigned hi_ok = (kk0 + 2 * e + 1) < k_end ? 0xFFFF0000u : 0u;
+          v[e] &= (lo_ok | hi_ok);
+        }
       }
       rv[i] = v;
     }
@@ -98,18 +139,20 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * 256;
       const int key = c / (DH / 8), dc = c - key * (DH / 8);
-      *(uint4*)(&sK[buf][key * KLDS + dc * 8]) = rk[i];
-      const int drow = c / (KT / 8), kc8 = c - drow * (KT / 8);
-      *(uint4*)(&sV[buf][drow * VLDS + kc8 * 8]) = rv[i];
+      *(u32x4*)(&sK[buf][key * KLDS + dc * 8]) = rk[i];
+      const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
+      *(u32x4*)(&sV[buf][drow * VLDS + kc8 * 8]) = rv[i];
     }
   };
 
   gload(0);
   lstore(0);
   __syncthreads();
+#pragma clang loop unroll(disable)
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < n_tiles) gload(kt + 1);
+    const int key0 = (t_begin + kt) * ATT_KT;
 
     f32x4 s[KB][QB];
 #pragma unroll
@@ -136,9 +179,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = kt * KT + kb * 16 + lg * 4 + r;
-          float v = s[kb][qb][r] * scale_log2;
-          if (key > qpos[qb] || key >= nk) v = -INFINITY;
+          const int key = key0 + kb * 16 + lg * 4 + r;
+          float v = s[kb][qb][r] * a.scale_log2;
+          if (key > qpos[qb] || key >= k_end) v = -INFINITY;
           s[kb][qb][r] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -163,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 
     // O^T += Vt P^T over two 32-key steps
 #pragma unroll
-    for (int c = 0; c < KT / 32; ++c) {
+    for (int c = 0; c < ATT_KT / 32; ++c) {
       bf16x8 pf[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -194,19 +237,94 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     float l = l_run[qb];
     l += __shfl_xor(l, 16, AF_WAVE);
     l += __shfl_xor(l, 32, AF_WAVE);
-    const float inv = 1.0f / l;
-    const int t = q_lo + wave * QWAVE + qb * 16 + l16;
-    if (t < R) {
-      bf16* orow = out + ((size_t)n * R + t) * d + head * DH;
+    const int tq = wave * QWAVE + qb * 16 + l16;   // query within the tile
+    const int t = q_lo + tq;
+    if (n_chunks == 1) {
+      if (t < R) {
+        const float inv = 1.0f / l;
+        bf16* orow = a.out + ((size_t)n * R + t) * d + head * DH;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x4 o;
+        for (int db = 0; db < DB; ++db) {
+          bf16x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc_o[db][qb][r] * inv);
-        *(bf16x4*)(orow + db * 16 + lg * 4) = o;
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc_o[db][qb][r] * inv);
+          *(bf16x4*)(orow + db * 16 + lg * 4) = o;
+        }
+      }
+    } else {
+      float* slot = a.part + (size_t)u * ATT_QT * (DH + 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *(f32x4*)(slot + (size_t)tq * DH + db * 16 + lg * 4) = acc_o[db][qb];
+      if (lg == 0) {
+        slot[ATT_QT * DH + tq] = m_run[qb];
+        slot[ATT_QT * DH + ATT_QT + tq] = l;
       }
     }
   }
+}
+
+// Merge the key chunks of every query tile that has more than one:
+// O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, chunks in order.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt) {
+  const int nh = blockIdx.x / n_qt, qt = blockIdx.x - nh * n_qt;
+  const int n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
+  if (n_chunks <= 1) return;
+  int u0 = nh * a.U_nh;
+  for (int q = 0; q < qt; ++q) u0 += att_chunks(q, a.R, a.pos_base, a.KC);
+  const int n = nh / a.H, head = nh - n * a.H;
+  constexpr int D4 = DH / 4;
+  for (int item = threadIdx.x; item < ATT_QT * D4; item += 256) {
+    const int tq = item / D4, e = (item - tq * D4) * 4;
+    const int t = qt * ATT_QT + tq;
+    if (t >= a.R) continue;
+    float m = -1e30f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float* slot = a.part + (size_t)(u0 + c) * ATT_QT * (DH + 2);
+      m = fmaxf(m, slot[ATT_QT * DH + tq]);
+    }
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float* slot = a.part + (size_t)(u0 + c) * ATT_QT * (DH + 2);
+      const float w = exp2f(slot[ATT_QT * DH + tq] - m);
+      const float4 v = *(const float4*)(slot + (size_t)tq * DH + e);
+      o.x += w * v.x;
+      o.y += w * v.y;
+      o.z += w * v.z;
+      o.w += w * v.w;
+      l += w * slot[ATT_QT * DH + ATT_QT + tq];
+    }
+    const float inv = 1.0f / l;
+    bf16x4 r = {(bf16)(o.x * inv), (bf16)(o.y * inv), (bf16)(o.z * inv), (bf16)(o.w * inv)};
+    *(bf16x4*)(a.out + ((size_t)n * a.R + t) * a.d + head * DH + e) = r;
+  }
+}
+
+// Key chunk length: the smallest multiple of 512 keys that keeps the number
+// of units near 1024 (4 per CU); whole ranges when that is already enough.
+static int att_units(int R, int pos_base, int KC, int n_qt) {
+  int s = 0;
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int nk = pos_base + std::min(R, (qt + 1) * ATT_QT);
+    s += (nk + KC - 1) / KC;
+  }
+  return s;
+}
+
+int attention_chunk(int N, int R, int H, int pos_base) {
+  const int n_qt = (R + ATT_QT - 1) / ATT_QT;
+  const int nk_max = pos_base + R;
+  int KC = 512;
+  while (KC < nk_max && (long)N * H * att_units(R, pos_base, KC, n_qt) > 1024) KC *= 2;
+  return KC;
+}
+
+size_t attention_partial_floats(int N, int R, int H, int dh, int pos_base) {
+  const int n_qt = (R + ATT_QT - 1) / ATT_QT;
+  const int KC = attention_chunk(N, R, H, pos_base);
+  return (size_t)N * H * att_units(R, pos_base, KC, n_qt) * ATT_QT * (dh + 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,27 +370,30 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 }
 
 hipError_t launch_attention(bool bf, const void* q, const void* kc,
-                            const void* vt, void* out, int N, int R, int H,
-                            int dh, int d, int Lcap, int pos_base, hipStream_t st) {
+                            const void* vt, void* out, float* part, int N, int R,
+                            int H, int dh, int d, int Lcap, int pos_base,
+                            hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf) {
-    dim3 grid((R + 127) / 128, H, N);
-    const float sl2 = scale * 1.4426950408889634f;
+    const int n_qt = (R + ATT_QT - 1) / ATT_QT;
+    const int KC = attention_chunk(N, R, H, pos_base);
+    const int U_nh = att_units(R, pos_base, KC, n_qt);
+    AttnArgs a{(const bf16*)q, (const bf16*)kc, (const bf16*)vt, (bf16*)out, part,
+               R, H, d, Lcap, pos_base, KC, U_nh, scale * 1.4426950408889634f};
+    const dim3 grid(N * H * U_nh), comb(N * H * n_qt);
+    const bool multi = U_nh > n_qt;
     switch (dh) {
       case 64:
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st,
-                           (const bf16*)q, (const bf16*)kc, (const bf16*)vt,
-                           (bf16*)out, R, H, d, Lcap, pos_base, sl2);
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a);
+        if (multi) hipLaunchKernelGGL(attn_combine_kernel<64>, comb, dim3(256), 0, st, a, n_qt);
         break;
       case 128:
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st,
-                           (const bf16*)q, (const bf16*)kc, (const bf16*)vt,
-                           (bf16*)out, R, H, d, Lcap, pos_base, sl2);
+        hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st, a);
+        if (multi) hipLaunchKernelGGL(attn_combine_kernel<128>, comb, dim3(256), 0, st, a, n_qt);
         break;
       case 32:
-        hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st,
-                           (const bf16*)q, (const bf16*)kc, (const bf16*)vt,
-                           (bf16*)out, R, H, d, Lcap, pos_base, sl2);
+        hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a);
+        if (multi) hipLaunchKernelGGL(attn_combine_kernel<32>, comb, dim3(256), 0, st, a, n_qt);
         break;
       default:
         return hipErrorInvalidValue;

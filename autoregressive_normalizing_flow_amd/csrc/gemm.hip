@@ -8,11 +8,26 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace af {
 
 // ---------------------------------------------------------------------------
-// epilogues: called once per output element with the fp32 accumulator
+// epilogues.  operator() takes one element (fp32 SIMT kernel); store4 takes
+// four consecutive output features n..n+3 of row m (bf16 MFMA kernel).
 // ---------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ void store_vec4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store_vec4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = float4{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store_vec4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4*)p = v;
+}
+
 template <class T>
 struct EpiQKV {
   const float* bias;
@@ -20,7 +35,7 @@ struct EpiQKV {
   T* kc;
   T* vt;
   int M, R, d, dh, H, Lcap, pos_base;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+  __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     v += bias[n];
     const int which = n / d, hd = n - which * d;
@@ -36,16 +51,49 @@ struct EpiQKV {
     else
       vt[(base * dh + e) * Lcap + p] = from_f32<T>(v);
   }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M) return;
+    const float4 b = *(const float4*)(bias + n);
+    const float v0 = v[0] + b.x, v1 = v[1] + b.y, v2 = v[2] + b.z, v3 = v[3] + b.w;
+    const int which = n / d, hd = n - which * d;
+    if (which == 0) {
+      store_vec4(q + (size_t)m * d + hd, v0, v1, v2, v3);
+      return;
+    }
+    const int nn = m / R, t = m - nn * R, p = pos_base + t;
+    const int head = hd / dh, e = hd - head * dh;
+    const size_t base = (size_t)nn * H + head;
+    if (which == 1) {
+      store_vec4(kc + (base * Lcap + p) * dh + e, v0, v1, v2, v3);
+    } else {
+      T* col = vt + (base * dh + e) * Lcap + p;
+      col[0] = from_f32<T>(v0);
+      col[Lcap] = from_f32<T>(v1);
+      col[2 * (size_t)Lcap] = from_f32<T>(v2);
+      col[3 * (size_t)Lcap] = from_f32<T>(v3);
+    }
+  }
 };
 
 struct EpiResid {
   const float* bias;
   float* h;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+  __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     float* p = h + (size_t)m * N + n;
     *p = *p + (v + bias[n]);
+  }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M) return;
+    float4* p = (float4*)(h + (size_t)m * N + n);
+    const float4 b = *(const float4*)(bias + n);
+    float4 o = *p;
+    o.x += v[0] + b.x;
+    o.y += v[1] + b.y;
+    o.z += v[2] + b.z;
+    o.w += v[3] + b.w;
+    *p = o;
   }
 };
 
@@ -54,9 +102,15 @@ struct EpiGelu {
   const float* bias;
   T* out;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+  __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     out[(size_t)m * N + n] = from_f32<T>(gelu_erf(v + bias[n]));
+  }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M) return;
+    const float4 b = *(const float4*)(bias + n);
+    store_vec4(out + (size_t)m * N + n, gelu_erf(v[0] + b.x), gelu_erf(v[1] + b.y),
+               gelu_erf(v[2] + b.z), gelu_erf(v[3] + b.w));
   }
 };
 
@@ -64,115 +118,214 @@ struct EpiF32 {
   const float* bias;
   float* out;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+  __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     out[(size_t)m * N + n] = v + (bias ? bias[n] : 0.f);
+  }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M) return;
+    float4 b = bias ? *(const float4*)(bias + n) : float4{0.f, 0.f, 0.f, 0.f};
+    *(float4*)(out + (size_t)m * N + n) =
+        float4{v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w};
+  }
+};
+
+// fp32 split-K partial planes out[s][M][N] (the consumer sums them).
+struct EpiPlane {
+  float* out;
+  int M, N;
+  __device__ __forceinline__ void operator()(int m, int n, float v, int split) const {
+    if (m >= M) return;
+    out[((size_t)split * M + m) * N + n] = v;
+  }
+};
+
+// Split-K partial: fp32 slab [S][M][N]; a reduce kernel adds the slabs in a
+// fixed order (deterministic) and applies the residual epilogue.
+struct EpiSlab {
+  float* slab;
+  int M, N, tiles;  // tiles per split: blockIdx.x / tiles is the split index
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M) return;
+    float* plane = slab + (size_t)(blockIdx.x / tiles) * M * N;
+    *(float4*)(plane + (size_t)m * N + n) = float4{v[0], v[1], v[2], v[3]};
   }
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM.  Block tile BM x BN x 64, waves arranged (BM/WM) x (BN/WN),
-// each wave owns a WM x WN sub-tile of 16x16 MFMA accumulators.
-// Requirements: N % BN == 0, K % 64 == 0; M arbitrary (rows clamped on load,
-// masked on store).
-// Fragment layout of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies
-// A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16], and receives
-// D[4*(l/16) + r][l%16] for r = 0..3.
+// bf16 MFMA GEMM (gfx950 v_mfma_f32_16x16x32_bf16, wave64).
+//
+// Computes the transposed product D = W A^T tile by tile so that each lane's
+// accumulator holds four consecutive output features of one row, which the
+// epilogues store as one vector.  Fragment layout of the MFMA: lane l
+// supplies A-operand row l%16 / B-operand column l%16 with k = 8*(l/16)..+8,
+// and receives D[4*(l/16) + r][l%16], r = 0..3.  Here the A operand is a W
+// row (output feature) and the B operand an activation row (token).
+//
+// Block tile BM = 32*TM tokens x BN = 32*TN features x 64, 4 waves in 2 x 2,
+// wave tile 16*TM x 16*TN.  TM = 7 gives 224-row tiles: a 1560-token frame
+// (and every multiple of it) then pads by only 0.5%.  Two LDS buffers (rows
+// padded to 144 B: conflict-free 16-byte fragment reads).  Blocks are mapped XCD-aware: consecutive block ids go to
+// different XCDs, so the tile grid is partitioned into 8 column groups and
+// XCD x walks the tiles of group x, keeping its W panels in its own L2.
+// One register stage: the global loads of tile k+1 are in flight while tile
+// k is multiplied (a second stage costs more registers than it hides).
+// blockIdx.x = split * tiles + position; split s covers K range
+// [s*k_len, (s+1)*k_len).  Requirements: N % BN == 0, k_len % 64 == 0.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, class Epi>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_kernel(
+template <int TM_, int TN_>
+struct GemmCfg {
+  static constexpr int TM = TM_, TN = TN_;
+  static constexpr int NT = 256, BK = 64, LDS = BK + 8, CPR = BK / 8;
+  static constexpr int WM = 16 * TM, WN = 16 * TN, BM = 2 * WM, BN = 2 * WN;
+  static constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/threads");
+};
+
+template <class G>
+__device__ __forceinline__ void gemm_gload(u32x4 (&ra)[G::CA], u32x4 (&rb)[G::CB],
+                                           const bf16* __restrict__ A,
+                                           const bf16* __restrict__ W, int m0,
+                                           int n0, int M, int K, int k0, int tid) {
+#pragma unroll
+  for (int i = 0; i < G::CA; ++i) {
+    const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
+    const int gm = min(m0 + row, M - 1);
+    ra[i] = *(const u32x4*)(A + (size_t)gm * K + k0 + kc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < G::CB; ++i) {
+    const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
+    rb[i] = *(const u32x4*)(W + (size_t)(n0 + row) * K + k0 + kc * 8);
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void gemm_lstore(const u32x4 (&ra)[G::CA],
+                                            const u32x4 (&rb)[G::CB], bf16* sA,
+                                            bf16* sB, int tid) {
+#pragma unroll
+  for (int i = 0; i < G::CA; ++i) {
+    const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
+    *(u32x4*)(sA + row * G::LDS + kc * 8) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < G::CB; ++i) {
+    const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
+    *(u32x4*)(sB + row * G::LDS + kc * 8) = rb[i];
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void gemm_compute(f32x4 (&acc)[G::TN][G::TM],
+                                             const bf16* sA, const bf16* sB, int wm,
+                                             int wn, int lane) {
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+  for (int ks = 0; ks < G::BK / 32; ++ks) {
+    bf16x8 wf[G::TN], af[G::TM];
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+      wf[j] = *(const bf16x8*)(sB + (wn * G::WN + j * 16 + fr) * G::LDS + ks * 32 + fk);
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+      af[i] = *(const bf16x8*)(sA + (wm * G::WM + i * 16 + fr) * G::LDS + ks * 32 + fk);
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+  }
+}
+
+// Tile (tm, tn) of the p-th block of a split: XCD-aware when the tile grid
+// splits evenly into 8 column groups, else row-major.
+__device__ __forceinline__ void gemm_tile_of(int p, int tiles_m, int tiles_n, int& tm,
+                                             int& tn) {
+  if ((tiles_n & 7) == 0) {
+    const int xcd = p & 7, local = p >> 3, gw = tiles_n >> 3;
+    tm = local / gw;
+    tn = xcd * gw + (local - tm * gw);
+  } else {
+    tm = p / tiles_n;
+    tn = p - tm * tiles_n;
+  }
+}
+
+template <int TM, int TN, class Epi>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
-    Epi epi) {
-  constexpr int WAVES_N = BN / WN;
-  constexpr int NT = (BM / WM) * WAVES_N * 64;
-  constexpr int BK = 64;
-  constexpr int LDS = BK + 8;  // padded row stride (bf16 elements, 144 B)
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
-  constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;
-  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/threads");
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * LDS];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * LDS];
+    int k_len, Epi epi) {
+  using G = GemmCfg<TM, TN>;
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][G::BM * G::LDS];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][G::BN * G::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave - wm * WAVES_N;
-  const int tiles_n = N / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = N / G::BN;
+  const int tiles_m = (M + G::BM - 1) / G::BM;
+  const int tiles = tiles_m * tiles_n;
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  gemm_tile_of(blockIdx.x - split * tiles, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * G::BM, n0 = tn * G::BN;
+  const int kb = split * k_len;
+  const int KT = k_len / G::BK;
 
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  f32x4 acc[G::TN][G::TM];
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * NT, row = c / CPR, kc = c - row * CPR;
-      const int gm = min(m0 + row, M - 1);
-      ra[i] = *(const uint4*)(A + (size_t)gm * K + k0 + kc * 8);
-    }
+  for (int j = 0; j < G::TN; ++j)
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * NT, row = c / CPR, kc = c - row * CPR;
-      rb[i] = *(const uint4*)(W + (size_t)(n0 + row) * K + k0 + kc * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * NT, row = c / CPR, kc = c - row * CPR;
-      *(uint4*)(&sA[buf][row * LDS + kc * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * NT, row = c / CPR, kc = c - row * CPR;
-      *(uint4*)(&sB[buf][row * LDS + kc * 8]) = rb[i];
-    }
-  };
+    for (int i = 0; i < G::TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int KT = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8*)(&sA[cur][(wm * WM + i * 16 + frag_row) * LDS +
-                                          ks * 32 + frag_k]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const bf16x8*)(&sB[cur][(wn * WN + j * 16 + frag_row) * LDS +
-                                           ks * 32 + frag_k]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(cur ^ 1);
+  {
+    u32x4 ra[G::CA], rb[G::CB];
+    gemm_gload<G>(ra, rb, A, W, m0, n0, M, K, kb, tid);
+    gemm_lstore<G>(ra, rb, sA[0], sB[0], tid);
     __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) gemm_gload<G>(ra, rb, A, W, m0, n0, M, K, kb + (kt + 1) * G::BK, tid);
+      gemm_compute<G>(acc, sA[cur], sB[cur], wm, wn, lane);
+      if (kt + 1 < KT) gemm_lstore<G>(ra, rb, sA[cur ^ 1], sB[cur ^ 1], tid);
+      __syncthreads();
+    }
   }
 
+  const int mb = m0 + wm * G::WM + (lane & 15);
+  const int nb = n0 + wn * G::WN + 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < G::TN; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + r;
-        const int n = n0 + wn * WN + j * 16 + (lane & 15);
-        epi(m, n, acc[i][j][r]);
-      }
+    for (int i = 0; i < G::TM; ++i) epi.store4(mb + i * 16, nb + j * 16, acc[j][i]);
+}
+
+// h[m, n] += bias[n] + sum_s slab[s][m][n], summed in split order.
+__global__ __launch_bounds__(256) void splitk_resid_kernel(
+    const float* __restrict__ slab, const float* __restrict__ bias,
+    float* __restrict__ h, int M, int N, int S) {
+  const size_t total4 = (size_t)M * N / 4;
+  const size_t plane = (size_t)M * N;
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < total4; e += (size_t)gridDim.x * 256) {
+    const size_t o = e * 4;
+    const int n = (int)(o % N);
+    float4 acc = *(const float4*)(slab + o);
+    for (int s = 1; s < S; ++s) {
+      const float4 v = *(const float4*)(slab + s * plane + o);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const float4 b = *(const float4*)(bias + n);
+    float4 hv = *(float4*)(h + o);
+    hv.x += acc.x + b.x;
+    hv.y += acc.y + b.y;
+    hv.z += acc.z + b.z;
+    hv.w += acc.w + b.w;
+    *(float4*)(h + o) = hv;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -182,18 +335,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_kernel(
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ W, int M, int N,
-    int K, Epi epi) {
+    int K, int k_len, Epi epi) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float sA[BK][BM + 4];
   __shared__ float sB[BK][BN + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int tiles_n = (N + BN - 1) / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int tiles = ((M + BM - 1) / BM) * tiles_n;
+  const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   float acc[4][4] = {};
   const int lrow = tid >> 2, lk = (tid & 3) * 4;
   const int gm = min(m0 + lrow, M - 1), gn = min(n0 + lrow, N - 1);
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = split * k_len; k0 < (split + 1) * k_len; k0 += BK) {
     const float4 va = *(const float4*)(A + (size_t)gm * K + k0 + lk);
     const float4 vb = *(const float4*)(W + (size_t)gn * K + k0 + lk);
     __syncthreads();
@@ -224,36 +379,98 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx + 16 * j;
-      if (n < N) epi(m0 + ty + 16 * i, n, acc[i][j]);
+      if (n < N) epi(m0 + ty + 16 * i, n, acc[i][j], split);
     }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <class Epi>
-static hipError_t run_bf16(const void* A, const void* W, int M, int N, int K,
-                           const Epi& epi, hipStream_t st) {
-  constexpr int BM = 128;
-  if (N % 128 == 0) {
-    const int tiles = ((M + BM - 1) / BM) * (N / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, 128, 64, 64, Epi>), dim3(tiles),
-                       dim3(256), 0, st, (const bf16*)A, (const bf16*)W, M, N, K, epi);
-  } else {
-    const int tiles = ((M + BM - 1) / BM) * (N / 64);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, 64, 32, 64, Epi>), dim3(tiles),
-                       dim3(256), 0, st, (const bf16*)A, (const bf16*)W, M, N, K, epi);
+// Tile configurations (TM, TN) of the bf16 GEMM, and the choice per shape:
+// the fewest "rounds" of 256 blocks (one per CU) weighted by the work per
+// block, with K splits allowed only where the epilogue can reduce them.
+struct TileChoice {
+  int tm, tn, splits;
+};
+static const int kTileCfgs[][2] = {{7, 4}, {7, 3}, {7, 2}, {4, 4}, {4, 2}};
+
+TileChoice gemm_choose(int M, int N, int K, bool allow_split) {
+  TileChoice best{4, 2, 1};
+  double best_cost = 1e300;
+  for (auto& c : kTileCfgs) {
+    const int BM = 32 * c[0], BN = 32 * c[1];
+    if (N % BN) continue;
+    const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
+    for (int s = 1; s <= (allow_split ? 8 : 1); s *= 2) {
+      if (K % (64 * s) || (s > 1 && K / s < 256)) break;
+      const long blocks = tiles * s;
+      const long rounds = (blocks + 255) / 256;
+      // per-block time ~ MFMA work + a fixed pipeline fill per block
+      const double per_block = (double)BM * BN * (K / s) * (1.0 + 0.35 * 64.0 / BN) +
+                               (double)BM * BN * 64 * 6;
+      const double cost = rounds * per_block * (s > 1 ? 1.02 : 1.0);
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = TileChoice{c[0], c[1], s};
+      }
+    }
   }
+  return best;
+}
+
+template <int TM, int TN, class Epi>
+static void launch_cfg(const void* A, const void* W, int M, int N, int K, int splits,
+                       const Epi& epi, hipStream_t st) {
+  using G = GemmCfg<TM, TN>;
+  const int tiles = ((M + G::BM - 1) / G::BM) * (N / G::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, Epi>), dim3(tiles * splits), dim3(256), 0,
+                     st, (const bf16*)A, (const bf16*)W, M, N, K, K / splits, epi);
+}
+
+template <class Epi>
+static hipError_t run_bf16_cfg(const void* A, const void* W, int M, int N, int K,
+                               TileChoice c, const Epi& epi, hipStream_t st) {
+  if (c.tm == 7 && c.tn == 4) launch_cfg<7, 4>(A, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 7 && c.tn == 3) launch_cfg<7, 3>(A, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 7 && c.tn == 2) launch_cfg<7, 2>(A, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 4 && c.tn == 4) launch_cfg<4, 4>(A, W, M, N, K, c.splits, epi, st);
+  else launch_cfg<4, 2>(A, W, M, N, K, c.splits, epi, st);
   return hipGetLastError();
 }
 
 template <class Epi>
+static hipError_t run_bf16(const void* A, const void* W, int M, int N, int K,
+                           const Epi& epi, hipStream_t st) {
+  TileChoice c = gemm_choose(M, N, K, false);
+  return run_bf16_cfg(A, W, M, N, K, c, epi, st);
+}
+
+int gemm_resid_splits(int M, int N, int K) { return gemm_choose(M, N, K, true).splits; }
+
+static int tiles_of(TileChoice c, int M, int N) {
+  return ((M + 32 * c.tm - 1) / (32 * c.tm)) * (N / (32 * c.tn));
+}
+
+template <class Epi>
 static hipError_t run_f32(const void* A, const void* W, int M, int N, int K,
-                          const Epi& epi, hipStream_t st) {
+                          const Epi& epi, hipStream_t st, int splits = 1) {
   const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  hipLaunchKernelGGL((gemm_f32_kernel<Epi>), dim3(tiles), dim3(256), 0, st,
-                     (const float*)A, (const float*)W, M, N, K, epi);
+  hipLaunchKernelGGL((gemm_f32_kernel<Epi>), dim3(tiles * splits), dim3(256), 0, st,
+                     (const float*)A, (const float*)W, M, N, K, K / splits, epi);
   return hipGetLastError();
+}
+
+int head_splits(int M, int N, int K) {
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int s = 1;
+  while (s < 16 && tiles * s * 2 <= 512 && K % (16 * s * 2) == 0 && K / (s * 2) >= 64) s *= 2;
+  return s;
+}
+
+hipError_t launch_gemm_f32_planes(const float* A, const float* W, float* out, int M,
+                                  int N, int K, int splits, hipStream_t st) {
+  EpiPlane e{out, M, N};
+  return run_f32(A, W, M, N, K, e, st, splits);
 }
 
 hipError_t launch_gemm_qkv(bool bf, const void* A, const void* W,
@@ -271,9 +488,24 @@ hipError_t launch_gemm_qkv(bool bf, const void* A, const void* W,
 
 hipError_t launch_gemm_resid(bool bf, const void* A, const void* W,
                              const float* bias, float* h, int M, int N, int K,
-                             hipStream_t st) {
-  EpiResid e{bias, h, M, N};
-  return bf ? run_bf16(A, W, M, N, K, e, st) : run_f32(A, W, M, N, K, e, st);
+                             float* slab, hipStream_t st) {
+  if (!bf) {
+    EpiResid e{bias, h, M, N};
+    return run_f32(A, W, M, N, K, e, st);
+  }
+  TileChoice c = gemm_choose(M, N, K, slab != nullptr);
+  if (c.splits == 1) {
+    EpiResid e{bias, h, M, N};
+    return run_bf16_cfg(A, W, M, N, K, c, e, st);
+  }
+  EpiSlab es{slab, M, N, tiles_of(c, M, N)};
+  hipError_t err = run_bf16_cfg(A, W, M, N, K, c, es, st);
+  if (err != hipSuccess) return err;
+  const size_t total4 = (size_t)M * N / 4;
+  const int blocks = (int)std::min<size_t>((total4 + 255) / 256, 2048);
+  hipLaunchKernelGGL(splitk_resid_kernel, dim3(blocks), dim3(256), 0, st, slab, bias, h,
+                     M, N, c.splits);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_gelu(bool bf, const void* A, const void* W,

@@ -28,7 +28,9 @@ hipError_t launch_init_block(float* x, const float* x_init, int mode, int N,
 hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st);
 
 struct AffineArgs {
-  const float* head;   // [N*R, 2C]: [mu | raw] per row
+  const float* head;   // head_splits planes of [N*R, 2C]: partial [mu | raw] per row
+  const float* head_bias;  // [2C] added to the plane sum, or NULL
+  int head_splits;
   const float* z;      // inverse: z tokens [N, L, C]
   float* x;            // inverse: x tokens, updated in place; forward: x tokens (read)
   float* zout;         // forward: z tokens (written)
@@ -40,7 +42,7 @@ struct AffineArgs {
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);
-int affine_groups(int R, int C);   // G, the partial slots per sample
+int affine_groups(int N, int R, int C);   // G, the partial slots per sample
 
 // ---- GEMMs: y[M, N] = A[M, K] W[N, K]^T + bias -----------------------------
 struct QKVDst {
@@ -52,21 +54,35 @@ struct QKVDst {
 hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* W,
                            const float* bias, int M, int N, int K, QKVDst dst,
                            hipStream_t st);
+// h += A W^T + bias.  With a non-NULL slab ([S][M][N] fp32, S =
+// gemm_resid_splits(M, N, K)) the bf16 path splits K and reduces the partial
+// planes in a fixed order in a second kernel.
 hipError_t launch_gemm_resid(bool bf16, const void* A, const void* W,
                              const float* bias, float* h, int M, int N, int K,
-                             hipStream_t st);
+                             float* slab, hipStream_t st);
+int gemm_resid_splits(int M, int N, int K);
 hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* W,
                             const float* bias, void* out, int M, int N, int K,
                             hipStream_t st);
 hipError_t launch_gemm_f32out(bool bf16, const void* A, const void* W,
                               const float* bias, float* out, int M, int N, int K,
                               hipStream_t st);
+// fp32 GEMM split over K into `splits` partial planes out[s][M][N] (no bias);
+// head_splits(M, N, K) picks the split count.
+hipError_t launch_gemm_f32_planes(const float* A, const float* W, float* out, int M,
+                                  int N, int K, int splits, hipStream_t st);
+int head_splits(int M, int N, int K);
 
 // ---- attention ---------------------------------------------------------------
 // out[m, h*dh:(h+1)*dh] = softmax(q k^T / sqrt(dh)) v over cached keys
 // 0..pos_base+t (inclusive) for chunk row m = n*R + t.
+// bf16: long key ranges are split into chunks whose partial results go to
+// `part` (attention_partial_floats(...) floats) and are merged by a second
+// kernel.
 hipError_t launch_attention(bool bf16, const void* q, const void* kc,
-                            const void* vt, void* out, int N, int R, int H,
-                            int dh, int d, int Lcap, int pos_base, hipStream_t st);
+                            const void* vt, void* out, float* part, int N, int R,
+                            int H, int dh, int d, int Lcap, int pos_base,
+                            hipStream_t st);
+size_t attention_partial_floats(int N, int R, int H, int dh, int pos_base);
 
 }  // namespace af

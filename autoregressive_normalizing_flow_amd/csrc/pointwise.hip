@@ -203,16 +203,19 @@ hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st) {
 // Fused affine kernel.
 //   mode 0 (inverse):  x <- mu + exp(ls) * z,  sums (x_new - x_old)^2, x_new^2
 //   mode 1 (forward):  z <- (x - mu) * exp(-ls), sums ls, #non-finite z
-// with ls = log sigma = 0.5 tanh(raw).  Each block reduces its range of one
-// sample into partials; the last block to finish (atomic ticket) sums the
-// partials in a fixed order, so results do not depend on block scheduling.
+// with ls = log sigma = 0.5 tanh(raw) and [mu | raw] = bias + the sum of the
+// head GEMM's split-K partial planes, added in plane order.  Work is split
+// into per-sample ranges of 4-channel quads (float4 I/O when C % 4 == 0);
+// each block reduces its range into partials and the last block to finish
+// (atomic ticket) sums the partials in a fixed order, so results do not
+// depend on block scheduling.
 // ---------------------------------------------------------------------------
-constexpr int AFF_EPT = 4;                 // elements per thread per block range
-constexpr int AFF_EB = 256 * AFF_EPT;      // elements per block
-
-int affine_groups(int R, int C) {
-  long total = (long)R * C;
-  return (int)((total + AFF_EB - 1) / AFF_EB);
+int affine_groups(int N, int R, int C) {
+  const long quads = ((long)R * C + 3) / 4;
+  long g = (quads + 1023) / 1024;           // ~4 quads per thread
+  const long cap = std::max(1, 2048 / std::max(N, 1));
+  if (g > cap) g = cap;
+  return (int)std::max(1L, g);
 }
 
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
@@ -229,34 +232,85 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   b = (red[1] + red[3]) + (red[5] + red[7]);
 }
 
-template <int MODE>
+template <int MODE, bool VEC>
 __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
   __shared__ float red[8];
   __shared__ unsigned ticket;
   const int n = blockIdx.y, g = blockIdx.x;
   const int C = a.C;
-  const long total = (long)a.R * C;
-  const long e_end = min(total, (long)(g + 1) * AFF_EB);
+  const int W = VEC ? 4 : 1;                      // channels per item
+  const unsigned CW = (unsigned)(C / W);          // items per token
+  const unsigned items = (unsigned)a.R * CW;
+  const unsigned chunk = (items + G - 1) / G;
+  const unsigned i_end = min(items, (g + 1) * chunk);
+  const size_t plane = (size_t)a.N * a.R * 2 * C;
   float s0 = 0.f, s1 = 0.f;
-  for (long e = (long)g * AFF_EB + threadIdx.x; e < e_end; e += 256) {
-    const int t = (int)(e / C), c = (int)(e - (long)t * C);
+  for (unsigned it = g * chunk + threadIdx.x; it < i_end; it += 256) {
+    const unsigned t = it / CW;
+    const int c = (int)(it - t * CW) * W;
     const size_t row = (size_t)n * a.R + t;
-    const float mu = a.head[row * 2 * C + c];
-    const float raw = a.head[row * 2 * C + C + c];
-    const float ls = 0.5f * tanhf(raw);
-    const size_t xi = ((size_t)n * a.L + storage_index(a.s + t, a.L, a.dir)) * C + c;
+    const size_t xi = ((size_t)n * a.L + storage_index(a.s + (int)t, a.L, a.dir)) * C + c;
+    const float* hp = a.head + row * 2 * C + c;
+    float mu[W], raw[W], in[W], out[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      mu[q] = a.head_bias ? a.head_bias[c + q] : 0.f;
+      raw[q] = a.head_bias ? a.head_bias[C + c + q] : 0.f;
+    }
+    for (int sp = 0; sp < a.head_splits; ++sp) {
+      const float* hs = hp + sp * plane;
+      if (VEC) {
+        const float4 m4 = *(const float4*)hs;
+        const float4 r4 = *(const float4*)(hs + C);
+        mu[0] += m4.x; mu[1 % W] += m4.y; mu[2 % W] += m4.z; mu[3 % W] += m4.w;
+        raw[0] += r4.x; raw[1 % W] += r4.y; raw[2 % W] += r4.z; raw[3 % W] += r4.w;
+      } else {
+        mu[0] += hs[0];
+        raw[0] += hs[C];
+      }
+    }
     if (MODE == 0) {
-      const float xo = a.x[xi];
-      const float xn = mu + expf(ls) * a.z[xi];
-      a.x[xi] = xn;
-      const float df = xn - xo;
-      s0 += df * df;
-      s1 += xn * xn;
+      // in = x_old, z read from a.z
+      if (VEC) {
+        const float4 xo = *(const float4*)(a.x + xi);
+        const float4 zz = *(const float4*)(a.z + xi);
+        in[0] = xo.x; in[1 % W] = xo.y; in[2 % W] = xo.z; in[3 % W] = xo.w;
+        out[0] = zz.x; out[1 % W] = zz.y; out[2 % W] = zz.z; out[3 % W] = zz.w;
+      } else {
+        in[0] = a.x[xi];
+        out[0] = a.z[xi];
+      }
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        const float xn = mu[q] + expf(0.5f * tanhf(raw[q])) * out[q];
+        const float df = xn - in[q];
+        s0 += df * df;
+        s1 += xn * xn;
+        out[q] = xn;
+      }
+      if (VEC)
+        *(float4*)(a.x + xi) = float4{out[0], out[1 % W], out[2 % W], out[3 % W]};
+      else
+        a.x[xi] = out[0];
     } else {
-      const float zv = (a.x[xi] - mu) * expf(-ls);
-      a.zout[xi] = zv;
-      s0 += ls;
-      s1 += isfinite(zv) ? 0.f : 1.f;
+      if (VEC) {
+        const float4 xv = *(const float4*)(a.x + xi);
+        in[0] = xv.x; in[1 % W] = xv.y; in[2 % W] = xv.z; in[3 % W] = xv.w;
+      } else {
+        in[0] = a.x[xi];
+      }
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        const float ls = 0.5f * tanhf(raw[q]);
+        const float zv = (in[q] - mu[q]) * expf(-ls);
+        out[q] = zv;
+        s0 += ls;
+        s1 += isfinite(zv) ? 0.f : 1.f;
+      }
+      if (VEC)
+        *(float4*)(a.zout + xi) = float4{out[0], out[1 % W], out[2 % W], out[3 % W]};
+      else
+        a.zout[xi] = out[0];
     }
   }
   block_sum2(s0, s1, red);
@@ -294,12 +348,16 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
 }
 
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st) {
-  const int G = affine_groups(a.R, a.C);
+  const int G = affine_groups(a.N, a.R, a.C);
   dim3 grid(G, a.N);
-  if (mode == 0)
-    hipLaunchKernelGGL(affine_kernel<0>, grid, dim3(256), 0, st, a, G);
-  else
-    hipLaunchKernelGGL(affine_kernel<1>, grid, dim3(256), 0, st, a, G);
+  const bool vec = (a.C % 4) == 0;
+  if (mode == 0) {
+    if (vec) hipLaunchKernelGGL((affine_kernel<0, true>), grid, dim3(256), 0, st, a, G);
+    else hipLaunchKernelGGL((affine_kernel<0, false>), grid, dim3(256), 0, st, a, G);
+  } else {
+    if (vec) hipLaunchKernelGGL((affine_kernel<1, true>), grid, dim3(256), 0, st, a, G);
+    else hipLaunchKernelGGL((affine_kernel<1, false>), grid, dim3(256), 0, st, a, G);
+  }
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -52,7 +53,7 @@ struct BlockW {
 // Byte offsets of the workspace regions for (batch, rows).
 struct WsLayout {
   size_t cache_layer;  // bytes of one layer's K (or V) cache
-  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, xtmp, total;
+  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, slab, attn_part, xtmp, total;
 };
 
 enum KClass { K_EMBED, K_LN, K_QKV, K_O, K_MLP1, K_MLP2, K_HEAD, K_ATTN, K_AFFINE, K_NCLASS };
@@ -79,6 +80,18 @@ struct af_plan {
 
 namespace {
 
+// Rows of head partial planes needed for any pass of at most M rows:
+// max over m <= M of head_splits(m) * m.
+size_t head_plane_rows(size_t M, int n_out, int d) {
+  size_t best = M;
+  for (size_t m = 64; m < M + 64; m += 64) {
+    const size_t mm = m < M ? m : M;
+    const size_t r = (size_t)af::head_splits((int)mm, n_out, d) * mm;
+    if (r > best) best = r;
+  }
+  return best;
+}
+
 WsLayout layout(const af_plan* p, int N, int rows) {
   WsLayout w{};
   const af_block_cfg& c = p->cfg;
@@ -93,10 +106,24 @@ WsLayout layout(const af_plan* p, int N, int rows) {
   w.att = off;      off += align256(M * c.d * p->esz);
   w.u = off;        off += align256(M * p->dmlp * p->esz);
   w.hf = off;       off += align256(M * c.d * 4);
-  w.head = off;     off += align256(M * 2 * c.C * 4);
-  w.partials = off; off += align256((size_t)N * af::affine_groups(rows, c.C) * 2 * 4);
+  w.head = off;     off += align256(head_plane_rows(M, 2 * c.C, c.d) * 2 * c.C * 4);
+  w.partials = off; off += align256((size_t)N * af::affine_groups(N, rows, c.C) * 2 * 4);
   w.res = off;      off += align256((size_t)N * 2 * 4);
   w.counter = off;  off += 256;
+  w.slab = off;
+  if (p->bf) {
+    const int s1 = af::gemm_resid_splits((int)M, c.d, c.d);
+    const int s2 = af::gemm_resid_splits((int)M, c.d, p->dmlp);
+    const int s = s1 > s2 ? s1 : s2;
+    if (s > 1) off += align256((size_t)s * M * c.d * 4);
+  }
+  w.attn_part = off;
+  if (p->bf) {
+    // key-chunk partials: at most max(1024, N*H*query tiles) units of
+    // 128 x (dh + 2) floats
+    const size_t units = std::max<size_t>(1024, (size_t)N * c.n_heads * ((rows + 127) / 128));
+    off += align256(units * 128 * (p->dh + 2) * 4);
+  }
   w.xtmp = off;
   if (p->T > 1) off += align256((size_t)N * c.max_len * c.C * 4);
   w.total = off;
@@ -159,18 +186,20 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
     af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base};
     LAUNCH(K_QKV, af::launch_gemm_qkv(p->bf, a, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
     if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
-    LAUNCH(K_ATTN, af::launch_attention(p->bf, q, kc, vt, att, ps.N, ps.R, c.n_heads,
+    LAUNCH(K_ATTN, af::launch_attention(p->bf, q, kc, vt, att, (float*)(ws + w.attn_part),
+                                        ps.N, ps.R, c.n_heads,
                                         p->dh, d, p->Lcap, pos_base, st));
-    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, lw.w_o, lw.b_o, h, M, d, d, st));
+    float* slab = (float*)(ws + w.slab);
+    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, lw.w_o, lw.b_o, h, M, d, d, slab, st));
     LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, p->bf, M, d, st));
     LAUNCH(K_MLP1, af::launch_gemm_gelu(p->bf, a, lw.w_1, lw.b_1, u, M, p->dmlp, d, st));
-    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, lw.w_2, lw.b_2, h, M, d, p->dmlp, st));
+    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, lw.w_2, lw.b_2, h, M, d, p->dmlp, slab, st));
   }
   float* hf = (float*)(ws + w.hf);
   float* head = (float*)(ws + w.head);
   LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
-  LAUNCH(K_HEAD, af::launch_gemm_f32out(false, hf, bw.w_head, bw.b_head, head, M,
-                                        2 * c.C, d, st));
+  LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
+                                            af::head_splits(M, 2 * c.C, d), st));
   return AF_OK;
 }
 
@@ -309,7 +338,9 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
     float* dst = ((p->T - 1 - t) % 2 == 0) ? z : xtmp;
     Pass ps{cur, nullptr, N, L, 0, L, 0, t & 1, false};
     if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st)) return s;
-    af::AffineArgs aa{(const float*)(ws + w.head), nullptr, const_cast<float*>(cur), dst,
+    af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
+                      af::head_splits(N * L, 2 * C, p->cfg.d), nullptr,
+                      const_cast<float*>(cur), dst,
                       N, L, C, L, 0, t & 1, (float*)(ws + w.partials),
                       (float*)(ws + w.res), (unsigned*)(ws + w.counter), logdet};
     LAUNCH(K_AFFINE, af::launch_affine(1, aa, st));
@@ -370,7 +401,8 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       const int kmax = max_iters <= 0 ? R : (max_iters < R ? max_iters : R);
       AF_HIP(af::launch_init_block(xo, x_init, (int)init, N, R, C, L, s, dir, frame_len, st));
       Pass ps{xo, x_last, N, L, s, R, prefix_len, dir, false};
-      af::AffineArgs aa{(const float*)(ws + w.head), zin, xo, nullptr, N, R, C, L, s,
+      af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
+                        af::head_splits(N * R, 2 * C, p->cfg.d), zin, xo, nullptr, N, R, C, L, s,
                         dir, (float*)(ws + w.partials), res,
                         (unsigned*)(ws + w.counter), nullptr};
       int k = 0;
@@ -449,7 +481,7 @@ af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
 
 size_t afk_affine_partials_bytes(int N, int rows_per_sample, int C) {
   if (N < 1 || rows_per_sample < 1 || C < 1) return 0;
-  return (size_t)N * af::affine_groups(rows_per_sample, C) * 2 * sizeof(float) + 256;
+  return (size_t)N * af::affine_groups(N, rows_per_sample, C) * 2 * sizeof(float) + 256;
 }
 
 af_status afk_affine(int mode, const float* head, const float* src, float* dst,
@@ -465,7 +497,7 @@ af_status afk_affine(int mode, const float* head, const float* src, float* dst,
   char* pb = (char*)partials;
   unsigned* counter = (unsigned*)(pb + need - 256);
   AF_HIP(af::launch_fill_u32(counter, 0u, 1, st));
-  af::AffineArgs aa{head, mode == 0 ? src : nullptr,
+  af::AffineArgs aa{head, nullptr, 1, mode == 0 ? src : nullptr,
                     mode == 0 ? dst : const_cast<float*>(src),
                     mode == 1 ? dst : nullptr, N, rows_per_sample, C,
                     rows_per_sample, 0, 0, (float*)pb, res, counter, nullptr};
