@@ -43,6 +43,12 @@ struct AttnArgs {
   const bf16* kc;
   const bf16* vt;
   bf16* out;
+  // split mode (higher-precision forward): lo halves of q, K, Vt and the
+  // output, so that every operand is the bf16 pair hi + lo; NULL otherwise
+  const bf16* q_lo;
+  const bf16* kc_lo;
+  const bf16* vt_lo;
+  bf16* out_lo;
   float* part;     // partial slots: [unit][ATT_QT][DH] O, then [ATT_QT] m, [ATT_QT] l
   int R, H, d, Lcap, pos_base, KC, U_nh;
   float scale_log2;
@@ -53,7 +59,9 @@ __device__ __forceinline__ int att_chunks(int qt, int R, int pos_base, int KC) {
   return (nk + KC - 1) / KC;
 }
 
-template <int DH>
+// SPLIT: products of bf16 pairs keep three of the four partial products,
+// (a + a')(b + b') ~ ab + a'b + ab', for both S = K Q^T and O = P V.
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int QWAVE = 32, QB = QWAVE / 16;
   constexpr int KB = ATT_KT / 16, KS = DH / 32, DB = DH / 16;
@@ -61,6 +69,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int CK = ATT_KT * DH / 8 / 256;  // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) bf16 sK[2][ATT_KT * KLDS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][DH * VLDS];
+  __shared__ __attribute__((aligned(16))) bf16 sKl[2][SPLIT ? ATT_KT * KLDS : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sVl[2][SPLIT ? DH * VLDS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // unit -> (sample, head, query tile, chunk)
@@ -85,18 +95,22 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const size_t hb = (size_t)n * a.H + head;
   const bf16* kbase = a.kc + hb * Lcap * DH;
   const bf16* vbase = a.vt + hb * DH * Lcap;
+  const bf16* klbase = SPLIT ? a.kc_lo + hb * Lcap * DH : nullptr;
+  const bf16* vlbase = SPLIT ? a.vt_lo + hb * DH * Lcap : nullptr;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  bf16x8 qf[QB][KS];
+  bf16x8 qf[QB][KS], qfl[QB][KS];
   int qpos[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int t = q_lo + wave * QWAVE + qb * 16 + l16;
     qpos[qb] = pos_base + t;
-    const bf16* qrow = a.q + ((size_t)n * R + min(t, R - 1)) * d + head * DH;
+    const size_t qo = ((size_t)n * R + min(t, R - 1)) * d + head * DH;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = *(const bf16x8*)(qrow + ks * 32 + lg * 8);
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[qb][ks] = *(const bf16x8*)(a.q + qo + ks * 32 + lg * 8);
+      if (SPLIT) qfl[qb][ks] = *(const bf16x8*)(a.q_lo + qo + ks * 32 + lg * 8);
+    }
   }
 
   float m_run[QB], l_run[QB];
@@ -109,7 +123,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) acc_o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 rk[CK], rv[CK];
+  u32x4 rk[CK], rv[CK], rkl[CK], rvl[CK];
   // keys outside [k_begin, k_end) are loaded as zeros (masked below)
   auto gload = [&](int kt) {
     const int k0 = (t_begin + kt) * ATT_KT;
@@ -118,20 +132,27 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       const int c = tid + i * 256;
       const int key = c / (DH / 8), dc = c - key * (DH / 8);
       const int kk = k0 + key;
-      rk[i] = kk < k_end ? *(const u32x4*)(kbase + (size_t)kk * DH + dc * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+      const bool kin = kk < k_end;
+      rk[i] = kin ? *(const u32x4*)(kbase + (size_t)kk * DH + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+      if (SPLIT)
+        rkl[i] = kin ? *(const u32x4*)(klbase + (size_t)kk * DH + dc * 8)
+                     : u32x4{0u, 0u, 0u, 0u};
       const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
       const int kk0 = k0 + kc8 * 8;  // k0 + 64 <= Lcap: always in bounds
       u32x4 v = *(const u32x4*)(vbase + (size_t)drow * Lcap + kk0);
+      u32x4 vl = SPLIT ? *(const u32x4*)(vlbase + (size_t)drow * Lcap + kk0)
+                       : u32x4{0u, 0u, 0u, 0u};
       if (kk0 + 8 > k_end) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const unsigned lo_ok = (kk0 + 2 * e) < k_end ? 0xFFFFu : 0u;
           const unsigned hi_ok = (kk0 + 2 * e + 1) < k_end ? 0xFFFF0000u : 0u;
           v[e] &= (lo_ok | hi_ok);
+          vl[e] &= (lo_ok | hi_ok);
         }
       }
       rv[i] = v;
+      rvl[i] = vl;
     }
   };
   auto lstore = [&](int buf) {
@@ -140,8 +161,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       const int c = tid + i * 256;
       const int key = c / (DH / 8), dc = c - key * (DH / 8);
       *(u32x4*)(&sK[buf][key * KLDS + dc * 8]) = rk[i];
+      if (SPLIT) *(u32x4*)(&sKl[buf][key * KLDS + dc * 8]) = rkl[i];
       const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
       *(u32x4*)(&sV[buf][drow * VLDS + kc8 * 8]) = rv[i];
+      if (SPLIT) *(u32x4*)(&sVl[buf][drow * VLDS + kc8 * 8]) = rvl[i];
     }
   };
 
@@ -169,6 +192,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks],
                                                               s[kb][qb], 0, 0, 0);
+        if (SPLIT) {
+          const bf16x8 kfl =
+              *(const bf16x8*)(&sKl[cur][(kb * 16 + l16) * KLDS + ks * 32 + lg * 8]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qfl[qb][ks],
+                                                                s[kb][qb], 0, 0, 0);
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl, qf[qb][ks],
+                                                                s[kb][qb], 0, 0, 0);
+          }
+        }
       }
 
     // online softmax (base 2) per query
@@ -207,13 +241,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     // O^T += Vt P^T over two 32-key steps
 #pragma unroll
     for (int c = 0; c < ATT_KT / 32; ++c) {
-      bf16x8 pf[QB];
+      bf16x8 pf[QB], pfl[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pf[qb][r] = (bf16)s[2 * c][qb][r];
           pf[qb][4 + r] = (bf16)s[2 * c + 1][qb][r];
+          if (SPLIT) {
+            pfl[qb][r] = (bf16)(s[2 * c][qb][r] - (float)pf[qb][r]);
+            pfl[qb][4 + r] = (bf16)(s[2 * c + 1][qb][r] - (float)pf[qb][4 + r]);
+          }
         }
       }
 #pragma unroll
@@ -226,6 +264,19 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               vf, pf[qb], acc_o[db][qb], 0, 0, 0);
+        if (SPLIT) {
+          const bf16* vlrow = &sVl[cur][(db * 16 + l16) * VLDS + c * 32 + lg * 4];
+          const bf16x4 llo = *(const bf16x4*)vlrow;
+          const bf16x4 lhi = *(const bf16x4*)(vlrow + 16);
+          const bf16x8 vfl = {llo[0], llo[1], llo[2], llo[3], lhi[0], lhi[1], lhi[2], lhi[3]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                vf, pfl[qb], acc_o[db][qb], 0, 0, 0);
+            acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                vfl, pf[qb], acc_o[db][qb], 0, 0, 0);
+          }
+        }
       }
     }
     if (kt + 1 < n_tiles) lstore(cur ^ 1);
@@ -242,13 +293,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     if (n_chunks == 1) {
       if (t < R) {
         const float inv = 1.0f / l;
-        bf16* orow = a.out + ((size_t)n * R + t) * d + head * DH;
+        const size_t oo = ((size_t)n * R + t) * d + head * DH;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          bf16x4 o;
+          bf16x4 o, ol;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc_o[db][qb][r] * inv);
-          *(bf16x4*)(orow + db * 16 + lg * 4) = o;
+          for (int r = 0; r < 4; ++r) {
+            const float y = acc_o[db][qb][r] * inv;
+            o[r] = (bf16)y;
+            ol[r] = (bf16)(y - (float)o[r]);
+          }
+          *(bf16x4*)(a.out + oo + db * 16 + lg * 4) = o;
+          if (SPLIT) *(bf16x4*)(a.out_lo + oo + db * 16 + lg * 4) = ol;
         }
       }
     } else {
@@ -297,8 +353,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt)
       l += w * slot[ATT_QT * DH + ATT_QT + tq];
     }
     const float inv = 1.0f / l;
-    bf16x4 r = {(bf16)(o.x * inv), (bf16)(o.y * inv), (bf16)(o.z * inv), (bf16)(o.w * inv)};
-    *(bf16x4*)(a.out + ((size_t)n * a.R + t) * a.d + head * DH + e) = r;
+    const float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    bf16x4 r, rl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = (bf16)y[j];
+      rl[j] = (bf16)(y[j] - (float)r[j]);
+    }
+    const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + e;
+    *(bf16x4*)(a.out + oo) = r;
+    if (a.out_lo) *(bf16x4*)(a.out_lo + oo) = rl;
   }
 }
 
@@ -369,34 +433,38 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   for (int e = 0; e < DH; ++e) orow[e] = acc[e] * inv;
 }
 
+template <int DH, bool SPLIT>
+static void attn_launch(const AttnArgs& a, dim3 grid, dim3 comb, bool multi, int n_qt,
+                        hipStream_t st) {
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
+  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(256), 0, st, a, n_qt);
+}
+
 hipError_t launch_attention(bool bf, const void* q, const void* kc,
                             const void* vt, void* out, float* part, int N, int R,
                             int H, int dh, int d, int Lcap, int pos_base,
-                            hipStream_t st) {
+                            hipStream_t st, const AttnSplit* split) {
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf) {
     const int n_qt = (R + ATT_QT - 1) / ATT_QT;
     const int KC = attention_chunk(N, R, H, pos_base);
     const int U_nh = att_units(R, pos_base, KC, n_qt);
-    AttnArgs a{(const bf16*)q, (const bf16*)kc, (const bf16*)vt, (bf16*)out, part,
+    AttnArgs a{(const bf16*)q, (const bf16*)kc, (const bf16*)vt, (bf16*)out,
+               split ? (const bf16*)split->q_lo : nullptr,
+               split ? (const bf16*)split->kc_lo : nullptr,
+               split ? (const bf16*)split->vt_lo : nullptr,
+               split ? (bf16*)split->out_lo : nullptr, part,
                R, H, d, Lcap, pos_base, KC, U_nh, scale * 1.4426950408889634f};
     const dim3 grid(N * H * U_nh), comb(N * H * n_qt);
     const bool multi = U_nh > n_qt;
-    switch (dh) {
-      case 64:
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a);
-        if (multi) hipLaunchKernelGGL(attn_combine_kernel<64>, comb, dim3(256), 0, st, a, n_qt);
-        break;
-      case 128:
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st, a);
-        if (multi) hipLaunchKernelGGL(attn_combine_kernel<128>, comb, dim3(256), 0, st, a, n_qt);
-        break;
-      case 32:
-        hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a);
-        if (multi) hipLaunchKernelGGL(attn_combine_kernel<32>, comb, dim3(256), 0, st, a, n_qt);
-        break;
-      default:
-        return hipErrorInvalidValue;
+    switch (dh * 2 + (split ? 1 : 0)) {
+      case 128: attn_launch<64, false>(a, grid, comb, multi, n_qt, st); break;
+      case 129: attn_launch<64, true>(a, grid, comb, multi, n_qt, st); break;
+      case 256: attn_launch<128, false>(a, grid, comb, multi, n_qt, st); break;
+      case 257: attn_launch<128, true>(a, grid, comb, multi, n_qt, st); break;
+      case 64: attn_launch<32, false>(a, grid, comb, multi, n_qt, st); break;
+      case 65: attn_launch<32, true>(a, grid, comb, multi, n_qt, st); break;
+      default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }

@@ -35,6 +35,9 @@ struct EpiQKV {
   T* kc;
   T* vt;
   int M, R, d, dh, H, Lcap, pos_base;
+  T* q_lo;    // split outputs (bf16 hi + lo) of the higher-precision forward, or NULL
+  T* kc_lo;
+  T* vt_lo;
   __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     v += bias[n];
@@ -56,8 +59,14 @@ struct EpiQKV {
     const float4 b = *(const float4*)(bias + n);
     const float v0 = v[0] + b.x, v1 = v[1] + b.y, v2 = v[2] + b.z, v3 = v[3] + b.w;
     const int which = n / d, hd = n - which * d;
+    const T h0 = from_f32<T>(v0), h1 = from_f32<T>(v1), h2 = from_f32<T>(v2),
+            h3 = from_f32<T>(v3);
+    const bool split = q_lo != nullptr;
+    const float l0 = v0 - to_f32(h0), l1 = v1 - to_f32(h1), l2 = v2 - to_f32(h2),
+                l3 = v3 - to_f32(h3);
     if (which == 0) {
       store_vec4(q + (size_t)m * d + hd, v0, v1, v2, v3);
+      if (split) store_vec4(q_lo + (size_t)m * d + hd, l0, l1, l2, l3);
       return;
     }
     const int nn = m / R, t = m - nn * R, p = pos_base + t;
@@ -65,12 +74,19 @@ struct EpiQKV {
     const size_t base = (size_t)nn * H + head;
     if (which == 1) {
       store_vec4(kc + (base * Lcap + p) * dh + e, v0, v1, v2, v3);
+      if (split) store_vec4(kc_lo + (base * Lcap + p) * dh + e, l0, l1, l2, l3);
     } else {
-      T* col = vt + (base * dh + e) * Lcap + p;
-      col[0] = from_f32<T>(v0);
-      col[Lcap] = from_f32<T>(v1);
-      col[2 * (size_t)Lcap] = from_f32<T>(v2);
-      col[3 * (size_t)Lcap] = from_f32<T>(v3);
+      const size_t o = (base * dh + e) * Lcap + p;
+      vt[o] = h0;
+      vt[o + Lcap] = h1;
+      vt[o + 2 * (size_t)Lcap] = h2;
+      vt[o + 3 * (size_t)Lcap] = h3;
+      if (split) {
+        vt_lo[o] = from_f32<T>(l0);
+        vt_lo[o + Lcap] = from_f32<T>(l1);
+        vt_lo[o + 2 * (size_t)Lcap] = from_f32<T>(l2);
+        vt_lo[o + 3 * (size_t)Lcap] = from_f32<T>(l3);
+      }
     }
   }
 };
@@ -102,6 +118,7 @@ struct EpiGelu {
   const float* bias;
   T* out;
   int M, N;
+  T* out_lo;   // split output of the higher-precision forward, or NULL
   __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     out[(size_t)m * N + n] = from_f32<T>(gelu_erf(v + bias[n]));
@@ -109,8 +126,13 @@ struct EpiGelu {
   __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
     if (m >= M) return;
     const float4 b = *(const float4*)(bias + n);
-    store_vec4(out + (size_t)m * N + n, gelu_erf(v[0] + b.x), gelu_erf(v[1] + b.y),
-               gelu_erf(v[2] + b.z), gelu_erf(v[3] + b.w));
+    const float g0 = gelu_erf(v[0] + b.x), g1 = gelu_erf(v[1] + b.y),
+                g2 = gelu_erf(v[2] + b.z), g3 = gelu_erf(v[3] + b.w);
+    store_vec4(out + (size_t)m * N + n, g0, g1, g2, g3);
+    if (out_lo)
+      store_vec4(out_lo + (size_t)m * N + n, g0 - to_f32(from_f32<T>(g0)),
+                 g1 - to_f32(from_f32<T>(g1)), g2 - to_f32(from_f32<T>(g2)),
+                 g3 - to_f32(from_f32<T>(g3)));
   }
 };
 
@@ -182,9 +204,11 @@ struct GemmCfg {
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/threads");
 };
 
-template <class G>
-__device__ __forceinline__ void gemm_gload(u32x4 (&ra)[G::CA], u32x4 (&rb)[G::CB],
+template <class G, bool SPLIT>
+__device__ __forceinline__ void gemm_gload(u32x4 (&ra)[G::CA], u32x4 (&ral)[G::CA],
+                                           u32x4 (&rb)[G::CB],
                                            const bf16* __restrict__ A,
+                                           const bf16* __restrict__ Alo,
                                            const bf16* __restrict__ W, int m0,
                                            int n0, int M, int K, int k0, int tid) {
 #pragma unroll
@@ -192,6 +216,7 @@ __device__ __forceinline__ void gemm_gload(u32x4 (&ra)[G::CA], u32x4 (&rb)[G::CB
     const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
     const int gm = min(m0 + row, M - 1);
     ra[i] = *(const u32x4*)(A + (size_t)gm * K + k0 + kc * 8);
+    if (SPLIT) ral[i] = *(const u32x4*)(Alo + (size_t)gm * K + k0 + kc * 8);
   }
 #pragma unroll
   for (int i = 0; i < G::CB; ++i) {
@@ -200,14 +225,16 @@ __device__ __forceinline__ void gemm_gload(u32x4 (&ra)[G::CA], u32x4 (&rb)[G::CB
   }
 }
 
-template <class G>
+template <class G, bool SPLIT>
 __device__ __forceinline__ void gemm_lstore(const u32x4 (&ra)[G::CA],
+                                            const u32x4 (&ral)[G::CA],
                                             const u32x4 (&rb)[G::CB], bf16* sA,
-                                            bf16* sB, int tid) {
+                                            bf16* sAl, bf16* sB, int tid) {
 #pragma unroll
   for (int i = 0; i < G::CA; ++i) {
     const int c = tid + i * G::NT, row = c / G::CPR, kc = c - row * G::CPR;
     *(u32x4*)(sA + row * G::LDS + kc * 8) = ra[i];
+    if (SPLIT) *(u32x4*)(sAl + row * G::LDS + kc * 8) = ral[i];
   }
 #pragma unroll
   for (int i = 0; i < G::CB; ++i) {
@@ -216,10 +243,12 @@ __device__ __forceinline__ void gemm_lstore(const u32x4 (&ra)[G::CA],
   }
 }
 
-template <class G>
+// SPLIT: the activation tile is a bf16 pair (hi + lo) and both halves are
+// multiplied by the (exact bf16) weights into the same accumulator.
+template <class G, bool SPLIT>
 __device__ __forceinline__ void gemm_compute(f32x4 (&acc)[G::TN][G::TM],
-                                             const bf16* sA, const bf16* sB, int wm,
-                                             int wn, int lane) {
+                                             const bf16* sA, const bf16* sAl,
+                                             const bf16* sB, int wm, int wn, int lane) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
 #pragma unroll
   for (int ks = 0; ks < G::BK / 32; ++ks) {
@@ -235,6 +264,16 @@ __device__ __forceinline__ void gemm_compute(f32x4 (&acc)[G::TN][G::TM],
 #pragma unroll
       for (int i = 0; i < G::TM; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+    if (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+        af[i] = *(const bf16x8*)(sAl + (wm * G::WM + i * 16 + fr) * G::LDS + ks * 32 + fk);
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int i = 0; i < G::TM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+    }
   }
 }
 
@@ -252,12 +291,13 @@ __device__ __forceinline__ void gemm_tile_of(int p, int tiles_m, int tiles_n, in
   }
 }
 
-template <int TM, int TN, class Epi>
+template <int TM, int TN, bool SPLIT, class Epi>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
-    int k_len, Epi epi) {
+    const bf16* __restrict__ A, const bf16* __restrict__ Alo,
+    const bf16* __restrict__ W, int M, int N, int K, int k_len, Epi epi) {
   using G = GemmCfg<TM, TN>;
   __shared__ __attribute__((aligned(16))) bf16 sA[2][G::BM * G::LDS];
+  __shared__ __attribute__((aligned(16))) bf16 sAl[2][SPLIT ? G::BM * G::LDS : 8];
   __shared__ __attribute__((aligned(16))) bf16 sB[2][G::BN * G::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -279,16 +319,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     for (int i = 0; i < G::TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   {
-    u32x4 ra[G::CA], rb[G::CB];
-    gemm_gload<G>(ra, rb, A, W, m0, n0, M, K, kb, tid);
-    gemm_lstore<G>(ra, rb, sA[0], sB[0], tid);
+    u32x4 ra[G::CA], ral[G::CA], rb[G::CB];
+    gemm_gload<G, SPLIT>(ra, ral, rb, A, Alo, W, m0, n0, M, K, kb, tid);
+    gemm_lstore<G, SPLIT>(ra, ral, rb, sA[0], sAl[0], sB[0], tid);
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int kt = 0; kt < KT; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < KT) gemm_gload<G>(ra, rb, A, W, m0, n0, M, K, kb + (kt + 1) * G::BK, tid);
-      gemm_compute<G>(acc, sA[cur], sB[cur], wm, wn, lane);
-      if (kt + 1 < KT) gemm_lstore<G>(ra, rb, sA[cur ^ 1], sB[cur ^ 1], tid);
+      if (kt + 1 < KT)
+        gemm_gload<G, SPLIT>(ra, ral, rb, A, Alo, W, m0, n0, M, K, kb + (kt + 1) * G::BK, tid);
+      gemm_compute<G, SPLIT>(acc, sA[cur], sAl[cur], sB[cur], wm, wn, lane);
+      if (kt + 1 < KT)
+        gemm_lstore<G, SPLIT>(ra, ral, rb, sA[cur ^ 1], sAl[cur ^ 1], sB[cur ^ 1], tid);
       __syncthreads();
     }
   }
@@ -394,10 +436,11 @@ struct TileChoice {
 };
 static const int kTileCfgs[][2] = {{7, 4}, {7, 3}, {7, 2}, {4, 4}, {4, 2}};
 
-TileChoice gemm_choose(int M, int N, int K, bool allow_split) {
+TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = false) {
   TileChoice best{4, 2, 1};
   double best_cost = 1e300;
   for (auto& c : kTileCfgs) {
+    if (split_a && c[0] > 4) continue;   // hi + lo activation tiles must fit LDS
     const int BM = 32 * c[0], BN = 32 * c[1];
     if (N % BN) continue;
     const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
@@ -418,34 +461,45 @@ TileChoice gemm_choose(int M, int N, int K, bool allow_split) {
   return best;
 }
 
-template <int TM, int TN, class Epi>
-static void launch_cfg(const void* A, const void* W, int M, int N, int K, int splits,
-                       const Epi& epi, hipStream_t st) {
+template <int TM, int TN, bool SPLIT, class Epi>
+static void launch_cfg(const void* A, const void* Alo, const void* W, int M, int N,
+                       int K, int splits, const Epi& epi, hipStream_t st) {
   using G = GemmCfg<TM, TN>;
   const int tiles = ((M + G::BM - 1) / G::BM) * (N / G::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, Epi>), dim3(tiles * splits), dim3(256), 0,
-                     st, (const bf16*)A, (const bf16*)W, M, N, K, K / splits, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, SPLIT, Epi>), dim3(tiles * splits),
+                     dim3(256), 0, st, (const bf16*)A, (const bf16*)Alo, (const bf16*)W,
+                     M, N, K, K / splits, epi);
 }
 
+// Alo != NULL selects the split (hi + lo) activation kernel.
 template <class Epi>
-static hipError_t run_bf16_cfg(const void* A, const void* W, int M, int N, int K,
-                               TileChoice c, const Epi& epi, hipStream_t st) {
-  if (c.tm == 7 && c.tn == 4) launch_cfg<7, 4>(A, W, M, N, K, c.splits, epi, st);
-  else if (c.tm == 7 && c.tn == 3) launch_cfg<7, 3>(A, W, M, N, K, c.splits, epi, st);
-  else if (c.tm == 7 && c.tn == 2) launch_cfg<7, 2>(A, W, M, N, K, c.splits, epi, st);
-  else if (c.tm == 4 && c.tn == 4) launch_cfg<4, 4>(A, W, M, N, K, c.splits, epi, st);
-  else launch_cfg<4, 2>(A, W, M, N, K, c.splits, epi, st);
+static hipError_t run_bf16_cfg(const void* A, const void* Alo, const void* W, int M,
+                               int N, int K, TileChoice c, const Epi& epi,
+                               hipStream_t st) {
+  if (Alo) {
+    if (c.tm == 4 && c.tn == 4) launch_cfg<4, 4, true>(A, Alo, W, M, N, K, c.splits, epi, st);
+    else launch_cfg<4, 2, true>(A, Alo, W, M, N, K, c.splits, epi, st);
+    return hipGetLastError();
+  }
+  if (c.tm == 7 && c.tn == 4) launch_cfg<7, 4, false>(A, Alo, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 7 && c.tn == 3) launch_cfg<7, 3, false>(A, Alo, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 7 && c.tn == 2) launch_cfg<7, 2, false>(A, Alo, W, M, N, K, c.splits, epi, st);
+  else if (c.tm == 4 && c.tn == 4) launch_cfg<4, 4, false>(A, Alo, W, M, N, K, c.splits, epi, st);
+  else launch_cfg<4, 2, false>(A, Alo, W, M, N, K, c.splits, epi, st);
   return hipGetLastError();
 }
 
 template <class Epi>
-static hipError_t run_bf16(const void* A, const void* W, int M, int N, int K,
-                           const Epi& epi, hipStream_t st) {
-  TileChoice c = gemm_choose(M, N, K, false);
-  return run_bf16_cfg(A, W, M, N, K, c, epi, st);
+static hipError_t run_bf16(const void* A, const void* Alo, const void* W, int M, int N,
+                           int K, const Epi& epi, hipStream_t st) {
+  TileChoice c = gemm_choose(M, N, K, false, Alo != nullptr);
+  return run_bf16_cfg(A, Alo, W, M, N, K, c, epi, st);
 }
 
-int gemm_resid_splits(int M, int N, int K) { return gemm_choose(M, N, K, true).splits; }
+int gemm_resid_splits(int M, int N, int K) {
+  const int a = gemm_choose(M, N, K, true).splits, b = gemm_choose(M, N, K, true, true).splits;
+  return a > b ? a : b;
+}
 
 static int tiles_of(TileChoice c, int M, int N) {
   return ((M + 32 * c.tm - 1) / (32 * c.tm)) * (N / (32 * c.tn));
@@ -473,33 +527,33 @@ hipError_t launch_gemm_f32_planes(const float* A, const float* W, float* out, in
   return run_f32(A, W, M, N, K, e, st, splits);
 }
 
-hipError_t launch_gemm_qkv(bool bf, const void* A, const void* W,
+hipError_t launch_gemm_qkv(bool bf, const void* A, const void* Alo, const void* W,
                            const float* bias, int M, int N, int K, QKVDst d,
                            hipStream_t st) {
   if (bf) {
-    EpiQKV<bf16> e{bias, (bf16*)d.q, (bf16*)d.kc, (bf16*)d.vt, M, d.R, d.d,
-                   d.dh, d.H, d.Lcap, d.pos_base};
-    return run_bf16(A, W, M, N, K, e, st);
+    EpiQKV<bf16> e{bias, (bf16*)d.q, (bf16*)d.kc, (bf16*)d.vt, M, d.R, d.d, d.dh, d.H,
+                   d.Lcap, d.pos_base, (bf16*)d.q_lo, (bf16*)d.kc_lo, (bf16*)d.vt_lo};
+    return run_bf16(A, Alo, W, M, N, K, e, st);
   }
-  EpiQKV<float> e{bias, (float*)d.q, (float*)d.kc, (float*)d.vt, M, d.R, d.d,
-                  d.dh, d.H, d.Lcap, d.pos_base};
+  EpiQKV<float> e{bias, (float*)d.q, (float*)d.kc, (float*)d.vt, M, d.R, d.d, d.dh, d.H,
+                  d.Lcap, d.pos_base, nullptr, nullptr, nullptr};
   return run_f32(A, W, M, N, K, e, st);
 }
 
-hipError_t launch_gemm_resid(bool bf, const void* A, const void* W,
+hipError_t launch_gemm_resid(bool bf, const void* A, const void* Alo, const void* W,
                              const float* bias, float* h, int M, int N, int K,
                              float* slab, hipStream_t st) {
   if (!bf) {
     EpiResid e{bias, h, M, N};
     return run_f32(A, W, M, N, K, e, st);
   }
-  TileChoice c = gemm_choose(M, N, K, slab != nullptr);
+  TileChoice c = gemm_choose(M, N, K, slab != nullptr, Alo != nullptr);
   if (c.splits == 1) {
     EpiResid e{bias, h, M, N};
-    return run_bf16_cfg(A, W, M, N, K, c, e, st);
+    return run_bf16_cfg(A, Alo, W, M, N, K, c, e, st);
   }
   EpiSlab es{slab, M, N, tiles_of(c, M, N)};
-  hipError_t err = run_bf16_cfg(A, W, M, N, K, c, es, st);
+  hipError_t err = run_bf16_cfg(A, Alo, W, M, N, K, c, es, st);
   if (err != hipSuccess) return err;
   const size_t total4 = (size_t)M * N / 4;
   const int blocks = (int)std::min<size_t>((total4 + 255) / 256, 2048);
@@ -508,14 +562,14 @@ hipError_t launch_gemm_resid(bool bf, const void* A, const void* W,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_gelu(bool bf, const void* A, const void* W,
-                            const float* bias, void* out, int M, int N, int K,
-                            hipStream_t st) {
+hipError_t launch_gemm_gelu(bool bf, const void* A, const void* Alo, const void* W,
+                            const float* bias, void* out, void* out_lo, int M, int N,
+                            int K, hipStream_t st) {
   if (bf) {
-    EpiGelu<bf16> e{bias, (bf16*)out, M, N};
-    return run_bf16(A, W, M, N, K, e, st);
+    EpiGelu<bf16> e{bias, (bf16*)out, M, N, (bf16*)out_lo};
+    return run_bf16(A, Alo, W, M, N, K, e, st);
   }
-  EpiGelu<float> e{bias, (float*)out, M, N};
+  EpiGelu<float> e{bias, (float*)out, M, N, nullptr};
   return run_f32(A, W, M, N, K, e, st);
 }
 
@@ -523,7 +577,7 @@ hipError_t launch_gemm_f32out(bool bf, const void* A, const void* W,
                               const float* bias, float* out, int M, int N, int K,
                               hipStream_t st) {
   EpiF32 e{bias, out, M, N};
-  return bf ? run_bf16(A, W, M, N, K, e, st) : run_f32(A, W, M, N, K, e, st);
+  return bf ? run_bf16(A, nullptr, W, M, N, K, e, st) : run_f32(A, W, M, N, K, e, st);
 }
 
 }  // namespace af

@@ -16,9 +16,11 @@ hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
                         hipStream_t st);
 
 // out = LayerNorm(h) * g + b over rows of width d (eps 1e-5); out is bf16 when
-// out_bf16, else fp32.
+// out_bf16, else fp32.  With out_lo (bf16 only) the value is also split as
+// out + out_lo, both bf16, for the higher-precision forward.
 hipError_t launch_layernorm(const float* h, const float* g, const float* b,
-                            void* out, bool out_bf16, int M, int d, hipStream_t st);
+                            void* out, bool out_bf16, int M, int d, hipStream_t st,
+                            void* out_lo = nullptr);
 
 // x^(0) of a Jacobi block: mode 0 zeros, 1 copy of x_init, 2 previous frame.
 hipError_t launch_init_block(float* x, const float* x_init, int mode, int N,
@@ -45,25 +47,31 @@ hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);
 int affine_groups(int N, int R, int C);   // G, the partial slots per sample
 
 // ---- GEMMs: y[M, N] = A[M, K] W[N, K]^T + bias -----------------------------
+// The bf16 kernels take an optional second activation operand A_lo: with it
+// the activations are the bf16 pair A + A_lo (the higher-precision forward),
+// and the QKV / GELU epilogues then also write the lo halves of their outputs.
 struct QKVDst {
   void* q;        // [M, d]
   void* kc;       // K cache of this layer  [Nb][H][Lcap][dh]
   void* vt;       // V cache (transposed)   [Nb][H][dh][Lcap]
   int R, d, dh, H, Lcap, pos_base;
+  void* q_lo;     // lo halves (split mode) or NULL
+  void* kc_lo;
+  void* vt_lo;
 };
-hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* W,
+hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* A_lo, const void* W,
                            const float* bias, int M, int N, int K, QKVDst dst,
                            hipStream_t st);
 // h += A W^T + bias.  With a non-NULL slab ([S][M][N] fp32, S =
 // gemm_resid_splits(M, N, K)) the bf16 path splits K and reduces the partial
 // planes in a fixed order in a second kernel.
-hipError_t launch_gemm_resid(bool bf16, const void* A, const void* W,
+hipError_t launch_gemm_resid(bool bf16, const void* A, const void* A_lo, const void* W,
                              const float* bias, float* h, int M, int N, int K,
                              float* slab, hipStream_t st);
 int gemm_resid_splits(int M, int N, int K);
-hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* W,
-                            const float* bias, void* out, int M, int N, int K,
-                            hipStream_t st);
+hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* A_lo, const void* W,
+                            const float* bias, void* out, void* out_lo, int M, int N,
+                            int K, hipStream_t st);
 hipError_t launch_gemm_f32out(bool bf16, const void* A, const void* W,
                               const float* bias, float* out, int M, int N, int K,
                               hipStream_t st);
@@ -79,10 +87,16 @@ int head_splits(int M, int N, int K);
 // bf16: long key ranges are split into chunks whose partial results go to
 // `part` (attention_partial_floats(...) floats) and are merged by a second
 // kernel.
+struct AttnSplit {   // lo halves of the split (higher-precision) mode
+  const void* q_lo;
+  const void* kc_lo;
+  const void* vt_lo;
+  void* out_lo;
+};
 hipError_t launch_attention(bool bf16, const void* q, const void* kc,
                             const void* vt, void* out, float* part, int N, int R,
                             int H, int dh, int d, int Lcap, int pos_base,
-                            hipStream_t st);
+                            hipStream_t st, const AttnSplit* split = nullptr);
 size_t attention_partial_floats(int N, int R, int H, int dh, int pos_base);
 
 }  // namespace af

@@ -101,7 +101,8 @@ hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
 template <int VPL, class OutT>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const float* __restrict__ h, const float* __restrict__ g,
-    const float* __restrict__ b, OutT* __restrict__ out, int M) {
+    const float* __restrict__ b, OutT* __restrict__ out, OutT* __restrict__ out_lo,
+    int M) {
   constexpr int D = VPL * AF_WAVE;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -123,34 +124,39 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   }
   const float rstd = rsqrtf(wave_sum(sq) * (1.0f / D) + 1e-5f);
   OutT* orow = out + (size_t)row * D;
+  OutT* lrow = out_lo ? out_lo + (size_t)row * D : nullptr;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     int j = lane + AF_WAVE * i;
-    orow[j] = from_f32<OutT>((v[i] - mean) * rstd * g[j] + b[j]);
+    const float y = (v[i] - mean) * rstd * g[j] + b[j];
+    const OutT hi = from_f32<OutT>(y);
+    orow[j] = hi;
+    if (lrow) lrow[j] = from_f32<OutT>(y - to_f32(hi));   // split: y = hi + lo
   }
 }
 
 template <class OutT>
 static hipError_t ln_dispatch(const float* h, const float* g, const float* b,
-                              OutT* out, int M, int d, hipStream_t st) {
+                              OutT* out, OutT* out_lo, int M, int d, hipStream_t st) {
   dim3 grid((M + 3) / 4), blk(256);
   switch (d / AF_WAVE) {
-    case 1: hipLaunchKernelGGL((layernorm_kernel<1, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 2: hipLaunchKernelGGL((layernorm_kernel<2, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 4: hipLaunchKernelGGL((layernorm_kernel<4, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 8: hipLaunchKernelGGL((layernorm_kernel<8, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 16: hipLaunchKernelGGL((layernorm_kernel<16, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 32: hipLaunchKernelGGL((layernorm_kernel<32, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
-    case 64: hipLaunchKernelGGL((layernorm_kernel<64, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+    case 1: hipLaunchKernelGGL((layernorm_kernel<1, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 2: hipLaunchKernelGGL((layernorm_kernel<2, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 4: hipLaunchKernelGGL((layernorm_kernel<4, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 8: hipLaunchKernelGGL((layernorm_kernel<8, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 16: hipLaunchKernelGGL((layernorm_kernel<16, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 32: hipLaunchKernelGGL((layernorm_kernel<32, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
+    case 64: hipLaunchKernelGGL((layernorm_kernel<64, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_layernorm(const float* h, const float* g, const float* b,
-                            void* out, bool out_bf16, int M, int d, hipStream_t st) {
-  if (out_bf16) return ln_dispatch(h, g, b, (bf16*)out, M, d, st);
-  return ln_dispatch(h, g, b, (float*)out, M, d, st);
+                            void* out, bool out_bf16, int M, int d, hipStream_t st,
+                            void* out_lo) {
+  if (out_bf16) return ln_dispatch(h, g, b, (bf16*)out, (bf16*)out_lo, M, d, st);
+  return ln_dispatch(h, g, b, (float*)out, (float*)nullptr, M, d, st);
 }
 
 // ---------------------------------------------------------------------------

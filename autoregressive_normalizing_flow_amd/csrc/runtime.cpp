@@ -53,7 +53,9 @@ struct BlockW {
 // Byte offsets of the workspace regions for (batch, rows).
 struct WsLayout {
   size_t cache_layer;  // bytes of one layer's K (or V) cache
-  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, slab, attn_part, xtmp, total;
+  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, slab, attn_part, xtmp;
+  // lo halves of the split (higher-precision) forward on the bf16 path
+  size_t cache_lo, a_lo, q_lo, att_lo, u_lo, total;
 };
 
 enum KClass { K_EMBED, K_LN, K_QKV, K_O, K_MLP1, K_MLP2, K_HEAD, K_ATTN, K_AFFINE, K_NCLASS };
@@ -126,6 +128,14 @@ WsLayout layout(const af_plan* p, int N, int rows) {
   }
   w.xtmp = off;
   if (p->T > 1) off += align256((size_t)N * c.max_len * c.C * 4);
+  w.cache_lo = w.a_lo = w.q_lo = w.att_lo = w.u_lo = 0;
+  if (p->bf) {
+    w.cache_lo = off; off += align256(2 * w.cache_layer * c.n_layers);
+    w.a_lo = off;     off += align256(M * c.d * 2);
+    w.q_lo = off;     off += align256(M * c.d * 2);
+    w.att_lo = off;   off += align256(M * c.d * 2);
+    w.u_lo = off;     off += align256(M * p->dmlp * 2);
+  }
   w.total = off;
   return w;
 }
@@ -161,6 +171,7 @@ struct Pass {
   const float* x_last;  // token before processing index 0, or NULL
   int N, L, s, R, P, dir;
   bool kv_only;         // stop after the last layer's K/V (cache refresh)
+  bool precise;         // bf16 path: carry activations as bf16 pairs (hi + lo)
 };
 
 // One pass of the network over chunk rows [s, s+R) of every sample:
@@ -174,6 +185,12 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   void* q = ws + w.q;
   void* att = ws + w.att;
   void* u = ws + w.u;
+  const bool sp = ps.precise && p->bf;
+  void* a_lo = sp ? ws + w.a_lo : nullptr;
+  void* q_lo = sp ? ws + w.q_lo : nullptr;
+  void* att_lo = sp ? ws + w.att_lo : nullptr;
+  void* u_lo = sp ? ws + w.u_lo : nullptr;
+  float* slab = (float*)(ws + w.slab);
   const int pos_base = ps.P + ps.s;
   LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
                                    ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
@@ -182,18 +199,22 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
     const LayerW& lw = bw.layers[l];
     char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
     char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
-    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, p->bf, M, d, st));
-    af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base};
-    LAUNCH(K_QKV, af::launch_gemm_qkv(p->bf, a, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+    char* kc_lo = sp ? ws + w.cache_lo + (size_t)(2 * l) * w.cache_layer : nullptr;
+    char* vt_lo = sp ? ws + w.cache_lo + (size_t)(2 * l + 1) * w.cache_layer : nullptr;
+    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, p->bf, M, d, st, a_lo));
+    af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
+    LAUNCH(K_QKV, af::launch_gemm_qkv(p->bf, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
     if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+    af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
     LAUNCH(K_ATTN, af::launch_attention(p->bf, q, kc, vt, att, (float*)(ws + w.attn_part),
-                                        ps.N, ps.R, c.n_heads,
-                                        p->dh, d, p->Lcap, pos_base, st));
-    float* slab = (float*)(ws + w.slab);
-    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, lw.w_o, lw.b_o, h, M, d, d, slab, st));
-    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, p->bf, M, d, st));
-    LAUNCH(K_MLP1, af::launch_gemm_gelu(p->bf, a, lw.w_1, lw.b_1, u, M, p->dmlp, d, st));
-    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, lw.w_2, lw.b_2, h, M, d, p->dmlp, slab, st));
+                                        ps.N, ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base,
+                                        st, sp ? &asp : nullptr));
+    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, att_lo, lw.w_o, lw.b_o, h, M, d, d, slab, st));
+    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, p->bf, M, d, st, a_lo));
+    LAUNCH(K_MLP1, af::launch_gemm_gelu(p->bf, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
+                                        d, st));
+    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, u_lo, lw.w_2, lw.b_2, h, M, d, p->dmlp,
+                                         slab, st));
   }
   float* hf = (float*)(ws + w.hf);
   float* head = (float*)(ws + w.head);
@@ -336,7 +357,9 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
   const float* cur = x;
   for (int t = 0; t < p->T; ++t) {
     float* dst = ((p->T - 1 - t) % 2 == 0) ? z : xtmp;
-    Pass ps{cur, nullptr, N, L, 0, L, 0, t & 1, false};
+    // the forward carries bf16 activations as hi + lo pairs, so that the
+    // log-det (a sum of many terms that largely cancel) keeps fp32 accuracy
+    Pass ps{cur, nullptr, N, L, 0, L, 0, t & 1, false, true};
     if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st)) return s;
     af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
                       af::head_splits(N * L, 2 * C, p->cfg.d), nullptr,
@@ -357,7 +380,7 @@ af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
   WsLayout w;
   if (af_status s = check_ws(p, N, P, ws_, ws_bytes, &w)) return s;
   hipStream_t st = (hipStream_t)stream;
-  Pass ps{x_prefix, nullptr, N, P, 0, P, 0, 0, true};
+  Pass ps{x_prefix, nullptr, N, P, 0, P, 0, 0, true, false};
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
 }
 
@@ -400,7 +423,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       const int s = b * B, R = (s + B < L ? s + B : L) - s;
       const int kmax = max_iters <= 0 ? R : (max_iters < R ? max_iters : R);
       AF_HIP(af::launch_init_block(xo, x_init, (int)init, N, R, C, L, s, dir, frame_len, st));
-      Pass ps{xo, x_last, N, L, s, R, prefix_len, dir, false};
+      Pass ps{xo, x_last, N, L, s, R, prefix_len, dir, false, false};
       af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
                         af::head_splits(N * R, 2 * C, p->cfg.d), zin, xo, nullptr, N, R, C, L, s,
                         dir, (float*)(ws + w.partials), res,
