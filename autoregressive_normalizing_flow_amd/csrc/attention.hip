@@ -322,6 +322,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge the key chunks of every query tile that has more than one:
 // O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, chunks in order.
+// Two threads per query row, each owning DH/2 dimensions; the chunk weights
+// are computed once per row.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt) {
   const int nh = blockIdx.x / n_qt, qt = blockIdx.x - nh * n_qt;
@@ -330,44 +332,50 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt)
   int u0 = nh * a.U_nh;
   for (int q = 0; q < qt; ++q) u0 += att_chunks(q, a.R, a.pos_base, a.KC);
   const int n = nh / a.H, head = nh - n * a.H;
-  constexpr int D4 = DH / 4;
-  for (int item = threadIdx.x; item < ATT_QT * D4; item += 256) {
-    const int tq = item / D4, e = (item - tq * D4) * 4;
-    const int t = qt * ATT_QT + tq;
-    if (t >= a.R) continue;
-    float m = -1e30f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float* slot = a.part + (size_t)(u0 + c) * ATT_QT * (DH + 2);
-      m = fmaxf(m, slot[ATT_QT * DH + tq]);
+  const int tq = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int t = qt * ATT_QT + tq;
+  if (t >= a.R) return;
+  constexpr int SLOT = ATT_QT * (DH + 2);
+  const float* base = a.part + (size_t)u0 * SLOT;
+  float m = -1e30f;
+  for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, base[(size_t)c * SLOT + ATT_QT * DH + tq]);
+  float l = 0.f;
+  constexpr int D4 = DH / 8;   // float4 per thread
+  float4 o[D4];
+#pragma unroll
+  for (int j = 0; j < D4; ++j) o[j] = float4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < n_chunks; ++c) {
+    const float* slot = base + (size_t)c * SLOT;
+    const float w = exp2f(slot[ATT_QT * DH + tq] - m);
+    l += w * slot[ATT_QT * DH + ATT_QT + tq];
+    const float4* src = (const float4*)(slot + (size_t)tq * DH + half * (DH / 2));
+#pragma unroll
+    for (int j = 0; j < D4; ++j) {
+      const float4 v = src[j];
+      o[j].x += w * v.x;
+      o[j].y += w * v.y;
+      o[j].z += w * v.z;
+      o[j].w += w * v.w;
     }
-    float4 o = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float* slot = a.part + (size_t)(u0 + c) * ATT_QT * (DH + 2);
-      const float w = exp2f(slot[ATT_QT * DH + tq] - m);
-      const float4 v = *(const float4*)(slot + (size_t)tq * DH + e);
-      o.x += w * v.x;
-      o.y += w * v.y;
-      o.z += w * v.z;
-      o.w += w * v.w;
-      l += w * slot[ATT_QT * DH + ATT_QT + tq];
-    }
-    const float inv = 1.0f / l;
-    const float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+  }
+  const float inv = 1.0f / l;
+  const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + half * (DH / 2);
+#pragma unroll
+  for (int j = 0; j < D4; ++j) {
+    const float y[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
     bf16x4 r, rl;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r[j] = (bf16)y[j];
-      rl[j] = (bf16)(y[j] - (float)r[j]);
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (bf16)y[e];
+      rl[e] = (bf16)(y[e] - (float)r[e]);
     }
-    const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + e;
-    *(bf16x4*)(a.out + oo) = r;
-    if (a.out_lo) *(bf16x4*)(a.out_lo + oo) = rl;
+    *(bf16x4*)(a.out + oo + 4 * j) = r;
+    if (a.out_lo) *(bf16x4*)(a.out_lo + oo + 4 * j) = rl;
   }
 }
 
 // Key chunk length: the smallest multiple of 512 keys that keeps the number
-// of units near 1024 (4 per CU); whole ranges when that is already enough.
+// of units at most 1024 (four per CU); whole ranges when that is already enough.
 static int att_units(int R, int pos_base, int KC, int n_qt) {
   int s = 0;
   for (int qt = 0; qt < n_qt; ++qt) {

@@ -343,6 +343,155 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     for (int i = 0; i < G::TM; ++i) epi.store4(mb + i * 16, nb + j * 16, acc[j][i]);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4).
+//
+// Same tiles, fragment layout and epilogues as gemm_bf16_kernel, but the
+// operand tiles go from global memory straight into LDS (no register
+// staging) through a 3-stage ring, so two k-tiles are in flight while one is
+// multiplied.  A DMA wave-instruction writes 64 consecutive 16-byte LDS slots
+// (lane i -> slot i); each lane therefore chooses which global chunk lands in
+// its slot, and the tile is stored XOR-swizzled: chunk c of row r sits at
+// slot 8r + (c ^ (r & 7)), which makes the 16-byte fragment reads (16 rows,
+// one chunk) conflict-free without padding.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int TM_, int TN_>
+struct DmaCfg {
+  static constexpr int TM = TM_, TN = TN_;
+  static constexpr int WM = 16 * TM, WN = 16 * TN, BM = 2 * WM, BN = 2 * WN, BK = 64;
+  static constexpr int IA = BM / 32, IB = BN / 32;   // DMA instructions per wave per stage
+  static constexpr int IPW = IA + IB;
+  static constexpr int STAGE = (BM + BN) * BK;         // bf16 elements per stage
+};
+
+// s_waitcnt with vmcnt <= n (other counters unconstrained), gfx9 encoding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <class G>
+__device__ __forceinline__ void dma_stage(const bf16* __restrict__ A,
+                                          const bf16* __restrict__ W, bf16* stage, int m0,
+                                          int n0, int M, int K, int k0, int wave, int lane) {
+  bf16* sA = stage;
+  bf16* sB = stage + G::BM * G::BK;
+#pragma unroll
+  for (int jj = 0; jj < G::IA; ++jj) {
+    const int j = jj * 4 + wave;
+    const int q = j * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ (r & 7);
+    const int gm = min(m0 + r, M - 1);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(A + (size_t)gm * K + k0 + c * 8),
+                                     (lds_void_t*)(sA + j * 512), 16, 0, 0);
+  }
+#pragma unroll
+  for (int jj = 0; jj < G::IB; ++jj) {
+    const int j = jj * 4 + wave;
+    const int q = j * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ (r & 7);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(W + (size_t)(n0 + r) * K + k0 + c * 8),
+                                     (lds_void_t*)(sB + j * 512), 16, 0, 0);
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void dma_compute(f32x4 (&acc)[G::TN][G::TM], const bf16* stage,
+                                            int wm, int wn, int lane) {
+  const bf16* sA = stage;
+  const bf16* sB = stage + G::BM * G::BK;
+  const int fr = lane & 15, sw = lane & 7;
+#pragma unroll
+  for (int ks = 0; ks < G::BK / 32; ++ks) {
+    const int c = ks * 4 + (lane >> 4);
+    bf16x8 wf[G::TN], af[G::TM];
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+      wf[j] = *(const bf16x8*)(sB + (wn * G::WN + j * 16 + fr) * 64 + ((c ^ sw) << 3));
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+      af[i] = *(const bf16x8*)(sA + (wm * G::WM + i * 16 + fr) * 64 + ((c ^ sw) << 3));
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+  }
+}
+
+// One k-step of the ring: tile kt sits in `cur`; the tile kt + 2 is issued
+// into `nxt` (the buffer read in step kt - 1) after the barrier.
+template <class G, int PENDING>
+__device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], const bf16* A,
+                                         const bf16* W, bf16* cur, bf16* nxt, int m0,
+                                         int n0, int M, int K, int k_next, bool issue,
+                                         int wave, int wm, int wn, int lane) {
+  wait_vmcnt<PENDING * G::IPW>();   // this wave's loads of tile kt are done
+  __builtin_amdgcn_s_barrier();     // ... and every wave's; step kt-1 is finished
+  if (issue) dma_stage<G>(A, W, nxt, m0, n0, M, K, k_next, wave, lane);
+  dma_compute<G>(acc, cur, wm, wn, lane);
+}
+
+template <int TM, int TN, class Epi>
+__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
+    int k_len, Epi epi) {
+  using G = DmaCfg<TM, TN>;
+  __shared__ __attribute__((aligned(1024))) bf16 s0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[G::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = N / G::BN;
+  const int tiles_m = (M + G::BM - 1) / G::BM;
+  const int tiles = tiles_m * tiles_n;
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  gemm_tile_of(blockIdx.x - split * tiles, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * G::BM, n0 = tn * G::BN;
+  const int kb = split * k_len;
+  const int KT = k_len / G::BK;
+
+  f32x4 acc[G::TN][G::TM];
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  dma_stage<G>(A, W, s0, m0, n0, M, K, kb, wave, lane);
+  if (KT > 1) dma_stage<G>(A, W, s1, m0, n0, M, K, kb + G::BK, wave, lane);
+  // steady state: one later tile pending while waiting for tile kt
+  int kt = 0;
+#pragma clang loop unroll(disable)
+  for (; kt + 3 <= KT - 1; kt += 3) {
+    dma_step<G, 1>(acc, A, W, s0, s2, m0, n0, M, K, kb + (kt + 2) * G::BK, true, wave, wm, wn, lane);
+    dma_step<G, 1>(acc, A, W, s1, s0, m0, n0, M, K, kb + (kt + 3) * G::BK, true, wave, wm, wn, lane);
+    dma_step<G, 1>(acc, A, W, s2, s1, m0, n0, M, K, kb + (kt + 4) * G::BK, kt + 4 < KT, wave, wm, wn, lane);
+  }
+  // tail: kt .. KT-1 (at most 3 steps); buffer of tile t is t % 3
+  for (; kt < KT; ++kt) {
+    bf16* cur = (kt % 3 == 0) ? s0 : (kt % 3 == 1) ? s1 : s2;
+    bf16* nxt = ((kt + 2) % 3 == 0) ? s0 : ((kt + 2) % 3 == 1) ? s1 : s2;
+    const bool issue = kt + 2 < KT;
+    if (kt + 1 < KT)
+      dma_step<G, 1>(acc, A, W, cur, nxt, m0, n0, M, K, kb + (kt + 2) * G::BK, issue, wave, wm, wn, lane);
+    else
+      dma_step<G, 0>(acc, A, W, cur, nxt, m0, n0, M, K, 0, false, wave, wm, wn, lane);
+  }
+
+  const int mb = m0 + wm * G::WM + (lane & 15);
+  const int nb = n0 + wn * G::WN + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) epi.store4(mb + i * 16, nb + j * 16, acc[j][i]);
+}
+
 // h[m, n] += bias[n] + sum_s slab[s][m][n], summed in split order.
 __global__ __launch_bounds__(256) void splitk_resid_kernel(
     const float* __restrict__ slab, const float* __restrict__ bias,
@@ -466,9 +615,14 @@ static void launch_cfg(const void* A, const void* Alo, const void* W, int M, int
                        int K, int splits, const Epi& epi, hipStream_t st) {
   using G = GemmCfg<TM, TN>;
   const int tiles = ((M + G::BM - 1) / G::BM) * (N / G::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, SPLIT, Epi>), dim3(tiles * splits),
-                     dim3(256), 0, st, (const bf16*)A, (const bf16*)Alo, (const bf16*)W,
-                     M, N, K, K / splits, epi);
+  if (SPLIT)
+    hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, SPLIT, Epi>), dim3(tiles * splits),
+                       dim3(256), 0, st, (const bf16*)A, (const bf16*)Alo, (const bf16*)W,
+                       M, N, K, K / splits, epi);
+  else
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<TM, TN, Epi>), dim3(tiles * splits),
+                       dim3(256), 0, st, (const bf16*)A, (const bf16*)W, M, N, K,
+                       K / splits, epi);
 }
 
 // Alo != NULL selects the split (hi + lo) activation kernel.
@@ -560,6 +714,15 @@ hipError_t launch_gemm_resid(bool bf, const void* A, const void* Alo, const void
   hipLaunchKernelGGL(splitk_resid_kernel, dim3(blocks), dim3(256), 0, st, slab, bias, h,
                      M, N, c.splits);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_partial(const void* A, const void* Alo, const void* W,
+                               float* slab, int M, int N, int K, int* splits,
+                               hipStream_t st) {
+  TileChoice c = gemm_choose(M, N, K, true, Alo != nullptr);
+  *splits = c.splits;
+  EpiSlab es{slab, M, N, tiles_of(c, M, N)};
+  return run_bf16_cfg(A, Alo, W, M, N, K, c, es, st);
 }
 
 hipError_t launch_gemm_gelu(bool bf, const void* A, const void* Alo, const void* W,

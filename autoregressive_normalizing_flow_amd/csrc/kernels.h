@@ -22,6 +22,12 @@ hipError_t launch_layernorm(const float* h, const float* g, const float* b,
                             void* out, bool out_bf16, int M, int d, hipStream_t st,
                             void* out_lo = nullptr);
 
+// h += bias + sum of S split-K planes (slab [S][M][d]); out = LayerNorm(h)
+// (bf16 with optional lo half, or fp32).
+hipError_t launch_resid_ln(const float* slab, int S, const float* bias, float* h,
+                           const float* g, const float* b, void* out, bool out_bf16,
+                           void* out_lo, int M, int d, hipStream_t st);
+
 // x^(0) of a Jacobi block: mode 0 zeros, 1 copy of x_init, 2 previous frame.
 hipError_t launch_init_block(float* x, const float* x_init, int mode, int N,
                              int R, int C, int L, int s, int dir, int F,
@@ -69,6 +75,11 @@ hipError_t launch_gemm_resid(bool bf16, const void* A, const void* A_lo, const v
                              const float* bias, float* h, int M, int N, int K,
                              float* slab, hipStream_t st);
 int gemm_resid_splits(int M, int N, int K);
+// The residual GEMMs of the bf16 path write fp32 partial planes only
+// (slab [S][M][N], S = the returned split count); launch_resid_ln finishes them.
+hipError_t launch_gemm_partial(const void* A, const void* A_lo, const void* W,
+                               float* slab, int M, int N, int K, int* splits,
+                               hipStream_t st);
 hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* A_lo, const void* W,
                             const float* bias, void* out, void* out_lo, int M, int N,
                             int K, hipStream_t st);

@@ -15,14 +15,15 @@
 namespace af {
 
 // ---------------------------------------------------------------------------
-// shift + embed.  Block: 256 output columns x 16 rows.  W_in is staged
-// transposed through LDS in chunks of 32 channels so that column reads are
-// conflict-free; the 16 shifted input rows are broadcast from LDS.
+// shift + embed.  Block: 256 output columns x 16 rows.  The 16 shifted input
+// rows are staged in LDS (broadcast reads); each thread keeps its column of
+// W_in (one row of W_in^T) in registers, loaded 64 channels at a time with
+// independent float4 loads.
 // ---------------------------------------------------------------------------
 constexpr int EMB_ROWS = 16;
 constexpr int EMB_COLS = 256;
-constexpr int EMB_CCH = 32;
 constexpr int EMB_MAXC = 256;
+constexpr int EMB_CCH = 64;
 
 __global__ __launch_bounds__(256) void embed_kernel(
     const float* __restrict__ x, const float* __restrict__ x_last,
@@ -30,7 +31,6 @@ __global__ __launch_bounds__(256) void embed_kernel(
     const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
     int d, int L, int s, int dir, int pos_base) {
   __shared__ float s_in[EMB_ROWS][EMB_MAXC];
-  __shared__ float s_w[EMB_CCH][EMB_COLS + 1];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * EMB_COLS;
   const int m0 = blockIdx.y * EMB_ROWS;
@@ -38,12 +38,12 @@ __global__ __launch_bounds__(256) void embed_kernel(
 
   // shifted inputs of the 16 rows
   for (int e = tid; e < EMB_ROWS * C; e += 256) {
-    int r = e / C, c = e - r * C;
-    int m = m0 + r;
+    const int r = e / C, c = e - r * C;
+    const int m = m0 + r;
     float v = 0.f;
     if (m < M) {
-      int n = m / R, t = m - n * R;
-      int i = s + t;  // processing index
+      const int n = m / R, t = m - n * R;
+      const int i = s + t;  // processing index
       if (i > 0) {
         v = x[((size_t)n * L + storage_index(i - 1, L, dir)) * C + c];
       } else if (x_last) {
@@ -52,34 +52,42 @@ __global__ __launch_bounds__(256) void embed_kernel(
     }
     s_in[r][c] = v;
   }
+  __syncthreads();
 
+  const int j = j0 + tid;
+  if (j >= d) return;
   float acc[EMB_ROWS];
 #pragma unroll
   for (int r = 0; r < EMB_ROWS; ++r) acc[r] = 0.f;
-  const int j = j0 + tid;
+  const float* wrow = w_in + (size_t)j * C;
   for (int c0 = 0; c0 < C; c0 += EMB_CCH) {
-    const int cc_n = min(EMB_CCH, C - c0);
-    __syncthreads();
-    for (int e = tid; e < EMB_COLS * EMB_CCH; e += 256) {
-      int jj = e / EMB_CCH, cc = e - jj * EMB_CCH;
-      float v = 0.f;
-      if (j0 + jj < d && cc < cc_n) v = w_in[(size_t)(j0 + jj) * C + c0 + cc];
-      s_w[cc][jj] = v;
-    }
-    __syncthreads();
-    for (int cc = 0; cc < cc_n; ++cc) {
-      float w = s_w[cc][tid];
+    float w[EMB_CCH];
+    const int cn = min(EMB_CCH, C - c0);
+    if ((C & 3) == 0) {
 #pragma unroll
-      for (int r = 0; r < EMB_ROWS; ++r) acc[r] += s_in[r][c0 + cc] * w;
+      for (int q = 0; q < EMB_CCH / 4; ++q)
+        if (4 * q < cn) {
+          const float4 v = *(const float4*)(wrow + c0 + 4 * q);
+          w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+      for (int q = 0; q < EMB_CCH; ++q)
+        if (q < cn) w[q] = wrow[c0 + q];
     }
+#pragma unroll
+    for (int q = 0; q < EMB_CCH; ++q)
+      if (q < cn) {
+#pragma unroll
+        for (int r = 0; r < EMB_ROWS; ++r) acc[r] += s_in[r][c0 + q] * w[q];
+      }
   }
-  if (j >= d) return;
   const float bj = b_in[j];
 #pragma unroll
   for (int r = 0; r < EMB_ROWS; ++r) {
-    int m = m0 + r;
+    const int m = m0 + r;
     if (m >= M) break;
-    int t = m % R;
+    const int t = m % R;
     h[(size_t)m * d + j] = acc[r] + bj + pos[(size_t)(pos_base + t) * d + j];
   }
 }
@@ -160,6 +168,138 @@ hipError_t launch_layernorm(const float* h, const float* g, const float* b,
 }
 
 // ---------------------------------------------------------------------------
+// Residual add + LayerNorm, fused: one wave per row.
+//   h[m] += bias + sum_s slab[s][m]          (split-K planes added in order)
+//   out[m] = LayerNorm(h[m]) * g + b          (bf16, optional lo half; or fp32)
+// It finishes the O-projection / MLP-down GEMMs and produces the next
+// LayerNorm's output in the same pass over the row.
+// ---------------------------------------------------------------------------
+template <class OutT>
+__device__ __forceinline__ void store4(OutT* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = float4{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4*)p = v;
+}
+
+// One wave per row, V4 = d / 256 float4 per lane, S split planes, LO: also
+// write the bf16 lo halves.  All loads of a row are issued before the sums.
+template <int V4, int S, bool LO, class OutT>
+__global__ __launch_bounds__(256) void resid_ln_kernel(
+    const float* __restrict__ slab, const float* __restrict__ bias,
+    float* __restrict__ h, const float* __restrict__ g, const float* __restrict__ b,
+    OutT* __restrict__ out, OutT* __restrict__ out_lo, int M) {
+  constexpr int D = V4 * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const size_t plane = (size_t)M * D;
+  float* hr = h + (size_t)row * D;
+  const float* sr = slab + (size_t)row * D;
+  float4 v[V4], pl[S][V4];
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    v[i] = *(const float4*)(hr + j);
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) pl[sp][i] = *(const float4*)(sr + sp * plane + j);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    const float4 bb = *(const float4*)(bias + j);
+    float4 acc = pl[0][i];
+#pragma unroll
+    for (int sp = 1; sp < S; ++sp) {
+      acc.x += pl[sp][i].x;
+      acc.y += pl[sp][i].y;
+      acc.z += pl[sp][i].z;
+      acc.w += pl[sp][i].w;
+    }
+    v[i].x += acc.x + bb.x;
+    v[i].y += acc.y + bb.y;
+    v[i].z += acc.z + bb.z;
+    v[i].w += acc.w + bb.w;
+    *(float4*)(hr + j) = v[i];
+    sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  const float mean = wave_sum(sum) * (1.0f / D);
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+    sq += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+  }
+  const float rstd = rsqrtf(wave_sum(sq) * (1.0f / D) + 1e-5f);
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    const float4 gg = *(const float4*)(g + j), be = *(const float4*)(b + j);
+    const float y0 = (v[i].x - mean) * rstd * gg.x + be.x;
+    const float y1 = (v[i].y - mean) * rstd * gg.y + be.y;
+    const float y2 = (v[i].z - mean) * rstd * gg.z + be.z;
+    const float y3 = (v[i].w - mean) * rstd * gg.w + be.w;
+    store4<OutT>(out + (size_t)row * D + j, y0, y1, y2, y3);
+    if (LO)
+      store4<OutT>(out_lo + (size_t)row * D + j, y0 - to_f32(from_f32<OutT>(y0)),
+                   y1 - to_f32(from_f32<OutT>(y1)), y2 - to_f32(from_f32<OutT>(y2)),
+                   y3 - to_f32(from_f32<OutT>(y3)));
+  }
+}
+
+template <int S, bool LO, class OutT>
+static hipError_t rln_v4(const float* slab, const float* bias, float* h, const float* g,
+                         const float* b, OutT* out, OutT* out_lo, int M, int d,
+                         hipStream_t st) {
+  dim3 grid((M + 3) / 4), blk(256);
+#define AF_RLN(V)                                                                     \
+  hipLaunchKernelGGL((resid_ln_kernel<V, S, LO, OutT>), grid, blk, 0, st, slab, bias, h, \
+                     g, b, out, out_lo, M)
+  switch (d / 256) {
+    case 1: AF_RLN(1); break;
+    case 2: AF_RLN(2); break;
+    case 4: AF_RLN(4); break;
+    case 8: AF_RLN(8); break;
+    case 16: AF_RLN(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef AF_RLN
+  return hipGetLastError();
+}
+
+template <class OutT>
+static hipError_t rln_dispatch(const float* slab, int S, const float* bias, float* h,
+                               const float* g, const float* b, OutT* out, OutT* out_lo,
+                               int M, int d, hipStream_t st) {
+  if (d % 256) return hipErrorInvalidValue;
+  const bool lo = out_lo != nullptr;
+  switch (S * 2 + (lo ? 1 : 0)) {
+    case 2: return rln_v4<1, false>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 3: return rln_v4<1, true>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 4: return rln_v4<2, false>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 5: return rln_v4<2, true>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 8: return rln_v4<4, false>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 9: return rln_v4<4, true>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 16: return rln_v4<8, false>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    case 17: return rln_v4<8, true>(slab, bias, h, g, b, out, out_lo, M, d, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_resid_ln(const float* slab, int S, const float* bias, float* h,
+                           const float* g, const float* b, void* out, bool out_bf16,
+                           void* out_lo, int M, int d, hipStream_t st) {
+  if (out_bf16)
+    return rln_dispatch<bf16>(slab, S, bias, h, g, b, (bf16*)out, (bf16*)out_lo, M, d, st);
+  return rln_dispatch<float>(slab, S, bias, h, g, b, (float*)out, (float*)nullptr, M, d, st);
+}
+
+// ---------------------------------------------------------------------------
 // Jacobi-block initial iterate, in processing order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void init_block_kernel(
@@ -218,7 +358,7 @@ hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st) {
 // ---------------------------------------------------------------------------
 int affine_groups(int N, int R, int C) {
   const long quads = ((long)R * C + 3) / 4;
-  long g = (quads + 1023) / 1024;           // ~4 quads per thread
+  long g = (quads + 255) / 256;             // one quad per thread per pass
   const long cap = std::max(1, 2048 / std::max(N, 1));
   if (g > cap) g = cap;
   return (int)std::max(1L, g);
@@ -263,6 +403,7 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
       mu[q] = a.head_bias ? a.head_bias[c + q] : 0.f;
       raw[q] = a.head_bias ? a.head_bias[C + c + q] : 0.f;
     }
+#pragma unroll 4
     for (int sp = 0; sp < a.head_splits; ++sp) {
       const float* hs = hp + sp * plane;
       if (VEC) {

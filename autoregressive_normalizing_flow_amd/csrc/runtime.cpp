@@ -117,7 +117,7 @@ WsLayout layout(const af_plan* p, int N, int rows) {
     const int s1 = af::gemm_resid_splits((int)M, c.d, c.d);
     const int s2 = af::gemm_resid_splits((int)M, c.d, p->dmlp);
     const int s = s1 > s2 ? s1 : s2;
-    if (s > 1) off += align256((size_t)s * M * c.d * 4);
+    off += align256((size_t)s * M * c.d * 4);
   }
   w.attn_part = off;
   if (p->bf) {
@@ -195,30 +195,65 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
                                    ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
                                    pos_base, st));
-  for (int l = 0; l < c.n_layers; ++l) {
-    const LayerW& lw = bw.layers[l];
-    char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
-    char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
-    char* kc_lo = sp ? ws + w.cache_lo + (size_t)(2 * l) * w.cache_layer : nullptr;
-    char* vt_lo = sp ? ws + w.cache_lo + (size_t)(2 * l + 1) * w.cache_layer : nullptr;
-    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, p->bf, M, d, st, a_lo));
-    af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
-    LAUNCH(K_QKV, af::launch_gemm_qkv(p->bf, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
-    if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
-    af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
-    LAUNCH(K_ATTN, af::launch_attention(p->bf, q, kc, vt, att, (float*)(ws + w.attn_part),
-                                        ps.N, ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base,
-                                        st, sp ? &asp : nullptr));
-    LAUNCH(K_O, af::launch_gemm_resid(p->bf, att, att_lo, lw.w_o, lw.b_o, h, M, d, d, slab, st));
-    LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, p->bf, M, d, st, a_lo));
-    LAUNCH(K_MLP1, af::launch_gemm_gelu(p->bf, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
-                                        d, st));
-    LAUNCH(K_MLP2, af::launch_gemm_resid(p->bf, u, u_lo, lw.w_2, lw.b_2, h, M, d, p->dmlp,
-                                         slab, st));
-  }
   float* hf = (float*)(ws + w.hf);
+  if (p->bf) {
+    // bf16 path: the O-projection and MLP-down GEMMs write fp32 partial planes
+    // and one row-wise kernel adds bias + residual and emits the next LN.
+    LAUNCH(K_LN, af::launch_layernorm(h, bw.layers[0].ln1_g, bw.layers[0].ln1_b, a, true, M,
+                                      d, st, a_lo));
+    for (int l = 0; l < c.n_layers; ++l) {
+      const LayerW& lw = bw.layers[l];
+      char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
+      char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
+      char* kc_lo = sp ? ws + w.cache_lo + (size_t)(2 * l) * w.cache_layer : nullptr;
+      char* vt_lo = sp ? ws + w.cache_lo + (size_t)(2 * l + 1) * w.cache_layer : nullptr;
+      af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
+      LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+      if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+      af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
+      LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
+                                          ps.N, ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base,
+                                          st, sp ? &asp : nullptr));
+      int S = 1;
+      LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st));
+      LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_o, h, lw.ln2_g, lw.ln2_b, a, true, a_lo,
+                                       M, d, st));
+      LAUNCH(K_MLP1, af::launch_gemm_gelu(true, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
+                                          d, st));
+      LAUNCH(K_MLP2, af::launch_gemm_partial(u, u_lo, lw.w_2, slab, M, d, p->dmlp, &S, st));
+      if (l + 1 < c.n_layers) {
+        const LayerW& nx = bw.layers[l + 1];
+        LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_2, h, nx.ln1_g, nx.ln1_b, a, true, a_lo,
+                                         M, d, st));
+      } else {
+        LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_2, h, bw.ln_f_g, bw.ln_f_b, hf, false,
+                                         nullptr, M, d, st));
+      }
+    }
+  } else {
+    for (int l = 0; l < c.n_layers; ++l) {
+      const LayerW& lw = bw.layers[l];
+      char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
+      char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
+      LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, false, M, d, st));
+      af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, nullptr,
+                     nullptr, nullptr};
+      LAUNCH(K_QKV, af::launch_gemm_qkv(false, a, nullptr, lw.w_qkv, lw.b_qkv, M, 3 * d, d,
+                                        dst, st));
+      if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+      LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, ps.N, ps.R,
+                                          c.n_heads, p->dh, d, p->Lcap, pos_base, st));
+      LAUNCH(K_O, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
+                                        nullptr, st));
+      LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, false, M, d, st));
+      LAUNCH(K_MLP1, af::launch_gemm_gelu(false, a, nullptr, lw.w_1, lw.b_1, u, nullptr, M,
+                                          p->dmlp, d, st));
+      LAUNCH(K_MLP2, af::launch_gemm_resid(false, u, nullptr, lw.w_2, lw.b_2, h, M, d,
+                                           p->dmlp, nullptr, st));
+    }
+    LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
+  }
   float* head = (float*)(ws + w.head);
-  LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
   LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
                                             af::head_splits(M, 2 * c.C, d), st));
   return AF_OK;
@@ -284,8 +319,8 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
   const int per_lane = c.d / 64;
   if (c.d % 64 || (per_lane & (per_lane - 1)))
     return fail(AF_ERR_UNSUPPORTED, "d must be 64 times a power of two");
-  if (c.dtype == AF_BF16 && c.d % 128)
-    return fail(AF_ERR_UNSUPPORTED, "bf16 path needs d % 128 == 0");
+  if (c.dtype == AF_BF16 && c.d % 256)
+    return fail(AF_ERR_UNSUPPORTED, "bf16 path needs d % 256 == 0");
   af_plan* p = new (std::nothrow) af_plan();
   if (!p) return fail(AF_ERR_ARG, "out of host memory");
   p->cfg = c;

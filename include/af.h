@@ -65,7 +65,7 @@ typedef enum { AF_INIT_ZERO = 0, AF_INIT_GIVEN = 1, AF_INIT_PREV_FRAME = 2 } af_
 
 typedef struct {
   int C;          /* channels per token, 1..256 */
-  int d;          /* model width; multiple of 64 (AF_F32) or of 128 (AF_BF16) */
+  int d;          /* model width: 64 times a power of two; AF_BF16 needs d % 256 == 0 */
   int n_heads;    /* d / n_heads in {32, 64, 128} */
   int n_layers;   /* >= 1; MLP width is 4d */
   int max_len;    /* positions 0..max_len-1 (rows of the position table) */

@@ -63,7 +63,7 @@ def make_plan(lib, C=16, d=64, H=2, layers=1, max_len=64, dtype=B.AF_F32, T=1):
     (dict(d=96, H=3), B.AF_ERR_UNSUPPORTED),     # d/64 not a power of two
     (dict(d=64, H=3), B.AF_ERR_ARG),             # d % H
     (dict(d=256, H=16), B.AF_ERR_UNSUPPORTED),   # dh = 16
-    (dict(d=64, H=1, dtype=B.AF_BF16), B.AF_ERR_UNSUPPORTED),  # bf16 needs d % 128
+    (dict(d=64, H=1, dtype=B.AF_BF16), B.AF_ERR_UNSUPPORTED),  # bf16 needs d % 256
     (dict(layers=0), B.AF_ERR_ARG),
     (dict(max_len=0), B.AF_ERR_ARG),
     (dict(dtype=7), B.AF_ERR_ARG),
