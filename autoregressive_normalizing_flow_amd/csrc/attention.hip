@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
   bf16x8 qf[QB][KS], qfl[QB][KS];
   int qpos[QB];
+  const int wave_qmin = pos_base + q_lo + wave * QWAVE;   // smallest query position
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int t = q_lo + wave * QWAVE + qb * 16 + l16;
@@ -205,31 +206,38 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         }
       }
 
-    // online softmax (base 2) per query
+    // online softmax (base 2) per query.  The running max is kept in scaled
+    // units (m = max(s) * scale_log2) so that p = 2^(s * scale_log2 - m) is one
+    // FMA and one exp.  Tiles that lie wholly below every query of the wave
+    // and inside [k_begin, k_end) skip the per-score masking.
+    const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float tmax = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = key0 + kb * 16 + lg * 4 + r;
+            if (key > qpos[qb] || key >= k_end) s[kb][qb][r] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kb * 16 + lg * 4 + r;
-          float v = s[kb][qb][r] * a.scale_log2;
-          if (key > qpos[qb] || key >= k_end) v = -INFINITY;
-          s[kb][qb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, AF_WAVE));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, AF_WAVE));
-      const float m_new = fmaxf(m_run[qb], tmax);
-      const float alpha = exp2f(m_run[qb] - m_new);
+      const float m_new = fmaxf(m_run[qb], tmax * a.scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
       m_run[qb] = m_new;
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[kb][qb][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], a.scale_log2, -m_new));
           s[kb][qb][r] = p;
           lsum += p;
         }
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt)
   for (int j = 0; j < D4; ++j) o[j] = float4{0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < n_chunks; ++c) {
     const float* slot = base + (size_t)c * SLOT;
-    const float w = exp2f(slot[ATT_QT * DH + tq] - m);
+    const float w = __builtin_amdgcn_exp2f(slot[ATT_QT * DH + tq] - m);
     l += w * slot[ATT_QT * DH + ATT_QT + tq];
     const float4* src = (const float4*)(slot + (size_t)tq * DH + half * (DH / 2));
 #pragma unroll

@@ -30,9 +30,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Exact GELU u * Phi(u) with the device erff.
+// GELU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erf from Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7; erf(-x) = -erf(x).
+// One reciprocal, one exponential and a few FMAs, against the bf16 output
+// rounding of 2^-9.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f +
+           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float y = 1.0f - poly * __expf(-ax * ax);
+  return copysignf(y, x);
+}
 __device__ __forceinline__ float gelu_erf(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  return 0.5f * u * (1.0f + erf_as7126(u * 0.70710678118654752f));
 }
 
 // Storage index of processing index i in a sequence of length L: right-to-left

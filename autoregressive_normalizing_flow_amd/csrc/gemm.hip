@@ -35,6 +35,7 @@ struct EpiQKV {
   T* kc;
   T* vt;
   int M, R, d, dh, H, Lcap, pos_base;
+  int log2d, log2dh;   // d and dh are powers of two
   T* q_lo;    // split outputs (bf16 hi + lo) of the higher-precision forward, or NULL
   T* kc_lo;
   T* vt_lo;
@@ -58,7 +59,7 @@ struct EpiQKV {
     if (m >= M) return;
     const float4 b = *(const float4*)(bias + n);
     const float v0 = v[0] + b.x, v1 = v[1] + b.y, v2 = v[2] + b.z, v3 = v[3] + b.w;
-    const int which = n / d, hd = n - which * d;
+    const int which = n >> log2d, hd = n & (d - 1);
     const T h0 = from_f32<T>(v0), h1 = from_f32<T>(v1), h2 = from_f32<T>(v2),
             h3 = from_f32<T>(v3);
     const bool split = q_lo != nullptr;
@@ -70,7 +71,7 @@ struct EpiQKV {
       return;
     }
     const int nn = m / R, t = m - nn * R, p = pos_base + t;
-    const int head = hd / dh, e = hd - head * dh;
+    const int head = hd >> log2dh, e = hd & (dh - 1);
     const size_t base = (size_t)nn * H + head;
     if (which == 1) {
       store_vec4(kc + (base * Lcap + p) * dh + e, v0, v1, v2, v3);
@@ -659,6 +660,12 @@ static int tiles_of(TileChoice c, int M, int N) {
   return ((M + 32 * c.tm - 1) / (32 * c.tm)) * (N / (32 * c.tn));
 }
 
+static int ilog2(int v) {
+  int r = 0;
+  while ((1 << (r + 1)) <= v) ++r;
+  return r;
+}
+
 template <class Epi>
 static hipError_t run_f32(const void* A, const void* W, int M, int N, int K,
                           const Epi& epi, hipStream_t st, int splits = 1) {
@@ -686,11 +693,12 @@ hipError_t launch_gemm_qkv(bool bf, const void* A, const void* Alo, const void* 
                            hipStream_t st) {
   if (bf) {
     EpiQKV<bf16> e{bias, (bf16*)d.q, (bf16*)d.kc, (bf16*)d.vt, M, d.R, d.d, d.dh, d.H,
-                   d.Lcap, d.pos_base, (bf16*)d.q_lo, (bf16*)d.kc_lo, (bf16*)d.vt_lo};
+                   d.Lcap, d.pos_base, ilog2(d.d), ilog2(d.dh), (bf16*)d.q_lo,
+                   (bf16*)d.kc_lo, (bf16*)d.vt_lo};
     return run_bf16(A, Alo, W, M, N, K, e, st);
   }
   EpiQKV<float> e{bias, (float*)d.q, (float*)d.kc, (float*)d.vt, M, d.R, d.d, d.dh, d.H,
-                  d.Lcap, d.pos_base, nullptr, nullptr, nullptr};
+                  d.Lcap, d.pos_base, ilog2(d.d), ilog2(d.dh), nullptr, nullptr, nullptr};
   return run_f32(A, W, M, N, K, e, st);
 }
 
