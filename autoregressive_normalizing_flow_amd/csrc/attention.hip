@@ -52,6 +52,7 @@ struct AttnArgs {
   float* part;     // partial slots: [unit][ATT_QT][DH] O, then [ATT_QT] m, [ATT_QT] l
   int R, H, d, Lcap, pos_base, KC, U_nh;
   float scale_log2;
+  int xcd_map;     // 1: deal (sample, head) pairs to XCDs (needs N*H % 8 == 0)
 };
 
 __device__ __forceinline__ int att_chunks(int qt, int R, int pos_base, int KC) {
@@ -65,7 +66,10 @@ template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int QWAVE = 32, QB = QWAVE / 16;
   constexpr int KB = ATT_KT / 16, KS = DH / 32, DB = DH / 16;
-  constexpr int KLDS = DH + 8, VLDS = ATT_KT + 8;
+  // K rows padded to DH + 8 (16-byte fragment reads of 16 rows hit distinct
+  // banks); Vt rows padded to 68 bf16 = 136 B so the 8-byte fragment reads of
+  // 16 consecutive rows are conflict-free (rows then are 8-byte aligned only).
+  constexpr int KLDS = DH + 8, VLDS = ATT_KT + 4;
   constexpr int CK = ATT_KT * DH / 8 / 256;  // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) bf16 sK[2][ATT_KT * KLDS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][DH * VLDS];
@@ -73,8 +77,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sVl[2][SPLIT ? DH * VLDS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // unit -> (sample, head, query tile, chunk)
-  const int u = blockIdx.x;
+  // unit -> (sample, head, query tile, chunk).  Block ids go round-robin over
+  // the 8 XCDs; when N*H is a multiple of 8, (sample, head) pairs are dealt so
+  // that all units of one head run on one XCD and share its K/V in that L2.
+  int u = blockIdx.x;
+  if (a.xcd_map) {
+    const int xcd = u & 7, local = u >> 3;
+    const int j = local / a.U_nh;
+    u = (j * 8 + xcd) * a.U_nh + (local - j * a.U_nh);
+  }
   const int nh = u / a.U_nh;
   int rem = u - nh * a.U_nh;
   const int n = nh / a.H, head = nh - n * a.H;
@@ -164,8 +175,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       *(u32x4*)(&sK[buf][key * KLDS + dc * 8]) = rk[i];
       if (SPLIT) *(u32x4*)(&sKl[buf][key * KLDS + dc * 8]) = rkl[i];
       const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
-      *(u32x4*)(&sV[buf][drow * VLDS + kc8 * 8]) = rv[i];
-      if (SPLIT) *(u32x4*)(&sVl[buf][drow * VLDS + kc8 * 8]) = rvl[i];
+      {
+        uint2* dv = (uint2*)(&sV[buf][drow * VLDS + kc8 * 8]);
+        dv[0] = uint2{rv[i][0], rv[i][1]};
+        dv[1] = uint2{rv[i][2], rv[i][3]};
+      }
+      if (SPLIT) {
+        uint2* dv = (uint2*)(&sVl[buf][drow * VLDS + kc8 * 8]);
+        dv[0] = uint2{rvl[i][0], rvl[i][1]};
+        dv[1] = uint2{rvl[i][2], rvl[i][3]};
+      }
     }
   };
 
@@ -470,7 +489,8 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
                split ? (const bf16*)split->kc_lo : nullptr,
                split ? (const bf16*)split->vt_lo : nullptr,
                split ? (bf16*)split->out_lo : nullptr, part,
-               R, H, d, Lcap, pos_base, KC, U_nh, scale * 1.4426950408889634f};
+               R, H, d, Lcap, pos_base, KC, U_nh, scale * 1.4426950408889634f,
+               (N * H) % 8 == 0 ? 1 : 0};
     const dim3 grid(N * H * U_nh), comb(N * H * n_qt);
     const bool multi = U_nh > n_qt;
     switch (dh * 2 + (split ? 1 : 0)) {

@@ -349,15 +349,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 //
 // Same tiles, fragment layout and epilogues as gemm_bf16_kernel, but the
 // operand tiles go from global memory straight into LDS (no register
-// staging) through a 3-stage ring, so two k-tiles are in flight while one is
-// multiplied.  A DMA wave-instruction writes 64 consecutive 16-byte LDS slots
-// (lane i -> slot i); each lane therefore chooses which global chunk lands in
-// its slot, and the tile is stored XOR-swizzled: chunk c of row r sits at
-// slot 8r + (c ^ (r & 7)), which makes the 16-byte fragment reads (16 rows,
-// one chunk) conflict-free without padding.
+// staging) through a 3-stage ring.  A DMA wave-instruction writes 64
+// consecutive 16-byte LDS slots (lane i -> slot i); each lane therefore
+// chooses which global chunk lands in its slot, and the tile is stored
+// XOR-swizzled: chunk c of row r sits at slot 8r + (c ^ (r & 7)), which makes
+// the 16-byte fragment reads (16 rows, one chunk) conflict-free without
+// padding.
+//
+// Pipeline of k-step kt (BK = 64 = two MFMA k-slices F0, F1):
+//   1. read F1(kt) fragments from LDS  ||  MFMAs on F0(kt) (registers)
+//   2. wait: this wave's DMA of tile kt+1 landed, F1(kt) in registers; barrier
+//      (every wave's DMA of kt+1 landed, nobody reads tile kt's buffer again)
+//   3. DMA tile kt+3 into tile kt's buffer
+//   4. read F0(kt+1) from LDS  ||  MFMAs on F1(kt)
+// so LDS latency hides under MFMAs and two tiles are in flight during a step.
+//
+// The DMA is issued from inline asm (saddr form: 64-bit uniform base in SGPRs
+// + 32-bit per-lane byte offset) and every wait on it is explicit.  With the
+// builtin, the compiler's own wait insertion cannot tell the three ring
+// buffers apart across the loop back-edge and drains every DMA at the loop
+// head.  Only these asm statements write M0 in the kernel.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 template <int TM_, int TN_>
 struct DmaCfg {
@@ -368,73 +381,123 @@ struct DmaCfg {
   static constexpr int STAGE = (BM + BN) * BK;         // bf16 elements per stage
 };
 
-// s_waitcnt with vmcnt <= n (other counters unconstrained), gfx9 encoding.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from base + voff into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and
+// all its LDS reads have returned, then barrier.  The asm is a compiler memory
+// barrier as well, so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void dma_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// Per-lane byte offsets of the DMA chunks (k offset 0), computed once.
 template <class G>
-__device__ __forceinline__ void dma_stage(const bf16* __restrict__ A,
-                                          const bf16* __restrict__ W, bf16* stage, int m0,
-                                          int n0, int M, int K, int k0, int wave, int lane) {
-  bf16* sA = stage;
-  bf16* sB = stage + G::BM * G::BK;
+__device__ __forceinline__ void dma_offsets(uint32_t (&va)[G::IA], uint32_t (&vb)[G::IB],
+                                            int m0, int n0, int M, int K, int wave,
+                                            int lane) {
 #pragma unroll
   for (int jj = 0; jj < G::IA; ++jj) {
-    const int j = jj * 4 + wave;
-    const int q = j * 64 + lane;
+    const int q = (jj * 4 + wave) * 64 + lane;
     const int r = q >> 3, c = (q & 7) ^ (r & 7);
-    const int gm = min(m0 + r, M - 1);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(A + (size_t)gm * K + k0 + c * 8),
-                                     (lds_void_t*)(sA + j * 512), 16, 0, 0);
+    va[jj] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 8) * 2u;
   }
 #pragma unroll
   for (int jj = 0; jj < G::IB; ++jj) {
-    const int j = jj * 4 + wave;
-    const int q = j * 64 + lane;
+    const int q = (jj * 4 + wave) * 64 + lane;
     const int r = q >> 3, c = (q & 7) ^ (r & 7);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(W + (size_t)(n0 + r) * K + k0 + c * 8),
-                                     (lds_void_t*)(sB + j * 512), 16, 0, 0);
+    vb[jj] = ((uint32_t)(n0 + r) * (uint32_t)K + c * 8) * 2u;
   }
+}
+
+// DMA of the k-tile starting at column k0 into the stage at LDS address `st`.
+template <class G>
+__device__ __forceinline__ void dma_issue(const bf16* A, const bf16* W,
+                                          const uint32_t (&va)[G::IA],
+                                          const uint32_t (&vb)[G::IB], uint32_t st, int k0,
+                                          int wave) {
+  const bf16* ak = A + k0;
+  const bf16* wk = W + k0;
+#pragma unroll
+  for (int jj = 0; jj < G::IA; ++jj) dma16(ak, va[jj], st + (jj * 4 + wave) * 1024);
+#pragma unroll
+  for (int jj = 0; jj < G::IB; ++jj)
+    dma16(wk, vb[jj], st + G::BM * G::BK * 2 + (jj * 4 + wave) * 1024);
 }
 
 template <class G>
-__device__ __forceinline__ void dma_compute(f32x4 (&acc)[G::TN][G::TM], const bf16* stage,
-                                            int wm, int wn, int lane) {
+struct Frags {
+  bf16x8 w[G::TN], a[G::TM];
+};
+
+// Fragments of k-slice ks (0 or 1) of a stage.
+template <class G>
+__device__ __forceinline__ void frag_load(Frags<G>& f, const bf16* stage, int ks, int wm,
+                                          int wn, int lane) {
   const bf16* sA = stage;
   const bf16* sB = stage + G::BM * G::BK;
-  const int fr = lane & 15, sw = lane & 7;
+  const int fr = lane & 15, c = ks * 4 + (lane >> 4), sw = (c ^ (lane & 7)) << 3;
 #pragma unroll
-  for (int ks = 0; ks < G::BK / 32; ++ks) {
-    const int c = ks * 4 + (lane >> 4);
-    bf16x8 wf[G::TN], af[G::TM];
+  for (int j = 0; j < G::TN; ++j)
+    f.w[j] = *(const bf16x8*)(sB + (wn * G::WN + j * 16 + fr) * 64 + sw);
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j)
-      wf[j] = *(const bf16x8*)(sB + (wn * G::WN + j * 16 + fr) * 64 + ((c ^ sw) << 3));
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i)
-      af[i] = *(const bf16x8*)(sA + (wm * G::WM + i * 16 + fr) * 64 + ((c ^ sw) << 3));
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j)
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
-  }
+  for (int i = 0; i < G::TM; ++i)
+    f.a[i] = *(const bf16x8*)(sA + (wm * G::WM + i * 16 + fr) * 64 + sw);
 }
 
-// One k-step of the ring: tile kt sits in `cur`; the tile kt + 2 is issued
-// into `nxt` (the buffer read in step kt - 1) after the barrier.
+template <class G>
+__device__ __forceinline__ void frag_mma(f32x4 (&acc)[G::TN][G::TM], const Frags<G>& f) {
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.a[i], acc[j][i], 0, 0, 0);
+}
+
+// Scheduling hint for a half step: each LDS read followed by two MFMAs.
+template <class G>
+__device__ __forceinline__ void interleave_reads_mfma() {
+  constexpr int R = G::TM + G::TN, M = G::TM * G::TN;
+  constexpr int P = (2 * R <= M) ? 2 : 1;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, P, 0);   // MFMA
+  }
+  if (M > P * R) __builtin_amdgcn_sched_group_barrier(0x008, M - P * R, 0);
+}
+
 template <class G, int PENDING>
-__device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], const bf16* A,
-                                         const bf16* W, bf16* cur, bf16* nxt, int m0,
-                                         int n0, int M, int K, int k_next, bool issue,
+__device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], Frags<G>& f0,
+                                         Frags<G>& f1, const bf16* A, const bf16* W,
+                                         const uint32_t (&va)[G::IA],
+                                         const uint32_t (&vb)[G::IB], const bf16* cur,
+                                         const bf16* nxt, int k_issue, bool issue, bool next,
                                          int wave, int wm, int wn, int lane) {
-  wait_vmcnt<PENDING * G::IPW>();   // this wave's loads of tile kt are done
-  __builtin_amdgcn_s_barrier();     // ... and every wave's; step kt-1 is finished
-  if (issue) dma_stage<G>(A, W, nxt, m0, n0, M, K, k_next, wave, lane);
-  dma_compute<G>(acc, cur, wm, wn, lane);
+  frag_load<G>(f1, cur, 1, wm, wn, lane);
+  frag_mma<G>(acc, f0);
+  interleave_reads_mfma<G>();
+  dma_sync<PENDING * G::IPW>();
+  if (issue) dma_issue<G>(A, W, va, vb, lds_address(cur), k_issue, wave);
+  if (next) {
+    frag_load<G>(f0, nxt, 0, wm, wn, lane);
+    frag_mma<G>(acc, f1);
+    interleave_reads_mfma<G>();
+  } else {
+    frag_mma<G>(acc, f1);
+  }
 }
 
 template <int TM, int TN, class Epi>
@@ -446,7 +509,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 s1[G::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s2[G::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = N / G::BN;
   const int tiles_m = (M + G::BM - 1) / G::BM;
@@ -464,25 +528,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  dma_stage<G>(A, W, s0, m0, n0, M, K, kb, wave, lane);
-  if (KT > 1) dma_stage<G>(A, W, s1, m0, n0, M, K, kb + G::BK, wave, lane);
-  // steady state: one later tile pending while waiting for tile kt
+  uint32_t va[G::IA], vb[G::IB];
+  dma_offsets<G>(va, vb, m0, n0, M, K, wave, lane);
+  dma_issue<G>(A, W, va, vb, lds_address(s0), kb, wave);
+  if (KT > 1) dma_issue<G>(A, W, va, vb, lds_address(s1), kb + G::BK, wave);
+  if (KT > 2) dma_issue<G>(A, W, va, vb, lds_address(s2), kb + 2 * G::BK, wave);
+  if (KT > 2) dma_sync<2 * G::IPW>();
+  else if (KT > 1) dma_sync<G::IPW>();
+  else dma_sync<0>();
+  Frags<G> f0, f1;
+  frag_load<G>(f0, s0, 0, wm, wn, lane);
+
+  // steady state: every step issues tile kt + 3 and has tile kt + 2 in flight
   int kt = 0;
 #pragma clang loop unroll(disable)
-  for (; kt + 3 <= KT - 1; kt += 3) {
-    dma_step<G, 1>(acc, A, W, s0, s2, m0, n0, M, K, kb + (kt + 2) * G::BK, true, wave, wm, wn, lane);
-    dma_step<G, 1>(acc, A, W, s1, s0, m0, n0, M, K, kb + (kt + 3) * G::BK, true, wave, wm, wn, lane);
-    dma_step<G, 1>(acc, A, W, s2, s1, m0, n0, M, K, kb + (kt + 4) * G::BK, kt + 4 < KT, wave, wm, wn, lane);
+  for (; kt + 5 < KT; kt += 3) {
+    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s0, s1, kb + (kt + 3) * G::BK, true, true, wave, wm, wn, lane);
+    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s1, s2, kb + (kt + 4) * G::BK, true, true, wave, wm, wn, lane);
+    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s2, s0, kb + (kt + 5) * G::BK, true, true, wave, wm, wn, lane);
   }
-  // tail: kt .. KT-1 (at most 3 steps); buffer of tile t is t % 3
+  // tail; the buffer of tile t is t % 3
   for (; kt < KT; ++kt) {
-    bf16* cur = (kt % 3 == 0) ? s0 : (kt % 3 == 1) ? s1 : s2;
-    bf16* nxt = ((kt + 2) % 3 == 0) ? s0 : ((kt + 2) % 3 == 1) ? s1 : s2;
-    const bool issue = kt + 2 < KT;
-    if (kt + 1 < KT)
-      dma_step<G, 1>(acc, A, W, cur, nxt, m0, n0, M, K, kb + (kt + 2) * G::BK, issue, wave, wm, wn, lane);
+    const int b = kt % 3;
+    const bf16* cur = b == 0 ? s0 : b == 1 ? s1 : s2;
+    const bf16* nxt = b == 0 ? s1 : b == 1 ? s2 : s0;
+    if (kt + 2 < KT)
+      dma_step<G, 1>(acc, f0, f1, A, W, va, vb, cur, nxt, kb + (kt + 3) * G::BK, kt + 3 < KT, true, wave, wm, wn, lane);
     else
-      dma_step<G, 0>(acc, A, W, cur, nxt, m0, n0, M, K, 0, false, wave, wm, wn, lane);
+      dma_step<G, 0>(acc, f0, f1, A, W, va, vb, cur, nxt, 0, false, kt + 1 < KT, wave, wm, wn, lane);
   }
 
   const int mb = m0 + wm * G::WM + (lane & 15);

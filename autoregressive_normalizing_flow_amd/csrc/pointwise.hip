@@ -16,79 +16,89 @@ namespace af {
 
 // ---------------------------------------------------------------------------
 // shift + embed.  Block: 256 output columns x 16 rows.  The 16 shifted input
-// rows are staged in LDS (broadcast reads); each thread keeps its column of
-// W_in (one row of W_in^T) in registers, loaded 64 channels at a time with
-// independent float4 loads.
+// rows are staged in LDS, zero-padded to CP channels (broadcast reads); each
+// thread keeps its row of W_in (column of W_in^T) in registers, loaded with
+// independent float4 loads (clamped in bounds and masked, no branches).
+// CP = C rounded up within {16, 32, 48, 64}; C % 4 == 0.  Wider C goes
+// through embed_generic_kernel.
 // ---------------------------------------------------------------------------
 constexpr int EMB_ROWS = 16;
 constexpr int EMB_COLS = 256;
-constexpr int EMB_MAXC = 256;
-constexpr int EMB_CCH = 64;
 
+__device__ __forceinline__ float shifted_input(const float* __restrict__ x,
+                                               const float* __restrict__ x_last, int m,
+                                               int c, int M, int R, int C, int L, int s,
+                                               int dir) {
+  if (m >= M || c >= C) return 0.f;
+  const int n = m / R, t = m - n * R;
+  const int i = s + t;  // processing index
+  if (i > 0) return x[((size_t)n * L + storage_index(i - 1, L, dir)) * C + c];
+  return x_last ? x_last[(size_t)n * C + c] : 0.f;
+}
+
+template <int CP>
 __global__ __launch_bounds__(256) void embed_kernel(
     const float* __restrict__ x, const float* __restrict__ x_last,
     const float* __restrict__ w_in, const float* __restrict__ b_in,
     const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
     int d, int L, int s, int dir, int pos_base) {
-  __shared__ float s_in[EMB_ROWS][EMB_MAXC];
+  __shared__ __attribute__((aligned(16))) float s_in[EMB_ROWS][CP];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * EMB_COLS;
   const int m0 = blockIdx.y * EMB_ROWS;
   const int M = N * R;
-
-  // shifted inputs of the 16 rows
-  for (int e = tid; e < EMB_ROWS * C; e += 256) {
-    const int r = e / C, c = e - r * C;
-    const int m = m0 + r;
-    float v = 0.f;
-    if (m < M) {
-      const int n = m / R, t = m - n * R;
-      const int i = s + t;  // processing index
-      if (i > 0) {
-        v = x[((size_t)n * L + storage_index(i - 1, L, dir)) * C + c];
-      } else if (x_last) {
-        v = x_last[(size_t)n * C + c];
-      }
-    }
-    s_in[r][c] = v;
+  for (int e = tid; e < EMB_ROWS * CP; e += 256) {
+    const int r = e / CP, c = e - r * CP;
+    s_in[r][c] = shifted_input(x, x_last, m0 + r, c, M, R, C, L, s, dir);
+  }
+  const int j = min(j0 + tid, d - 1);
+  const float* wrow = w_in + (size_t)j * C;
+  float w[CP];
+#pragma unroll
+  for (int q = 0; q < CP / 4; ++q) {
+    const int c4 = min(4 * q, C - 4);   // in bounds; masked below
+    const float4 v = *(const float4*)(wrow + c4);
+    const float keep = (4 * q < C) ? 1.f : 0.f;
+    w[4 * q] = v.x * keep;
+    w[4 * q + 1] = v.y * keep;
+    w[4 * q + 2] = v.z * keep;
+    w[4 * q + 3] = v.w * keep;
   }
   __syncthreads();
-
-  const int j = j0 + tid;
-  if (j >= d) return;
-  float acc[EMB_ROWS];
-#pragma unroll
-  for (int r = 0; r < EMB_ROWS; ++r) acc[r] = 0.f;
-  const float* wrow = w_in + (size_t)j * C;
-  for (int c0 = 0; c0 < C; c0 += EMB_CCH) {
-    float w[EMB_CCH];
-    const int cn = min(EMB_CCH, C - c0);
-    if ((C & 3) == 0) {
-#pragma unroll
-      for (int q = 0; q < EMB_CCH / 4; ++q)
-        if (4 * q < cn) {
-          const float4 v = *(const float4*)(wrow + c0 + 4 * q);
-          w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-      for (int q = 0; q < EMB_CCH; ++q)
-        if (q < cn) w[q] = wrow[c0 + q];
-    }
-#pragma unroll
-    for (int q = 0; q < EMB_CCH; ++q)
-      if (q < cn) {
-#pragma unroll
-        for (int r = 0; r < EMB_ROWS; ++r) acc[r] += s_in[r][c0 + q] * w[q];
-      }
-  }
+  if (j0 + tid >= d) return;
   const float bj = b_in[j];
-#pragma unroll
+  // One row at a time (not unrolled): keeps only W's row and one float4 of
+  // input live, instead of every row's staged input.
+#pragma unroll 1
   for (int r = 0; r < EMB_ROWS; ++r) {
     const int m = m0 + r;
     if (m >= M) break;
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < CP / 4; ++q) {
+      const float4 in = *(const float4*)(&s_in[r][4 * q]);
+      a += in.x * w[4 * q] + in.y * w[4 * q + 1] + in.z * w[4 * q + 2] + in.w * w[4 * q + 3];
+    }
     const int t = m % R;
-    h[(size_t)m * d + j] = acc[r] + bj + pos[(size_t)(pos_base + t) * d + j];
+    h[(size_t)m * d + j] = a + bj + pos[(size_t)(pos_base + t) * d + j];
+  }
+}
+
+// Any C: one thread per output element, scalar loop (not on the hot path of
+// the workloads; kept for generality).
+__global__ __launch_bounds__(256) void embed_generic_kernel(
+    const float* __restrict__ x, const float* __restrict__ x_last,
+    const float* __restrict__ w_in, const float* __restrict__ b_in,
+    const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
+    int d, int L, int s, int dir, int pos_base) {
+  const int M = N * R;
+  const size_t total = (size_t)M * d;
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const int m = (int)(e / d), j = (int)(e - (size_t)m * d);
+    float a = b_in[j];
+    for (int c = 0; c < C; ++c)
+      a += shifted_input(x, x_last, m, c, M, R, C, L, s, dir) * w_in[(size_t)j * C + c];
+    h[e] = a + pos[(size_t)(pos_base + m % R) * d + j];
   }
 }
 
@@ -97,8 +107,20 @@ hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
                         int R, int C, int d, int L, int s, int dir, int pos_base,
                         hipStream_t st) {
   dim3 grid((d + EMB_COLS - 1) / EMB_COLS, (N * R + EMB_ROWS - 1) / EMB_ROWS);
-  hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, st, x, x_last, w_in, b_in,
-                     pos, h, N, R, C, d, L, s, dir, pos_base);
+#define AF_EMB(CP)                                                                    \
+  hipLaunchKernelGGL(embed_kernel<CP>, grid, dim3(256), 0, st, x, x_last, w_in, b_in, \
+                     pos, h, N, R, C, d, L, s, dir, pos_base)
+  if (C % 4 == 0 && C <= 16) AF_EMB(16);
+  else if (C % 4 == 0 && C <= 32) AF_EMB(32);
+  else if (C % 4 == 0 && C <= 48) AF_EMB(48);
+  else if (C % 4 == 0 && C <= 64) AF_EMB(64);
+  else {
+    const size_t total = (size_t)N * R * d;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(embed_generic_kernel, dim3(blocks), dim3(256), 0, st, x, x_last, w_in,
+                       b_in, pos, h, N, R, C, d, L, s, dir, pos_base);
+  }
+#undef AF_EMB
   return hipGetLastError();
 }
 

@@ -263,6 +263,9 @@ af_status check_ws(const af_plan* p, int N, int rows, void* ws, size_t ws_bytes,
                    WsLayout* out) {
   if (!ws) return fail(AF_ERR_ARG, "ws is NULL");
   if (((uintptr_t)ws & 255) != 0) return fail(AF_ERR_ARG, "ws must be 256-byte aligned");
+  // the bf16 GEMMs address activation rows with 32-bit byte offsets
+  if (p->bf && (uint64_t)N * rows * std::max(p->dmlp, p->cfg.d) * 2 >= (1ull << 32))
+    return fail(AF_ERR_UNSUPPORTED, "batch x rows too large: activations above 4 GiB");
   *out = layout(p, N, rows);
   if (ws_bytes < out->total)
     return fail(AF_ERR_WORKSPACE, "workspace too small: need " +
@@ -579,6 +582,8 @@ af_status afk_gemm_bf16(const void* a, const void* w, const float* bias, float* 
   if (!a || !w || !y) return fail(AF_ERR_ARG, "NULL argument");
   if (M < 1 || N < 64 || K < 64 || N % 64 || K % 64)
     return fail(AF_ERR_ARG, "need M >= 1, N % 64 == 0, K % 64 == 0");
+  if ((uint64_t)std::max(M, N) * K * 2 >= (1ull << 32))
+    return fail(AF_ERR_UNSUPPORTED, "a or w above 4 GiB");
   hipError_t e = af::launch_gemm_f32out(true, a, w, bias, y, M, N, K, (hipStream_t)stream);
   if (e != hipSuccess) return fail(AF_ERR_HIP, hipGetErrorString(e));
   return AF_OK;

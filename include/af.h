@@ -65,7 +65,8 @@ typedef enum { AF_INIT_ZERO = 0, AF_INIT_GIVEN = 1, AF_INIT_PREV_FRAME = 2 } af_
 
 typedef struct {
   int C;          /* channels per token, 1..256 */
-  int d;          /* model width: 64 times a power of two; AF_BF16 needs d % 256 == 0 */
+  int d;          /* model width: 64 times a power of two; AF_BF16 needs d % 256 == 0,
+                     and batch x rows x 4d x 2 bytes below 4 GiB per call */
   int n_heads;    /* d / n_heads in {32, 64, 128} */
   int n_layers;   /* >= 1; MLP width is 4d */
   int max_len;    /* positions 0..max_len-1 (rows of the position table) */
@@ -195,7 +196,8 @@ af_status afk_affine(int mode, const float *head, const float *src, float *dst,
 
 /* bf16 MFMA GEMM y[M, N] = a[M, K] * w[N, K]^T + bias[N] (bias may be NULL),
  * fp32 out, for unit parity.  a, w are bf16 bit patterns, row-major;
- * K % 64 == 0, N % 64 == 0.  Stream-ordered. */
+ * K % 64 == 0, N % 64 == 0; a and w below 4 GiB each (AF_ERR_UNSUPPORTED
+ * otherwise).  Stream-ordered. */
 af_status afk_gemm_bf16(const void *a, const void *w, const float *bias,
                         float *y, int M, int N, int K, void *stream);
 
