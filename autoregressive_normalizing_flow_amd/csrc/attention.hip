@@ -37,6 +37,7 @@ namespace af {
 // ---------------------------------------------------------------------------
 constexpr int ATT_QT = 128;   // queries per unit
 constexpr int ATT_KT = 64;    // keys per tile
+constexpr float RESCALE_LOG2 = 8.0f;   // lazy max: p stays below 2^8
 
 struct AttnArgs {
   const bf16* q;
@@ -63,7 +64,7 @@ __device__ __forceinline__ int att_chunks(int qt, int R, int pos_base, int KC) {
 // SPLIT: products of bf16 pairs keep three of the four partial products,
 // (a + a')(b + b') ~ ab + a'b + ab', for both S = K Q^T and O = P V.
 template <int DH, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   constexpr int QWAVE = 32, QB = QWAVE / 16;
   constexpr int KB = ATT_KT / 16, KS = DH / 32, DB = DH / 16;
   // K rows padded to DH + 8 (16-byte fragment reads of 16 rows hit distinct
@@ -125,19 +126,30 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  float m_run[QB], l_run[QB];
-  f32x4 acc_o[DB][QB];
+  float m_run[QB];
+  f32x4 acc_o[DB][QB], acc_l[QB];
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -1e30f;
-    l_run[qb] = 0.f;
+    acc_l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 rk[CK], rv[CK], rkl[CK], rvl[CK];
+  // Two register stages: tile kt+2 is loaded while kt is multiplied and
+  // tile kt+1 waits in registers to be stored into the other LDS buffer.
+  struct Stage {
+    u32x4 k[CK], v[CK], kl[CK], vl[CK];
+  } ra, rb;
   // keys outside [k_begin, k_end) are loaded as zeros (masked below)
-  auto gload = [&](int kt) {
+  auto gload = [&](Stage& st, int kt) {
+    u32x4(&rk)[CK] = st.k;
+    u32x4(&rv)[CK] = st.v;
+    u32x4(&rkl)[CK] = st.kl;
+    u32x4(&rvl)[CK] = st.vl;
     const int k0 = (t_begin + kt) * ATT_KT;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
@@ -167,7 +179,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       rvl[i] = vl;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Stage& st, int buf) {
+    const u32x4(&rk)[CK] = st.k;
+    const u32x4(&rv)[CK] = st.v;
+    const u32x4(&rkl)[CK] = st.kl;
+    const u32x4(&rvl)[CK] = st.vl;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * 256;
@@ -188,13 +204,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-#pragma clang loop unroll(disable)
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < n_tiles) gload(kt + 1);
+  auto compute = [&](int kt, int cur) {
     const int key0 = (t_begin + kt) * ATT_KT;
 
     f32x4 s[KB][QB];
@@ -225,15 +235,20 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         }
       }
 
-    // online softmax (base 2) per query.  The running max is kept in scaled
-    // units (m = max(s) * scale_log2) so that p = 2^(s * scale_log2 - m) is one
-    // FMA and one exp.  Tiles that lie wholly below every query of the wave
-    // and inside [k_begin, k_end) skip the per-score masking.
+    // online softmax (base 2) per query.  The running max m is kept in
+    // scaled units (p = 2^(s * scale_log2 - m): one FMA and one exp) and is
+    // raised only when some score of the wave exceeds it by more than
+    // RESCALE_LOG2: until then p may reach 2^RESCALE_LOG2, harmless in fp32
+    // and in bf16, and the accumulators are not touched.  The same m scales
+    // O and the row sum, so the result is that of the exact update.  Tiles
+    // wholly below every query of the wave and inside [k_begin, k_end) skip
+    // the masking; both tests are wave-uniform branches (the empty asm keeps
+    // the compiler from turning them into per-element selects).
     const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
+    if (need_mask) {
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float tmax = -INFINITY;
-      if (need_mask) {
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -241,29 +256,40 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
             const int key = key0 + kb * 16 + lg * 4 + r;
             if (key > qpos[qb] || key >= k_end) s[kb][qb][r] = -INFINITY;
           }
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, AF_WAVE));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, AF_WAVE));
-      const float m_new = fmaxf(m_run[qb], tmax * a.scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], a.scale_log2, -m_new));
-          s[kb][qb][r] = p;
-          lsum += p;
-        }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc_o[db][qb] *= alpha;
     }
+    float tmax[QB];
+    bool raise = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t = fmaxf(t, s[kb][qb][r]);
+      t = fmaxf(t, __shfl_xor(t, 16, AF_WAVE));
+      t = fmaxf(t, __shfl_xor(t, 32, AF_WAVE));
+      tmax[qb] = t * a.scale_log2;
+      raise |= tmax[qb] > m_run[qb] + RESCALE_LOG2;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], tmax[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        acc_l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc_o[db][qb] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[kb][qb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], a.scale_log2, -m_run[qb]));
 
     // O^T += Vt P^T over two 32-key steps
 #pragma unroll
@@ -280,6 +306,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
             pfl[qb][4 + r] = (bf16)(s[2 * c + 1][qb][r] - (float)pf[qb][4 + r]);
           }
         }
+      }
+      // row sums: an all-ones A operand sums P^T over the keys
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], acc_l[qb], 0, 0, 0);
+        if (SPLIT)
+          acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pfl[qb], acc_l[qb], 0, 0, 0);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -306,15 +339,29 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         }
       }
     }
-    if (kt + 1 < n_tiles) lstore(cur ^ 1);
+  };
+
+  gload(ra, 0);
+  if (n_tiles > 1) gload(rb, 1);
+  lstore(ra, 0);
+  __syncthreads();
+  // the buffer of tile t is t & 1
+#pragma clang loop unroll(disable)
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    if (kt + 2 < n_tiles) gload(ra, kt + 2);
+    compute(kt, 0);
+    if (kt + 1 < n_tiles) lstore(rb, 1);
+    __syncthreads();
+    if (kt + 1 >= n_tiles) break;
+    if (kt + 3 < n_tiles) gload(rb, kt + 3);
+    compute(kt + 1, 1);
+    if (kt + 2 < n_tiles) lstore(ra, 0);
     __syncthreads();
   }
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16, AF_WAVE);
-    l += __shfl_xor(l, 32, AF_WAVE);
+    const float l = acc_l[qb][0];
     const int tq = wave * QWAVE + qb * 16 + l16;   // query within the tile
     const int t = q_lo + tq;
     if (n_chunks == 1) {
@@ -345,6 +392,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   }
+}
+
+// Two waves per SIMD are the target: the compiler then keeps the MFMA
+// results in VGPRs (with a 512-register budget it moves them through AGPRs
+// around every VALU step of the softmax).  The wider variants need more than
+// 256 registers and keep the default budget.
+template <int DH, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+attn_bf16_kernel_o2(AttnArgs a) {
+  attn_bf16_body<DH, SPLIT>(a);
+}
+
+template <int DH, bool SPLIT>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+  attn_bf16_body<DH, SPLIT>(a);
 }
 
 // Merge the key chunks of every query tile that has more than one:
@@ -471,7 +533,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 template <int DH, bool SPLIT>
 static void attn_launch(const AttnArgs& a, dim3 grid, dim3 comb, bool multi, int n_qt,
                         hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
+  if constexpr (DH <= 64 && !SPLIT)
+    hipLaunchKernelGGL((attn_bf16_kernel_o2<DH, SPLIT>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
   if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(256), 0, st, a, n_qt);
 }
 

@@ -347,28 +347,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4).
 //
-// Same tiles, fragment layout and epilogues as gemm_bf16_kernel, but the
-// operand tiles go from global memory straight into LDS (no register
-// staging) through a 3-stage ring.  A DMA wave-instruction writes 64
-// consecutive 16-byte LDS slots (lane i -> slot i); each lane therefore
-// chooses which global chunk lands in its slot, and the tile is stored
-// XOR-swizzled: chunk c of row r sits at slot 8r + (c ^ (r & 7)), which makes
-// the 16-byte fragment reads (16 rows, one chunk) conflict-free without
-// padding.
+// Same block tiles, fragment layout and epilogues as gemm_bf16_kernel, with
+// 8 waves (two per SIMD).  The per-CU rate of LDS DMA grows with the number
+// of waves issuing it (about 26 B/clk with four waves, 37 with eight, from an
+// L2-resident source), so all eight waves load, and they split the work of a
+// k-tile instead of the output tile: waves 0-3 (group 0) multiply k-slice
+// 0..31 of every 64-wide k-tile and waves 4-7 (group 1) slice 32..63, each
+// over the full 2 x 2 wave-tile grid.  The two partial accumulators are added
+// through LDS at the end (fixed order: deterministic).
 //
-// Pipeline of k-step kt (BK = 64 = two MFMA k-slices F0, F1):
-//   1. read F1(kt) fragments from LDS  ||  MFMAs on F0(kt) (registers)
-//   2. wait: this wave's DMA of tile kt+1 landed, F1(kt) in registers; barrier
-//      (every wave's DMA of kt+1 landed, nobody reads tile kt's buffer again)
-//   3. DMA tile kt+3 into tile kt's buffer
-//   4. read F0(kt+1) from LDS  ||  MFMAs on F1(kt)
-// so LDS latency hides under MFMAs and two tiles are in flight during a step.
+// Operand tiles go from global memory straight into LDS through a 3-stage
+// ring (tiles kt+1 and kt+2 in flight while kt is multiplied).  A DMA
+// wave-instruction writes 64 consecutive 16-byte LDS slots (lane i -> slot
+// i); each lane therefore chooses which global chunk lands in its slot, and
+// the tile is stored XOR-swizzled: chunk c of row r sits at slot
+// 8r + (c ^ (r & 7)), which makes the 16-byte fragment reads (16 rows, one
+// chunk) conflict-free without padding.  One instruction moves 8 rows; the
+// BM/8 + BN/8 instructions of a stage are dealt round-robin to the 8 waves.
 //
 // The DMA is issued from inline asm (saddr form: 64-bit uniform base in SGPRs
-// + 32-bit per-lane byte offset) and every wait on it is explicit.  With the
-// builtin, the compiler's own wait insertion cannot tell the three ring
-// buffers apart across the loop back-edge and drains every DMA at the loop
-// head.  Only these asm statements write M0 in the kernel.
+// + 32-bit per-lane byte offset) and every wait on it is explicit; with the
+// builtin, the compiler's own wait insertion cannot tell the ring buffers
+// apart across the loop back-edge and drains every DMA at the loop head.
+// Only these asm statements write M0 in the kernel.
+// Requirements: N % BN == 0, k_len % 64 == 0, M * K * 2 and N * K * 2 below
+// 4 GiB (32-bit offsets).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -376,8 +379,12 @@ template <int TM_, int TN_>
 struct DmaCfg {
   static constexpr int TM = TM_, TN = TN_;
   static constexpr int WM = 16 * TM, WN = 16 * TN, BM = 2 * WM, BN = 2 * WN, BK = 64;
-  static constexpr int IA = BM / 32, IB = BN / 32;   // DMA instructions per wave per stage
-  static constexpr int IPW = IA + IB;
+  static constexpr int NA = BM / 8, NB = BN / 8;       // DMA instructions per stage
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "instructions split evenly per wave group");
+  static constexpr int CA = (NA + 7) / 8, CB = (NB + 7) / 8;   // per wave, at most
+  // instructions per stage of a wave in group 0 / group 1
+  static constexpr int IPW0 = (NA + 7) / 8 + (NB + 7) / 8;
+  static constexpr int IPW1 = (NA + 3) / 8 + (NB + 3) / 8;
   static constexpr int STAGE = (BM + BN) * BK;         // bf16 elements per stage
 };
 
@@ -403,38 +410,48 @@ __device__ __forceinline__ void dma_sync() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// Per-lane byte offsets of the DMA chunks (k offset 0), computed once.
+// The same with the vmcnt of this wave's group; PENDING = stages issued
+// after the one waited for.
+template <class G, int PENDING>
+__device__ __forceinline__ void dma_sync_group(int grp) {
+  if (grp == 0) dma_sync<PENDING * G::IPW0>();
+  else dma_sync<PENDING * G::IPW1>();
+}
+
+// Per-lane byte offsets of this wave's DMA chunks (k offset 0).
 template <class G>
-__device__ __forceinline__ void dma_offsets(uint32_t (&va)[G::IA], uint32_t (&vb)[G::IB],
+__device__ __forceinline__ void dma_offsets(uint32_t (&va)[G::CA], uint32_t (&vb)[G::CB],
                                             int m0, int n0, int M, int K, int wave,
                                             int lane) {
 #pragma unroll
-  for (int jj = 0; jj < G::IA; ++jj) {
-    const int q = (jj * 4 + wave) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ (r & 7);
-    va[jj] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 8) * 2u;
+  for (int i = 0; i < G::CA; ++i) {
+    const int q = min(wave + 8 * i, G::NA - 1);
+    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ (r & 7);
+    va[i] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 8) * 2u;
   }
 #pragma unroll
-  for (int jj = 0; jj < G::IB; ++jj) {
-    const int q = (jj * 4 + wave) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ (r & 7);
-    vb[jj] = ((uint32_t)(n0 + r) * (uint32_t)K + c * 8) * 2u;
+  for (int i = 0; i < G::CB; ++i) {
+    const int q = min(wave + 8 * i, G::NB - 1);
+    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ (r & 7);
+    vb[i] = ((uint32_t)(n0 + r) * (uint32_t)K + c * 8) * 2u;
   }
 }
 
-// DMA of the k-tile starting at column k0 into the stage at LDS address `st`.
+// This wave's share of the DMA of the k-tile at column k0 into the stage at
+// LDS address st.
 template <class G>
 __device__ __forceinline__ void dma_issue(const bf16* A, const bf16* W,
-                                          const uint32_t (&va)[G::IA],
-                                          const uint32_t (&vb)[G::IB], uint32_t st, int k0,
+                                          const uint32_t (&va)[G::CA],
+                                          const uint32_t (&vb)[G::CB], uint32_t st, int k0,
                                           int wave) {
   const bf16* ak = A + k0;
   const bf16* wk = W + k0;
 #pragma unroll
-  for (int jj = 0; jj < G::IA; ++jj) dma16(ak, va[jj], st + (jj * 4 + wave) * 1024);
+  for (int i = 0; i < G::CA; ++i)
+    if (wave + 8 * i < G::NA) dma16(ak, va[i], st + (wave + 8 * i) * 1024);
 #pragma unroll
-  for (int jj = 0; jj < G::IB; ++jj)
-    dma16(wk, vb[jj], st + G::BM * G::BK * 2 + (jj * 4 + wave) * 1024);
+  for (int i = 0; i < G::CB; ++i)
+    if (wave + 8 * i < G::NB) dma16(wk, vb[i], st + G::BM * 128 + (wave + 8 * i) * 1024);
 }
 
 template <class G>
@@ -466,52 +483,34 @@ __device__ __forceinline__ void frag_mma(f32x4 (&acc)[G::TN][G::TM], const Frags
       acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.a[i], acc[j][i], 0, 0, 0);
 }
 
-// Scheduling hint for a half step: each LDS read followed by two MFMAs.
-template <class G>
-__device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int R = G::TM + G::TN, M = G::TM * G::TN;
-  constexpr int P = (2 * R <= M) ? 2 : 1;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, P, 0);   // MFMA
-  }
-  if (M > P * R) __builtin_amdgcn_sched_group_barrier(0x008, M - P * R, 0);
-}
-
+// One k-step: wait for tile kt, issue tile kt+2 into the buffer of tile kt-1,
+// multiply this group's k-slice of tile kt.
 template <class G, int PENDING>
-__device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], Frags<G>& f0,
-                                         Frags<G>& f1, const bf16* A, const bf16* W,
-                                         const uint32_t (&va)[G::IA],
-                                         const uint32_t (&vb)[G::IB], const bf16* cur,
-                                         const bf16* nxt, int k_issue, bool issue, bool next,
-                                         int wave, int wm, int wn, int lane) {
-  frag_load<G>(f1, cur, 1, wm, wn, lane);
-  frag_mma<G>(acc, f0);
-  interleave_reads_mfma<G>();
-  dma_sync<PENDING * G::IPW>();
-  if (issue) dma_issue<G>(A, W, va, vb, lds_address(cur), k_issue, wave);
-  if (next) {
-    frag_load<G>(f0, nxt, 0, wm, wn, lane);
-    frag_mma<G>(acc, f1);
-    interleave_reads_mfma<G>();
-  } else {
-    frag_mma<G>(acc, f1);
-  }
+__device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], const bf16* A,
+                                         const bf16* W, const uint32_t (&va)[G::CA],
+                                         const uint32_t (&vb)[G::CB], const bf16* cur,
+                                         const bf16* nxt, int k_issue, bool issue, int wave,
+                                         int grp, int wm, int wn, int lane) {
+  dma_sync_group<G, PENDING>(grp);
+  if (issue) dma_issue<G>(A, W, va, vb, lds_address(nxt), k_issue, wave);
+  Frags<G> f;
+  frag_load<G>(f, cur, grp, wm, wn, lane);
+  frag_mma<G>(acc, f);
 }
 
 template <int TM, int TN, class Epi>
-__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(
+__global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
     int k_len, Epi epi) {
   using G = DmaCfg<TM, TN>;
-  __shared__ __attribute__((aligned(1024))) bf16 s0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 s1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 s2[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 ring[3 * G::STAGE];
+  bf16* const s0 = ring;
+  bf16* const s1 = ring + G::STAGE;
+  bf16* const s2 = ring + 2 * G::STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_n = N / G::BN;
   const int tiles_m = (M + G::BM - 1) / G::BM;
   const int tiles = tiles_m * tiles_n;
@@ -528,42 +527,62 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t va[G::IA], vb[G::IB];
+  uint32_t va[G::CA], vb[G::CB];
   dma_offsets<G>(va, vb, m0, n0, M, K, wave, lane);
   dma_issue<G>(A, W, va, vb, lds_address(s0), kb, wave);
   if (KT > 1) dma_issue<G>(A, W, va, vb, lds_address(s1), kb + G::BK, wave);
-  if (KT > 2) dma_issue<G>(A, W, va, vb, lds_address(s2), kb + 2 * G::BK, wave);
-  if (KT > 2) dma_sync<2 * G::IPW>();
-  else if (KT > 1) dma_sync<G::IPW>();
-  else dma_sync<0>();
-  Frags<G> f0, f1;
-  frag_load<G>(f0, s0, 0, wm, wn, lane);
 
-  // steady state: every step issues tile kt + 3 and has tile kt + 2 in flight
+  // steady state: tile kt + 1 stays in flight while waiting for tile kt
   int kt = 0;
 #pragma clang loop unroll(disable)
-  for (; kt + 5 < KT; kt += 3) {
-    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s0, s1, kb + (kt + 3) * G::BK, true, true, wave, wm, wn, lane);
-    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s1, s2, kb + (kt + 4) * G::BK, true, true, wave, wm, wn, lane);
-    dma_step<G, 1>(acc, f0, f1, A, W, va, vb, s2, s0, kb + (kt + 5) * G::BK, true, true, wave, wm, wn, lane);
+  for (; kt + 3 < KT; kt += 3) {
+    dma_step<G, 1>(acc, A, W, va, vb, s0, s2, kb + (kt + 2) * G::BK, true, wave, grp, wm, wn, lane);
+    dma_step<G, 1>(acc, A, W, va, vb, s1, s0, kb + (kt + 3) * G::BK, true, wave, grp, wm, wn, lane);
+    dma_step<G, 1>(acc, A, W, va, vb, s2, s1, kb + (kt + 4) * G::BK, kt + 4 < KT, wave, grp, wm, wn, lane);
   }
   // tail; the buffer of tile t is t % 3
   for (; kt < KT; ++kt) {
     const int b = kt % 3;
     const bf16* cur = b == 0 ? s0 : b == 1 ? s1 : s2;
-    const bf16* nxt = b == 0 ? s1 : b == 1 ? s2 : s0;
-    if (kt + 2 < KT)
-      dma_step<G, 1>(acc, f0, f1, A, W, va, vb, cur, nxt, kb + (kt + 3) * G::BK, kt + 3 < KT, true, wave, wm, wn, lane);
+    const bf16* nxt = b == 0 ? s2 : b == 1 ? s0 : s1;
+    if (kt + 1 < KT)
+      dma_step<G, 1>(acc, A, W, va, vb, cur, nxt, kb + (kt + 2) * G::BK, kt + 2 < KT, wave, grp, wm, wn, lane);
     else
-      dma_step<G, 0>(acc, f0, f1, A, W, va, vb, cur, nxt, 0, false, kt + 1 < KT, wave, wm, wn, lane);
+      dma_step<G, 0>(acc, A, W, va, vb, cur, nxt, 0, false, wave, grp, wm, wn, lane);
   }
 
+  // Add the two groups' partial sums: group 0 finishes column fragments
+  // j < JH, group 1 the rest; each hands the other half to its partner wave
+  // (same wm, wn) through LDS, which the ring no longer needs.
+  constexpr int JH = (G::TN + 1) / 2;
+  static_assert(G::TN * G::TM * 4 * 64 * 16 <= 3 * G::STAGE * 2, "reduction fits the ring");
+  float4* red = (float4*)ring;
+  const int wq = wave & 3;
+  dma_sync<0>();   // every wave is done reading the ring
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    if ((j < JH) == (grp == 0)) continue;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+      red[((wq * G::TN + j) * G::TM + i) * 64 + lane] =
+          float4{acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
+  }
+  dma_sync<0>();
   const int mb = m0 + wm * G::WM + (lane & 15);
   const int nb = n0 + wn * G::WN + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < G::TN; ++j)
+  for (int j = 0; j < G::TN; ++j) {
+    if ((j < JH) != (grp == 0)) continue;
 #pragma unroll
-    for (int i = 0; i < G::TM; ++i) epi.store4(mb + i * 16, nb + j * 16, acc[j][i]);
+    for (int i = 0; i < G::TM; ++i) {
+      const float4 o = red[((wq * G::TN + j) * G::TM + i) * 64 + lane];
+      f32x4 v = acc[j][i];
+      // group 0's partial first: the same order in both halves
+      if (grp == 0) v = f32x4{v[0] + o.x, v[1] + o.y, v[2] + o.z, v[3] + o.w};
+      else v = f32x4{o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]};
+      epi.store4(mb + i * 16, nb + j * 16, v);
+    }
+  }
 }
 
 // h[m, n] += bias[n] + sum_s slab[s][m][n], summed in split order.
@@ -695,7 +714,7 @@ static void launch_cfg(const void* A, const void* Alo, const void* W, int M, int
                        M, N, K, K / splits, epi);
   else
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<TM, TN, Epi>), dim3(tiles * splits),
-                       dim3(256), 0, st, (const bf16*)A, (const bf16*)W, M, N, K,
+                       dim3(512), 0, st, (const bf16*)A, (const bf16*)W, M, N, K,
                        K / splits, epi);
 }
 

@@ -17,23 +17,49 @@ namespace af {
 // ---------------------------------------------------------------------------
 // shift + embed.  Block: 256 output columns x 16 rows.  The 16 shifted input
 // rows are staged in LDS, zero-padded to CP channels (broadcast reads); each
-// thread keeps its row of W_in (column of W_in^T) in registers, loaded with
-// independent float4 loads (clamped in bounds and masked, no branches).
+// thread keeps its row of W_in (column of W_in^T) in registers.  Every global
+// load (staged inputs, W row, position values) is issued up front without
+// branches, so the kernel waits for memory once; the rows are then computed
+// with the next row's LDS operands in flight.
 // CP = C rounded up within {16, 32, 48, 64}; C % 4 == 0.  Wider C goes
 // through embed_generic_kernel.
 // ---------------------------------------------------------------------------
 constexpr int EMB_ROWS = 16;
 constexpr int EMB_COLS = 256;
 
-__device__ __forceinline__ float shifted_input(const float* __restrict__ x,
-                                               const float* __restrict__ x_last, int m,
-                                               int c, int M, int R, int C, int L, int s,
-                                               int dir) {
-  if (m >= M || c >= C) return 0.f;
-  const int n = m / R, t = m - n * R;
-  const int i = s + t;  // processing index
-  if (i > 0) return x[((size_t)n * L + storage_index(i - 1, L, dir)) * C + c];
-  return x_last ? x_last[(size_t)n * C + c] : 0.f;
+// Address and validity of shifted input element (m, c): token m's input is
+// the previous token (in processing order) of its sample, x_last (or zero)
+// for the first one.  Invalid elements read x[0] and are masked.
+__device__ __forceinline__ const float* shifted_src(const float* __restrict__ x,
+                                                   const float* __restrict__ x_last,
+                                                   int m, int c, int M, int R, int C,
+                                                   int L, int s, int dir, bool& valid) {
+  const int mm = min(m, M - 1), cc = min(c, C - 1);
+  const int n = mm / R, i = s + (mm - n * R);   // processing index
+  const bool first = i == 0;
+  valid = m < M && c < C && (!first || x_last != nullptr);
+  if (!valid) return x;
+  return first ? x_last + (size_t)n * C + cc
+               : x + ((size_t)n * L + storage_index(max(i - 1, 0), L, dir)) * C + cc;
+}
+
+template <int CP>
+__device__ __forceinline__ void emb_row(float4 (&v)[CP / 4], const float (*s_in)[CP], int r) {
+#pragma unroll
+  for (int q = 0; q < CP / 4; ++q) v[q] = *(const float4*)(&s_in[r][4 * q]);
+}
+
+template <int CP>
+__device__ __forceinline__ float emb_dot(const float4 (&v)[CP / 4], const float (&w)[CP]) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int q = 0; q < CP / 4; ++q) {
+    a0 = fmaf(v[q].x, w[4 * q], a0);
+    a1 = fmaf(v[q].y, w[4 * q + 1], a1);
+    a2 = fmaf(v[q].z, w[4 * q + 2], a2);
+    a3 = fmaf(v[q].w, w[4 * q + 3], a3);
+  }
+  return (a0 + a1) + (a2 + a3);
 }
 
 template <int CP>
@@ -42,46 +68,69 @@ __global__ __launch_bounds__(256) void embed_kernel(
     const float* __restrict__ w_in, const float* __restrict__ b_in,
     const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
     int d, int L, int s, int dir, int pos_base) {
+  constexpr int NF = (EMB_ROWS * CP + 255) / 256;   // staged inputs per thread
   __shared__ __attribute__((aligned(16))) float s_in[EMB_ROWS][CP];
+  __shared__ float s_pos[EMB_ROWS][EMB_COLS];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * EMB_COLS;
   const int m0 = blockIdx.y * EMB_ROWS;
   const int M = N * R;
-  for (int e = tid; e < EMB_ROWS * CP; e += 256) {
-    const int r = e / CP, c = e - r * CP;
-    s_in[r][c] = shifted_input(x, x_last, m0 + r, c, M, R, C, L, s, dir);
-  }
   const int j = min(j0 + tid, d - 1);
+
+  float xin[NF];
+  bool xok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int e = min(tid + f * 256, EMB_ROWS * CP - 1);
+    const int r = e / CP, c = e - r * CP;
+    xin[f] = *shifted_src(x, x_last, m0 + r, c, M, R, C, L, s, dir, xok[f]);
+  }
   const float* wrow = w_in + (size_t)j * C;
   float w[CP];
 #pragma unroll
   for (int q = 0; q < CP / 4; ++q) {
-    const int c4 = min(4 * q, C - 4);   // in bounds; masked below
-    const float4 v = *(const float4*)(wrow + c4);
-    const float keep = (4 * q < C) ? 1.f : 0.f;
+    const float4 v = *(const float4*)(wrow + min(4 * q, C - 4));   // in bounds
+    const float keep = (4 * q < C) ? 1.f : 0.f;                      // masked
     w[4 * q] = v.x * keep;
     w[4 * q + 1] = v.y * keep;
     w[4 * q + 2] = v.z * keep;
     w[4 * q + 3] = v.w * keep;
   }
+  float pv[EMB_ROWS];
+#pragma unroll
+  for (int r = 0; r < EMB_ROWS; ++r)
+    pv[r] = pos[(size_t)(pos_base + min(m0 + r, M - 1) % R) * d + j];
+  const float bj = b_in[j];
+
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int e = tid + f * 256;
+    if (e < EMB_ROWS * CP) (&s_in[0][0])[e] = xok[f] ? xin[f] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < EMB_ROWS; ++r) s_pos[r][tid] = pv[r];
   __syncthreads();
   if (j0 + tid >= d) return;
-  const float bj = b_in[j];
-  // One row at a time (not unrolled): keeps only W's row and one float4 of
-  // input live, instead of every row's staged input.
+
+  float4 va[CP / 4], vb[CP / 4];
+  emb_row<CP>(va, s_in, 0);
 #pragma unroll 1
-  for (int r = 0; r < EMB_ROWS; ++r) {
+  for (int r = 0; r < EMB_ROWS; r += 2) {
+    emb_row<CP>(vb, s_in, r + 1);
     const int m = m0 + r;
-    if (m >= M) break;
-    float a = 0.f;
-#pragma unroll
-    for (int q = 0; q < CP / 4; ++q) {
-      const float4 in = *(const float4*)(&s_in[r][4 * q]);
-      a += in.x * w[4 * q] + in.y * w[4 * q + 1] + in.z * w[4 * q + 2] + in.w * w[4 * q + 3];
-    }
-    const int t = m % R;
-    h[(size_t)m * d + j] = a + bj + pos[(size_t)(pos_base + t) * d + j];
+    if (m < M) h[(size_t)m * d + j] = emb_dot<CP>(va, w) + bj + s_pos[r][tid];
+    if (r + 2 < EMB_ROWS) emb_row<CP>(va, s_in, r + 2);
+    if (m + 1 < M) h[(size_t)(m + 1) * d + j] = emb_dot<CP>(vb, w) + bj + s_pos[r + 1][tid];
   }
+}
+
+__device__ __forceinline__ float shifted_input(const float* __restrict__ x,
+                                               const float* __restrict__ x_last, int m,
+                                               int c, int M, int R, int C, int L, int s,
+                                               int dir) {
+  bool ok;
+  const float v = *shifted_src(x, x_last, m, c, M, R, C, L, s, dir, ok);
+  return ok ? v : 0.f;
 }
 
 // Any C: one thread per output element, scalar loop (not on the hot path of
