@@ -411,44 +411,72 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge the key chunks of every query tile that has more than one:
 // O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, chunks in order.
-// Two threads per query row, each owning DH/2 dimensions; the chunk weights
-// are computed once per row.
+// Four threads per query row, each owning DH/4 dimensions; every load of a
+// thread (the chunks' m, l and O values) is issued before the first use, so
+// the kernel waits for memory once.  At most ATT_MAXC chunks are merged in
+// registers; longer ranges loop over groups of that many.
+constexpr int ATT_MAXC = 4;
+
 template <int DH>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt) {
+__global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a, int n_qt) {
   const int nh = blockIdx.x / n_qt, qt = blockIdx.x - nh * n_qt;
   const int n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
   if (n_chunks <= 1) return;
   int u0 = nh * a.U_nh;
   for (int q = 0; q < qt; ++q) u0 += att_chunks(q, a.R, a.pos_base, a.KC);
   const int n = nh / a.H, head = nh - n * a.H;
-  const int tq = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int tq = threadIdx.x >> 2, part = threadIdx.x & 3;
   const int t = qt * ATT_QT + tq;
   if (t >= a.R) return;
   constexpr int SLOT = ATT_QT * (DH + 2);
+  constexpr int DP = DH / 4, D4 = DP / 4;   // dimensions / float4 per thread
   const float* base = a.part + (size_t)u0 * SLOT;
-  float m = -1e30f;
-  for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, base[(size_t)c * SLOT + ATT_QT * DH + tq]);
-  float l = 0.f;
-  constexpr int D4 = DH / 8;   // float4 per thread
+  float m = -1e30f, l = 0.f;
   float4 o[D4];
 #pragma unroll
   for (int j = 0; j < D4; ++j) o[j] = float4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < n_chunks; ++c) {
-    const float* slot = base + (size_t)c * SLOT;
-    const float w = __builtin_amdgcn_exp2f(slot[ATT_QT * DH + tq] - m);
-    l += w * slot[ATT_QT * DH + ATT_QT + tq];
-    const float4* src = (const float4*)(slot + (size_t)tq * DH + half * (DH / 2));
+  for (int c0 = 0; c0 < n_chunks; c0 += ATT_MAXC) {
+    float mc[ATT_MAXC], lc[ATT_MAXC];
+    float4 oc[ATT_MAXC][D4];
+#pragma unroll
+    for (int c = 0; c < ATT_MAXC; ++c) {
+      const float* slot = base + (size_t)min(c0 + c, n_chunks - 1) * SLOT;
+      mc[c] = slot[ATT_QT * DH + tq];
+      lc[c] = slot[ATT_QT * DH + ATT_QT + tq];
+      const float4* src = (const float4*)(slot + (size_t)tq * DH + part * DP);
+#pragma unroll
+      for (int j = 0; j < D4; ++j) oc[c][j] = src[j];
+    }
+    float mg = m;
+#pragma unroll
+    for (int c = 0; c < ATT_MAXC; ++c)
+      if (c0 + c < n_chunks) mg = fmaxf(mg, mc[c]);
+    const float alpha = __builtin_amdgcn_exp2f(m - mg);
+    l *= alpha;
 #pragma unroll
     for (int j = 0; j < D4; ++j) {
-      const float4 v = src[j];
-      o[j].x += w * v.x;
-      o[j].y += w * v.y;
-      o[j].z += w * v.z;
-      o[j].w += w * v.w;
+      o[j].x *= alpha;
+      o[j].y *= alpha;
+      o[j].z *= alpha;
+      o[j].w *= alpha;
     }
+#pragma unroll
+    for (int c = 0; c < ATT_MAXC; ++c) {
+      if (c0 + c >= n_chunks) break;
+      const float w = __builtin_amdgcn_exp2f(mc[c] - mg);
+      l += w * lc[c];
+#pragma unroll
+      for (int j = 0; j < D4; ++j) {
+        o[j].x += w * oc[c][j].x;
+        o[j].y += w * oc[c][j].y;
+        o[j].z += w * oc[c][j].z;
+        o[j].w += w * oc[c][j].w;
+      }
+    }
+    m = mg;
   }
   const float inv = 1.0f / l;
-  const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + half * (DH / 2);
+  const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + part * DP;
 #pragma unroll
   for (int j = 0; j < D4; ++j) {
     const float y[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
@@ -537,7 +565,7 @@ static void attn_launch(const AttnArgs& a, dim3 grid, dim3 comb, bool multi, int
     hipLaunchKernelGGL((attn_bf16_kernel_o2<DH, SPLIT>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
-  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(256), 0, st, a, n_qt);
+  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(512), 0, st, a, n_qt);
 }
 
 hipError_t launch_attention(bool bf, const void* q, const void* kc,

@@ -54,3 +54,19 @@ __device__ __forceinline__ float gelu_erf(float u) {
 __device__ __forceinline__ int storage_index(int i, int L, int dir) {
   return dir ? (L - 1 - i) : i;
 }
+
+// Cross-workgroup hand-off without L2 maintenance.  The L2 of each XCD is not
+// coherent with the others, and an agent-scope fence (__threadfence) writes
+// back and invalidates the whole L2 of the XCD, which costs every other block
+// there its cached data.  Data passed between blocks therefore goes through
+// agent-scope (sc1) stores and loads, and the writer waits for its stores to
+// be acknowledged before it takes the ticket.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this lane's outstanding memory operations (stores included) are complete
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+

@@ -47,6 +47,8 @@ struct AffineArgs {
   float* res;          // [N][2]
   unsigned* counter;   // zero before the first launch; the kernel leaves it zero
   float* logdet;       // forward: logdet[n] += -sum log sigma (may be NULL)
+  unsigned* bad;       // inverse: set to `tag` (if still 0) when a residual sum is
+  unsigned tag;        // not finite; may be NULL
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

@@ -533,28 +533,26 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
   }
   block_sum2(s0, s1, red);
   if (threadIdx.x == 0) {
-    a.partials[((size_t)n * G + g) * 2] = s0;
-    a.partials[((size_t)n * G + g) * 2 + 1] = s1;
-    __threadfence();
+    coherent_store(&a.partials[((size_t)n * G + g) * 2], s0);
+    coherent_store(&a.partials[((size_t)n * G + g) * 2 + 1], s1);
+    wait_stores();
     ticket = atomicAdd(a.counter, 1u);
   }
   __syncthreads();
   if (ticket != (unsigned)(gridDim.x * gridDim.y) - 1) return;
   // last block: fixed-order final sums for every sample
-  __threadfence();
   for (int nn = 0; nn < a.N; ++nn) {
     float p0 = 0.f, p1 = 0.f;
     for (int gg = threadIdx.x; gg < G; gg += 256) {
-      p0 += __hip_atomic_load(&a.partials[((size_t)nn * G + gg) * 2],
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      p1 += __hip_atomic_load(&a.partials[((size_t)nn * G + gg) * 2 + 1],
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p0 += coherent_load(&a.partials[((size_t)nn * G + gg) * 2]);
+      p1 += coherent_load(&a.partials[((size_t)nn * G + gg) * 2 + 1]);
     }
     block_sum2(p0, p1, red);
     if (threadIdx.x == 0) {
       if (MODE == 0) {
         a.res[2 * nn] = p0;
         a.res[2 * nn + 1] = p1;
+        if (a.bad && !(isfinite(p0) && isfinite(p1))) atomicCAS(a.bad, 0u, a.tag);
       } else {
         a.res[2 * nn] = -p0;
         a.res[2 * nn + 1] = p1;
@@ -562,7 +560,7 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
       }
     }
   }
-  if (threadIdx.x == 0) *a.counter = 0u;
+  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
 }
 
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st) {

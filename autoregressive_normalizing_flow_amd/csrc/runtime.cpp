@@ -451,7 +451,9 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   const int nb = (L + B - 1) / B;
   float* xtmp = (float*)(ws + w.xtmp);
   float* res = (float*)(ws + w.res);
-  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 1, st));
+  // counter word of the affine kernel and the sticky non-finite tag after it
+  unsigned* bad = (unsigned*)(ws + w.counter) + 1;
+  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 2, st));
 
   const float* zin = z;
   for (int t = p->T - 1; t >= 0; --t) {
@@ -465,14 +467,17 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
                         af::head_splits(N * R, 2 * C, p->cfg.d), zin, xo, nullptr, N, R, C, L, s,
                         dir, (float*)(ws + w.partials), res,
-                        (unsigned*)(ws + w.counter), nullptr};
+                        (unsigned*)(ws + w.counter), nullptr, bad,
+                        (unsigned)(1 + t * nb + b)};
       int k = 0;
       bool nonfinite = false;
       for (k = 1; k <= kmax; ++k) {
         if (af_status e = run_net(p, p->blocks[t], ps, ws, w, st)) return e;
         LAUNCH(K_AFFINE, af::launch_affine(0, aa, st));
-        const bool test = tau > 0.f || k == kmax;
-        if (!test) continue;
+        // the residual is read back only for the stop test; at the cap (and
+        // in forced-count mode) a non-finite residual is caught through the
+        // sticky tag read once at the end
+        if (!(tau > 0.f && k < kmax)) continue;
         AF_HIP(hipMemcpyAsync(p->host_res, res, (size_t)N * 2 * sizeof(float),
                               hipMemcpyDeviceToHost, st));
         AF_HIP(hipStreamSynchronize(st));
@@ -501,7 +506,15 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     }
     zin = xo;
   }
+  AF_HIP(hipMemcpyAsync(p->host_res, bad, sizeof(unsigned), hipMemcpyDeviceToHost, st));
   AF_HIP(hipStreamSynchronize(st));
+  unsigned tag;
+  std::memcpy(&tag, p->host_res, sizeof(unsigned));
+  if (tag != 0) {
+    const int t = (int)(tag - 1) / nb, b = (int)(tag - 1) % nb;
+    return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +
+                                      ", Jacobi block " + std::to_string(b));
+  }
   return AF_OK;
 }
 

@@ -140,6 +140,67 @@ def affine_sweep(torch, binding, tokens, reps=5):
             "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
+def timed_call(torch, fn, reps):
+    """Median wall time (ms) of fn() over reps calls after one warm-up call."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return float(np.median(ts)), out
+
+
+def schedule_sweep(torch, binding, synth, reps):
+    """Jacobi block size, warm start and schedule on the deep block (the
+    frame480p and video21 shapes): tokens/s and iterations per block.  B = 1
+    is sequential decoding on the GPU (one update per token), the baseline
+    the Jacobi speed-up is quoted against."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    w = synth.WORKLOADS["frame480p"]
+    params = synth.make_params(w.block, 0)
+    plan = binding.AFPlan(w.block, params)
+    F = w.length
+    z = dev(synth.normal((1, F, w.block.C), 1))
+    rows = []
+    for B in (1, 64, 128, 256, 512, F):
+        ms, (x, it) = timed_call(torch, lambda: plan.inverse_jacobi(z, B, w.tau),
+                                 1 if B == 1 else reps)
+        rows.append({"B": B, "ms": round(ms, 2), "tokens_per_s": round(F / ms * 1e3, 1),
+                     "iters_total": int(it.sum()), "iters_max": int(it.max()),
+                     "blocks": int(it.size)})
+    seq = next(r for r in rows if r["B"] == 1)
+    for r in rows:
+        r["speedup_vs_sequential"] = round(seq["ms"] / r["ms"], 2)
+
+    v = synth.WORKLOADS["video21"]
+    T = v.length // F
+    vplan = binding.AFPlan(v.block, synth.make_params(v.block, 0))
+    zv = dev(synth.normal((1, v.length, v.block.C), 1))
+    warm = {}
+    for init in ("zero", "prev_frame"):
+        kw = dict(init=init, frame_len=F) if init == "prev_frame" else {}
+        ms, (xv, it) = timed_call(torch, lambda: vplan.inverse_jacobi(zv, F, v.tau, **kw), 1)
+        warm[init] = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1),
+                      "iters": it[0].tolist()}
+    # asymmetric schedule: frame 0 with B = 64, then its K/V as the prefix of
+    # frames 1.. solved with B = 512 and the previous-frame warm start
+    def asym():
+        x0, it0 = vplan.inverse_jacobi(zv[:, :F].contiguous(), 64, v.tau)
+        vplan.prefill(x0, rows=512)
+        x1, it1 = vplan.inverse_jacobi(zv[:, F:].contiguous(), 512, v.tau, init="prev_frame",
+                                       frame_len=F, prefix_len=F, x_last=x0[:, -1].contiguous())
+        return it0, it1
+    ms, (it0, it1) = timed_call(torch, asym, 1)
+    asym_row = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1),
+                "frame0_B64_iters_total": int(it0.sum()),
+                "frames1_B512_iters_total": int(it1.sum()), "frames": T}
+    return {"block_sweep_frame480p": rows, "warm_start_video21": warm,
+            "asymmetric_video21": asym_row}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +213,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to scale HBM counters)")
+    ap.add_argument("--schedule-sweep", action="store_true",
+                    help="only run the block-size / warm-start / schedule sweep "
+                         "(B = 1 is the GPU sequential baseline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -172,6 +236,9 @@ def main():
     from autoregressive_normalizing_flow_amd import binding, synth
     binding.load_library()
     assert torch.cuda.is_available(), "no GPU"
+    if args.schedule_sweep:
+        print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
+        return
 
     r = Runner(args.workload, torch, binding, synth)
     cfg, w = r.cfg, r.w

@@ -92,6 +92,23 @@ def test_affine_flags_nonfinite(B):
     assert ei.value.status == B.AF_ERR_NONFINITE
 
 
+@pytest.mark.parametrize("tau", [1e-3, 0.0])
+def test_inverse_flags_nonfinite(B, tau):
+    """A NaN latent in the second Jacobi block: reported as AF_ERR_NONFINITE
+    whether the residual is read back every iteration (tau > 0) or only the
+    sticky tag at the end (forced count)."""
+    say("inverse nonfinite", tau)
+    w = synth.WORKLOADS["tiny_f32"]
+    params = synth.make_params(w.block, 0)
+    plan = B.AFPlan(w.block, params)
+    z = synth.normal((1, 64, 16), 1)
+    z[0, 20, 5] = np.nan
+    with pytest.raises(B.AFError) as ei:
+        plan.inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
+    assert ei.value.status == B.AF_ERR_NONFINITE
+    assert "Jacobi block 1" in str(ei.value)
+
+
 # ---------------------------------------------------------------------------
 # fp32 path, end to end
 # ---------------------------------------------------------------------------
