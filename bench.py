@@ -140,6 +140,37 @@ def affine_sweep(torch, binding, tokens, reps=5):
             "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
+def kernel_sources_hash():
+    """Short hash of the HIP kernel sources (names and contents)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "autoregressive_normalizing_flow_amd", "csrc")
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, cls):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (scaled by the copy calibration), or None
+    when there is none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_sources_hash()
+    with open(path) as f:
+        for line in f:
+            t = line.split()
+            if len(t) >= 3 and t[0] == "traffic-per-launch" and t[1] == cls:
+                src = [x for x in t if x.startswith("sources=")]
+                if src and src[0] == "sources=" + sha:
+                    return int(t[2])
+    return None
+
+
 def timed_call(torch, fn, reps):
     """Median wall time (ms) of fn() over reps calls after one warm-up call."""
     fn()
@@ -207,7 +238,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="frame480p")
-    ap.add_argument("--cpu-tokens", type=int, default=768,
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
@@ -276,8 +307,8 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "flops_per_launch": flops, "avg_ms": round(avg_ms, 5),
-                "launches": n_launch}
+                "traffic": counter_traffic(w.name, dominant), "flops_per_launch": flops,
+                "avg_ms": round(avg_ms, 5), "launches": n_launch}
 
     # all GEMMs together (algorithmic flops / summed kernel time, one step)
     g_flops = sum(gemm_flops_per_launch(c, r.M, cfg) * breakdown[c]["launches"]
