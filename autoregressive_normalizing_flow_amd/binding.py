@@ -84,6 +84,8 @@ def load_library() -> ctypes.CDLL:
     L.af_forward.restype = st
     L.af_prefill.argtypes = [_P, _P, i, i, _P, sz, _P]
     L.af_prefill.restype = st
+    L.af_refresh_kv.argtypes = [_P, _P, i, i, i, _P, _P, sz, _P]
+    L.af_refresh_kv.restype = st
     L.af_inverse_jacobi.argtypes = [_P, _P, i, i, i, f, i, i, _P, i, i, _P, _P,
                                     ctypes.POINTER(ctypes.c_int32), _P, sz, _P]
     L.af_inverse_jacobi.restype = st
@@ -221,6 +223,14 @@ class AFPlan:
         ws = self.workspace(N, max(P, rows or 0))
         af_prefill(self, x_prefix, ws, stream)
 
+    def refresh_kv(self, x: torch.Tensor, prefix_len: int = 0,
+                   x_last: Optional[torch.Tensor] = None, stream=None):
+        """Recompute the cache rows prefix_len.. from their final tokens x."""
+        _tok(x, "x")
+        N, L, C = x.shape
+        ws = self.workspace(N, max(L, self._ws_key[1] if self._ws_key else 0))
+        af_refresh_kv(self, x, prefix_len, x_last, ws, stream)
+
     def inverse_jacobi(self, z: torch.Tensor, B: int, tau: float = 1e-3,
                        max_iters: int = 0, init: str = "zero",
                        x_init: Optional[torch.Tensor] = None, frame_len: int = 0,
@@ -265,6 +275,12 @@ def af_prefill(plan: AFPlan, x_prefix, ws, stream=None):
     N, P, C = x_prefix.shape
     _check(plan.L.af_prefill(plan.handle, _ptr(x_prefix), N, P, _ptr(ws),
                              ws.numel(), _stream(stream)), "af_prefill")
+
+
+def af_refresh_kv(plan: AFPlan, x, prefix_len: int, x_last, ws, stream=None):
+    N, L, C = x.shape
+    _check(plan.L.af_refresh_kv(plan.handle, _ptr(x), N, L, prefix_len, _ptr(x_last),
+                                _ptr(ws), ws.numel(), _stream(stream)), "af_refresh_kv")
 
 
 def af_inverse_jacobi(plan: AFPlan, z, B, tau, max_iters, init, x_init, frame_len,

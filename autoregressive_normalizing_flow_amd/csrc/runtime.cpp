@@ -422,6 +422,20 @@ af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
 }
 
+af_status af_refresh_kv(af_plan* p, const float* x, int N, int L, int prefix_len,
+                        const float* x_last, void* ws_, size_t ws_bytes, void* stream) {
+  if (!p || !x) return fail(AF_ERR_ARG, "NULL argument");
+  if (p->T != 1) return fail(AF_ERR_UNSUPPORTED, "af_refresh_kv needs a single-block plan");
+  if (N < 1 || L < 1 || prefix_len < 0 || prefix_len + L > p->cfg.max_len)
+    return fail(AF_ERR_ARG, "need N, L >= 1, prefix_len >= 0 and prefix_len + L <= max_len");
+  if (prefix_len > 0 && !x_last) return fail(AF_ERR_ARG, "x_last is required when prefix_len > 0");
+  WsLayout w;
+  if (af_status s = check_ws(p, N, L, ws_, ws_bytes, &w)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Pass ps{x, x_last, N, L, 0, L, prefix_len, 0, true, false};
+  return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
+}
+
 af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                             float tau, int max_iters, af_init init,
                             const float* x_init, int frame_len, int prefix_len,

@@ -232,6 +232,39 @@ def schedule_sweep(torch, binding, synth, reps):
             "asymmetric_video21": asym_row}
 
 
+def pipeline_bench(torch, binding, synth, reps):
+    """End-to-end inverse of the deep o shallow flow over 21 frames (deep:
+    the video21 block, shallow: the shallow_stack stack), three schedules:
+    stages (the deep block over all frames in one call, then the shallow
+    stack on all frames batched), frames one after another on one stream,
+    and the pipeline (shallow stack of frame n on a second stream and host
+    thread while the deep block solves frame n+1)."""
+    from autoregressive_normalizing_flow_amd.pipeline import DeepShallowFlow
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    v, sh = synth.WORKLOADS["video21"], synth.WORKLOADS["shallow_stack"]
+    F = v.frame_len
+    deep = binding.AFPlan(v.block, synth.make_params(v.block, 0))
+    shallow = binding.AFPlan(sh.block, synth.make_params(sh.block, 0, n_blocks=sh.n_blocks))
+    flow = DeepShallowFlow(deep, shallow, F)
+    z = dev(synth.normal((1, v.length, v.block.C), 1))
+    nf = v.length // F
+    out = {"frames": nf, "tokens": v.length}
+
+    def stages():
+        u, itd = deep.inverse_jacobi(z, F, v.tau, init="prev_frame", frame_len=F)
+        x, its = shallow.inverse_jacobi(u.reshape(nf, F, -1).contiguous(), F, v.tau)
+        return itd, its
+    for name, fn in (("stages", stages),
+                     ("frames_serial", lambda: flow.inverse(z, v.tau, pipelined=False)),
+                     ("pipelined", lambda: flow.inverse(z, v.tau, pipelined=True))):
+        ms, _ = timed_call(torch, fn, reps)
+        out[name] = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1)}
+    ms, _ = timed_call(torch, lambda: deep.inverse_jacobi(z, F, v.tau, init="prev_frame",
+                                                          frame_len=F), reps)
+    out["deep_only"] = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +277,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to scale HBM counters)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="only run the deep o shallow end-to-end inverse (stages, "
+                         "frames serial, pipelined)")
     ap.add_argument("--schedule-sweep", action="store_true",
                     help="only run the block-size / warm-start / schedule sweep "
                          "(B = 1 is the GPU sequential baseline)")
@@ -267,6 +303,9 @@ def main():
     from autoregressive_normalizing_flow_amd import binding, synth
     binding.load_library()
     assert torch.cuda.is_available(), "no GPU"
+    if args.pipeline:
+        print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1))), flush=True)
+        return
     if args.schedule_sweep:
         print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
         return

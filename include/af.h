@@ -135,6 +135,17 @@ af_status af_forward(af_plan *p, const float *x, float *z, float *logdet,
 af_status af_prefill(af_plan *p, const float *x_prefix, int N, int P,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Recompute the K/V cache rows of positions P..P+L-1 from their final tokens
+ * x [N, L, C] (STARFlow-V notes, 关键设计 3: the state of a finished block
+ * feeds the cache of the blocks after it; 一个完整示例, streaming: the last
+ * overlap latents are re-run through the deep block to rebuild the cache).
+ * Positions 0..P-1 must already be in ws; x_last [N, C] is the token at
+ * position P-1 (required when P > 0, NULL for zeros when P == 0).  With
+ * P == 0 this is af_prefill.  Only for n_blocks == 1.  Needs P + L <= max_len
+ * and ws_bytes >= af_workspace_bytes(p, N, L).  Stream-ordered. */
+af_status af_refresh_kv(af_plan *p, const float *x, int N, int L, int prefix_len,
+                        const float *x_last, void *ws, size_t ws_bytes, void *stream);
+
 /* Invert the stack by video-aware block-wise Jacobi (STARFlow-V notes, 关键设计
  * 3).  Blocks t = n_blocks-1..0 in turn; inside each, Jacobi blocks
  * [s, e) = [b*B, min(L, (b+1)*B)) in sequence.  A Jacobi block repeats
@@ -145,7 +156,9 @@ af_status af_prefill(af_plan *p, const float *x_prefix, int N, int P,
  * min(max_iters, e-s) updates (max_iters <= 0 means e-s).  tau <= 0 forces
  * that many updates.  The finished block's K/V are then recomputed from its
  * final x and kept in the cache (skipped when the block ran e-s updates, as
- * its last inputs were already final).
+ * its last inputs were already final, and for the call's last Jacobi block,
+ * which nothing in the call reads: a later call that continues after it
+ * refreshes those rows with af_refresh_kv).
  *   z        [N, L, C]   input
  *   x        [N, L, C]   output (may not alias z)
  *   x_init   [N, L, C]   AF_INIT_GIVEN only, else may be NULL

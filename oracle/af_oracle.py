@@ -21,6 +21,11 @@ Modeling with Autoregressive Normalizing Flows"), cited below as [notes, <sectio
 * [notes, 损失函数, L_NF]  the objective carries log|det J| of the forward map.
 * [notes, 一个完整示例, I2V]  observed frames are forward-encoded into the KV
   cache before autoregressive continuation.
+* [notes, 整体框架 and 关键设计 1]  the full flow is f = f_D o f_S: the shallow
+  stack maps each frame on its own (u_n = f_S(x_n)), the deep causal block maps
+  the whole sequence (z = f_D(u)); the likelihood factorises into the deep
+  term and one shallow Jacobian factor per frame; sampling inverts f_D frame
+  by frame and then f_S per frame.
 
 Readings where the notes leave a step open (each one plain and standard):
   R1  mask m: shift the sequence by one token (zero at the start of the
@@ -60,7 +65,8 @@ __all__ = [
     "to64", "layernorm", "gelu", "attention", "net_rows", "shift",
     "forward_block", "forward_stack", "inverse_sequential_block",
     "inverse_sequential_stack", "inverse_jacobi_block", "inverse_jacobi_stack",
-    "prefill", "jacobian_bruteforce", "direction_of",
+    "prefill", "jacobian_bruteforce", "direction_of", "forward_deep_shallow",
+    "inverse_deep_shallow",
 ]
 
 
@@ -361,6 +367,51 @@ def inverse_jacobi_stack(ps: Sequence[Dict], z: np.ndarray, n_heads: int,
                                      forced_iters=f)
         all_iters[t] = it
     return x, np.stack(all_iters)
+
+
+# --------------------------------------------------------------------------
+# deep o shallow composition  [notes, 整体框架; 关键设计 1, frame factorisation]
+# --------------------------------------------------------------------------
+def _frames(a: np.ndarray, frame_len: int) -> np.ndarray:
+    N, L, C = a.shape
+    return a.reshape(N * (L // frame_len), frame_len, C)
+
+
+def forward_deep_shallow(p_deep: Dict, ps_shallow: Sequence[Dict], x: np.ndarray,
+                         h_deep: int, h_shallow: int, frame_len: int):
+    """z = f_D(f_S(x)) with f_S applied to every frame of F = frame_len tokens
+    on its own and f_D to the whole sequence; returns (z, logdet) with
+    logdet[n] = log|det dz/dx| = logdet_D(u) + sum over frames of logdet_S."""
+    x = np.asarray(x, dtype=np.float64)
+    N, L, C = x.shape
+    u_f, ld_s = forward_stack(ps_shallow, _frames(x, frame_len), h_shallow)
+    z, ld_d = forward_block(p_deep, u_f.reshape(N, L, C), h_deep)
+    return z, ld_d + ld_s.reshape(N, L // frame_len).sum(axis=1)
+
+
+def inverse_deep_shallow(p_deep: Dict, ps_shallow: Sequence[Dict], z: np.ndarray,
+                         h_deep: int, h_shallow: int, frame_len: int,
+                         tau: float = 1e-3, max_iters: int = 0,
+                         deep_forced: Optional[Sequence[int]] = None,
+                         shallow_forced: Optional[Sequence] = None):
+    """x = f_S^-1(f_D^-1(z)).  f_D^-1 by block-wise Jacobi with one frame per
+    block and the previous-frame warm start; then f_S^-1 of every frame on its
+    own (its own stop test), each stack block by Jacobi over the frame.
+    Returns (x, deep iters [n_frames], shallow iters [N*n_frames][T][1])."""
+    z = np.asarray(z, dtype=np.float64)
+    N, L, C = z.shape
+    u, it_d = inverse_jacobi_block(p_deep, z, h_deep, frame_len, tau, max_iters,
+                                   "prev_frame", None, frame_len,
+                                   forced_iters=deep_forced)
+    u_f = _frames(u, frame_len)
+    xs, its = [], []
+    for i in range(u_f.shape[0]):
+        f = None if shallow_forced is None else shallow_forced[i]
+        x_i, it_i = inverse_jacobi_stack(ps_shallow, u_f[i:i + 1], h_shallow, frame_len,
+                                         tau, max_iters, forced_iters=f)
+        xs.append(x_i)
+        its.append(it_i)
+    return np.concatenate(xs, axis=0).reshape(N, L, C), it_d, np.stack(its)
 
 
 # --------------------------------------------------------------------------

@@ -147,6 +147,22 @@ def test_stack_restrictions(lib):
                                  0, None, x, iters, ctypes.c_void_p(1 << 20), big,
                                  None) == B.AF_ERR_UNSUPPORTED
     assert lib.af_prefill(h, buf, 1, 8, ctypes.c_void_p(1 << 20), big, None) == B.AF_ERR_UNSUPPORTED
+    assert lib.af_refresh_kv(h, buf, 1, 8, 0, None, ctypes.c_void_p(1 << 20), big,
+                             None) == B.AF_ERR_UNSUPPORTED
+    lib.af_plan_destroy(h)
+
+
+def test_refresh_kv_validation(lib):
+    st, h = make_plan(lib)          # max_len 64
+    assert st == B.AF_OK
+    buf = ctypes.c_void_p(_FAKE.ctypes.data)
+    ws = ctypes.c_void_p(1 << 20)
+    big = lib.af_workspace_bytes(h, 1, 64)
+    assert lib.af_refresh_kv(h, None, 1, 8, 0, None, ws, big, None) == B.AF_ERR_ARG
+    assert lib.af_refresh_kv(h, buf, 1, 8, 8, None, ws, big, None) == B.AF_ERR_ARG   # no x_last
+    assert lib.af_refresh_kv(h, buf, 1, 60, 8, buf, ws, big, None) == B.AF_ERR_ARG   # past max_len
+    assert lib.af_refresh_kv(h, buf, 1, 0, 0, None, ws, big, None) == B.AF_ERR_ARG
+    assert lib.af_refresh_kv(h, buf, 1, 8, 0, None, ws, 16, None) == B.AF_ERR_WORKSPACE
     lib.af_plan_destroy(h)
 
 

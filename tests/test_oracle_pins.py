@@ -356,3 +356,50 @@ def test_frames_are_independent_in_a_batch():
         np.testing.assert_allclose(ldn[0], ld[n], rtol=1e-14)
     xj, _ = O.inverse_jacobi_stack(ps, z, 2, B=3, tau=0.0)
     np.testing.assert_allclose(xj, x, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# 6. deep o shallow composition  [notes, 整体框架; 关键设计 1]
+# ---------------------------------------------------------------------------
+def deep_shallow(F=3, frames=2, C=2, seed=21):
+    L = F * frames
+    _, (pd,) = tiny(C=C, d=16, H=2, layers=1, max_len=L, seed=seed)
+    _, ps = tiny(C=C, d=16, H=2, layers=1, max_len=F, seed=seed + 1, n_blocks=2)
+    return scaled([pd], 4.0)[0], scaled(ps, 4.0), L
+
+
+def test_deep_shallow_jacobian_logdet_and_frame_causality():
+    """Brute force: log|det dz/dx| of z = f_D(f_S(x)) equals the returned
+    log-det, and z of frame n does not depend on x of a later frame (f_S
+    stays inside a frame, f_D is causal), while inside a frame the map is
+    dense (f_S alternates directions)."""
+    F, frames, C = 3, 2, 2
+    pd, ps, L = deep_shallow(F, frames, C)
+    x = np.random.default_rng(5).standard_normal((1, L, C))
+    f = lambda xx: O.forward_deep_shallow(pd, ps, xx, 2, 2, F)[0]
+    J = O.jacobian_bruteforce(f, x).reshape(L, C, L, C)
+    _, logdet = O.forward_deep_shallow(pd, ps, x, 2, 2, F)
+    _, lad = np.linalg.slogdet(J.reshape(L * C, L * C))
+    np.testing.assert_allclose(lad, logdet[0], rtol=0, atol=1e-8)
+    # frame 0 of z ignores frame 1 of x; frame 1 of z sees frame 0 of x
+    assert np.abs(J[:F, :, F:, :]).max() < 1e-9
+    assert np.abs(J[F:, :, :F, :]).max() > 1e-6
+    # within frame 0 the first token depends on the last (shallow R->L block)
+    assert np.abs(J[0, :, F - 1, :]).max() > 1e-6
+
+
+def test_deep_shallow_roundtrip_and_jacobi_schedule():
+    """The inverse with every Jacobi block run to its length is exact, and the
+    deep part equals block-wise Jacobi over frames with the warm start."""
+    F, frames, C = 4, 3, 2
+    pd, ps, L = deep_shallow(F, frames, C, seed=31)
+    x = np.random.default_rng(8).standard_normal((2, L, C))
+    z, _ = O.forward_deep_shallow(pd, ps, x, 2, 2, F)
+    xr, it_d, it_s = O.inverse_deep_shallow(pd, ps, z, 2, 2, F, tau=0.0)
+    np.testing.assert_allclose(xr, x, rtol=0, atol=1e-10)
+    assert np.all(it_d == F) and it_s.shape == (2 * frames, 2, 1) and np.all(it_s == F)
+    # with a stop threshold: the deep stage is the frame-block schedule
+    xt, it_d, _ = O.inverse_deep_shallow(pd, ps, z, 2, 2, F, tau=1e-3)
+    u, it_ref = O.inverse_jacobi_block(pd, z, 2, F, 1e-3, init="prev_frame", frame_len=F)
+    assert np.array_equal(it_d, it_ref)
+    assert np.abs(xt - x).max() < 0.2
