@@ -154,3 +154,42 @@ class DeepShallowFlow:
         torch.cuda.current_stream().wait_stream(s_deep)
         torch.cuda.current_stream().wait_stream(s_shallow)
         return x, it_d, it_s
+
+
+def stream_inverse(plan: AFPlan, z: torch.Tensor, window: int, overlap: int, B: int,
+                   tau: float = 1e-3, max_iters: int = 0, frame_len: int = 0,
+                   stream=None):
+    """Invert a sequence longer than the block's positions by a sliding window
+    (STARFlow-V notes, 一个完整示例, streaming generation): the first chunk
+    inverts z[:, :window] at positions 0..window-1; each later chunk re-encodes
+    the last ``overlap`` generated tokens into a fresh KV cache at positions
+    0..overlap-1 (af_prefill) and inverts the next window - overlap latents
+    after them.  Inside a chunk: block-wise Jacobi with blocks of B tokens,
+    zero init or the previous-frame warm start (frame_len > 0).  Needs
+    window <= the plan's max_len.  Returns (x, per-chunk iteration arrays)."""
+    if plan.T != 1:
+        raise ValueError("streaming runs on a single AF block")
+    if not 0 <= overlap < window <= plan.cfg.max_len:
+        raise ValueError("need 0 <= overlap < window <= max_len")
+    N, L, C = z.shape
+    kw = dict(init="prev_frame", frame_len=frame_len) if frame_len > 0 else {}
+    x = torch.empty_like(z)
+    plan.workspace(N, max(B, overlap))
+    its, done = [], 0
+    while done < L:
+        if done == 0:
+            n = min(window, L)
+            xc, it = plan.inverse_jacobi(z[:, :n].contiguous(), B, tau, max_iters,
+                                         stream=stream, **kw)
+        else:
+            n = min(window - overlap, L - done)
+            ov = x[:, done - overlap:done].contiguous()
+            if overlap > 0:
+                plan.prefill(ov, rows=B, stream=stream)
+            xc, it = plan.inverse_jacobi(
+                z[:, done:done + n].contiguous(), B, tau, max_iters, prefix_len=overlap,
+                x_last=ov[:, -1].contiguous() if overlap > 0 else None, stream=stream, **kw)
+        x[:, done:done + n].copy_(xc)
+        its.append(it[0].copy())
+        done += n
+    return x, its

@@ -262,6 +262,14 @@ def pipeline_bench(torch, binding, synth, reps):
     ms, _ = timed_call(torch, lambda: deep.inverse_jacobi(z, F, v.tau, init="prev_frame",
                                                           frame_len=F), reps)
     out["deep_only"] = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1)}
+    # the deep block alone by a sliding window of 7 frames with 1 frame of
+    # overlap re-encoded per chunk (chunks of 7, 6, 6 and 2 frames)
+    from autoregressive_normalizing_flow_amd.pipeline import stream_inverse
+    ms, (_, its) = timed_call(torch, lambda: stream_inverse(deep, z, 7 * F, F, F, v.tau,
+                                                            frame_len=F), reps)
+    out["deep_streaming_w7_o1"] = {"ms": round(ms, 2),
+                                   "tokens_per_s": round(v.length / ms * 1e3, 1),
+                                   "chunk_iters": [i.tolist() for i in its]}
     return out
 
 

@@ -21,6 +21,9 @@ Modeling with Autoregressive Normalizing Flows"), cited below as [notes, <sectio
 * [notes, 损失函数, L_NF]  the objective carries log|det J| of the forward map.
 * [notes, 一个完整示例, I2V]  observed frames are forward-encoded into the KV
   cache before autoregressive continuation.
+* [notes, 一个完整示例, streaming]  beyond the trained length the deep block
+  slides a window: after a chunk, the last overlap latents are re-run through
+  f_D to rebuild the KV cache and the next chunk continues from them.
 * [notes, 整体框架 and 关键设计 1]  the full flow is f = f_D o f_S: the shallow
   stack maps each frame on its own (u_n = f_S(x_n)), the deep causal block maps
   the whole sequence (z = f_D(u)); the likelihood factorises into the deep
@@ -66,7 +69,7 @@ __all__ = [
     "forward_block", "forward_stack", "inverse_sequential_block",
     "inverse_sequential_stack", "inverse_jacobi_block", "inverse_jacobi_stack",
     "prefill", "jacobian_bruteforce", "direction_of", "forward_deep_shallow",
-    "inverse_deep_shallow",
+    "inverse_deep_shallow", "inverse_streaming",
 ]
 
 
@@ -412,6 +415,47 @@ def inverse_deep_shallow(p_deep: Dict, ps_shallow: Sequence[Dict], z: np.ndarray
         xs.append(x_i)
         its.append(it_i)
     return np.concatenate(xs, axis=0).reshape(N, L, C), it_d, np.stack(its)
+
+
+# --------------------------------------------------------------------------
+# streaming: sliding window over the deep block  [notes, 一个完整示例, 流式生成]
+# --------------------------------------------------------------------------
+def inverse_streaming(p: Dict, z: np.ndarray, n_heads: int, window: int, overlap: int,
+                      B: int, tau: float = 1e-3, max_iters: int = 0, frame_len: int = 0,
+                      forced_iters: Optional[Sequence[Sequence[int]]] = None):
+    """Generate a sequence longer than the block's positions chunk by chunk.
+    The first chunk inverts z[:, :window] at positions 0..window-1.  Each later
+    chunk re-encodes the last `overlap` generated tokens into the KV cache at
+    positions 0..overlap-1 (a fresh cache) and inverts the next
+    window - overlap latents at positions overlap.. conditioned on them.
+    Inside a chunk: block-wise Jacobi with blocks of B tokens, zero init, or
+    the previous-frame warm start when frame_len > 0 (frames of the chunk).
+    Returns (x, per-chunk iteration arrays)."""
+    z = np.asarray(z, dtype=np.float64)
+    N, L, C = z.shape
+    if not 0 <= overlap < window:
+        raise ValueError("need 0 <= overlap < window")
+    init = "prev_frame" if frame_len > 0 else "zero"
+    xs, its = [], []
+    done, c = 0, 0
+    while done < L:
+        f = None if forced_iters is None else forced_iters[c]
+        if done == 0:
+            n = min(window, L)
+            x_c, it = inverse_jacobi_block(p, z[:, :n], n_heads, B, tau, max_iters, init,
+                                           None, frame_len, forced_iters=f)
+        else:
+            n = min(window - overlap, L - done)
+            ov = np.concatenate(xs, axis=1)[:, done - overlap:done]
+            cache, x_last = prefill(p, ov, n_heads) if overlap > 0 else (None, None)
+            x_c, it = inverse_jacobi_block(p, z[:, done:done + n], n_heads, B, tau, max_iters,
+                                           init, None, frame_len, pos0=overlap, cache=cache,
+                                           x_last=x_last, forced_iters=f)
+        xs.append(x_c)
+        its.append(it)
+        done += n
+        c += 1
+    return np.concatenate(xs, axis=1), its
 
 
 # --------------------------------------------------------------------------

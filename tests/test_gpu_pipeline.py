@@ -80,3 +80,21 @@ def test_deep_frames_equal_one_video_call(B):
     torch.cuda.synchronize()
     assert its == it_one[0].tolist()
     assert torch.equal(u, u_one)
+
+
+@pytest.mark.parametrize("frame_len", [0, 16])
+def test_streaming_window_vs_oracle(B, frame_len):
+    """Sliding-window generation past the block's positions: every chunk
+    against the oracle's same schedule, forced to the GPU's counts."""
+    from autoregressive_normalizing_flow_amd.pipeline import stream_inverse
+    say("streaming window", frame_len)
+    cfg = synth.BlockCfg(C=16, d=64, n_heads=2, n_layers=1, max_len=48, dtype="f32")
+    params = synth.make_params(cfg, 3, randomize_aux=True)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((2, 112, 16), 4)
+    xg, its = stream_inverse(plan, to_dev(z), window=48, overlap=16, B=16, tau=1e-3,
+                             frame_len=frame_len)
+    print("chunk iters", [i.tolist() for i in its])
+    xo, _ = O.inverse_streaming(O.to64(params[0]), z, 2, 48, 16, 16, 1e-3,
+                                frame_len=frame_len, forced_iters=[list(i) for i in its])
+    assert rel_l2(to_np(xg), xo) < TOL_F32

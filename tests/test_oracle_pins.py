@@ -403,3 +403,37 @@ def test_deep_shallow_roundtrip_and_jacobi_schedule():
     u, it_ref = O.inverse_jacobi_block(pd, z, 2, F, 1e-3, init="prev_frame", frame_len=F)
     assert np.array_equal(it_d, it_ref)
     assert np.abs(xt - x).max() < 0.2
+
+
+# ---------------------------------------------------------------------------
+# 7. streaming window  [notes, 一个完整示例, 流式生成]
+# ---------------------------------------------------------------------------
+def test_streaming_window_chunks_are_fixed_points_of_their_window():
+    """Run to the block length, each chunk solves its window exactly: the
+    forward pass over [re-encoded overlap ++ chunk] at positions 0.. returns
+    the chunk's latents; a window covering the whole sequence is plain
+    block-wise Jacobi."""
+    W, ov, L, C = 8, 3, 18, 2
+    _, (p,) = tiny(C=C, d=16, H=2, layers=1, max_len=W, seed=41)
+    p = scaled([p], 4.0)[0]
+    z = np.random.default_rng(9).standard_normal((2, L, C))
+    x, its = O.inverse_streaming(p, z, 2, W, ov, B=4, tau=0.0)
+    assert [len(i) for i in its] == [2, 2, 2]    # chunks of 8, 5 and 5 tokens
+    done = 0
+    for c, it in enumerate(its):
+        n = W if c == 0 else min(W - ov, L - done)
+        if c == 0:
+            zc, _ = O.forward_block(p, x[:, :n], 2)
+        else:
+            win = x[:, done - ov:done + n]
+            zc = O.forward_block(p, win, 2)[0][:, ov:]
+        np.testing.assert_allclose(zc, z[:, done:done + n], rtol=0, atol=1e-10)
+        done += n
+    assert done == L
+    # whole sequence inside one window
+    _, (q,) = tiny(C=C, d=16, H=2, layers=1, max_len=L, seed=41)
+    q = scaled([q], 4.0)[0]
+    xw, itw = O.inverse_streaming(q, z, 2, L, 2, B=4, tau=1e-3)
+    xj, itj = O.inverse_jacobi_block(q, z, 2, 4, 1e-3)
+    np.testing.assert_array_equal(xw, xj)
+    assert np.array_equal(itw[0], itj)
