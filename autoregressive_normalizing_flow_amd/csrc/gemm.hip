@@ -55,9 +55,9 @@ struct EpiQKV {
     else
       vt[(base * dh + e) * Lcap + p] = from_f32<T>(v);
   }
-  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
-    const float4 b = *(const float4*)(bias + n);
     const float v0 = v[0] + b.x, v1 = v[1] + b.y, v2 = v[2] + b.z, v3 = v[3] + b.w;
     const int which = n >> log2d, hd = n & (d - 1);
     const T h0 = from_f32<T>(v0), h1 = from_f32<T>(v1), h2 = from_f32<T>(v2),
@@ -101,10 +101,10 @@ struct EpiResid {
     float* p = h + (size_t)m * N + n;
     *p = *p + (v + bias[n]);
   }
-  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
     float4* p = (float4*)(h + (size_t)m * N + n);
-    const float4 b = *(const float4*)(bias + n);
     float4 o = *p;
     o.x += v[0] + b.x;
     o.y += v[1] + b.y;
@@ -124,9 +124,9 @@ struct EpiGelu {
     if (m >= M) return;
     out[(size_t)m * N + n] = from_f32<T>(gelu_erf(v + bias[n]));
   }
-  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
-    const float4 b = *(const float4*)(bias + n);
     const float g0 = gelu_erf(v[0] + b.x), g1 = gelu_erf(v[1] + b.y),
                 g2 = gelu_erf(v[2] + b.z), g3 = gelu_erf(v[3] + b.w);
     store_vec4(out + (size_t)m * N + n, g0, g1, g2, g3);
@@ -145,9 +145,11 @@ struct EpiF32 {
     if (m >= M) return;
     out[(size_t)m * N + n] = v + (bias ? bias[n] : 0.f);
   }
-  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ float4 bias4(int n) const {
+    return bias ? *(const float4*)(bias + n) : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
-    float4 b = bias ? *(const float4*)(bias + n) : float4{0.f, 0.f, 0.f, 0.f};
     *(float4*)(out + (size_t)m * N + n) =
         float4{v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w};
   }
@@ -168,7 +170,8 @@ struct EpiPlane {
 struct EpiSlab {
   float* slab;
   int M, N, tiles;  // tiles per split: blockIdx.x / tiles is the split index
-  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ float4 bias4(int) const { return float4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4) const {
     if (m >= M) return;
     float* plane = slab + (size_t)(blockIdx.x / tiles) * M * N;
     *(float4*)(plane + (size_t)m * N + n) = float4{v[0], v[1], v[2], v[3]};
@@ -341,7 +344,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < G::TN; ++j)
 #pragma unroll
-    for (int i = 0; i < G::TM; ++i) epi.store4(mb + i * 16, nb + j * 16, acc[j][i]);
+    for (int i = 0; i < G::TM; ++i)
+      epi.store4(mb + i * 16, nb + j * 16, acc[j][i], epi.bias4(nb + j * 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -553,11 +557,20 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(
 
   // Add the two groups' partial sums: group 0 finishes column fragments
   // j < JH, group 1 the rest; each hands the other half to its partner wave
-  // (same wm, wn) through LDS, which the ring no longer needs.
+  // (same wm, wn) through LDS, which the ring no longer needs.  The epilogue's
+  // bias values are loaded first, so their latency hides under the exchange.
   constexpr int JH = (G::TN + 1) / 2;
   static_assert(G::TN * G::TM * 4 * 64 * 16 <= 3 * G::STAGE * 2, "reduction fits the ring");
   float4* red = (float4*)ring;
   const int wq = wave & 3;
+  const int mb = m0 + wm * G::WM + (lane & 15);
+  const int nb = n0 + wn * G::WN + 4 * (lane >> 4);
+  float4 bv[JH];
+#pragma unroll
+  for (int jl = 0; jl < JH; ++jl) {
+    const int j = grp == 0 ? jl : min(JH + jl, G::TN - 1);
+    bv[jl] = epi.bias4(nb + j * 16);
+  }
   dma_sync<0>();   // every wave is done reading the ring
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
@@ -568,11 +581,12 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(
           float4{acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
   }
   dma_sync<0>();
-  const int mb = m0 + wm * G::WM + (lane & 15);
-  const int nb = n0 + wn * G::WN + 4 * (lane >> 4);
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
     if ((j < JH) != (grp == 0)) continue;
+    // j is a compile-time constant here: group 0 holds j < JH in bv[j],
+    // group 1 holds j >= JH in bv[j - JH]
+    const float4 b = j < JH ? bv[j < JH ? j : 0] : bv[j >= JH ? j - JH : 0];
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
       const float4 o = red[((wq * G::TN + j) * G::TM + i) * 64 + lane];
@@ -580,7 +594,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(
       // group 0's partial first: the same order in both halves
       if (grp == 0) v = f32x4{v[0] + o.x, v[1] + o.y, v[2] + o.z, v[3] + o.w};
       else v = f32x4{o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]};
-      epi.store4(mb + i * 16, nb + j * 16, v);
+      epi.store4(mb + i * 16, nb + j * 16, v, b);
     }
   }
 }
