@@ -96,6 +96,11 @@ def load_library() -> ctypes.CDLL:
     L.af_profile_read.argtypes = [_P, ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_double)]
     L.af_profile_read.restype = st
+    L.af_plan_set_graphs.argtypes = [_P, i]
+    L.af_plan_set_graphs.restype = st
+    L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
+                                      ctypes.POINTER(ctypes.c_longlong)]
+    L.af_plan_graph_stats.restype = st
     L.afk_affine_partials_bytes.argtypes = [i, i, i]
     L.afk_affine_partials_bytes.restype = sz
     L.afk_affine.argtypes = [i, _P, _P, _P, i, i, i, _P, _P, sz, i, _P]
@@ -260,6 +265,17 @@ class AFPlan:
         _check(self.L.af_profile_read(self.handle, ctypes.byref(n), ctypes.byref(ms)),
                "af_profile_read")
         return n.value, ms.value
+
+    # graph replay of the Jacobi update ------------------------------------
+    def set_graphs(self, enable: bool):
+        _check(self.L.af_plan_set_graphs(self.handle, int(bool(enable))), "af_plan_set_graphs")
+
+    def graph_stats(self) -> Tuple[int, int]:
+        c = ctypes.c_longlong()
+        r = ctypes.c_longlong()
+        _check(self.L.af_plan_graph_stats(self.handle, ctypes.byref(c), ctypes.byref(r)),
+               "af_plan_graph_stats")
+        return c.value, r.value
 
 
 # ---------------------------------------------------------------------------

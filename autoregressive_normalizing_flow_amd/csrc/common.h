@@ -67,6 +67,11 @@ __device__ __forceinline__ void coherent_store(float* p, float v) {
 __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// store that bypasses the device caches, for host-mapped memory the host
+// reads once the stream has drained
+__device__ __forceinline__ void system_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 // this lane's outstanding memory operations (stores included) are complete
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -49,6 +49,7 @@ struct AffineArgs {
   float* logdet;       // forward: logdet[n] += -sum log sigma (may be NULL)
   unsigned* bad;       // inverse: set to `tag` (if still 0) when a residual sum is
   unsigned tag;        // not finite; may be NULL
+  float* res_host;     // inverse: host-mapped copy of res written at the end, or NULL
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

@@ -552,6 +552,10 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
       if (MODE == 0) {
         a.res[2 * nn] = p0;
         a.res[2 * nn + 1] = p1;
+        if (a.res_host) {
+          system_store(&a.res_host[2 * nn], p0);
+          system_store(&a.res_host[2 * nn + 1], p1);
+        }
         if (a.bad && !(isfinite(p0) && isfinite(p1))) atomicCAS(a.bad, 0u, a.tag);
       } else {
         a.res[2 * nn] = -p0;

@@ -26,8 +26,12 @@ namespace {
 
 thread_local std::string g_err;
 
+// Record the failure; a failed HIP call's error is also taken out of the
+// runtime's per-thread last-error state, so that it does not surface in the
+// caller's next unrelated HIP call.
 af_status fail(af_status s, const std::string& msg) {
   g_err = msg;
+  if (s == AF_ERR_HIP) (void)hipGetLastError();
   return s;
 }
 
@@ -63,6 +67,27 @@ const char* kclass_names[K_NCLASS] = {"embed", "layernorm", "gemm_qkv", "gemm_o"
                                       "gemm_mlp1", "gemm_mlp2", "gemm_head",
                                       "attention", "affine"};
 
+// Key of a captured Jacobi update: every host value its launches bake in.
+struct GraphKey {
+  const void* block;
+  const float *src, *x_last, *z;
+  float* res_host;
+  const char* ws;
+  int device, N, L, s, R, P, dir, rows;
+  unsigned tag;
+  bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
+};
+
+static_assert(sizeof(GraphKey) == 6 * sizeof(void*) + 10 * sizeof(int), "GraphKey has padding");
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec = nullptr;
+  uint64_t used = 0;
+};
+
+constexpr int kGraphCacheCap = 128;
+
 }  // namespace
 
 struct af_plan {
@@ -74,10 +99,17 @@ struct af_plan {
   std::vector<BlockW> blocks;
   float* host_res = nullptr;  // pinned [res_cap][2]
   int res_cap = 0;
+  float* host_res_dev = nullptr;  // the same memory as the device sees it
   // profiling
   int prof_class = -1;
   std::vector<hipEvent_t> ev;  // pairs
   int prof_n = 0;
+  // HIP graphs of one Jacobi update, replayed once per iteration
+  bool graphs = false;
+  hipStream_t cap_stream = nullptr;
+  std::vector<GraphEntry> gcache;
+  uint64_t gclock = 0;
+  long long g_captures = 0, g_replays = 0;
 };
 
 namespace {
@@ -140,21 +172,20 @@ WsLayout layout(const af_plan* p, int N, int rows) {
   return w;
 }
 
-// Launch helper with optional per-class event timing.
+// Launch helper with optional per-class event timing (direct launches only:
+// nothing is captured into a graph while a class is profiled).
 struct Launch {
-  af_plan* p;
   hipStream_t st;
-  int cls;
-  bool on;
-  Launch(af_plan* p_, hipStream_t s, int c) : p(p_), st(s), cls(c) {
-    on = p->prof_class == cls && p->prof_n < (int)p->ev.size() / 2;
-    if (on) (void)hipEventRecord(p->ev[2 * p->prof_n], st);
+  hipEvent_t e1 = nullptr;
+  Launch(af_plan* p, hipStream_t s, int cls) : st(s) {
+    if (p->prof_class != cls || p->prof_n >= (int)p->ev.size() / 2) return;
+    const hipEvent_t e0 = p->ev[2 * p->prof_n];
+    e1 = p->ev[2 * p->prof_n + 1];
+    ++p->prof_n;
+    (void)hipEventRecord(e0, st);
   }
   ~Launch() {
-    if (on) {
-      (void)hipEventRecord(p->ev[2 * p->prof_n + 1], st);
-      ++p->prof_n;
-    }
+    if (e1) (void)hipEventRecord(e1, st);
   }
 };
 
@@ -274,16 +305,81 @@ af_status check_ws(const af_plan* p, int N, int rows, void* ws, size_t ws_bytes,
   return AF_OK;
 }
 
+// Pinned, host-coherent [N][2] residual buffer that the affine kernel writes
+// directly, so the stop test needs no copy command.
 af_status ensure_host_res(af_plan* p, int N) {
   if (p->res_cap >= N) return AF_OK;
   if (p->host_res) (void)hipHostFree(p->host_res);
-  p->host_res = nullptr;
+  p->host_res = p->host_res_dev = nullptr;
   p->res_cap = 0;
   AF_HIP(hipHostMalloc((void**)&p->host_res, (size_t)N * 2 * sizeof(float),
-                       hipHostMallocDefault));
+                       hipHostMallocMapped | hipHostMallocCoherent));
+  AF_HIP(hipHostGetDevicePointer((void**)&p->host_res_dev, p->host_res, 0));
   p->res_cap = N;
   return AF_OK;
 }
+
+// One Jacobi update: the network pass over the block, then the affine update.
+af_status jacobi_update(af_plan* p, const BlockW& bw, const Pass& ps, const af::AffineArgs& aa,
+                        char* ws, const WsLayout& w, hipStream_t st) {
+  if (af_status e = run_net(p, bw, ps, ws, w, st)) return e;
+  LAUNCH(K_AFFINE, af::launch_affine(0, aa, st));
+  return AF_OK;
+}
+
+void destroy_entry(GraphEntry& e) {
+  if (e.exec) (void)hipGraphExecDestroy(e.exec);
+  e.exec = nullptr;
+}
+
+GraphEntry* graph_lookup(af_plan* p, const GraphKey& key) {
+  for (GraphEntry& e : p->gcache)
+    if (e.key == key) {
+      e.used = ++p->gclock;
+      return &e;
+    }
+  return nullptr;
+}
+
+// Capture one Jacobi update on the plan's private stream (nothing runs) and
+// instantiate it.  The least recently used entry is dropped when the cache is
+// full, after `st` (the only stream this call replays on) has drained.
+af_status graph_capture(af_plan* p, const GraphKey& key, const BlockW& bw, const Pass& ps,
+                        const af::AffineArgs& aa, char* ws, const WsLayout& w,
+                        hipStream_t st, GraphEntry** out) {
+  *out = nullptr;
+  if (!p->cap_stream) AF_HIP(hipStreamCreateWithFlags(&p->cap_stream, hipStreamNonBlocking));
+  GraphEntry e;
+  e.key = key;
+  hipError_t he = hipStreamBeginCapture(p->cap_stream, hipStreamCaptureModeRelaxed);
+  if (he != hipSuccess)
+    return fail(AF_ERR_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(he));
+  const af_status s = jacobi_update(p, bw, ps, aa, ws, w, p->cap_stream);
+  hipGraph_t graph = nullptr;
+  he = hipStreamEndCapture(p->cap_stream, &graph);
+  if (s != AF_OK || he != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return s != AF_OK ? s
+                      : fail(AF_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(he));
+  }
+  he = hipGraphInstantiate(&e.exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (he != hipSuccess)
+    return fail(AF_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(he));
+  if ((int)p->gcache.size() >= kGraphCacheCap) {
+    AF_HIP(hipStreamSynchronize(st));
+    auto lru = std::min_element(p->gcache.begin(), p->gcache.end(),
+                                [](const GraphEntry& a, const GraphEntry& b) { return a.used < b.used; });
+    destroy_entry(*lru);
+    p->gcache.erase(lru);
+  }
+  e.used = ++p->gclock;
+  p->gcache.push_back(std::move(e));
+  ++p->g_captures;
+  *out = &p->gcache.back();
+  return AF_OK;
+}
+
 
 }  // namespace
 
@@ -364,6 +460,8 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
 
 void af_plan_destroy(af_plan* p) {
   if (!p) return;
+  for (GraphEntry& e : p->gcache) destroy_entry(e);
+  if (p->cap_stream) (void)hipStreamDestroy(p->cap_stream);
   if (p->host_res) (void)hipHostFree(p->host_res);
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   delete p;
@@ -463,6 +561,8 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   char* ws = (char*)ws_;
   const int C = p->cfg.C;
   const int nb = (L + B - 1) / B;
+  int device = 0;
+  if (p->graphs) AF_HIP(hipGetDevice(&device));
   float* xtmp = (float*)(ws + w.xtmp);
   float* res = (float*)(ws + w.res);
   // counter word of the affine kernel and the sticky non-finite tag after it
@@ -482,18 +582,32 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                         af::head_splits(N * R, 2 * C, p->cfg.d), zin, xo, nullptr, N, R, C, L, s,
                         dir, (float*)(ws + w.partials), res,
                         (unsigned*)(ws + w.counter), nullptr, bad,
-                        (unsigned)(1 + t * nb + b)};
+                        (unsigned)(1 + t * nb + b), p->host_res_dev};
+      // the update is the same launch sequence on every iteration of the
+      // block: replay it as one graph when there are several to run (or it is
+      // cached from an earlier call).  Profiled calls launch directly, as
+      // event records inside a graph carry no timing on this runtime.
+      GraphEntry* g = nullptr;
+      if (p->graphs && p->prof_class < 0) {
+        const GraphKey key{&p->blocks[t], xo, x_last, zin, p->host_res_dev, ws, device,
+                           N, L, s, R, prefix_len, dir, Bc, (unsigned)(1 + t * nb + b)};
+        g = graph_lookup(p, key);
+        if (!g && kmax >= 2)
+          if (af_status e = graph_capture(p, key, p->blocks[t], ps, aa, ws, w, st, &g)) return e;
+      }
       int k = 0;
       bool nonfinite = false;
       for (k = 1; k <= kmax; ++k) {
-        if (af_status e = run_net(p, p->blocks[t], ps, ws, w, st)) return e;
-        LAUNCH(K_AFFINE, af::launch_affine(0, aa, st));
-        // the residual is read back only for the stop test; at the cap (and
-        // in forced-count mode) a non-finite residual is caught through the
+        if (g) {
+          AF_HIP(hipGraphLaunch(g->exec, st));
+          ++p->g_replays;
+        } else if (af_status e = jacobi_update(p, p->blocks[t], ps, aa, ws, w, st)) {
+          return e;
+        }
+        // the residual is read only for the stop test; at the cap (and in
+        // forced-count mode) a non-finite residual is caught through the
         // sticky tag read once at the end
         if (!(tau > 0.f && k < kmax)) continue;
-        AF_HIP(hipMemcpyAsync(p->host_res, res, (size_t)N * 2 * sizeof(float),
-                              hipMemcpyDeviceToHost, st));
         AF_HIP(hipStreamSynchronize(st));
         bool all_below = true;
         for (int n = 0; n < N; ++n) {
@@ -540,7 +654,10 @@ af_status af_profile_enable(af_plan* p, const char* kernel_class) {
   if (cls < 0) return fail(AF_ERR_ARG, std::string("unknown kernel class ") + kernel_class);
   if (p->ev.empty()) {
     p->ev.resize(2 * 4096);
-    for (auto& e : p->ev) AF_HIP(hipEventCreate(&e));
+    // timing-only events: no system-scope fence (cache writeback and
+    // invalidate) when recorded, which would add its own cost to the
+    // bracketed launch
+    for (auto& e : p->ev) AF_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   }
   p->prof_class = cls;
   p->prof_n = 0;
@@ -564,6 +681,19 @@ af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
   }
   *launches = p->prof_n;
   *total_ms = tot;
+  return AF_OK;
+}
+
+af_status af_plan_set_graphs(af_plan* p, int enable) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->graphs = enable != 0;
+  return AF_OK;
+}
+
+af_status af_plan_graph_stats(const af_plan* p, long long* captures, long long* replays) {
+  if (!p || !captures || !replays) return fail(AF_ERR_ARG, "NULL argument");
+  *captures = p->g_captures;
+  *replays = p->g_replays;
   return AF_OK;
 }
 

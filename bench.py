@@ -73,15 +73,22 @@ class Runner:
                            x_last=dev(xp[:, -1]))
         elif w.init == "prev_frame":
             self.kw = dict(init="prev_frame", frame_len=w.frame_len)
+        # output, iteration counts and workspace allocated once: every step
+        # makes the same call on the same buffers
+        self.binding = binding
+        self.x = torch.empty_like(self.z)
+        self.iters = np.zeros((w.n_blocks, -(-L // w.jacobi_block)), np.int32)
+        self.ws = self.plan.workspace(N, self.rows)
         torch.cuda.synchronize()
         self.tokens_per_step = N * L
-        self.iters = None
 
     def step(self):
-        x, it = self.plan.inverse_jacobi(self.z, self.w.jacobi_block, self.w.tau, **self.kw)
-        self.iters = it
-        self.x = x
-        return x
+        kw = self.kw
+        self.binding.af_inverse_jacobi(
+            self.plan, self.z, self.w.jacobi_block, self.w.tau, 0, kw.get("init", "zero"),
+            kw.get("x_init"), kw.get("frame_len", 0), kw.get("prefix_len", 0),
+            kw.get("x_last"), self.x, self.iters, self.ws)
+        return self.x
 
 
 def cpu_baseline(runner, synth, budget_tokens):
@@ -232,7 +239,7 @@ def schedule_sweep(torch, binding, synth, reps):
             "asymmetric_video21": asym_row}
 
 
-def pipeline_bench(torch, binding, synth, reps):
+def pipeline_bench(torch, binding, synth, reps, graphs=False):
     """End-to-end inverse of the deep o shallow flow over 21 frames (deep:
     the video21 block, shallow: the shallow_stack stack), three schedules:
     stages (the deep block over all frames in one call, then the shallow
@@ -245,6 +252,8 @@ def pipeline_bench(torch, binding, synth, reps):
     F = v.frame_len
     deep = binding.AFPlan(v.block, synth.make_params(v.block, 0))
     shallow = binding.AFPlan(sh.block, synth.make_params(sh.block, 0, n_blocks=sh.n_blocks))
+    deep.set_graphs(graphs)
+    shallow.set_graphs(graphs)
     flow = DeepShallowFlow(deep, shallow, F)
     z = dev(synth.normal((1, v.length, v.block.C), 1))
     nf = v.length // F
@@ -283,6 +292,9 @@ def main():
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay the captured Jacobi update as a HIP graph instead "
+                         "of launching every kernel directly")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to scale HBM counters)")
     ap.add_argument("--pipeline", action="store_true",
@@ -312,7 +324,8 @@ def main():
     binding.load_library()
     assert torch.cuda.is_available(), "no GPU"
     if args.pipeline:
-        print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1))), flush=True)
+        print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1),
+                                        args.graphs)), flush=True)
         return
     if args.schedule_sweep:
         print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
@@ -320,6 +333,7 @@ def main():
 
     r = Runner(args.workload, torch, binding, synth)
     cfg, w = r.cfg, r.w
+    r.plan.set_graphs(args.graphs)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -334,19 +348,30 @@ def main():
         breakdown[cls] = {"launches": n, "ms": round(ms, 4)}
     dominant = max(GEMM_CLASSES, key=lambda c: breakdown[c]["ms"])
 
-    # timed region, with the dominant kernel timed live by HIP events on the
-    # stream it is launched on
-    r.plan.profile_enable(dominant)
+    # timed region: K steps as a user runs them (Jacobi updates launched
+    # directly, or replayed as graphs with --graphs)
+    r.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         r.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    n_launch, dom_ms = r.plan.profile_read()
-    r.plan.profile_disable()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = r.tokens_per_step / ((t1 - t0) / args.steps)
+
+    # the dominant kernel timed live by HIP events on the stream it is launched
+    # on, over K more steps of the same workload; these launch directly, as
+    # events recorded inside a graph carry no timing on this runtime
+    r.plan.profile_enable(dominant)
+    torch.cuda.synchronize()
+    p0 = time.perf_counter()
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    p1 = time.perf_counter()
+    n_launch, dom_ms = r.plan.profile_read()
+    r.plan.profile_disable()
 
     flops = gemm_flops_per_launch(dominant, r.M, cfg)
     avg_ms = dom_ms / max(n_launch, 1)
@@ -355,7 +380,9 @@ def main():
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": counter_traffic(w.name, dominant), "flops_per_launch": flops,
-                "avg_ms": round(avg_ms, 5), "launches": n_launch}
+                "avg_ms": round(avg_ms, 5), "launches": n_launch,
+                "timing": f"HIP events, {args.steps} direct-launch steps after the timed region",
+                "ms_per_step_profiled": round((p1 - p0) * 1e3 / args.steps, 3)}
 
     # all GEMMs together (algorithmic flops / summed kernel time, one step)
     g_flops = sum(gemm_flops_per_launch(c, r.M, cfg) * breakdown[c]["launches"]
@@ -389,6 +416,7 @@ def main():
         "affine_in_path": {"bound": "hbm", "GB/s": round(aff_gbs, 1),
                            "frac": round(aff_gbs / PEAK_HBM_GBS, 4),
                            "bytes_per_launch": aff_bytes},
+        "graphs": args.graphs,
         "kernel_ms_per_step": breakdown,
         "forward_ms": round(fwd_ms, 3),
     }

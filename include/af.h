@@ -29,8 +29,9 @@
  *     a thread-local detail string for the last failure.
  *   - `stream` is a hipStream_t (NULL = the default stream).  af_forward and
  *     af_prefill are stream-ordered and return without waiting.
- *     af_inverse_jacobi blocks: it reads each update's residual back to the
- *     host for the stop test and returns once x and iters are final.
+ *     af_inverse_jacobi blocks: the affine kernel writes each update's
+ *     residual into pinned host memory of the plan for the stop test, and the
+ *     call returns once x and iters are final.
  */
 #ifndef AF_H
 #define AF_H
@@ -188,6 +189,29 @@ af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
 af_status af_profile_enable(af_plan *p, const char *kernel_class);
 af_status af_profile_disable(af_plan *p);
 af_status af_profile_read(af_plan *p, int *launches, double *total_ms);
+
+/* ---- graph replay of the Jacobi update (opt-in) ---------------------------
+ * Every update of a Jacobi block (关键设计 3) runs the same launch sequence on
+ * the same buffers.  With graphs enabled, af_inverse_jacobi captures it once
+ * into a HIP graph (on a private stream of the plan, where nothing runs) and
+ * replays that graph on `stream` once per iteration, which takes the per-kernel
+ * launch work off the host thread.  Off by default: where every kernel runs for
+ * several microseconds the host already launches ahead of the device, and
+ * direct launches measured no slower.  Graphs are cached in the plan (at most 128,
+ * least recently used dropped) under every value they depend on: the stack
+ * block, the z / x / x_last / workspace pointers, the device, N, L, the block
+ * bounds and prefix_len; a later call with the same values replays without
+ * capturing.  A block that may run a single update is launched directly
+ * unless already cached, and so is every update while a kernel class is
+ * profiled (af_profile_enable: the runtime gives no timing for events
+ * recorded inside a graph).  Results are identical with and without graphs.
+ * A plan must not be used by two calls at once.
+ *   af_plan_set_graphs: enable != 0 turns graph replay on, 0 (the default)
+ *     launches every kernel directly; AF_ERR_ARG if p is NULL.
+ *   af_plan_graph_stats: graphs captured and graph launches made by this plan
+ *     since it was created; AF_ERR_ARG on a NULL argument. */
+af_status af_plan_set_graphs(af_plan *p, int enable);
+af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *replays);
 
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
  * The fused affine kernel on its own, over N samples of rows_per_sample

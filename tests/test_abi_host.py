@@ -171,3 +171,17 @@ def test_profile_class_names(lib):
     assert lib.af_profile_enable(h, b"nope") == B.AF_ERR_ARG
     assert lib.af_profile_disable(h) == B.AF_OK
     lib.af_plan_destroy(h)
+
+
+def test_graph_controls(lib):
+    st, h = make_plan(lib)
+    assert st == B.AF_OK
+    c = ctypes.c_longlong(-1)
+    r = ctypes.c_longlong(-1)
+    assert lib.af_plan_graph_stats(h, ctypes.byref(c), ctypes.byref(r)) == B.AF_OK
+    assert (c.value, r.value) == (0, 0)
+    assert lib.af_plan_graph_stats(h, None, ctypes.byref(r)) == B.AF_ERR_ARG
+    assert lib.af_plan_set_graphs(h, 0) == B.AF_OK
+    assert lib.af_plan_set_graphs(h, 1) == B.AF_OK
+    assert lib.af_plan_set_graphs(None, 1) == B.AF_ERR_ARG
+    lib.af_plan_destroy(h)
