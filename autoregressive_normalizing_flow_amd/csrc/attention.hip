@@ -144,39 +144,58 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   struct Stage {
     u32x4 k[CK], v[CK], kl[CK], vl[CK];
   } ra, rb;
-  // keys outside [k_begin, k_end) are loaded as zeros (masked below)
+  // This thread's 16-byte chunks of a tile, the same in every tile: chunk
+  // c = tid + 256 i is K row c / (DH/8), columns 8 (c % (DH/8)).., and Vt row
+  // c / (ATT_KT/8), keys 8 (c % (ATT_KT/8)).. of the tile.  Element offsets
+  // from the tile's (uniform) base.
+  uint32_t koff[CK], voff[CK];
+#pragma unroll
+  for (int i = 0; i < CK; ++i) {
+    const int c = tid + i * 256;
+    const int key = c / (DH / 8), dc = c - key * (DH / 8);
+    const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
+    koff[i] = (uint32_t)(key * DH + dc * 8);
+    voff[i] = (uint32_t)(drow * Lcap + kc8 * 8);
+  }
   auto gload = [&](Stage& st, int kt) {
     u32x4(&rk)[CK] = st.k;
     u32x4(&rv)[CK] = st.v;
     u32x4(&rkl)[CK] = st.kl;
     u32x4(&rvl)[CK] = st.vl;
     const int k0 = (t_begin + kt) * ATT_KT;
+    const bf16* kp = kbase + (size_t)k0 * DH;
+    const bf16* vp = vbase + k0;
+    const bf16* klp = SPLIT ? klbase + (size_t)k0 * DH : nullptr;
+    const bf16* vlp = SPLIT ? vlbase + k0 : nullptr;
+    // every address is inside the allocation (k0 + 64 <= Lcap)
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (DH / 8), dc = c - key * (DH / 8);
-      const int kk = k0 + key;
-      const bool kin = kk < k_end;
-      rk[i] = kin ? *(const u32x4*)(kbase + (size_t)kk * DH + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-      if (SPLIT)
-        rkl[i] = kin ? *(const u32x4*)(klbase + (size_t)kk * DH + dc * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
-      const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
-      const int kk0 = k0 + kc8 * 8;  // k0 + 64 <= Lcap: always in bounds
-      u32x4 v = *(const u32x4*)(vbase + (size_t)drow * Lcap + kk0);
-      u32x4 vl = SPLIT ? *(const u32x4*)(vlbase + (size_t)drow * Lcap + kk0)
-                       : u32x4{0u, 0u, 0u, 0u};
-      if (kk0 + 8 > k_end) {
+      rk[i] = *(const u32x4*)(kp + koff[i]);
+      rv[i] = *(const u32x4*)(vp + voff[i]);
+      if (SPLIT) {
+        rkl[i] = *(const u32x4*)(klp + koff[i]);
+        rvl[i] = *(const u32x4*)(vlp + voff[i]);
+      }
+    }
+    if (k0 + ATT_KT > k_end) {
+      // ragged last tile: keys at or past k_end become zeros (in place, so
+      // that only this rare branch waits for the loads)
+#pragma unroll
+      for (int i = 0; i < CK; ++i) {
+        const int c = tid + i * 256;
+        if (k0 + c / (DH / 8) >= k_end) {
+          rk[i] = u32x4{0u, 0u, 0u, 0u};
+          if (SPLIT) rkl[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        const int kk0 = k0 + (c % (ATT_KT / 8)) * 8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const unsigned lo_ok = (kk0 + 2 * e) < k_end ? 0xFFFFu : 0u;
           const unsigned hi_ok = (kk0 + 2 * e + 1) < k_end ? 0xFFFF0000u : 0u;
-          v[e] &= (lo_ok | hi_ok);
-          vl[e] &= (lo_ok | hi_ok);
+          rv[i][e] &= (lo_ok | hi_ok);
+          if (SPLIT) rvl[i][e] &= (lo_ok | hi_ok);
         }
       }
-      rv[i] = v;
-      rvl[i] = vl;
     }
   };
   auto lstore = [&](const Stage& st, int buf) {

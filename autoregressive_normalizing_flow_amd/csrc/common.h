@@ -30,23 +30,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// GELU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erf from Abramowitz &
+// GELU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erfc from Abramowitz &
 // Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
-//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7; erf(-x) = -erf(x).
-// One reciprocal, one exponential and a few FMAs, against the bf16 output
-// rounding of 2^-9.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
-  const float poly =
-      t * (0.254829592f +
-           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  const float y = 1.0f - poly * __expf(-ax * ax);
-  return copysignf(y, x);
-}
+//   erfc(x) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7.
+// With Q = 0.5 erfc(|u| / sqrt 2), Phi(u) is 1 - Q for u >= 0 and Q for
+// u < 0, so u Phi(u) = max(u, 0) - |u| Q: one reciprocal, one exponential and
+// a few FMAs, and no cancellation in the negative tail.
 __device__ __forceinline__ float gelu_erf(float u) {
-  return 0.5f * u * (1.0f + erf_as7126(u * 0.70710678118654752f));
+  const float au = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, au, 1.0f));
+  const float half_poly =
+      t * (0.5f * 0.254829592f +
+           t * (0.5f * -0.284496736f +
+                t * (0.5f * 1.421413741f + t * (0.5f * -1.453152027f + t * (0.5f * 1.061405429f)))));
+  // exp(-u^2 / 2) = 2^(-u^2 log2(e) / 2)
+  const float e = __builtin_amdgcn_exp2f(u * (u * (-0.5f * 1.4426950408889634f)));
+  return fmaf(-au, half_poly * e, fmaxf(u, 0.0f));
 }
 
 // Storage index of processing index i in a sequence of length L: right-to-left

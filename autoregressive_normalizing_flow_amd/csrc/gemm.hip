@@ -55,6 +55,7 @@ struct EpiQKV {
     else
       vt[(base * dh + e) * Lcap + p] = from_f32<T>(v);
   }
+  __device__ __forceinline__ void at_split(int) {}
   __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
   __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
@@ -101,6 +102,7 @@ struct EpiResid {
     float* p = h + (size_t)m * N + n;
     *p = *p + (v + bias[n]);
   }
+  __device__ __forceinline__ void at_split(int) {}
   __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
   __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
@@ -124,6 +126,7 @@ struct EpiGelu {
     if (m >= M) return;
     out[(size_t)m * N + n] = from_f32<T>(gelu_erf(v + bias[n]));
   }
+  __device__ __forceinline__ void at_split(int) {}
   __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
   __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
@@ -145,6 +148,7 @@ struct EpiF32 {
     if (m >= M) return;
     out[(size_t)m * N + n] = v + (bias ? bias[n] : 0.f);
   }
+  __device__ __forceinline__ void at_split(int) {}
   __device__ __forceinline__ float4 bias4(int n) const {
     return bias ? *(const float4*)(bias + n) : float4{0.f, 0.f, 0.f, 0.f};
   }
@@ -168,13 +172,13 @@ struct EpiPlane {
 // Split-K partial: fp32 slab [S][M][N]; a reduce kernel adds the slabs in a
 // fixed order (deterministic) and applies the residual epilogue.
 struct EpiSlab {
-  float* slab;
-  int M, N, tiles;  // tiles per split: blockIdx.x / tiles is the split index
+  float* slab;   // plane s of split s at slab + s * M * N
+  int M, N;
+  __device__ __forceinline__ void at_split(int s) { slab += (size_t)s * M * N; }
   __device__ __forceinline__ float4 bias4(int) const { return float4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4) const {
     if (m >= M) return;
-    float* plane = slab + (size_t)(blockIdx.x / tiles) * M * N;
-    *(float4*)(plane + (size_t)m * N + n) = float4{v[0], v[1], v[2], v[3]};
+    *(float4*)(slab + (size_t)m * N + n) = float4{v[0], v[1], v[2], v[3]};
   }
 };
 
@@ -191,13 +195,13 @@ struct EpiSlab {
 // Block tile BM = 32*TM tokens x BN = 32*TN features x 64, 4 waves in 2 x 2,
 // wave tile 16*TM x 16*TN.  TM = 7 gives 224-row tiles: a 1560-token frame
 // (and every multiple of it) then pads by only 0.5%.  Two LDS buffers (rows
-// padded to 144 B: conflict-free 16-byte fragment reads).  Blocks are mapped XCD-aware: consecutive block ids go to
-// different XCDs, so the tile grid is partitioned into 8 column groups and
-// XCD x walks the tiles of group x, keeping its W panels in its own L2.
+// padded to 144 B: conflict-free 16-byte fragment reads).  Blocks are mapped
+// XCD-aware by gemm_unit_of (each XCD works on one split's K range and one
+// column group of tiles, keeping its operand panels in its own L2).
 // One register stage: the global loads of tile k+1 are in flight while tile
 // k is multiplied (a second stage costs more registers than it hides).
-// blockIdx.x = split * tiles + position; split s covers K range
-// [s*k_len, (s+1)*k_len).  Requirements: N % BN == 0, k_len % 64 == 0.
+// The grid holds tiles * S blocks; split s covers K range [s*k_len,
+// (s+1)*k_len).  Requirements: N % BN == 0, k_len % 64 == 0.
 // ---------------------------------------------------------------------------
 template <int TM_, int TN_>
 struct GemmCfg {
@@ -281,15 +285,23 @@ __device__ __forceinline__ void gemm_compute(f32x4 (&acc)[G::TN][G::TM],
   }
 }
 
-// Tile (tm, tn) of the p-th block of a split: XCD-aware when the tile grid
-// splits evenly into 8 column groups, else row-major.
-__device__ __forceinline__ void gemm_tile_of(int p, int tiles_m, int tiles_n, int& tm,
-                                             int& tn) {
-  if ((tiles_n & 7) == 0) {
-    const int xcd = p & 7, local = p >> 3, gw = tiles_n >> 3;
+// Split index and tile (tm, tn) of block b among S splits of a
+// tiles_m x tiles_n grid.  Consecutive block ids go to different XCDs (b & 7),
+// so when the splits and the tile columns divide over the 8 XCDs, XCD x takes
+// split x / (8 / S) and column group x % (8 / S) of it: each XCD then reads
+// one split's K range of the activations and one column group's rows of W,
+// and keeps them in its own L2.  Other shapes are mapped row-major.
+__device__ __forceinline__ void gemm_unit_of(int b, int S, int tiles_m, int tiles_n,
+                                             int& tm, int& tn, int& split) {
+  if (S <= 8 && (8 % S) == 0 && tiles_n % (8 / S) == 0) {
+    const int xcd = b & 7, local = b >> 3, G = 8 / S, gw = tiles_n / G;
+    split = xcd / G;
     tm = local / gw;
-    tn = xcd * gw + (local - tm * gw);
+    tn = (xcd - split * G) * gw + (local - tm * gw);
   } else {
+    const int tiles = tiles_m * tiles_n;
+    split = b / tiles;
+    const int p = b - split * tiles;
     tm = p / tiles_n;
     tn = p - tm * tiles_n;
   }
@@ -308,10 +320,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = N / G::BN;
   const int tiles_m = (M + G::BM - 1) / G::BM;
-  const int tiles = tiles_m * tiles_n;
-  const int split = blockIdx.x / tiles;
-  int tm, tn;
-  gemm_tile_of(blockIdx.x - split * tiles, tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  gemm_unit_of(blockIdx.x, gridDim.x / (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn, split);
+  epi.at_split(split);
   const int m0 = tm * G::BM, n0 = tn * G::BN;
   const int kb = split * k_len;
   const int KT = k_len / G::BK;
@@ -517,10 +528,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(
   const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_n = N / G::BN;
   const int tiles_m = (M + G::BM - 1) / G::BM;
-  const int tiles = tiles_m * tiles_n;
-  const int split = blockIdx.x / tiles;
-  int tm, tn;
-  gemm_tile_of(blockIdx.x - split * tiles, tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  gemm_unit_of(blockIdx.x, gridDim.x / (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn, split);
+  epi.at_split(split);
   const int m0 = tm * G::BM, n0 = tn * G::BN;
   const int kb = split * k_len;
   const int KT = k_len / G::BK;
@@ -762,10 +772,6 @@ int gemm_resid_splits(int M, int N, int K) {
   return a > b ? a : b;
 }
 
-static int tiles_of(TileChoice c, int M, int N) {
-  return ((M + 32 * c.tm - 1) / (32 * c.tm)) * (N / (32 * c.tn));
-}
-
 static int ilog2(int v) {
   int r = 0;
   while ((1 << (r + 1)) <= v) ++r;
@@ -820,7 +826,7 @@ hipError_t launch_gemm_resid(bool bf, const void* A, const void* Alo, const void
     EpiResid e{bias, h, M, N};
     return run_bf16_cfg(A, Alo, W, M, N, K, c, e, st);
   }
-  EpiSlab es{slab, M, N, tiles_of(c, M, N)};
+  EpiSlab es{slab, M, N};
   hipError_t err = run_bf16_cfg(A, Alo, W, M, N, K, c, es, st);
   if (err != hipSuccess) return err;
   const size_t total4 = (size_t)M * N / 4;
@@ -835,7 +841,7 @@ hipError_t launch_gemm_partial(const void* A, const void* Alo, const void* W,
                                hipStream_t st) {
   TileChoice c = gemm_choose(M, N, K, true, Alo != nullptr);
   *splits = c.splits;
-  EpiSlab es{slab, M, N, tiles_of(c, M, N)};
+  EpiSlab es{slab, M, N};
   return run_bf16_cfg(A, Alo, W, M, N, K, c, es, st);
 }
 
