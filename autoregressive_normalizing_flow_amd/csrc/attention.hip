@@ -37,7 +37,11 @@ namespace af {
 // ---------------------------------------------------------------------------
 constexpr int ATT_QT = 128;   // queries per unit
 constexpr int ATT_KT = 64;    // keys per tile
-constexpr float RESCALE_LOG2 = 8.0f;   // lazy max: p stays below 2^8
+// Lazy softmax reference: p = 2^(s - m) with m moved only when the tile's
+// largest score leaves [m - RESCALE_LOW, m + RESCALE_LOG2], so p of a row's
+// largest score stays in [2^-32, 2^8] (no overflow, no underflow to zero).
+constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float RESCALE_LOW = 32.0f;
 
 struct AttnArgs {
   const bf16* q;
@@ -52,7 +56,6 @@ struct AttnArgs {
   bf16* out_lo;
   float* part;     // partial slots: [unit][ATT_QT][DH] O, then [ATT_QT] m, [ATT_QT] l
   int R, H, d, Lcap, pos_base, KC, U_nh;
-  float scale_log2;
   int xcd_map;     // 1: deal (sample, head) pairs to XCDs (needs N*H % 8 == 0)
 };
 
@@ -133,7 +136,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -1e30f;
+    m_run[qb] = 0.f;
     acc_l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -223,14 +226,16 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
     }
   };
 
+  // -m of each query, the accumulator seed of S: the MFMAs then produce
+  // s - m directly
+  f32x4 negm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) negm[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   auto compute = [&](int kt, int cur) {
     const int key0 = (t_begin + kt) * ATT_KT;
 
     f32x4 s[KB][QB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -239,8 +244,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
             *(const bf16x8*)(&sK[cur][(kb * 16 + l16) * KLDS + ks * 32 + lg * 8]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks],
-                                                              s[kb][qb], 0, 0, 0);
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf, qf[qb][ks], ks == 0 ? negm[qb] : s[kb][qb], 0, 0, 0);
         if (SPLIT) {
           const bf16x8 kfl =
               *(const bf16x8*)(&sKl[cur][(kb * 16 + l16) * KLDS + ks * 32 + lg * 8]);
@@ -254,15 +259,15 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
         }
       }
 
-    // online softmax (base 2) per query.  The running max m is kept in
-    // scaled units (p = 2^(s * scale_log2 - m): one FMA and one exp) and is
-    // raised only when some score of the wave exceeds it by more than
-    // RESCALE_LOG2: until then p may reach 2^RESCALE_LOG2, harmless in fp32
-    // and in bf16, and the accumulators are not touched.  The same m scales
-    // O and the row sum, so the result is that of the exact update.  Tiles
-    // wholly below every query of the wave and inside [k_begin, k_end) skip
-    // the masking; both tests are wave-uniform branches (the empty asm keeps
-    // the compiler from turning them into per-element selects).
+    // online softmax (base 2; q carries log2(e) / sqrt(dh)) per query.  The
+    // reference m is lazy: it moves only when some row's largest score in the
+    // tile leaves [m - RESCALE_LOW, m + RESCALE_LOG2]; until then p = 2^(s - m)
+    // is at most 2^RESCALE_LOG2 (harmless in fp32 and in bf16) and the
+    // accumulators are not touched.  The same m scales O and the row sum, so
+    // the result is that of the exact update.  Tiles wholly below every query
+    // of the wave and inside [k_begin, k_end) skip the masking; both tests are
+    // wave-uniform branches (the empty asm keeps the compiler from turning
+    // them into per-element selects).
     const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
     if (need_mask) {
       asm volatile("" ::: "memory");
@@ -276,8 +281,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
             if (key > qpos[qb] || key >= k_end) s[kb][qb][r] = -INFINITY;
           }
     }
-    float tmax[QB];
-    bool raise = false;
+    float tmax[QB];   // largest s - m of the row in this tile
+    bool move = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float t = -INFINITY;
@@ -287,19 +292,26 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
         for (int r = 0; r < 4; ++r) t = fmaxf(t, s[kb][qb][r]);
       t = fmaxf(t, __shfl_xor(t, 16, AF_WAVE));
       t = fmaxf(t, __shfl_xor(t, 32, AF_WAVE));
-      tmax[qb] = t * a.scale_log2;
-      raise |= tmax[qb] > m_run[qb] + RESCALE_LOG2;
+      tmax[qb] = t;
+      // (a row with every key masked, t = -inf, keeps its reference)
+      move |= t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
     }
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], tmax[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
+        const float t = tmax[qb];
+        const float dm = (t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY)) ? t : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-dm);
+        m_run[qb] += dm;
+        negm[qb] = f32x4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
         acc_l[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc_o[db][qb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[kb][qb][r] -= dm;
       }
     }
 #pragma unroll
@@ -307,8 +319,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s[kb][qb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], a.scale_log2, -m_run[qb]));
+        for (int r = 0; r < 4; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
 
     // O^T += Vt P^T over two 32-key steps
 #pragma unroll
@@ -406,7 +417,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
       for (int db = 0; db < DB; ++db)
         *(f32x4*)(slot + (size_t)tq * DH + db * 16 + lg * 4) = acc_o[db][qb];
       if (lg == 0) {
-        slot[ATT_QT * DH + tq] = m_run[qb];
+        // a row with no key in this chunk (l = 0) must not set the merge's max
+        slot[ATT_QT * DH + tq] = l > 0.f ? m_run[qb] : -1e30f;
         slot[ATT_QT * DH + ATT_QT + tq] = l;
       }
     }
@@ -430,25 +442,31 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge the key chunks of every query tile that has more than one:
 // O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, chunks in order.
-// Four threads per query row, each owning DH/4 dimensions; every load of a
-// thread (the chunks' m, l and O values) is issued before the first use, so
-// the kernel waits for memory once.  At most ATT_MAXC chunks are merged in
-// registers; longer ranges loop over groups of that many.
+// ATT_CTPQ threads per query row, each owning DH/ATT_CTPQ dimensions, and
+// ATT_CQPB query rows per block (a quarter tile), so the grid has four
+// blocks per query tile; every load of a thread (the chunks' m, l and O
+// values) is issued before the first use, so the kernel waits for memory
+// once.  At most ATT_MAXC chunks are merged in registers; longer ranges loop
+// over groups of that many.
 constexpr int ATT_MAXC = 4;
+constexpr int ATT_CTPQ = 8, ATT_CQPB = 256 / ATT_CTPQ;
 
 template <int DH>
-__global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a, int n_qt) {
-  const int nh = blockIdx.x / n_qt, qt = blockIdx.x - nh * n_qt;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt) {
+  constexpr int SUB = ATT_QT / ATT_CQPB;
+  const int tile = blockIdx.x / SUB, sub = blockIdx.x - tile * SUB;
+  const int nh = tile / n_qt, qt = tile - nh * n_qt;
   const int n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
   if (n_chunks <= 1) return;
   int u0 = nh * a.U_nh;
   for (int q = 0; q < qt; ++q) u0 += att_chunks(q, a.R, a.pos_base, a.KC);
   const int n = nh / a.H, head = nh - n * a.H;
-  const int tq = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int tq = sub * ATT_CQPB + threadIdx.x / ATT_CTPQ, part = threadIdx.x % ATT_CTPQ;
   const int t = qt * ATT_QT + tq;
   if (t >= a.R) return;
   constexpr int SLOT = ATT_QT * (DH + 2);
-  constexpr int DP = DH / 4, D4 = DP / 4;   // dimensions / float4 per thread
+  constexpr int DP = DH / ATT_CTPQ, D4 = DP / 4;   // dimensions / float4 per thread
+  static_assert(DP % 4 == 0, "a float4 per thread at least");
   const float* base = a.part + (size_t)u0 * SLOT;
   float m = -1e30f, l = 0.f;
   float4 o[D4];
@@ -584,7 +602,7 @@ static void attn_launch(const AttnArgs& a, dim3 grid, dim3 comb, bool multi, int
     hipLaunchKernelGGL((attn_bf16_kernel_o2<DH, SPLIT>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
-  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(512), 0, st, a, n_qt);
+  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(256), 0, st, a, n_qt);
 }
 
 hipError_t launch_attention(bool bf, const void* q, const void* kc,
@@ -601,9 +619,8 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
                split ? (const bf16*)split->kc_lo : nullptr,
                split ? (const bf16*)split->vt_lo : nullptr,
                split ? (bf16*)split->out_lo : nullptr, part,
-               R, H, d, Lcap, pos_base, KC, U_nh, scale * 1.4426950408889634f,
-               (N * H) % 8 == 0 ? 1 : 0};
-    const dim3 grid(N * H * U_nh), comb(N * H * n_qt);
+               R, H, d, Lcap, pos_base, KC, U_nh, (N * H) % 8 == 0 ? 1 : 0};
+    const dim3 grid(N * H * U_nh), comb(N * H * n_qt * (ATT_QT / ATT_CQPB));
     const bool multi = U_nh > n_qt;
     switch (dh * 2 + (split ? 1 : 0)) {
       case 128: attn_launch<64, false>(a, grid, comb, multi, n_qt, st); break;

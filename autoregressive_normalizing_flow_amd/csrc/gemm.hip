@@ -39,12 +39,13 @@ struct EpiQKV {
   T* q_lo;    // split outputs (bf16 hi + lo) of the higher-precision forward, or NULL
   T* kc_lo;
   T* vt_lo;
+  float qscale;  // Q is stored times qscale (rounded once, after the scaling)
   __device__ __forceinline__ void operator()(int m, int n, float v, int = 0) const {
     if (m >= M) return;
     v += bias[n];
     const int which = n / d, hd = n - which * d;
     if (which == 0) {
-      q[(size_t)m * d + hd] = from_f32<T>(v);
+      q[(size_t)m * d + hd] = from_f32<T>(v * qscale);
       return;
     }
     const int nn = m / R, t = m - nn * R, p = pos_base + t;
@@ -59,8 +60,10 @@ struct EpiQKV {
   __device__ __forceinline__ float4 bias4(int n) const { return *(const float4*)(bias + n); }
   __device__ __forceinline__ void store4(int m, int n, f32x4 v, float4 b) const {
     if (m >= M) return;
-    const float v0 = v[0] + b.x, v1 = v[1] + b.y, v2 = v[2] + b.z, v3 = v[3] + b.w;
     const int which = n >> log2d, hd = n & (d - 1);
+    const float sc = which == 0 ? qscale : 1.0f;
+    const float v0 = (v[0] + b.x) * sc, v1 = (v[1] + b.y) * sc, v2 = (v[2] + b.z) * sc,
+                v3 = (v[3] + b.w) * sc;
     const T h0 = from_f32<T>(v0), h1 = from_f32<T>(v1), h2 = from_f32<T>(v2),
             h3 = from_f32<T>(v3);
     const bool split = q_lo != nullptr;
@@ -804,13 +807,16 @@ hipError_t launch_gemm_qkv(bool bf, const void* A, const void* Alo, const void* 
                            const float* bias, int M, int N, int K, QKVDst d,
                            hipStream_t st) {
   if (bf) {
+    // the bf16 attention takes Q in base-2 softmax units: Q / sqrt(dh) * log2(e)
     EpiQKV<bf16> e{bias, (bf16*)d.q, (bf16*)d.kc, (bf16*)d.vt, M, d.R, d.d, d.dh, d.H,
                    d.Lcap, d.pos_base, ilog2(d.d), ilog2(d.dh), (bf16*)d.q_lo,
-                   (bf16*)d.kc_lo, (bf16*)d.vt_lo};
+                   (bf16*)d.kc_lo, (bf16*)d.vt_lo,
+                   1.4426950408889634f / sqrtf((float)d.dh)};
     return run_bf16(A, Alo, W, M, N, K, e, st);
   }
   EpiQKV<float> e{bias, (float*)d.q, (float*)d.kc, (float*)d.vt, M, d.R, d.d, d.dh, d.H,
-                  d.Lcap, d.pos_base, ilog2(d.d), ilog2(d.dh), nullptr, nullptr, nullptr};
+                  d.Lcap, d.pos_base, ilog2(d.d), ilog2(d.dh), nullptr, nullptr, nullptr,
+                  1.0f};
   return run_f32(A, W, M, N, K, e, st);
 }
 

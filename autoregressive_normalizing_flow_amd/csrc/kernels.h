@@ -55,6 +55,14 @@ struct AffineArgs {
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);
 int affine_groups(int N, int R, int C);   // G, the partial slots per sample
 
+// Head GEMM on the fp32 matrix cores: planes[s] = hf W^T over the s-th of
+// `splits` equal K ranges, planes [splits][M][2C] as launch_affine reads them.
+// Needs head_mfma_supported(C, d) and d % (64 * splits) == 0.
+bool head_mfma_supported(int C, int d);
+int head_mfma_splits(int M, int d);
+hipError_t launch_head_mfma(const float* hf, const float* w, float* planes, int M, int C,
+                            int d, int splits, hipStream_t st);
+
 // ---- GEMMs: y[M, N] = A[M, K] W[N, K]^T + bias -----------------------------
 // The bf16 kernels take an optional second activation operand A_lo: with it
 // the activations are the bf16 pair A + A_lo (the higher-precision forward),
@@ -68,6 +76,8 @@ struct QKVDst {
   void* kc_lo;
   void* vt_lo;
 };
+// The bf16 path stores Q times log2(e) / sqrt(dh), the base-2 softmax units
+// the bf16 attention takes (scaled in fp32 before the one rounding to bf16).
 hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* A_lo, const void* W,
                            const float* bias, int M, int N, int K, QKVDst dst,
                            hipStream_t st);
@@ -98,9 +108,10 @@ int head_splits(int M, int N, int K);
 // ---- attention ---------------------------------------------------------------
 // out[m, h*dh:(h+1)*dh] = softmax(q k^T / sqrt(dh)) v over cached keys
 // 0..pos_base+t (inclusive) for chunk row m = n*R + t.
-// bf16: long key ranges are split into chunks whose partial results go to
-// `part` (attention_partial_floats(...) floats) and are merged by a second
-// kernel.
+// bf16: q comes from launch_gemm_qkv already times log2(e) / sqrt(dh), so
+// the softmax is 2^(q k^T) normalised; long key ranges are split into chunks
+// whose partial results go to `part` (attention_partial_floats(...) floats)
+// and are merged by a second kernel.
 struct AttnSplit {   // lo halves of the split (higher-precision) mode
   const void* q_lo;
   const void* kc_lo;

@@ -435,10 +435,12 @@ int affine_groups(int N, int R, int C) {
   return (int)std::max(1L, g);
 }
 
+// Block-wide sums of a and b (red: 2 floats per wave; blocks of 4..16 waves),
+// in a fixed order.
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   a = wave_sum(a);
   b = wave_sum(b);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   __syncthreads();
   if (lane == 0) {
     red[2 * wv] = a;
@@ -447,6 +449,41 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   __syncthreads();
   a = (red[0] + red[2]) + (red[4] + red[6]);
   b = (red[1] + red[3]) + (red[5] + red[7]);
+  for (int w = 4; w < nw; ++w) {
+    a += red[2 * w];
+    b += red[2 * w + 1];
+  }
+}
+
+// Run by the last block to finish: the per-sample sums of the G partial
+// pairs of every sample, added in a fixed order, into res (and res_host, the
+// sticky non-finite tag, or the log-det); then the ticket counter is reset.
+template <int MODE>
+__device__ void finish_sums(const AffineArgs& a, const float* partials, int G, float* red) {
+  for (int nn = 0; nn < a.N; ++nn) {
+    float p0 = 0.f, p1 = 0.f;
+    for (int gg = threadIdx.x; gg < G; gg += blockDim.x) {
+      p0 += coherent_load(&partials[((size_t)nn * G + gg) * 2]);
+      p1 += coherent_load(&partials[((size_t)nn * G + gg) * 2 + 1]);
+    }
+    block_sum2(p0, p1, red);
+    if (threadIdx.x == 0) {
+      if (MODE == 0) {
+        a.res[2 * nn] = p0;
+        a.res[2 * nn + 1] = p1;
+        if (a.res_host) {
+          system_store(&a.res_host[2 * nn], p0);
+          system_store(&a.res_host[2 * nn + 1], p1);
+        }
+        if (a.bad && !(isfinite(p0) && isfinite(p1))) atomicCAS(a.bad, 0u, a.tag);
+      } else {
+        a.res[2 * nn] = -p0;
+        a.res[2 * nn + 1] = p1;
+        if (a.logdet) a.logdet[nn] += -p0;
+      }
+    }
+  }
+  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
 }
 
 template <int MODE, bool VEC>
@@ -540,31 +577,7 @@ __global__ __launch_bounds__(256) void affine_kernel(AffineArgs a, int G) {
   }
   __syncthreads();
   if (ticket != (unsigned)(gridDim.x * gridDim.y) - 1) return;
-  // last block: fixed-order final sums for every sample
-  for (int nn = 0; nn < a.N; ++nn) {
-    float p0 = 0.f, p1 = 0.f;
-    for (int gg = threadIdx.x; gg < G; gg += 256) {
-      p0 += coherent_load(&a.partials[((size_t)nn * G + gg) * 2]);
-      p1 += coherent_load(&a.partials[((size_t)nn * G + gg) * 2 + 1]);
-    }
-    block_sum2(p0, p1, red);
-    if (threadIdx.x == 0) {
-      if (MODE == 0) {
-        a.res[2 * nn] = p0;
-        a.res[2 * nn + 1] = p1;
-        if (a.res_host) {
-          system_store(&a.res_host[2 * nn], p0);
-          system_store(&a.res_host[2 * nn + 1], p1);
-        }
-        if (a.bad && !(isfinite(p0) && isfinite(p1))) atomicCAS(a.bad, 0u, a.tag);
-      } else {
-        a.res[2 * nn] = -p0;
-        a.res[2 * nn + 1] = p1;
-        if (a.logdet) a.logdet[nn] += -p0;
-      }
-    }
-  }
-  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
+  finish_sums<MODE>(a, a.partials, G, red);
 }
 
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st) {
@@ -579,6 +592,103 @@ hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL((affine_kernel<1, false>), grid, dim3(256), 0, st, a, G);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Head GEMM on the fp32 matrix cores: planes[s][m][:] = hf[m] W_head^T over
+// the s-th of S equal K ranges (the affine kernel adds bias and planes).
+// One wave per (16-row tile, K range): it computes all 2C = 16 NT columns of
+// its rows with v_mfma_f32_16x16x4f32.  Lane (i = l % 16, g = l / 16) feeds
+// hf row i and W row i of each column tile with the float4 at k + 4g; the four
+// components are four MFMA steps, so both operands load 16 contiguous bytes
+// per lane, and the loads of U steps of 16 are issued before their MFMAs.
+// ---------------------------------------------------------------------------
+bool head_mfma_supported(int C, int d) {
+  const int nt = C / 8;
+  return C % 8 == 0 && d % 64 == 0 &&
+         (nt == 1 || nt == 2 || nt == 3 || nt == 4 || nt == 6 || nt == 8 || nt == 12 || nt == 16);
+}
+
+template <int NT>
+__global__ __launch_bounds__(64) void head_mfma_kernel(const float* __restrict__ hf,
+                                                       const float* __restrict__ w,
+                                                       float* __restrict__ planes, int M,
+                                                       int d, int k_len) {
+  // U steps of 16 loaded at a time: all of a 128-long K range when 2C <= 96
+  // (fewer than one wave per SIMD here, so registers are plentiful)
+  constexpr int NC = 16 * NT, U = NT <= 6 ? 8 : NT <= 12 ? 4 : 2;
+  const int tiles = (M + 15) / 16;
+  const int s = blockIdx.x / tiles, m0 = (blockIdx.x - s * tiles) * 16;
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int kb = s * k_len + 4 * g;
+  // rows past M read row M-1; their results are not stored
+  const float* ap = hf + (size_t)min(m0 + l16, M - 1) * d + kb;
+  const float* wp = w + (size_t)l16 * d + kb;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < k_len; k += 16 * U) {
+    float4 av[U], bv[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool on = k + 16 * u < k_len;
+      av[u] = on ? *(const float4*)(ap + k + 16 * u) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        bv[u][t] = on ? *(const float4*)(wp + (size_t)t * 16 * d + k + 16 * u)
+                      : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].x, bv[u][t].x, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].y, bv[u][t].y, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].z, bv[u][t].z, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].w, bv[u][t].w, acc[t], 0, 0, 0);
+      }
+  }
+  // lane (l16, g) holds rows 4g..4g+3 of column l16 of every column tile
+  float* out = planes + (size_t)s * M * NC;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + 4 * g + r;
+    if (m < M) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) out[(size_t)m * NC + t * 16 + l16] = acc[t][r];
+    }
+  }
+}
+
+hipError_t launch_head_mfma(const float* hf, const float* w, float* planes, int M, int C,
+                            int d, int splits, hipStream_t st) {
+  const dim3 grid(((M + 15) / 16) * splits);
+  const int k_len = d / splits;
+#define AF_HM(NT)                                                                        \
+  hipLaunchKernelGGL((head_mfma_kernel<NT>), grid, dim3(64), 0, st, hf, w, planes, M, d, \
+                     k_len);                                                             \
+  break;
+  switch (C / 8) {
+    case 1: AF_HM(1)
+    case 2: AF_HM(2)
+    case 3: AF_HM(3)
+    case 4: AF_HM(4)
+    case 6: AF_HM(6)
+    case 8: AF_HM(8)
+    case 12: AF_HM(12)
+    case 16: AF_HM(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef AF_HM
+  return hipGetLastError();
+}
+
+int head_mfma_splits(int M, int d) {
+  const long tiles = (M + 15) / 16;
+  int S = 1;
+  // K ranges of at least 64 (four steps), grid of at most ~1024 waves
+  while (S < 8 && tiles * S * 2 <= 1024 && d % (64 * S * 2) == 0) S *= 2;
+  return S;
 }
 
 }  // namespace af

@@ -115,13 +115,15 @@ struct af_plan {
 namespace {
 
 // Rows of head partial planes needed for any pass of at most M rows:
-// max over m <= M of head_splits(m) * m.
+// max over m <= M of splits(m) * m, for either head kernel (both use one
+// split above 16384 rows).
 size_t head_plane_rows(size_t M, int n_out, int d) {
   size_t best = M;
-  for (size_t m = 64; m < M + 64; m += 64) {
-    const size_t mm = m < M ? m : M;
-    const size_t r = (size_t)af::head_splits((int)mm, n_out, d) * mm;
-    if (r > best) best = r;
+  const size_t top = std::min<size_t>(M, 16384);
+  for (size_t m = 16; m < top + 16; m += 16) {
+    const size_t mm = m < top ? m : top;
+    const size_t s = std::max(af::head_splits((int)mm, n_out, d), af::head_mfma_splits((int)mm, d));
+    if (s * mm > best) best = s * mm;
   }
   return best;
 }
@@ -208,7 +210,8 @@ struct Pass {
 // One pass of the network over chunk rows [s, s+R) of every sample:
 // shift+embed, n_layers pre-LN layers (K/V into the cache), final LN + head.
 af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
-                  const WsLayout& w, hipStream_t st) {
+                  const WsLayout& w, hipStream_t st, const af::AffineArgs* aa = nullptr,
+                  int mode = 0) {
   const af_block_cfg& c = p->cfg;
   const int M = ps.N * ps.R, d = c.d;
   float* h = (float*)(ws + w.h);
@@ -284,9 +287,20 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
     }
     LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
   }
+  // final head (split-K planes: on the fp32 matrix cores where the shape
+  // allows) and the affine update of the caller's AffineArgs
   float* head = (float*)(ws + w.head);
-  LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
-                                            af::head_splits(M, 2 * c.C, d), st));
+  af::AffineArgs fa = *aa;
+  fa.head = head;
+  if (af::head_mfma_supported(c.C, d)) {
+    fa.head_splits = af::head_mfma_splits(M, d);
+    LAUNCH(K_HEAD, af::launch_head_mfma(hf, bw.w_head, head, M, c.C, d, fa.head_splits, st));
+  } else {
+    fa.head_splits = af::head_splits(M, 2 * c.C, d);
+    LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
+                                              fa.head_splits, st));
+  }
+  LAUNCH(K_AFFINE, af::launch_affine(mode, fa, st));
   return AF_OK;
 }
 
@@ -322,9 +336,7 @@ af_status ensure_host_res(af_plan* p, int N) {
 // One Jacobi update: the network pass over the block, then the affine update.
 af_status jacobi_update(af_plan* p, const BlockW& bw, const Pass& ps, const af::AffineArgs& aa,
                         char* ws, const WsLayout& w, hipStream_t st) {
-  if (af_status e = run_net(p, bw, ps, ws, w, st)) return e;
-  LAUNCH(K_AFFINE, af::launch_affine(0, aa, st));
-  return AF_OK;
+  return run_net(p, bw, ps, ws, w, st, &aa, 0);
 }
 
 void destroy_entry(GraphEntry& e) {
@@ -496,13 +508,12 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
     // the forward carries bf16 activations as hi + lo pairs, so that the
     // log-det (a sum of many terms that largely cancel) keeps fp32 accuracy
     Pass ps{cur, nullptr, N, L, 0, L, 0, t & 1, false, true};
-    if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st)) return s;
     af::AffineArgs aa{(const float*)(ws + w.head), p->blocks[t].b_head,
                       af::head_splits(N * L, 2 * C, p->cfg.d), nullptr,
                       const_cast<float*>(cur), dst,
                       N, L, C, L, 0, t & 1, (float*)(ws + w.partials),
                       (float*)(ws + w.res), (unsigned*)(ws + w.counter), logdet};
-    LAUNCH(K_AFFINE, af::launch_affine(1, aa, st));
+    if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st, &aa, 1)) return s;
     cur = dst;
   }
   return AF_OK;

@@ -389,9 +389,11 @@ def main():
                   for c in GEMM_CLASSES)
     g_ms = sum(breakdown[c]["ms"] for c in GEMM_CLASSES)
     # fused affine kernel in the path: 20*C bytes per token per launch
+    # (no separate launches when the affine update is fused into the head
+    # GEMM's kernel, which the gemm_head class then times)
     aff = breakdown["affine"]
     aff_bytes = 20 * cfg.C * r.M
-    aff_gbs = aff_bytes * aff["launches"] / (aff["ms"] * 1e-3) / 1e9 if aff["ms"] else 0.0
+    aff_gbs = aff_bytes * aff["launches"] / (aff["ms"] * 1e-3) / 1e9 if aff["ms"] else None
 
     # forward pass (af_forward) time, untimed by the metric
     torch.cuda.synchronize()
@@ -413,9 +415,10 @@ def main():
         "roofline": roofline,
         "gemm_all": {"TFLOP/s": round(g_flops / (g_ms * 1e-3) / 1e12, 2) if g_ms else None,
                      "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / peak, 4) if g_ms else None},
-        "affine_in_path": {"bound": "hbm", "GB/s": round(aff_gbs, 1),
-                           "frac": round(aff_gbs / PEAK_HBM_GBS, 4),
-                           "bytes_per_launch": aff_bytes},
+        "affine_in_path": ({"bound": "hbm", "GB/s": round(aff_gbs, 1),
+                            "frac": round(aff_gbs / PEAK_HBM_GBS, 4),
+                            "bytes_per_launch": aff_bytes} if aff_gbs is not None
+                           else {"fused_into": "gemm_head"}),
         "graphs": args.graphs,
         "kernel_ms_per_step": breakdown,
         "forward_ms": round(fwd_ms, 3),

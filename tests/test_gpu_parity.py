@@ -159,6 +159,36 @@ def test_f32_stack_ragged_r2l(B):
     assert rel_l2(to_np(xg), xo) < TOL_F32
 
 
+@pytest.mark.parametrize("C,d,N,L,Bj", [(24, 128, 2, 70, 32), (64, 256, 1, 50, 50),
+                                         (8, 512, 3, 33, 16)])
+def test_f32_fused_head_shapes(B, C, d, N, L, Bj):
+    """The fused head + affine kernel at other channel counts (2C = 48, 128,
+    16 columns), K split over 1..8 workgroups, ragged 16-row tiles, batch."""
+    say("f32 fused head", C, d, N, L, Bj)
+    H = d // 64
+    cfg, params, (p64,) = problem(C=C, d=d, H=H, layers=1, max_len=L, dtype="f32",
+                                  seed=C + d)
+    plan = B.AFPlan(cfg, params)
+    x_in = synth.normal((N, L, C), C + 1)
+    zg, ldg = plan.forward(to_dev(x_in))
+    zo, ldo = O.forward_block(p64, x_in, H)
+    assert rel_l2(to_np(zg), zo) < TOL_F32
+    assert np.all(rel_err(to_np(ldg), ldo) < TOL_LOGDET)
+    z = synth.normal((N, L, C), C + 2)
+    xg, itg = plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+    xo, ito = O.inverse_jacobi_block(p64, z, H, Bj, 1e-3)
+    print("iters gpu", itg.tolist(), "oracle", ito.tolist())
+    assert np.array_equal(itg[0], ito)
+    assert rel_l2(to_np(xg), xo) < TOL_F32
+
+
+def test_bf16_unfused_head(B):
+    """C = 20 (2C not a multiple of 16): the head GEMM and the affine kernel
+    run as two launches."""
+    say("bf16 C=20 L=150 B=64")
+    _bf16_block_case(B, d=256, H=4, layers=1, L=150, Bj=64, N=2, seed=23, C=20)
+
+
 def test_f32_forced_count_and_sequential(B):
     say("f32 forced + B=1")
     cfg, params, (p64,) = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
