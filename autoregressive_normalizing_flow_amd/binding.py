@@ -96,6 +96,8 @@ def load_library() -> ctypes.CDLL:
     L.af_profile_read.argtypes = [_P, ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_double)]
     L.af_profile_read.restype = st
+    L.af_plan_set_fused_refresh.argtypes = [_P, i]
+    L.af_plan_set_fused_refresh.restype = st
     L.af_plan_set_graphs.argtypes = [_P, i]
     L.af_plan_set_graphs.restype = st
     L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
@@ -208,8 +210,13 @@ class AFPlan:
         cache survives between calls with the same batch."""
         need = self.workspace_bytes(batch, rows)
         if self._ws is None or self._ws_key[0] != batch or self._ws.numel() < need:
+            old, old_batch = self._ws, (self._ws_key[0] if self._ws_key else None)
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
             self._ws_key = (batch, rows)
+            if old is not None and old_batch == batch:
+                # a larger workspace for the same batch keeps the KV cache
+                cache = int(self.L.af_cache_bytes(self.handle, batch))
+                self._ws[:cache].copy_(old[:cache])
         return self._ws
 
     # entry points ----------------------------------------------------------
@@ -246,7 +253,10 @@ class AFPlan:
         x = torch.empty_like(z)
         nb = (L + B - 1) // B
         iters = np.zeros((self.T, nb), dtype=np.int32)
-        ws = self.workspace(N, max(min(B, L), self._ws_key[1] if self._ws_key else 0))
+        # rows for two blocks when a block's cache refresh shares the next
+        # block's first pass
+        rows = min(2 * B, L) if nb > 1 and getattr(self, "_fused_refresh", False) else min(B, L)
+        ws = self.workspace(N, max(rows, self._ws_key[1] if self._ws_key else 0))
         af_inverse_jacobi(self, z, B, tau, max_iters, init, x_init, frame_len,
                           prefix_len, x_last, x, iters, ws, stream)
         return x, iters
@@ -265,6 +275,11 @@ class AFPlan:
         _check(self.L.af_profile_read(self.handle, ctypes.byref(n), ctypes.byref(ms)),
                "af_profile_read")
         return n.value, ms.value
+
+    def set_fused_refresh(self, enable: bool):
+        _check(self.L.af_plan_set_fused_refresh(self.handle, int(bool(enable))),
+               "af_plan_set_fused_refresh")
+        self._fused_refresh = bool(enable)
 
     # graph replay of the Jacobi update ------------------------------------
     def set_graphs(self, enable: bool):

@@ -57,11 +57,13 @@ int affine_groups(int N, int R, int C);   // G, the partial slots per sample
 
 // Head GEMM on the fp32 matrix cores: planes[s] = hf W^T over the s-th of
 // `splits` equal K ranges, planes [splits][M][2C] as launch_affine reads them.
-// Needs head_mfma_supported(C, d) and d % (64 * splits) == 0.
+// Output row m reads hf row (m / r_out) * r_in + off + m % r_out (r_out =
+// r_in = M, off = 0: row m), so a pass may cover more rows per sample than
+// the head.  Needs head_mfma_supported(C, d) and d % (64 * splits) == 0.
 bool head_mfma_supported(int C, int d);
 int head_mfma_splits(int M, int d);
 hipError_t launch_head_mfma(const float* hf, const float* w, float* planes, int M, int C,
-                            int d, int splits, hipStream_t st);
+                            int d, int splits, hipStream_t st, int r_out, int r_in, int off);
 
 // ---- GEMMs: y[M, N] = A[M, K] W[N, K]^T + bias -----------------------------
 // The bf16 kernels take an optional second activation operand A_lo: with it

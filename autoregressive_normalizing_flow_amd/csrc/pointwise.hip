@@ -609,11 +609,14 @@ bool head_mfma_supported(int C, int d) {
          (nt == 1 || nt == 2 || nt == 3 || nt == 4 || nt == 6 || nt == 8 || nt == 12 || nt == 16);
 }
 
+// Output row m (sample m / r_out, row m % r_out) reads hf row
+// (m / r_out) * r_in + off + m % r_out: the last r_out of every r_in rows.
 template <int NT>
 __global__ __launch_bounds__(64) void head_mfma_kernel(const float* __restrict__ hf,
                                                        const float* __restrict__ w,
                                                        float* __restrict__ planes, int M,
-                                                       int d, int k_len) {
+                                                       int d, int k_len, int r_out, int r_in,
+                                                       int off) {
   // U steps of 16 loaded at a time: all of a 128-long K range when 2C <= 96
   // (fewer than one wave per SIMD here, so registers are plentiful)
   constexpr int NC = 16 * NT, U = NT <= 6 ? 8 : NT <= 12 ? 4 : 2;
@@ -622,7 +625,8 @@ __global__ __launch_bounds__(64) void head_mfma_kernel(const float* __restrict__
   const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
   const int kb = s * k_len + 4 * g;
   // rows past M read row M-1; their results are not stored
-  const float* ap = hf + (size_t)min(m0 + l16, M - 1) * d + kb;
+  const int mr = min(m0 + l16, M - 1), smp = mr / r_out;
+  const float* ap = hf + ((size_t)smp * r_in + off + (mr - smp * r_out)) * d + kb;
   const float* wp = w + (size_t)l16 * d + kb;
   f32x4 acc[NT];
 #pragma unroll
@@ -661,12 +665,12 @@ __global__ __launch_bounds__(64) void head_mfma_kernel(const float* __restrict__
 }
 
 hipError_t launch_head_mfma(const float* hf, const float* w, float* planes, int M, int C,
-                            int d, int splits, hipStream_t st) {
+                            int d, int splits, hipStream_t st, int r_out, int r_in, int off) {
   const dim3 grid(((M + 15) / 16) * splits);
   const int k_len = d / splits;
 #define AF_HM(NT)                                                                        \
   hipLaunchKernelGGL((head_mfma_kernel<NT>), grid, dim3(64), 0, st, hf, w, planes, M, d, \
-                     k_len);                                                             \
+                     k_len, r_out, r_in, off);                                           \
   break;
   switch (C / 8) {
     case 1: AF_HM(1)

@@ -104,6 +104,8 @@ struct af_plan {
   int prof_class = -1;
   std::vector<hipEvent_t> ev;  // pairs
   int prof_n = 0;
+  // a block's cache refresh merged into the next block's first update
+  bool fuse_refresh = false;
   // HIP graphs of one Jacobi update, replayed once per iteration
   bool graphs = false;
   hipStream_t cap_stream = nullptr;
@@ -205,6 +207,7 @@ struct Pass {
   int N, L, s, R, P, dir;
   bool kv_only;         // stop after the last layer's K/V (cache refresh)
   bool precise;         // bf16 path: carry activations as bf16 pairs (hi + lo)
+  int hskip = 0;        // head and affine skip the first hskip rows of each sample
 };
 
 // One pass of the network over chunk rows [s, s+R) of every sample:
@@ -293,9 +296,12 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   af::AffineArgs fa = *aa;
   fa.head = head;
   if (af::head_mfma_supported(c.C, d)) {
-    fa.head_splits = af::head_mfma_splits(M, d);
-    LAUNCH(K_HEAD, af::launch_head_mfma(hf, bw.w_head, head, M, c.C, d, fa.head_splits, st));
+    const int rh = ps.R - ps.hskip, mh = ps.N * rh;
+    fa.head_splits = af::head_mfma_splits(mh, d);
+    LAUNCH(K_HEAD, af::launch_head_mfma(hf, bw.w_head, head, mh, c.C, d, fa.head_splits, st,
+                                        rh, ps.R, ps.hskip));
   } else {
+    if (ps.hskip != 0) return fail(AF_ERR_UNSUPPORTED, "head row offset needs C % 8 == 0");
     fa.head_splits = af::head_splits(M, 2 * c.C, d);
     LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
                                               fa.head_splits, st));
@@ -568,10 +574,27 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   WsLayout w;
   if (af_status s = check_ws(p, N, Bc, ws_, ws_bytes, &w)) return s;
   if (af_status s = ensure_host_res(p, N)) return s;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)ws_;
   const int C = p->cfg.C;
   const int nb = (L + B - 1) / B;
+  // A block that stops early has its cache rows recomputed from its final
+  // tokens.  With a workspace for two blocks of rows, that pass is merged into
+  // the next block's first update (one pass over both blocks' rows; the head
+  // and the affine update cover the new block only), else it runs on its own.
+  int rows = Bc;
+  bool fuse = false;
+  if (p->fuse_refresh && nb > 1 && af::head_mfma_supported(C, p->cfg.d)) {
+    const int r2 = std::min(2 * Bc, L);
+    WsLayout w2;
+    if (check_ws(p, N, r2, ws_, ws_bytes, &w2) == AF_OK) {
+      w = w2;
+      rows = r2;
+      fuse = true;
+    } else {
+      g_err.clear();
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_;
   int device = 0;
   if (p->graphs) AF_HIP(hipGetDevice(&device));
   float* xtmp = (float*)(ws + w.xtmp);
@@ -584,6 +607,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   for (int t = p->T - 1; t >= 0; --t) {
     float* xo = (t % 2 == 0) ? x : xtmp;
     const int dir = t & 1;
+    int pending = 0;   // rows of the previous block whose refresh is merged here
     for (int b = 0; b < nb; ++b) {
       const int s = b * B, R = (s + B < L ? s + B : L) - s;
       const int kmax = max_iters <= 0 ? R : (max_iters < R ? max_iters : R);
@@ -601,7 +625,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       GraphEntry* g = nullptr;
       if (p->graphs && p->prof_class < 0) {
         const GraphKey key{&p->blocks[t], xo, x_last, zin, p->host_res_dev, ws, device,
-                           N, L, s, R, prefix_len, dir, Bc, (unsigned)(1 + t * nb + b)};
+                           N, L, s, R, prefix_len, dir, rows, (unsigned)(1 + t * nb + b)};
         g = graph_lookup(p, key);
         if (!g && kmax >= 2)
           if (af_status e = graph_capture(p, key, p->blocks[t], ps, aa, ws, w, st, &g)) return e;
@@ -609,7 +633,14 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       int k = 0;
       bool nonfinite = false;
       for (k = 1; k <= kmax; ++k) {
-        if (g) {
+        if (k == 1 && pending > 0) {
+          // previous block's refresh + this block's first update, one pass
+          Pass pf = ps;
+          pf.s = s - pending;
+          pf.R = R + pending;
+          pf.hskip = pending;
+          if (af_status e = jacobi_update(p, p->blocks[t], pf, aa, ws, w, st)) return e;
+        } else if (g) {
           AF_HIP(hipGraphLaunch(g->exec, st));
           ++p->g_replays;
         } else if (af_status e = jacobi_update(p, p->blocks[t], ps, aa, ws, w, st)) {
@@ -637,10 +668,15 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       }
       if (k > kmax) k = kmax;
       iters[t * nb + b] = k;
+      pending = 0;
       if (k < R && b + 1 < nb) {
-        Pass pr = ps;
-        pr.kv_only = true;
-        if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) return e;
+        if (fuse) {
+          pending = R;
+        } else {
+          Pass pr = ps;
+          pr.kv_only = true;
+          if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) return e;
+        }
       }
     }
     zin = xo;
@@ -692,6 +728,12 @@ af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
   }
   *launches = p->prof_n;
   *total_ms = tot;
+  return AF_OK;
+}
+
+af_status af_plan_set_fused_refresh(af_plan* p, int enable) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->fuse_refresh = enable != 0;
   return AF_OK;
 }
 

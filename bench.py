@@ -78,7 +78,10 @@ class Runner:
         self.binding = binding
         self.x = torch.empty_like(self.z)
         self.iters = np.zeros((w.n_blocks, -(-L // w.jacobi_block)), np.int32)
-        self.ws = self.plan.workspace(N, self.rows)
+        nb = -(-L // w.jacobi_block)
+        # (rows for two blocks: --fused-refresh may merge a block's cache
+        # refresh into the next block's first pass)
+        self.ws = self.plan.workspace(N, min(2 * w.jacobi_block, L) if nb > 1 else self.rows)
         torch.cuda.synchronize()
         self.tokens_per_step = N * L
 
@@ -239,7 +242,7 @@ def schedule_sweep(torch, binding, synth, reps):
             "asymmetric_video21": asym_row}
 
 
-def pipeline_bench(torch, binding, synth, reps, graphs=False):
+def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=False):
     """End-to-end inverse of the deep o shallow flow over 21 frames (deep:
     the video21 block, shallow: the shallow_stack stack), three schedules:
     stages (the deep block over all frames in one call, then the shallow
@@ -252,8 +255,9 @@ def pipeline_bench(torch, binding, synth, reps, graphs=False):
     F = v.frame_len
     deep = binding.AFPlan(v.block, synth.make_params(v.block, 0))
     shallow = binding.AFPlan(sh.block, synth.make_params(sh.block, 0, n_blocks=sh.n_blocks))
-    deep.set_graphs(graphs)
-    shallow.set_graphs(graphs)
+    for plan in (deep, shallow):
+        plan.set_graphs(graphs)
+        plan.set_fused_refresh(fused_refresh)
     flow = DeepShallowFlow(deep, shallow, F)
     z = dev(synth.normal((1, v.length, v.block.C), 1))
     nf = v.length // F
@@ -292,6 +296,9 @@ def main():
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--fused-refresh", action="store_true",
+                    help="recompute an early-stopped block's K/V in the next block's "
+                         "first update instead of in a pass of its own")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the captured Jacobi update as a HIP graph instead "
                          "of launching every kernel directly")
@@ -325,7 +332,7 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     if args.pipeline:
         print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1),
-                                        args.graphs)), flush=True)
+                                        args.graphs, args.fused_refresh)), flush=True)
         return
     if args.schedule_sweep:
         print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
@@ -334,6 +341,7 @@ def main():
     r = Runner(args.workload, torch, binding, synth)
     cfg, w = r.cfg, r.w
     r.plan.set_graphs(args.graphs)
+    r.plan.set_fused_refresh(args.fused_refresh)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -420,6 +428,7 @@ def main():
                             "bytes_per_launch": aff_bytes} if aff_gbs is not None
                            else {"fused_into": "gemm_head"}),
         "graphs": args.graphs,
+        "fused_refresh": args.fused_refresh,
         "kernel_ms_per_step": breakdown,
         "forward_ms": round(fwd_ms, 3),
     }

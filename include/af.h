@@ -171,8 +171,13 @@ af_status af_refresh_kv(af_plan *p, const float *x, int N, int L, int prefix_len
  *   iters    HOST int32 [n_blocks][ceil(L/B)]: updates made per Jacobi block,
  *                        row t for stack block t
  * For n_blocks > 1 only AF_INIT_ZERO and P == 0 are supported.  Needs
- * ws_bytes >= af_workspace_bytes(p, N, min(B, L)).  Returns AF_ERR_NONFINITE
- * if an update produced a non-finite value. */
+ * ws_bytes >= af_workspace_bytes(p, N, min(B, L)).  With
+ * af_plan_set_fused_refresh(p, 1) and ws_bytes >= af_workspace_bytes(p, N,
+ * min(2B, L)) the recomputation of a block's K/V runs in the same network pass
+ * as the next block's first update, over the rows of both blocks (the update
+ * covers the new block's rows only); results equal those of the separate pass
+ * up to floating-point summation order.  Returns AF_ERR_NONFINITE if an update
+ * produced a non-finite value. */
 af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
                             float tau, int max_iters, af_init init,
                             const float *x_init, int frame_len, int prefix_len,
@@ -211,6 +216,12 @@ af_status af_profile_read(af_plan *p, int *launches, double *total_ms);
  *   af_plan_graph_stats: graphs captured and graph launches made by this plan
  *     since it was created; AF_ERR_ARG on a NULL argument. */
 af_status af_plan_set_graphs(af_plan *p, int enable);
+
+/* Merge a Jacobi block's K/V recomputation into the next block's first update
+ * when the workspace allows (see af_inverse_jacobi): enable != 0, or 0 (the
+ * default) for a pass of its own, which stops after the last layer's K/V and
+ * measured faster for full-frame blocks; AF_ERR_ARG if p is NULL. */
+af_status af_plan_set_fused_refresh(af_plan *p, int enable);
 af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *replays);
 
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---

@@ -184,4 +184,6 @@ def test_graph_controls(lib):
     assert lib.af_plan_set_graphs(h, 0) == B.AF_OK
     assert lib.af_plan_set_graphs(h, 1) == B.AF_OK
     assert lib.af_plan_set_graphs(None, 1) == B.AF_ERR_ARG
+    assert lib.af_plan_set_fused_refresh(h, 0) == B.AF_OK
+    assert lib.af_plan_set_fused_refresh(None, 1) == B.AF_ERR_ARG
     lib.af_plan_destroy(h)

@@ -161,10 +161,10 @@ def test_f32_stack_ragged_r2l(B):
 
 @pytest.mark.parametrize("C,d,N,L,Bj", [(24, 128, 2, 70, 32), (64, 256, 1, 50, 50),
                                          (8, 512, 3, 33, 16)])
-def test_f32_fused_head_shapes(B, C, d, N, L, Bj):
-    """The fused head + affine kernel at other channel counts (2C = 48, 128,
-    16 columns), K split over 1..8 workgroups, ragged 16-row tiles, batch."""
-    say("f32 fused head", C, d, N, L, Bj)
+def test_f32_head_mfma_shapes(B, C, d, N, L, Bj):
+    """The fp32-MFMA head at other channel counts (2C = 48, 128, 16 columns),
+    K split over 1..8 ranges, ragged 16-row tiles, batch."""
+    say("f32 head mfma", C, d, N, L, Bj)
     H = d // 64
     cfg, params, (p64,) = problem(C=C, d=d, H=H, layers=1, max_len=L, dtype="f32",
                                   seed=C + d)
@@ -182,11 +182,51 @@ def test_f32_fused_head_shapes(B, C, d, N, L, Bj):
     assert rel_l2(to_np(xg), xo) < TOL_F32
 
 
-def test_bf16_unfused_head(B):
-    """C = 20 (2C not a multiple of 16): the head GEMM and the affine kernel
-    run as two launches."""
+def test_bf16_head_vector_path(B):
+    """C = 20 (2C not a multiple of 16): the head runs on the vector-ALU fp32
+    GEMM, and block refreshes run as separate passes."""
     say("bf16 C=20 L=150 B=64")
     _bf16_block_case(B, d=256, H=4, layers=1, L=150, Bj=64, N=2, seed=23, C=20)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_refresh_matches_separate_pass(B, dtype):
+    """A block that stops early has its K/V recomputed from its final tokens;
+    merged into the next block's first update (one pass over both blocks'
+    rows) the result equals the separate pass: bit for bit on the fp32 path,
+    to summation order on the bf16 path; both match the oracle."""
+    say("fused refresh", dtype)
+    if dtype == "f32":
+        cfg, params, (p64,) = problem(C=8, d=64, H=2, layers=2, max_len=100, dtype="f32",
+                                      seed=60)
+        N, L, Bj, C, H = 2, 100, 32, 8, 2
+    else:
+        cfg, params, (p64,) = problem(C=48, d=256, H=4, layers=2, max_len=300, dtype="bf16",
+                                      seed=61)
+        N, L, Bj, C, H = 2, 300, 96, 48, 4
+    plan = B.AFPlan(cfg, params)
+    z = to_dev(synth.normal((N, L, C), 62))
+    ws = plan.workspace(N, min(2 * Bj, L))
+    out = {}
+    for fused in (False, True):
+        plan.set_fused_refresh(fused)
+        x = torch.empty_like(z)
+        it = np.zeros((1, -(-L // Bj)), np.int32)
+        B.af_inverse_jacobi(plan, z, Bj, 1e-3, 0, "zero", None, 0, 0, None, x, it, ws)
+        torch.cuda.synchronize()
+        out[fused] = (x, it)
+    (x0, it0), (x1, it1) = out[False], out[True]
+    print("iters separate", it0.tolist(), "fused", it1.tolist())
+    assert np.all(it0[0][:-1] < Bj)                 # early stops: refreshes happen
+    xo, ito = oracle_jacobi_like(p64, to_np(z), H, Bj, 1e-3, it1[0])
+    if dtype == "f32":
+        assert np.array_equal(it0, it1) and torch.equal(x0, x1)
+        assert np.array_equal(it1[0], ito)
+        assert rel_l2(to_np(x1), xo) < TOL_F32
+    else:
+        assert np.all(np.abs(it0 - it1) <= 1)
+        assert rel_l2(to_np(x1), to_np(x0)) < 1e-2
+        assert rel_l2(to_np(x1), xo) < TOL_BF16
 
 
 def test_f32_forced_count_and_sequential(B):
