@@ -705,6 +705,11 @@ struct TileChoice {
 };
 static const int kTileCfgs[][2] = {{7, 4}, {7, 3}, {7, 2}, {4, 4}, {4, 2}};
 
+// Tile and split choice from a cost model fitted to measured launches at
+// 1560 rows (bf16, d = 1024): a block's time grows with its operand bytes,
+// (BM + BN) * K / S (the per-CU load path sets the pace), and with its output
+// tile, BM * BN (epilogue); blocks beyond 256 take another round; each extra
+// split plane costs its consumer one more fp32 [M, N] read.
 TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = false) {
   TileChoice best{4, 2, 1};
   double best_cost = 1e300;
@@ -715,12 +720,9 @@ TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = fal
     const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
     for (int s = 1; s <= (allow_split ? 8 : 1); s *= 2) {
       if (K % (64 * s) || (s > 1 && K / s < 256)) break;
-      const long blocks = tiles * s;
-      const long rounds = (blocks + 255) / 256;
-      // per-block time ~ MFMA work + a fixed pipeline fill per block
-      const double per_block = (double)BM * BN * (K / s) * (1.0 + 0.35 * 64.0 / BN) +
-                               (double)BM * BN * 64 * 6;
-      const double cost = rounds * per_block * (s > 1 ? 1.02 : 1.0);
+      const long rounds = (tiles * s + 255) / 256;
+      const double per_block = 4.28e-5 * (BM + BN) * (double)(K / s) + 4.66e-4 * BM * BN;
+      const double cost = rounds * per_block + 4.0e-7 * (s - 1) * (double)M * N;
       if (cost < best_cost) {
         best_cost = cost;
         best = TileChoice{c[0], c[1], s};
