@@ -50,6 +50,9 @@ struct AffineArgs {
   unsigned* bad;       // inverse: set to `tag` (if still 0) when a residual sum is
   unsigned tag;        // not finite; may be NULL
   float* res_host;     // inverse: host-mapped copy of res written at the end, or NULL
+  unsigned* seq_dev;   // inverse: device counter of finished updates, or NULL
+  unsigned* seq_host;  // inverse: host-mapped word that receives the counter after
+                       // res_host is written (the host polls it), or NULL
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

@@ -483,7 +483,14 @@ __device__ void finish_sums(const AffineArgs& a, const float* partials, int G, f
       }
     }
   }
-  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
+  if (threadIdx.x == 0) {
+    if (MODE == 0 && a.seq_host) {
+      // publish the update's number once its residuals have reached the host
+      wait_stores();
+      system_store(a.seq_host, atomicAdd(a.seq_dev, 1u) + 1u);
+    }
+    atomicExch(a.counter, 0u);
+  }
 }
 
 template <int MODE, bool VEC>

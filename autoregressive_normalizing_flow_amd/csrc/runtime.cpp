@@ -11,6 +11,7 @@
 //   一个完整示例 - conditioning by forward-encoding observed tokens into the cache.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <algorithm>
@@ -97,7 +98,7 @@ struct af_plan {
   bool bf;
   size_t esz;  // bytes per element of the per-layer operand type
   std::vector<BlockW> blocks;
-  float* host_res = nullptr;  // pinned [res_cap][2]
+  float* host_res = nullptr;  // pinned [res_cap][2], then one sequence word
   int res_cap = 0;
   float* host_res_dev = nullptr;  // the same memory as the device sees it
   // profiling
@@ -208,7 +209,11 @@ struct Pass {
   bool kv_only;         // stop after the last layer's K/V (cache refresh)
   bool precise;         // bf16 path: carry activations as bf16 pairs (hi + lo)
   int hskip = 0;        // head and affine skip the first hskip rows of each sample
+  // PASS_ALL: the whole pass; PASS_PREFIX: shift + embed, first LayerNorm and
+  // layer 0's QKV only; PASS_REST: the remainder after a PASS_PREFIX
+  int part = 0;
 };
+constexpr int PASS_ALL = 0, PASS_PREFIX = 1, PASS_REST = 2;
 
 // One pass of the network over chunk rows [s, s+R) of every sample:
 // shift+embed, n_layers pre-LN layers (K/V into the cache), final LN + head.
@@ -229,15 +234,18 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   void* u_lo = sp ? ws + w.u_lo : nullptr;
   float* slab = (float*)(ws + w.slab);
   const int pos_base = ps.P + ps.s;
-  LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
-                                   ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
-                                   pos_base, st));
+  const bool pre = ps.part != PASS_REST, post = ps.part != PASS_PREFIX;
+  if (pre)
+    LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
+                                     ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
+                                     pos_base, st));
   float* hf = (float*)(ws + w.hf);
   if (p->bf) {
     // bf16 path: the O-projection and MLP-down GEMMs write fp32 partial planes
     // and one row-wise kernel adds bias + residual and emits the next LN.
-    LAUNCH(K_LN, af::launch_layernorm(h, bw.layers[0].ln1_g, bw.layers[0].ln1_b, a, true, M,
-                                      d, st, a_lo));
+    if (pre)
+      LAUNCH(K_LN, af::launch_layernorm(h, bw.layers[0].ln1_g, bw.layers[0].ln1_b, a, true, M,
+                                        d, st, a_lo));
     for (int l = 0; l < c.n_layers; ++l) {
       const LayerW& lw = bw.layers[l];
       char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
@@ -245,8 +253,10 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       char* kc_lo = sp ? ws + w.cache_lo + (size_t)(2 * l) * w.cache_layer : nullptr;
       char* vt_lo = sp ? ws + w.cache_lo + (size_t)(2 * l + 1) * w.cache_layer : nullptr;
       af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
-      LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+      if (l > 0 || pre)
+        LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+      if (!post) return AF_OK;
       af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
       LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
                                           ps.N, ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base,
@@ -272,12 +282,15 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       const LayerW& lw = bw.layers[l];
       char* kc = ws + w.cache + (size_t)(2 * l) * w.cache_layer;
       char* vt = ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer;
-      LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, false, M, d, st));
       af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, nullptr,
                      nullptr, nullptr};
-      LAUNCH(K_QKV, af::launch_gemm_qkv(false, a, nullptr, lw.w_qkv, lw.b_qkv, M, 3 * d, d,
-                                        dst, st));
+      if (l > 0 || pre) {
+        LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, false, M, d, st));
+        LAUNCH(K_QKV, af::launch_gemm_qkv(false, a, nullptr, lw.w_qkv, lw.b_qkv, M, 3 * d, d,
+                                          dst, st));
+      }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+      if (!post) return AF_OK;
       LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, ps.N, ps.R,
                                           c.n_heads, p->dh, d, p->Lcap, pos_base, st));
       LAUNCH(K_O, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
@@ -332,10 +345,38 @@ af_status ensure_host_res(af_plan* p, int N) {
   if (p->host_res) (void)hipHostFree(p->host_res);
   p->host_res = p->host_res_dev = nullptr;
   p->res_cap = 0;
-  AF_HIP(hipHostMalloc((void**)&p->host_res, (size_t)N * 2 * sizeof(float),
+  AF_HIP(hipHostMalloc((void**)&p->host_res, ((size_t)N * 2 + 64) * sizeof(float),
                        hipHostMallocMapped | hipHostMallocCoherent));
   AF_HIP(hipHostGetDevicePointer((void**)&p->host_res_dev, p->host_res, 0));
   p->res_cap = N;
+  return AF_OK;
+}
+
+unsigned* seq_word(const af_plan* p, bool dev) {
+  return (unsigned*)((dev ? p->host_res_dev : p->host_res) + 2 * (size_t)p->res_cap);
+}
+
+// Wait until the update numbered `want` of this call has published its
+// residuals: the affine kernel writes them to pinned memory and then the
+// update's number to the sequence word.  Polling that word avoids a stream
+// synchronisation per update; the stream is queried now and then so that a
+// failed launch is reported instead of waited on.
+af_status wait_update(af_plan* p, unsigned want, hipStream_t st) {
+  volatile unsigned* f = seq_word(p, false);
+  for (unsigned long it = 1;; ++it) {
+    if (*f == want) break;
+    if ((it & 4095) == 0) {
+      const hipError_t q = hipStreamQuery(st);
+      if (q == hipSuccess) {
+        if (*f == want) break;
+        return fail(AF_ERR_HIP, "update finished without publishing its residual");
+      }
+      if (q != hipErrorNotReady)
+        return fail(AF_ERR_HIP, std::string("hipStreamQuery: ") + hipGetErrorString(q));
+    }
+    __builtin_ia32_pause();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
   return AF_OK;
 }
 
@@ -599,9 +640,13 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   if (p->graphs) AF_HIP(hipGetDevice(&device));
   float* xtmp = (float*)(ws + w.xtmp);
   float* res = (float*)(ws + w.res);
-  // counter word of the affine kernel and the sticky non-finite tag after it
+  // counter word of the affine kernel, the sticky non-finite tag after it,
+  // then the count of finished updates, published to the host's sequence word
   unsigned* bad = (unsigned*)(ws + w.counter) + 1;
-  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 2, st));
+  unsigned* seq_dev = (unsigned*)(ws + w.counter) + 2;
+  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 3, st));
+  *(volatile unsigned*)seq_word(p, false) = 0u;   // no update of this plan is in flight
+  unsigned n_updates = 0;
 
   const float* zin = z;
   for (int t = p->T - 1; t >= 0; --t) {
@@ -617,7 +662,8 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                         af::head_splits(N * R, 2 * C, p->cfg.d), zin, xo, nullptr, N, R, C, L, s,
                         dir, (float*)(ws + w.partials), res,
                         (unsigned*)(ws + w.counter), nullptr, bad,
-                        (unsigned)(1 + t * nb + b), p->host_res_dev};
+                        (unsigned)(1 + t * nb + b), p->host_res_dev, seq_dev,
+                        seq_word(p, true)};
       // the update is the same launch sequence on every iteration of the
       // block: replay it as one graph when there are several to run (or it is
       // cached from an earlier call).  Profiled calls launch directly, as
@@ -632,8 +678,14 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       }
       int k = 0;
       bool nonfinite = false;
+      bool prefixed = false;   // the next update's first kernels are already enqueued
       for (k = 1; k <= kmax; ++k) {
-        if (k == 1 && pending > 0) {
+        if (prefixed) {
+          Pass pr = ps;
+          pr.part = PASS_REST;
+          if (af_status e = jacobi_update(p, p->blocks[t], pr, aa, ws, w, st)) return e;
+          prefixed = false;
+        } else if (k == 1 && pending > 0) {
           // previous block's refresh + this block's first update, one pass
           Pass pf = ps;
           pf.s = s - pending;
@@ -646,14 +698,28 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         } else if (af_status e = jacobi_update(p, p->blocks[t], ps, aa, ws, w, st)) {
           return e;
         }
+        ++n_updates;
         // the residual is read only for the stop test; at the cap (and in
         // forced-count mode) a non-finite residual is caught through the
         // sticky tag read once at the end
         if (!(tau > 0.f && k < kmax)) continue;
-        AF_HIP(hipStreamSynchronize(st));
+        // While the host waits for the residual, the device runs the next
+        // update's first kernels (shift + embed, first LayerNorm, layer 0's
+        // QKV).  They write only scratch and this block's layer-0 K/V rows,
+        // which the next update would write identically and which the
+        // refresh after an early stop recomputes, so a stop leaves the result
+        // unchanged.  (Graph replay keeps whole updates.)
+        if (!g) {
+          Pass pp = ps;
+          pp.part = PASS_PREFIX;
+          if (af_status e = run_net(p, p->blocks[t], pp, ws, w, st)) return e;
+          prefixed = true;
+        }
+        if (af_status e = wait_update(p, n_updates, st)) return e;
+        const volatile float* hr = p->host_res;
         bool all_below = true;
         for (int n = 0; n < N; ++n) {
-          const float num = p->host_res[2 * n], den = p->host_res[2 * n + 1];
+          const float num = hr[2 * n], den = hr[2 * n + 1];
           if (!std::isfinite(num) || !std::isfinite(den)) nonfinite = true;
           const float r = den > 0.f ? num / den : (num == 0.f ? 0.f : INFINITY);
           if (!(r < tau)) all_below = false;

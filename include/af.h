@@ -159,7 +159,8 @@ af_status af_refresh_kv(af_plan *p, const float *x, int N, int L, int prefix_len
  * final x and kept in the cache (skipped when the block ran e-s updates, as
  * its last inputs were already final, and for the call's last Jacobi block,
  * which nothing in the call reads: a later call that continues after it
- * refreshes those rows with af_refresh_kv).
+ * refreshes those rows with af_refresh_kv; its layer-0 rows may already hold
+ * the K/V of its final tokens).
  *   z        [N, L, C]   input
  *   x        [N, L, C]   output (may not alias z)
  *   x_init   [N, L, C]   AF_INIT_GIVEN only, else may be NULL
