@@ -24,8 +24,10 @@ namespace af {
 // into chunks processed by separate workgroups, so the grid fills the chip
 // and no workgroup walks the whole prefix; a query tile with one chunk writes
 // its normalised output directly, otherwise each chunk writes its unnormalised
-// output and running (max, sum) to a partial slot and attn_combine merges the
-// chunks.  Units are numbered sample-head major, then query tile, then chunk.
+// output and running (max, sum) to a partial slot, takes a ticket of its query
+// tile, and the chunk that takes the last ticket merges the tile's slots (in
+// chunk order, so the result does not depend on which chunk merges).  Units
+// are numbered sample-head major, then query tile, then chunk.
 //
 // Inside a unit each of the 4 waves owns 32 queries (two 16-query blocks).
 // Per 64-key tile:  S^T = K Q^T  (A = K rows from LDS, B = Q held in
@@ -42,6 +44,17 @@ constexpr int ATT_KT = 64;    // keys per tile
 // largest score stays in [2^-32, 2^8] (no overflow, no underflow to zero).
 constexpr float RESCALE_LOG2 = 8.0f;
 constexpr float RESCALE_LOW = 32.0f;
+// Chunk slots merged per memory round trip.
+constexpr int ATT_MAXC = 4;
+// Cache-policy operand of the buffer builtins: sc1, agent-coherent access.
+constexpr int ATT_SC1 = 16;
+
+// Raw buffer resource over one partial slot (byte offsets from its start).
+template <int DH>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc_dh(const float* slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(slot), 0,
+                                           ATT_QT * (DH + 2) * 4, 0x00020000);
+}
 
 struct AttnArgs {
   const bf16* q;
@@ -55,7 +68,8 @@ struct AttnArgs {
   const bf16* vt_lo;
   bf16* out_lo;
   float* part;     // partial slots: [unit][ATT_QT][DH] O, then [ATT_QT] m, [ATT_QT] l
-  int R, H, d, Lcap, pos_base, KC, U_nh;
+  unsigned* tickets;   // [sample * H + head][query tile], zero between launches
+  int R, H, d, Lcap, pos_base, KC, U_nh, n_qt;
   int xcd_map;     // 1: deal (sample, head) pairs to XCDs (needs N*H % 8 == 0)
 };
 
@@ -389,38 +403,143 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
     __syncthreads();
   }
 
+  // bf16 hi + lo of the normalised output row of query t, dimensions
+  // db*16 + lg*4 .. +3
+  auto store_out = [&](int t, int db, const f32x4& v, float inv) {
+    const size_t oo = ((size_t)n * R + t) * d + head * DH + db * 16 + lg * 4;
+    bf16x4 o, ol;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = acc_l[qb][0];
-    const int tq = wave * QWAVE + qb * 16 + l16;   // query within the tile
-    const int t = q_lo + tq;
-    if (n_chunks == 1) {
+    for (int r = 0; r < 4; ++r) {
+      const float y = v[r] * inv;
+      o[r] = (bf16)y;
+      ol[r] = (bf16)(y - (float)o[r]);
+    }
+    *(bf16x4*)(a.out + oo) = o;
+    if (SPLIT) *(bf16x4*)(a.out_lo + oo) = ol;
+  };
+
+  if (n_chunks == 1) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int t = q_lo + wave * QWAVE + qb * 16 + l16;
       if (t < R) {
-        const float inv = 1.0f / l;
-        const size_t oo = ((size_t)n * R + t) * d + head * DH;
+        const float inv = 1.0f / acc_l[qb][0];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          bf16x4 o, ol;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float y = acc_o[db][qb][r] * inv;
-            o[r] = (bf16)y;
-            ol[r] = (bf16)(y - (float)o[r]);
-          }
-          *(bf16x4*)(a.out + oo + db * 16 + lg * 4) = o;
-          if (SPLIT) *(bf16x4*)(a.out_lo + oo + db * 16 + lg * 4) = ol;
-        }
+        for (int db = 0; db < DB; ++db) store_out(t, db, acc_o[db][qb], inv);
       }
-    } else {
-      float* slot = a.part + (size_t)u * ATT_QT * (DH + 2);
+    }
+    return;
+  }
+
+  // Partial slot of this chunk, written with agent-coherent (sc1) stores so
+  // that the merging block reads it from any XCD without an L2 writeback.
+  constexpr int SLOT = ATT_QT * (DH + 2);
+  {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)u * SLOT);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = acc_l[qb][0];
+      const int tq = wave * QWAVE + qb * 16 + l16;   // query within the tile
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *(f32x4*)(slot + (size_t)tq * DH + db * 16 + lg * 4) = acc_o[db][qb];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc_o[db][qb]), rs,
+                                               (tq * DH + db * 16 + lg * 4) * 4, 0, ATT_SC1);
       if (lg == 0) {
         // a row with no key in this chunk (l = 0) must not set the merge's max
-        slot[ATT_QT * DH + tq] = l > 0.f ? m_run[qb] : -1e30f;
-        slot[ATT_QT * DH + ATT_QT + tq] = l;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l > 0.f ? m_run[qb] : -1e30f),
+                                              rs, (ATT_QT * DH + tq) * 4, 0, ATT_SC1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs,
+                                              (ATT_QT * DH + ATT_QT + tq) * 4, 0, ATT_SC1);
       }
+    }
+  }
+  wait_stores();
+  __syncthreads();   // every store of the block is complete before the ticket
+  __shared__ unsigned s_last;
+  if (tid == 0) {
+    unsigned* tk = a.tickets + (size_t)nh * a.n_qt + qt;
+    const unsigned last = atomicAdd(tk, 1u) + 1u == (unsigned)n_chunks;
+    if (last) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // Merge: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the chunks in
+  // order, MC chunks per memory round trip (every load of a group, for both
+  // query blocks, is issued before the first use; this block's own chunk comes
+  // from its registers), with a running max across groups.
+  constexpr int MC = DH <= 64 ? ATT_MAXC : ATT_MAXC / 2;
+  const float* tile0 = a.part + (size_t)(u - chunk) * SLOT;   // the tile's chunk 0
+  float m[QB], l[QB];
+  f32x4 o[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -1e30f;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int c0 = 0; c0 < n_chunks; c0 += MC) {
+    float mc[MC][QB], lc[MC][QB];
+    f32x4 oc[MC][QB][DB];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      const int cc = min(c0 + c, n_chunks - 1);
+      if (cc == chunk) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          lc[c][qb] = acc_l[qb][0];
+          mc[c][qb] = lc[c][qb] > 0.f ? m_run[qb] : -1e30f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oc[c][qb][db] = acc_o[db][qb];
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(tile0 + (size_t)cc * SLOT);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int tq = wave * QWAVE + qb * 16 + l16;
+          mc[c][qb] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, (ATT_QT * DH + tq) * 4, 0, ATT_SC1));
+          lc[c][qb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rs, (ATT_QT * DH + ATT_QT + tq) * 4, 0, ATT_SC1));
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oc[c][qb][db] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (tq * DH + db * 16 + lg * 4) * 4, 0, ATT_SC1));
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mg = m[qb];
+#pragma unroll
+      for (int c = 0; c < MC; ++c)
+        if (c0 + c < n_chunks) mg = fmaxf(mg, mc[c][qb]);
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mg);
+      l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+#pragma unroll
+      for (int c = 0; c < MC; ++c) {
+        if (c0 + c >= n_chunks) break;
+        const float w = __builtin_amdgcn_exp2f(mc[c][qb] - mg);
+        l[qb] = fmaf(w, lc[c][qb], l[qb]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[qb][db][r] = fmaf(w, oc[c][qb][db][r], o[qb][db][r]);
+      }
+      m[qb] = mg;
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = q_lo + wave * QWAVE + qb * 16 + l16;
+    if (t < R) {
+      const float inv = 1.0f / l[qb];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) store_out(t, db, o[qb][db], inv);
     }
   }
 }
@@ -438,94 +557,6 @@ attn_bf16_kernel_o2(AttnArgs a) {
 template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   attn_bf16_body<DH, SPLIT>(a);
-}
-
-// Merge the key chunks of every query tile that has more than one:
-// O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, chunks in order.
-// ATT_CTPQ threads per query row, each owning DH/ATT_CTPQ dimensions, and
-// ATT_CQPB query rows per block (a quarter tile), so the grid has four
-// blocks per query tile; every load of a thread (the chunks' m, l and O
-// values) is issued before the first use, so the kernel waits for memory
-// once.  At most ATT_MAXC chunks are merged in registers; longer ranges loop
-// over groups of that many.
-constexpr int ATT_MAXC = 4;
-constexpr int ATT_CTPQ = 8, ATT_CQPB = 256 / ATT_CTPQ;
-
-template <int DH>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_qt) {
-  constexpr int SUB = ATT_QT / ATT_CQPB;
-  const int tile = blockIdx.x / SUB, sub = blockIdx.x - tile * SUB;
-  const int nh = tile / n_qt, qt = tile - nh * n_qt;
-  const int n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
-  if (n_chunks <= 1) return;
-  int u0 = nh * a.U_nh;
-  for (int q = 0; q < qt; ++q) u0 += att_chunks(q, a.R, a.pos_base, a.KC);
-  const int n = nh / a.H, head = nh - n * a.H;
-  const int tq = sub * ATT_CQPB + threadIdx.x / ATT_CTPQ, part = threadIdx.x % ATT_CTPQ;
-  const int t = qt * ATT_QT + tq;
-  if (t >= a.R) return;
-  constexpr int SLOT = ATT_QT * (DH + 2);
-  constexpr int DP = DH / ATT_CTPQ, D4 = DP / 4;   // dimensions / float4 per thread
-  static_assert(DP % 4 == 0, "a float4 per thread at least");
-  const float* base = a.part + (size_t)u0 * SLOT;
-  float m = -1e30f, l = 0.f;
-  float4 o[D4];
-#pragma unroll
-  for (int j = 0; j < D4; ++j) o[j] = float4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < n_chunks; c0 += ATT_MAXC) {
-    float mc[ATT_MAXC], lc[ATT_MAXC];
-    float4 oc[ATT_MAXC][D4];
-#pragma unroll
-    for (int c = 0; c < ATT_MAXC; ++c) {
-      const float* slot = base + (size_t)min(c0 + c, n_chunks - 1) * SLOT;
-      mc[c] = slot[ATT_QT * DH + tq];
-      lc[c] = slot[ATT_QT * DH + ATT_QT + tq];
-      const float4* src = (const float4*)(slot + (size_t)tq * DH + part * DP);
-#pragma unroll
-      for (int j = 0; j < D4; ++j) oc[c][j] = src[j];
-    }
-    float mg = m;
-#pragma unroll
-    for (int c = 0; c < ATT_MAXC; ++c)
-      if (c0 + c < n_chunks) mg = fmaxf(mg, mc[c]);
-    const float alpha = __builtin_amdgcn_exp2f(m - mg);
-    l *= alpha;
-#pragma unroll
-    for (int j = 0; j < D4; ++j) {
-      o[j].x *= alpha;
-      o[j].y *= alpha;
-      o[j].z *= alpha;
-      o[j].w *= alpha;
-    }
-#pragma unroll
-    for (int c = 0; c < ATT_MAXC; ++c) {
-      if (c0 + c >= n_chunks) break;
-      const float w = __builtin_amdgcn_exp2f(mc[c] - mg);
-      l += w * lc[c];
-#pragma unroll
-      for (int j = 0; j < D4; ++j) {
-        o[j].x += w * oc[c][j].x;
-        o[j].y += w * oc[c][j].y;
-        o[j].z += w * oc[c][j].z;
-        o[j].w += w * oc[c][j].w;
-      }
-    }
-    m = mg;
-  }
-  const float inv = 1.0f / l;
-  const size_t oo = ((size_t)n * a.R + t) * a.d + head * DH + part * DP;
-#pragma unroll
-  for (int j = 0; j < D4; ++j) {
-    const float y[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
-    bf16x4 r, rl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      r[e] = (bf16)y[e];
-      rl[e] = (bf16)(y[e] - (float)r[e]);
-    }
-    *(bf16x4*)(a.out + oo + 4 * j) = r;
-    if (a.out_lo) *(bf16x4*)(a.out_lo + oo + 4 * j) = rl;
-  }
 }
 
 // Key chunk length: the smallest multiple of 512 keys that keeps the number
@@ -596,18 +627,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 }
 
 template <int DH, bool SPLIT>
-static void attn_launch(const AttnArgs& a, dim3 grid, dim3 comb, bool multi, int n_qt,
-                        hipStream_t st) {
+static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (DH <= 64 && !SPLIT)
     hipLaunchKernelGGL((attn_bf16_kernel_o2<DH, SPLIT>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
-  if (multi) hipLaunchKernelGGL(attn_combine_kernel<DH>, comb, dim3(256), 0, st, a, n_qt);
 }
 
 hipError_t launch_attention(bool bf, const void* q, const void* kc,
-                            const void* vt, void* out, float* part, int N, int R,
-                            int H, int dh, int d, int Lcap, int pos_base,
+                            const void* vt, void* out, float* part, unsigned* tickets,
+                            int N, int R, int H, int dh, int d, int Lcap, int pos_base,
                             hipStream_t st, const AttnSplit* split) {
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf) {
@@ -618,17 +647,17 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
                split ? (const bf16*)split->q_lo : nullptr,
                split ? (const bf16*)split->kc_lo : nullptr,
                split ? (const bf16*)split->vt_lo : nullptr,
-               split ? (bf16*)split->out_lo : nullptr, part,
-               R, H, d, Lcap, pos_base, KC, U_nh, (N * H) % 8 == 0 ? 1 : 0};
-    const dim3 grid(N * H * U_nh), comb(N * H * n_qt * (ATT_QT / ATT_CQPB));
-    const bool multi = U_nh > n_qt;
+               split ? (bf16*)split->out_lo : nullptr, part, tickets,
+               R, H, d, Lcap, pos_base, KC, U_nh, n_qt, (N * H) % 8 == 0 ? 1 : 0};
+    if (U_nh > n_qt && (!part || !tickets)) return hipErrorInvalidValue;
+    const dim3 grid(N * H * U_nh);
     switch (dh * 2 + (split ? 1 : 0)) {
-      case 128: attn_launch<64, false>(a, grid, comb, multi, n_qt, st); break;
-      case 129: attn_launch<64, true>(a, grid, comb, multi, n_qt, st); break;
-      case 256: attn_launch<128, false>(a, grid, comb, multi, n_qt, st); break;
-      case 257: attn_launch<128, true>(a, grid, comb, multi, n_qt, st); break;
-      case 64: attn_launch<32, false>(a, grid, comb, multi, n_qt, st); break;
-      case 65: attn_launch<32, true>(a, grid, comb, multi, n_qt, st); break;
+      case 128: attn_launch<64, false>(a, grid, st); break;
+      case 129: attn_launch<64, true>(a, grid, st); break;
+      case 256: attn_launch<128, false>(a, grid, st); break;
+      case 257: attn_launch<128, true>(a, grid, st); break;
+      case 64: attn_launch<32, false>(a, grid, st); break;
+      case 65: attn_launch<32, true>(a, grid, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -115,8 +115,10 @@ int head_splits(int M, int N, int K);
 // 0..pos_base+t (inclusive) for chunk row m = n*R + t.
 // bf16: q comes from launch_gemm_qkv already times log2(e) / sqrt(dh), so
 // the softmax is 2^(q k^T) normalised; long key ranges are split into chunks
-// whose partial results go to `part` (attention_partial_floats(...) floats)
-// and are merged by a second kernel.
+// whose partial results go to `part` (attention_partial_floats(...) floats),
+// and the last chunk of a query tile to finish merges them.  `tickets` holds
+// attention_tickets(N, R, H) words that must be zero before the first launch;
+// every launch leaves them zero again.
 struct AttnSplit {   // lo halves of the split (higher-precision) mode
   const void* q_lo;
   const void* kc_lo;
@@ -124,9 +126,12 @@ struct AttnSplit {   // lo halves of the split (higher-precision) mode
   void* out_lo;
 };
 hipError_t launch_attention(bool bf16, const void* q, const void* kc,
-                            const void* vt, void* out, float* part, int N, int R,
-                            int H, int dh, int d, int Lcap, int pos_base,
+                            const void* vt, void* out, float* part, unsigned* tickets,
+                            int N, int R, int H, int dh, int d, int Lcap, int pos_base,
                             hipStream_t st, const AttnSplit* split = nullptr);
 size_t attention_partial_floats(int N, int R, int H, int dh, int pos_base);
+inline size_t attention_tickets(int N, int R, int H) {
+  return (size_t)N * H * ((R + 127) / 128);
+}
 
 }  // namespace af

@@ -58,7 +58,7 @@ struct BlockW {
 // Byte offsets of the workspace regions for (batch, rows).
 struct WsLayout {
   size_t cache_layer;  // bytes of one layer's K (or V) cache
-  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, slab, attn_part, xtmp;
+  size_t cache, h, a, q, att, u, hf, head, partials, res, counter, tickets, slab, attn_part, xtmp;
   // lo halves of the split (higher-precision) forward on the bf16 path
   size_t cache_lo, a_lo, q_lo, att_lo, u_lo, total;
 };
@@ -148,7 +148,10 @@ WsLayout layout(const af_plan* p, int N, int rows) {
   w.head = off;     off += align256(head_plane_rows(M, 2 * c.C, c.d) * 2 * c.C * 4);
   w.partials = off; off += align256((size_t)N * af::affine_groups(N, rows, c.C) * 2 * 4);
   w.res = off;      off += align256((size_t)N * 2 * 4);
+  // 64 counter words, then the attention merge tickets (zero between
+  // launches; cleared with the counters at the start of every call)
   w.counter = off;  off += 256;
+  w.tickets = off;  off += align256(p->bf ? af::attention_tickets(N, rows, c.n_heads) * 4 : 0);
   w.slab = off;
   if (p->bf) {
     const int s1 = af::gemm_resid_splits((int)M, c.d, c.d);
@@ -259,7 +262,8 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       if (!post) return AF_OK;
       af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
       LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
-                                          ps.N, ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base,
+                                          (unsigned*)(ws + w.tickets), ps.N, ps.R,
+                                          c.n_heads, p->dh, d, p->Lcap, pos_base,
                                           st, sp ? &asp : nullptr));
       int S = 1;
       LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st));
@@ -291,7 +295,7 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
       if (!post) return AF_OK;
-      LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, ps.N, ps.R,
+      LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, nullptr, ps.N, ps.R,
                                           c.n_heads, p->dh, d, p->Lcap, pos_base, st));
       LAUNCH(K_O, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
                                         nullptr, st));
@@ -321,6 +325,11 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   }
   LAUNCH(K_AFFINE, af::launch_affine(mode, fa, st));
   return AF_OK;
+}
+
+// Zero the counter words and the attention merge tickets behind them.
+hipError_t clear_counters(const WsLayout& w, char* ws, hipStream_t st) {
+  return af::launch_fill_u32(ws + w.counter, 0u, (w.slab - w.counter) / 4, st);
 }
 
 af_status check_ws(const af_plan* p, int N, int rows, void* ws, size_t ws_bytes,
@@ -546,7 +555,7 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)ws_;
   const int C = p->cfg.C;
-  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 1, st));
+  AF_HIP(clear_counters(w, ws, st));
   AF_HIP(af::launch_fill_u32(logdet, 0u, (size_t)N, st));
   float* xtmp = (float*)(ws + w.xtmp);
   const float* cur = x;
@@ -575,6 +584,7 @@ af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
   if (af_status s = check_ws(p, N, P, ws_, ws_bytes, &w)) return s;
   hipStream_t st = (hipStream_t)stream;
   Pass ps{x_prefix, nullptr, N, P, 0, P, 0, 0, true, false};
+  AF_HIP(clear_counters(w, (char*)ws_, st));
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
 }
 
@@ -589,6 +599,7 @@ af_status af_refresh_kv(af_plan* p, const float* x, int N, int L, int prefix_len
   if (af_status s = check_ws(p, N, L, ws_, ws_bytes, &w)) return s;
   hipStream_t st = (hipStream_t)stream;
   Pass ps{x, x_last, N, L, 0, L, prefix_len, 0, true, false};
+  AF_HIP(clear_counters(w, (char*)ws_, st));
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
 }
 
@@ -644,7 +655,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   // then the count of finished updates, published to the host's sequence word
   unsigned* bad = (unsigned*)(ws + w.counter) + 1;
   unsigned* seq_dev = (unsigned*)(ws + w.counter) + 2;
-  AF_HIP(af::launch_fill_u32(ws + w.counter, 0u, 3, st));
+  AF_HIP(clear_counters(w, ws, st));
   *(volatile unsigned*)seq_word(p, false) = 0u;   // no update of this plan is in flight
   unsigned n_updates = 0;
 

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 
 from autoregressive_normalizing_flow_amd import synth  # noqa: E402
 from oracle import af_oracle as O  # noqa: E402
-from parity_util import TOL_BF16, rel_l2, say, to_dev, to_np  # noqa: E402
+from parity_util import TOL_BF16, problem, rel_l2, say, to_dev, to_np  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 PREFIX = 256   # tokens of a block compared element by element
@@ -48,6 +48,32 @@ def test_bf16_long_sequence_multichunk_attention(B):
     xg, itg = plan.inverse_jacobi(to_dev(z), 550, 1e-3)
     xo, _ = O.inverse_jacobi_block(p64, z, 4, 550, 1e-3, forced_iters=list(itg[0]))
     print("iters", itg.tolist(), "x rel_l2", rel_l2(to_np(xg), xo))
+    assert rel_l2(to_np(xg), xo) < TOL_BF16
+
+
+@pytest.mark.parametrize("H", [4, 2], ids=["dh64", "dh128"])
+def test_bf16_long_prefix_many_chunks(B, H):
+    """A 2600-token prefix and a 200-token block, one or two samples' worth of
+    heads: every query tile's keys span six 512-key chunks, so the merge runs
+    over more than one group of slots (in the prefill as well as in the
+    Jacobi updates), checked against the oracle."""
+    say("bf16 long prefix, many chunks", H)
+    P, F = 2600, 200
+    cfg, params, p64 = problem(C=48, d=256, H=H, layers=2, max_len=P + F, dtype="bf16",
+                               seed=60 + H)
+    plan = B.AFPlan(cfg, params)
+    xp = synth.normal((1, P, 48), 61)
+    z = synth.normal((1, F, 48), 62)
+    plan.prefill(to_dev(xp), rows=F)
+    xg, itg = plan.inverse_jacobi(to_dev(z), F, 1e-3, prefix_len=P, x_last=to_dev(xp[:, -1]))
+    cache, x_last = O.prefill(p64[0], xp, H)
+    x_t, it_t = O.inverse_jacobi_block(p64[0], z, H, F, 1e-3, pos0=P, cache=cache,
+                                       x_last=x_last)
+    xo = x_t
+    if not np.array_equal(it_t, itg[0]):
+        xo, _ = O.inverse_jacobi_block(p64[0], z, H, F, 1e-3, pos0=P, cache=cache,
+                                       x_last=x_last, forced_iters=list(itg[0]))
+    print("iters gpu", itg.tolist(), "oracle", it_t.tolist(), "x rel_l2", rel_l2(to_np(xg), xo))
     assert rel_l2(to_np(xg), xo) < TOL_BF16
 
 
