@@ -15,17 +15,19 @@
 namespace af {
 
 // ---------------------------------------------------------------------------
-// shift + embed.  Block: 256 output columns x 16 rows.  The 16 shifted input
-// rows are staged in LDS, zero-padded to CP channels (broadcast reads); each
-// thread keeps its row of W_in (column of W_in^T) in registers.  Every global
-// load (staged inputs, W row, position values) is issued up front without
-// branches, so the kernel waits for memory once; the rows are then computed
-// with the next row's LDS operands in flight.
-// CP = C rounded up within {16, 32, 48, 64}; C % 4 == 0.  Wider C goes
-// through embed_generic_kernel.
+// shift + embed on the fp32 matrix cores.  Per 16-feature x 16-token tile,
+// D = W_in . inp^T with v_mfma_f32_16x16x4f32: lane (i = l % 16, g = l / 16)
+// feeds W_in row (feature) i and the shifted input of token i at the same k
+// slot g, and receives features 4g..4g+3 of token i, so h is stored as float4s.
+// The k order is permuted the same way in both operands (slot g of step
+// 4t + e is channel 4g + 16t + e), so every lane loads whole float4s of W_in
+// and of its token's input.  Block: 4 waves x 64 features, 16 tokens; all
+// loads are issued before the first MFMA.
+// CP = C rounded up within {16, 32, 48, 64}; C % 4 == 0, d % 64 == 0.  Other
+// shapes go through embed_generic_kernel.
 // ---------------------------------------------------------------------------
-constexpr int EMB_ROWS = 16;
-constexpr int EMB_COLS = 256;
+constexpr int EMB_ROWS = 16;    // tokens per block
+constexpr int EMB_COLS = 256;   // features per block (64 per wave)
 
 // Address and validity of shifted input element (m, c): token m's input is
 // the previous token (in processing order) of its sample, x_last (or zero)
@@ -44,83 +46,67 @@ __device__ __forceinline__ const float* shifted_src(const float* __restrict__ x,
 }
 
 template <int CP>
-__device__ __forceinline__ void emb_row(float4 (&v)[CP / 4], const float (*s_in)[CP], int r) {
-#pragma unroll
-  for (int q = 0; q < CP / 4; ++q) v[q] = *(const float4*)(&s_in[r][4 * q]);
-}
-
-template <int CP>
-__device__ __forceinline__ float emb_dot(const float4 (&v)[CP / 4], const float (&w)[CP]) {
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-  for (int q = 0; q < CP / 4; ++q) {
-    a0 = fmaf(v[q].x, w[4 * q], a0);
-    a1 = fmaf(v[q].y, w[4 * q + 1], a1);
-    a2 = fmaf(v[q].z, w[4 * q + 2], a2);
-    a3 = fmaf(v[q].w, w[4 * q + 3], a3);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-template <int CP>
 __global__ __launch_bounds__(256) void embed_kernel(
     const float* __restrict__ x, const float* __restrict__ x_last,
     const float* __restrict__ w_in, const float* __restrict__ b_in,
     const float* __restrict__ pos, float* __restrict__ h, int N, int R, int C,
     int d, int L, int s, int dir, int pos_base) {
-  constexpr int NF = (EMB_ROWS * CP + 255) / 256;   // staged inputs per thread
-  __shared__ __attribute__((aligned(16))) float s_in[EMB_ROWS][CP];
-  __shared__ float s_pos[EMB_ROWS][EMB_COLS];
-  const int tid = threadIdx.x;
-  const int j0 = blockIdx.x * EMB_COLS;
-  const int m0 = blockIdx.y * EMB_ROWS;
+  constexpr int T = CP / 16;   // float4s per lane and operand row (4 k-steps each)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int f0 = blockIdx.x * EMB_COLS + wave * 64;   // first feature of the wave
+  if (f0 >= d) return;                                // d % 64 == 0: whole waves
   const int M = N * R;
-  const int j = min(j0 + tid, d - 1);
+  const int m = blockIdx.y * EMB_ROWS + i;            // this lane's token
 
-  float xin[NF];
-  bool xok[NF];
+  // B operand: token m's shifted input, channels 4g + 16t .. +3 (zero past C
+  // and for an invalid token)
+  bool ok;
+  const float* src = shifted_src(x, x_last, m, 0, M, R, C, L, s, dir, ok);
+  float4 xb[T];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int e = min(tid + f * 256, EMB_ROWS * CP - 1);
-    const int r = e / CP, c = e - r * CP;
-    xin[f] = *shifted_src(x, x_last, m0 + r, c, M, R, C, L, s, dir, xok[f]);
+  for (int t = 0; t < T; ++t) {
+    const int c = 4 * g + 16 * t;
+    const float4 v = *(const float4*)(src + min(c, C - 4));   // in bounds
+    const bool use = ok && c < C;
+    xb[t] = use ? v : float4{0.f, 0.f, 0.f, 0.f};
   }
-  const float* wrow = w_in + (size_t)j * C;
-  float w[CP];
+  // A operand: W_in rows f0 + 16 ft + i, the same channels (zero past C)
+  float4 wa[4][T];
 #pragma unroll
-  for (int q = 0; q < CP / 4; ++q) {
-    const float4 v = *(const float4*)(wrow + min(4 * q, C - 4));   // in bounds
-    const float keep = (4 * q < C) ? 1.f : 0.f;                      // masked
-    w[4 * q] = v.x * keep;
-    w[4 * q + 1] = v.y * keep;
-    w[4 * q + 2] = v.z * keep;
-    w[4 * q + 3] = v.w * keep;
+  for (int ft = 0; ft < 4; ++ft) {
+    const float* wr = w_in + (size_t)(f0 + 16 * ft + i) * C;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int c = 4 * g + 16 * t;
+      const float4 v = *(const float4*)(wr + min(c, C - 4));
+      wa[ft][t] = c < C ? v : float4{0.f, 0.f, 0.f, 0.f};
+    }
   }
-  float pv[EMB_ROWS];
+  // bias and position rows of the outputs this lane holds: token m,
+  // features f0 + 16 ft + 4g .. +3
+  const float* prow = pos + (size_t)(pos_base + min(m, M - 1) % R) * d;
+  float4 add[4];
 #pragma unroll
-  for (int r = 0; r < EMB_ROWS; ++r)
-    pv[r] = pos[(size_t)(pos_base + min(m0 + r, M - 1) % R) * d + j];
-  const float bj = b_in[j];
+  for (int ft = 0; ft < 4; ++ft) {
+    const int f = f0 + 16 * ft + 4 * g;
+    const float4 bb = *(const float4*)(b_in + f), pp = *(const float4*)(prow + f);
+    add[ft] = float4{bb.x + pp.x, bb.y + pp.y, bb.z + pp.z, bb.w + pp.w};
+  }
 
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int e = tid + f * 256;
-    if (e < EMB_ROWS * CP) (&s_in[0][0])[e] = xok[f] ? xin[f] : 0.f;
-  }
+  for (int ft = 0; ft < 4; ++ft) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < EMB_ROWS; ++r) s_pos[r][tid] = pv[r];
-  __syncthreads();
-  if (j0 + tid >= d) return;
-
-  float4 va[CP / 4], vb[CP / 4];
-  emb_row<CP>(va, s_in, 0);
-#pragma unroll 1
-  for (int r = 0; r < EMB_ROWS; r += 2) {
-    emb_row<CP>(vb, s_in, r + 1);
-    const int m = m0 + r;
-    if (m < M) h[(size_t)m * d + j] = emb_dot<CP>(va, w) + bj + s_pos[r][tid];
-    if (r + 2 < EMB_ROWS) emb_row<CP>(va, s_in, r + 2);
-    if (m + 1 < M) h[(size_t)(m + 1) * d + j] = emb_dot<CP>(vb, w) + bj + s_pos[r + 1][tid];
+    for (int t = 0; t < T; ++t) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[ft][t].x, xb[t].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[ft][t].y, xb[t].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[ft][t].z, xb[t].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[ft][t].w, xb[t].w, acc, 0, 0, 0);
+    }
+    if (m < M)
+      *(float4*)(h + (size_t)m * d + f0 + 16 * ft + 4 * g) =
+          float4{acc[0] + add[ft].x, acc[1] + add[ft].y, acc[2] + add[ft].z, acc[3] + add[ft].w};
   }
 }
 
@@ -159,10 +145,11 @@ hipError_t launch_embed(const float* x, const float* x_last, const float* w_in,
 #define AF_EMB(CP)                                                                    \
   hipLaunchKernelGGL(embed_kernel<CP>, grid, dim3(256), 0, st, x, x_last, w_in, b_in, \
                      pos, h, N, R, C, d, L, s, dir, pos_base)
-  if (C % 4 == 0 && C <= 16) AF_EMB(16);
-  else if (C % 4 == 0 && C <= 32) AF_EMB(32);
-  else if (C % 4 == 0 && C <= 48) AF_EMB(48);
-  else if (C % 4 == 0 && C <= 64) AF_EMB(64);
+  const bool mfma = C % 4 == 0 && d % 64 == 0;
+  if (mfma && C <= 16) AF_EMB(16);
+  else if (mfma && C <= 32) AF_EMB(32);
+  else if (mfma && C <= 48) AF_EMB(48);
+  else if (mfma && C <= 64) AF_EMB(64);
   else {
     const size_t total = (size_t)N * R * d;
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
@@ -214,10 +201,81 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Residual add + LayerNorm, fused: one wave per row.
+//   h[m] += bias + sum_s slab[s][m]          (split-K planes added in order)
+//   out[m] = LayerNorm(h[m]) * g + b          (bf16, optional lo half; or fp32)
+// It finishes the O-projection / MLP-down GEMMs and produces the next
+// LayerNorm's output in the same pass over the row.
+// ---------------------------------------------------------------------------
+template <class OutT>
+__device__ __forceinline__ void store4(OutT* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = float4{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4*)p = v;
+}
+
+// LayerNorm for d % 256 == 0: one wave per row, V4 = d / 256 float4s per lane;
+// the row and the gain / shift vectors are loaded before the first use.
+template <int V4, class OutT>
+__global__ __launch_bounds__(256) void ln4_kernel(
+    const float* __restrict__ h, const float* __restrict__ g, const float* __restrict__ b,
+    OutT* __restrict__ out, int M) {
+  constexpr int D = V4 * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* hr = h + (size_t)row * D;
+  float4 v[V4], gg[V4], be[V4];
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    v[i] = *(const float4*)(hr + j);
+    gg[i] = *(const float4*)(g + j);
+    be[i] = *(const float4*)(b + j);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = wave_sum(sum) * (1.0f / D);
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+    sq += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+  }
+  const float rstd = rsqrtf(wave_sum(sq) * (1.0f / D) + 1e-5f);
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    store4<OutT>(out + (size_t)row * D + j, (v[i].x - mean) * rstd * gg[i].x + be[i].x,
+                 (v[i].y - mean) * rstd * gg[i].y + be[i].y,
+                 (v[i].z - mean) * rstd * gg[i].z + be[i].z,
+                 (v[i].w - mean) * rstd * gg[i].w + be[i].w);
+  }
+}
+
 template <class OutT>
 static hipError_t ln_dispatch(const float* h, const float* g, const float* b,
                               OutT* out, OutT* out_lo, int M, int d, hipStream_t st) {
   dim3 grid((M + 3) / 4), blk(256);
+  const bool lo = out_lo != nullptr;
+  if (d % 256 == 0 && !lo) {
+    switch (d / 256) {
+      case 1: hipLaunchKernelGGL((ln4_kernel<1, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+      case 2: hipLaunchKernelGGL((ln4_kernel<2, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+      case 4: hipLaunchKernelGGL((ln4_kernel<4, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+      case 8: hipLaunchKernelGGL((ln4_kernel<8, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+      case 16: hipLaunchKernelGGL((ln4_kernel<16, OutT>), grid, blk, 0, st, h, g, b, out, M); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (d / AF_WAVE) {
     case 1: hipLaunchKernelGGL((layernorm_kernel<1, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
     case 2: hipLaunchKernelGGL((layernorm_kernel<2, OutT>), grid, blk, 0, st, h, g, b, out, out_lo, M); break;
@@ -236,25 +294,6 @@ hipError_t launch_layernorm(const float* h, const float* g, const float* b,
                             void* out_lo) {
   if (out_bf16) return ln_dispatch(h, g, b, (bf16*)out, (bf16*)out_lo, M, d, st);
   return ln_dispatch(h, g, b, (float*)out, (float*)nullptr, M, d, st);
-}
-
-// ---------------------------------------------------------------------------
-// Residual add + LayerNorm, fused: one wave per row.
-//   h[m] += bias + sum_s slab[s][m]          (split-K planes added in order)
-//   out[m] = LayerNorm(h[m]) * g + b          (bf16, optional lo half; or fp32)
-// It finishes the O-projection / MLP-down GEMMs and produces the next
-// LayerNorm's output in the same pass over the row.
-// ---------------------------------------------------------------------------
-template <class OutT>
-__device__ __forceinline__ void store4(OutT* p, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
-  *(float4*)p = float4{a, b, c, d};
-}
-template <>
-__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *(bf16x4*)p = v;
 }
 
 // One wave per row, V4 = d / 256 float4 per lane, S split planes, LO: also

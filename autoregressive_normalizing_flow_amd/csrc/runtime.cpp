@@ -45,6 +45,13 @@ af_status fail(af_status s, const std::string& msg) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The kernels read weights and token rows as 16-byte vectors.
+bool misaligned(const void* q) { return q && ((uintptr_t)q & 15) != 0; }
+template <class... P>
+bool any_misaligned(const P*... q) {
+  return (misaligned(q) || ...);
+}
+
 struct LayerW {
   const float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
   const void *w_qkv, *w_o, *w_1, *w_2;
@@ -212,8 +219,9 @@ struct Pass {
   bool kv_only;         // stop after the last layer's K/V (cache refresh)
   bool precise;         // bf16 path: carry activations as bf16 pairs (hi + lo)
   int hskip = 0;        // head and affine skip the first hskip rows of each sample
-  // PASS_ALL: the whole pass; PASS_PREFIX: shift + embed, first LayerNorm and
-  // layer 0's QKV only; PASS_REST: the remainder after a PASS_PREFIX
+  // PASS_ALL: the whole pass; PASS_PREFIX: shift + embed, first LayerNorm,
+  // layer 0's QKV and attention only; PASS_REST: the remainder after a
+  // PASS_PREFIX
   int part = 0;
 };
 constexpr int PASS_ALL = 0, PASS_PREFIX = 1, PASS_REST = 2;
@@ -259,12 +267,13 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       if (l > 0 || pre)
         LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
-      if (!post) return AF_OK;
       af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
-      LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
-                                          (unsigned*)(ws + w.tickets), ps.N, ps.R,
-                                          c.n_heads, p->dh, d, p->Lcap, pos_base,
-                                          st, sp ? &asp : nullptr));
+      if (l > 0 || pre)
+        LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
+                                            (unsigned*)(ws + w.tickets), ps.N, ps.R,
+                                            c.n_heads, p->dh, d, p->Lcap, pos_base,
+                                            st, sp ? &asp : nullptr));
+      if (!post) return AF_OK;
       int S = 1;
       LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st));
       LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_o, h, lw.ln2_g, lw.ln2_b, a, true, a_lo,
@@ -294,9 +303,10 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
                                           dst, st));
       }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
+      if (l > 0 || pre)
+        LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, nullptr, ps.N,
+                                            ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base, st));
       if (!post) return AF_OK;
-      LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, nullptr, ps.N, ps.R,
-                                          c.n_heads, p->dh, d, p->Lcap, pos_base, st));
       LAUNCH(K_O, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
                                         nullptr, st));
       LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, false, M, d, st));
@@ -508,6 +518,10 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
       delete p;
       return fail(AF_ERR_ARG, "NULL weight pointer in block " + std::to_string(t));
     }
+    if (any_misaligned(b.w_in, b.b_in, b.pos, b.ln_f_g, b.ln_f_b, b.w_head, b.b_head)) {
+      delete p;
+      return fail(AF_ERR_ARG, "weight pointer not 16-byte aligned in block " + std::to_string(t));
+    }
     for (int l = 0; l < c.n_layers; ++l) {
       LayerW lw{bw.ln1_g[l], bw.ln1_b[l], bw.b_qkv[l], bw.b_o[l], bw.ln2_g[l],
                 bw.ln2_b[l], bw.b_1[l], bw.b_2[l], bw.w_qkv[l], bw.w_o[l],
@@ -516,6 +530,12 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
           !lw.b_1 || !lw.b_2 || !lw.w_qkv || !lw.w_o || !lw.w_1 || !lw.w_2) {
         delete p;
         return fail(AF_ERR_ARG, "NULL layer weight pointer in block " +
+                                    std::to_string(t) + " layer " + std::to_string(l));
+      }
+      if (any_misaligned(lw.ln1_g, lw.ln1_b, lw.b_qkv, lw.b_o, lw.ln2_g, lw.ln2_b, lw.b_1,
+                         lw.b_2, lw.w_qkv, lw.w_o, lw.w_1, lw.w_2)) {
+        delete p;
+        return fail(AF_ERR_ARG, "layer weight pointer not 16-byte aligned in block " +
                                     std::to_string(t) + " layer " + std::to_string(l));
       }
       b.layers.push_back(lw);
@@ -548,6 +568,7 @@ size_t af_cache_bytes(const af_plan* p, int batch) {
 af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
                      int L, void* ws_, size_t ws_bytes, void* stream) {
   if (!p || !x || !z || !logdet) return fail(AF_ERR_ARG, "NULL argument");
+  if (any_misaligned(x, z)) return fail(AF_ERR_ARG, "x and z must be 16-byte aligned");
   if (N < 1 || L < 1 || L > p->cfg.max_len) return fail(AF_ERR_ARG, "need N >= 1 and 1 <= L <= max_len");
   if (x == z) return fail(AF_ERR_ARG, "x and z may not alias");
   WsLayout w;
@@ -578,6 +599,7 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
 af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
                      size_t ws_bytes, void* stream) {
   if (!p || !x_prefix) return fail(AF_ERR_ARG, "NULL argument");
+  if (misaligned(x_prefix)) return fail(AF_ERR_ARG, "x_prefix must be 16-byte aligned");
   if (p->T != 1) return fail(AF_ERR_UNSUPPORTED, "af_prefill needs a single-block plan");
   if (N < 1 || P < 1 || P > p->cfg.max_len) return fail(AF_ERR_ARG, "need N >= 1 and 1 <= P <= max_len");
   WsLayout w;
@@ -591,6 +613,7 @@ af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
 af_status af_refresh_kv(af_plan* p, const float* x, int N, int L, int prefix_len,
                         const float* x_last, void* ws_, size_t ws_bytes, void* stream) {
   if (!p || !x) return fail(AF_ERR_ARG, "NULL argument");
+  if (any_misaligned(x, x_last)) return fail(AF_ERR_ARG, "x and x_last must be 16-byte aligned");
   if (p->T != 1) return fail(AF_ERR_UNSUPPORTED, "af_refresh_kv needs a single-block plan");
   if (N < 1 || L < 1 || prefix_len < 0 || prefix_len + L > p->cfg.max_len)
     return fail(AF_ERR_ARG, "need N, L >= 1, prefix_len >= 0 and prefix_len + L <= max_len");
@@ -609,6 +632,8 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                             const float* x_last, float* x, int32_t* iters,
                             void* ws_, size_t ws_bytes, void* stream) {
   if (!p || !z || !x || !iters) return fail(AF_ERR_ARG, "NULL argument");
+  if (any_misaligned(z, x, x_init, x_last))
+    return fail(AF_ERR_ARG, "z, x, x_init and x_last must be 16-byte aligned");
   if (N < 1 || L < 1 || B < 1) return fail(AF_ERR_ARG, "need N, L, B >= 1");
   if (std::isnan(tau)) return fail(AF_ERR_ARG, "tau is NaN");
   if (init != AF_INIT_ZERO && init != AF_INIT_GIVEN && init != AF_INIT_PREV_FRAME)
@@ -716,10 +741,10 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         if (!(tau > 0.f && k < kmax)) continue;
         // While the host waits for the residual, the device runs the next
         // update's first kernels (shift + embed, first LayerNorm, layer 0's
-        // QKV).  They write only scratch and this block's layer-0 K/V rows,
-        // which the next update would write identically and which the
-        // refresh after an early stop recomputes, so a stop leaves the result
-        // unchanged.  (Graph replay keeps whole updates.)
+        // QKV and attention).  They write only scratch and this block's
+        // layer-0 K/V rows, which the next update would write identically and
+        // which the refresh after an early stop recomputes, so a stop leaves
+        // the result unchanged.  (Graph replay keeps whole updates.)
         if (!g) {
           Pass pp = ps;
           pp.part = PASS_PREFIX;

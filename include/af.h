@@ -74,7 +74,10 @@ typedef struct {
   af_dtype dtype;
 } af_block_cfg;
 
-/* One block's parameters: borrowed device pointers that must outlive the plan.
+/* One block's parameters: borrowed device pointers that must outlive the plan
+ * and be 16-byte aligned (the kernels read them as 16-byte vectors;
+ * af_plan_create returns AF_ERR_ARG otherwise).  Token buffers passed to the
+ * calls below (x, z, x_prefix, x_init, x_last) must be 16-byte aligned too.
  * Matrices are row-major [out, in] (y = x W^T + b).  The four per-layer
  * matrices have the element type of cfg.dtype (fp32 or bf16 bit patterns);
  * everything else is fp32.  The per-layer fields are HOST arrays of

@@ -80,6 +80,22 @@ def test_plan_create_validation(lib, kw, expect):
         assert lib.af_last_error()
 
 
+@pytest.mark.parametrize("field", ["pos", "b_head", "ln1_g", "w_2"])
+def test_plan_create_rejects_misaligned_weights(lib, field):
+    ws, keep = fake_weights(2)
+    odd = ctypes.c_void_p(_FAKE.ctypes.data + 4)
+    if field in ("pos", "b_head"):
+        setattr(ws[0], field, odd)
+    else:
+        arr = (ctypes.c_void_p * 2)(ctypes.c_void_p(_FAKE.ctypes.data), odd)
+        keep.append(arr)
+        setattr(ws[0], field, ctypes.cast(arr, B._PP))
+    cfg = B.af_block_cfg(16, 64, 2, 2, 64, B.AF_F32)
+    h = ctypes.c_void_p()
+    assert lib.af_plan_create(ctypes.byref(cfg), 1, ws, ctypes.byref(h)) == B.AF_ERR_ARG
+    assert b"16-byte" in lib.af_last_error()
+
+
 def test_workspace_bytes_monotone_and_cache_first(lib):
     st, h = make_plan(lib, C=48, d=1024, H=16, layers=8, max_len=1560, dtype=B.AF_BF16)
     assert st == B.AF_OK
@@ -103,19 +119,19 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     # NULL inputs
     assert lib.af_forward(h, None, buf, buf, 1, 64, buf, big, None) == B.AF_ERR_ARG
     # L beyond max_len
-    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 65,
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 65,
                           buf, 1 << 40, None) == B.AF_ERR_ARG
     # workspace too small (checked before any launch)
     aligned = ctypes.c_void_p(1 << 20)
-    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 64,
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
                           aligned, 16, None) == B.AF_ERR_WORKSPACE
     # misaligned workspace
-    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 4), buf, 1, 64,
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
                           ctypes.c_void_p((1 << 20) + 4), big, None) == B.AF_ERR_ARG
 
     def inv(**kw):
         a = dict(z=buf, N=1, L=64, B=16, tau=1e-3, max_iters=0, init=0, x_init=None,
-                 F=0, P=0, x_last=None, x=ctypes.c_void_p(_FAKE.ctypes.data + 8),
+                 F=0, P=0, x_last=None, x=ctypes.c_void_p(_FAKE.ctypes.data + 128),
                  ws=aligned, wsb=big)
         a.update(kw)
         return lib.af_inverse_jacobi(h, a["z"], a["N"], a["L"], a["B"],
@@ -132,6 +148,12 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     assert inv(P=10, x_last=buf) == B.AF_ERR_ARG       # P + L > max_len
     assert inv(x=buf) == B.AF_ERR_ARG                  # x aliases z
     assert inv(wsb=8) == B.AF_ERR_WORKSPACE
+    # token buffers are read as 16-byte vectors
+    odd = ctypes.c_void_p(_FAKE.ctypes.data + 132)
+    assert inv(x=odd) == B.AF_ERR_ARG
+    assert inv(init=1, x_init=odd) == B.AF_ERR_ARG
+    assert lib.af_forward(h, odd, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
+                          aligned, big, None) == B.AF_ERR_ARG
     assert lib.af_prefill(h, None, 1, 8, aligned, big, None) == B.AF_ERR_ARG
     lib.af_plan_destroy(h)
 
@@ -142,7 +164,7 @@ def test_stack_restrictions(lib):
     buf = ctypes.c_void_p(_FAKE.ctypes.data)
     iters = (ctypes.c_int32 * 16)()
     big = lib.af_workspace_bytes(h, 1, 16)
-    x = ctypes.c_void_p(_FAKE.ctypes.data + 8)
+    x = ctypes.c_void_p(_FAKE.ctypes.data + 128)
     assert lib.af_inverse_jacobi(h, buf, 1, 64, 16, ctypes.c_float(1e-3), 0, 2, None, 16,
                                  0, None, x, iters, ctypes.c_void_p(1 << 20), big,
                                  None) == B.AF_ERR_UNSUPPORTED
