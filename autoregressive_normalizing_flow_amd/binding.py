@@ -100,6 +100,8 @@ def load_library() -> ctypes.CDLL:
     L.af_plan_set_fused_refresh.restype = st
     L.af_plan_set_graphs.argtypes = [_P, i]
     L.af_plan_set_graphs.restype = st
+    L.af_plan_set_row_split.argtypes = [_P, i]
+    L.af_plan_set_row_split.restype = st
     L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
                                       ctypes.POINTER(ctypes.c_longlong)]
     L.af_plan_graph_stats.restype = st
@@ -282,6 +284,10 @@ class AFPlan:
         self._fused_refresh = bool(enable)
 
     # graph replay of the Jacobi update ------------------------------------
+    def set_row_split(self, enable: bool):
+        _check(self.L.af_plan_set_row_split(self.handle, int(bool(enable))),
+               "af_plan_set_row_split")
+
     def set_graphs(self, enable: bool):
         _check(self.L.af_plan_set_graphs(self.handle, int(bool(enable))), "af_plan_set_graphs")
 

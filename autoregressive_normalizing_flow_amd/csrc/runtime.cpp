@@ -120,6 +120,10 @@ struct af_plan {
   std::vector<GraphEntry> gcache;
   uint64_t gclock = 0;
   long long g_captures = 0, g_replays = 0;
+  // row split of a Jacobi update over two streams (see af_inverse_jacobi)
+  bool row_split = true;
+  hipStream_t split_stream = nullptr;
+  std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
 };
 
 namespace {
@@ -187,6 +191,39 @@ WsLayout layout(const af_plan* p, int N, int rows) {
   return w;
 }
 
+// Row split of a Jacobi update over two streams: rows [0, ra) of the block
+// (half A) and [ra, R) (half B) run as two passes side by side, so that each
+// fills the GPU where the other's launches leave it idle.  The halves'
+// kernels are smaller and less efficient, which the overlap repays only when
+// attention over a long prefix dominates: the split is used on the bf16 path
+// for long blocks of a small batch (split_possible) with at least 8 R keys
+// before the block (measured on 1560-token frames: 7% slower after 1 frame of
+// prefix, even after 4, 4-13% faster from 8 frames on).  Returns ra, or 0.
+constexpr int kSplitPrefixBlocks = 8;
+bool split_possible(const af_plan* p, int N, int R) {
+  return p->bf && R >= 1024 && (long)N * R <= 4096;
+}
+int split_rows_a(const af_plan* p, int N, int R, int keys_before) {
+  if (!split_possible(p, N, R) || keys_before < kSplitPrefixBlocks * R) return 0;
+  return (R / 2) / 128 * 128;
+}
+
+// Scratch of half B behind the whole-block layout w (the KV cache region is
+// shared), for halves of at most rows / 2 + 128 rows.
+WsLayout layout_b(const af_plan* p, int N, int rows, const WsLayout& w) {
+  WsLayout b = layout(p, N, rows / 2 + 128);
+  // the per-pass scratch runs from h up to xtmp; the stack's token buffer and
+  // the higher-precision forward's lo halves are not needed by half B
+  const size_t shift = w.total - b.h;
+  size_t* f[] = {&b.h, &b.a, &b.q, &b.att, &b.u, &b.hf, &b.head, &b.partials, &b.res,
+                 &b.counter, &b.tickets, &b.slab, &b.attn_part};
+  for (size_t* x : f) *x += shift;
+  b.total = b.xtmp + shift;
+  b.xtmp = w.xtmp;
+  b.cache_lo = b.a_lo = b.q_lo = b.att_lo = b.u_lo = 0;
+  return b;
+}
+
 // Launch helper with optional per-class event timing (direct launches only:
 // nothing is captured into a graph while a class is profiled).
 struct Launch {
@@ -226,11 +263,31 @@ struct Pass {
 };
 constexpr int PASS_ALL = 0, PASS_PREFIX = 1, PASS_REST = 2;
 
+// Cross-stream ordering of a pass that runs beside another one (row split):
+// events waited for or recorded on the pass's stream around its embed, its
+// QKV GEMMs, its attentions and its affine update (NULL: none).
+struct XSync {
+  hipEvent_t wait_embed = nullptr;
+  hipEvent_t rec_embed = nullptr;
+  hipEvent_t wait_affine = nullptr;
+  const hipEvent_t* wait_qkv = nullptr;    // [n_layers]
+  const hipEvent_t* rec_qkv = nullptr;     // [n_layers]
+  const hipEvent_t* wait_attn = nullptr;   // [n_layers]
+  const hipEvent_t* rec_attn = nullptr;    // [n_layers]
+  hipEvent_t rec_affine = nullptr;
+};
+
 // One pass of the network over chunk rows [s, s+R) of every sample:
 // shift+embed, n_layers pre-LN layers (K/V into the cache), final LN + head.
 af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
                   const WsLayout& w, hipStream_t st, const af::AffineArgs* aa = nullptr,
-                  int mode = 0) {
+                  int mode = 0, const XSync* xs = nullptr) {
+  auto wait_ev = [&](const hipEvent_t* e, int l) -> hipError_t {
+    return (e && e[l]) ? hipStreamWaitEvent(st, e[l], 0) : hipSuccess;
+  };
+  auto rec_ev = [&](const hipEvent_t* e, int l) -> hipError_t {
+    return (e && e[l]) ? hipEventRecord(e[l], st) : hipSuccess;
+  };
   const af_block_cfg& c = p->cfg;
   const int M = ps.N * ps.R, d = c.d;
   float* h = (float*)(ws + w.h);
@@ -246,10 +303,12 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   float* slab = (float*)(ws + w.slab);
   const int pos_base = ps.P + ps.s;
   const bool pre = ps.part != PASS_REST, post = ps.part != PASS_PREFIX;
+  if (pre && xs && xs->wait_embed) AF_HIP(hipStreamWaitEvent(st, xs->wait_embed, 0));
   if (pre)
     LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
                                      ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
                                      pos_base, st));
+  if (pre && xs && xs->rec_embed) AF_HIP(hipEventRecord(xs->rec_embed, st));
   float* hf = (float*)(ws + w.hf);
   if (p->bf) {
     // bf16 path: the O-projection and MLP-down GEMMs write fp32 partial planes
@@ -264,15 +323,21 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       char* kc_lo = sp ? ws + w.cache_lo + (size_t)(2 * l) * w.cache_layer : nullptr;
       char* vt_lo = sp ? ws + w.cache_lo + (size_t)(2 * l + 1) * w.cache_layer : nullptr;
       af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
-      if (l > 0 || pre)
+      if (l > 0 || pre) {
+        if (xs) AF_HIP(wait_ev(xs->wait_qkv, l));
         LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+        if (xs) AF_HIP(rec_ev(xs->rec_qkv, l));
+      }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
       af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
-      if (l > 0 || pre)
+      if (l > 0 || pre) {
+        if (xs) AF_HIP(wait_ev(xs->wait_attn, l));
         LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
                                             (unsigned*)(ws + w.tickets), ps.N, ps.R,
                                             c.n_heads, p->dh, d, p->Lcap, pos_base,
                                             st, sp ? &asp : nullptr));
+        if (xs) AF_HIP(rec_ev(xs->rec_attn, l));
+      }
       if (!post) return AF_OK;
       int S = 1;
       LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st));
@@ -333,7 +398,9 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
     LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
                                               fa.head_splits, st));
   }
+  if (xs && xs->wait_affine) AF_HIP(hipStreamWaitEvent(st, xs->wait_affine, 0));
   LAUNCH(K_AFFINE, af::launch_affine(mode, fa, st));
+  if (xs && xs->rec_affine) AF_HIP(hipEventRecord(xs->rec_affine, st));
   return AF_OK;
 }
 
@@ -380,14 +447,19 @@ unsigned* seq_word(const af_plan* p, bool dev) {
 // update's number to the sequence word.  Polling that word avoids a stream
 // synchronisation per update; the stream is queried now and then so that a
 // failed launch is reported instead of waited on.
-af_status wait_update(af_plan* p, unsigned want, hipStream_t st) {
+// With a row split, half B publishes to the next word (want2 updates) and
+// both words must have arrived.
+af_status wait_update(af_plan* p, unsigned want, hipStream_t st, hipStream_t st2 = nullptr,
+                      unsigned want2 = 0) {
   volatile unsigned* f = seq_word(p, false);
+  auto done = [&]() { return f[0] == want && (!st2 || f[1] == want2); };
   for (unsigned long it = 1;; ++it) {
-    if (*f == want) break;
+    if (done()) break;
     if ((it & 4095) == 0) {
-      const hipError_t q = hipStreamQuery(st);
+      hipError_t q = hipStreamQuery(st);
+      if (q == hipSuccess && st2) q = hipStreamQuery(st2);
       if (q == hipSuccess) {
-        if (*f == want) break;
+        if (done()) break;
         return fail(AF_ERR_HIP, "update finished without publishing its residual");
       }
       if (q != hipErrorNotReady)
@@ -550,6 +622,8 @@ void af_plan_destroy(af_plan* p) {
   if (!p) return;
   for (GraphEntry& e : p->gcache) destroy_entry(e);
   if (p->cap_stream) (void)hipStreamDestroy(p->cap_stream);
+  if (p->split_stream) (void)hipStreamDestroy(p->split_stream);
+  for (hipEvent_t e : p->split_ev) (void)hipEventDestroy(e);
   if (p->host_res) (void)hipHostFree(p->host_res);
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   delete p;
@@ -557,7 +631,10 @@ void af_plan_destroy(af_plan* p) {
 
 size_t af_workspace_bytes(const af_plan* p, int batch, int rows) {
   if (!p || batch < 1 || rows < 1) return 0;
-  return layout(p, batch, rows).total;
+  const WsLayout w = layout(p, batch, rows);
+  // room for the row split's second half when a block of `rows` rows uses it
+  if (split_possible(p, batch, rows)) return layout_b(p, batch, rows, w).total;
+  return w.total;
 }
 
 size_t af_cache_bytes(const af_plan* p, int batch) {
@@ -674,6 +751,38 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   char* ws = (char*)ws_;
   int device = 0;
   if (p->graphs) AF_HIP(hipGetDevice(&device));
+  // Row split (two streams, see split_rows_a): only with direct launches,
+  // without the fused refresh, and when the workspace has room for half B.
+  WsLayout wb{};
+  bool split_ok = p->row_split && !p->graphs && !fuse && split_possible(p, N, Bc);
+  if (split_ok) {
+    wb = layout_b(p, N, Bc, w);
+    split_ok = ws_bytes >= wb.total;
+  }
+  const int nl = p->cfg.n_layers;
+  if (split_ok) {
+    if (!p->split_stream)
+      AF_HIP(hipStreamCreateWithFlags(&p->split_stream, hipStreamNonBlocking));
+    if (p->split_ev.empty()) {
+      p->split_ev.resize(2 * nl + 4);
+      for (auto& e : p->split_ev) AF_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    }
+    if (af_status e = ensure_host_res(p, 2 * N)) return e;
+  }
+  hipStream_t sb = p->split_stream;
+  const hipEvent_t* ev_qkv = split_ok ? p->split_ev.data() : nullptr;        // A: QKV(l) done
+  const hipEvent_t* ev_att = split_ok ? p->split_ev.data() + nl : nullptr;   // B: attention(l) done
+  hipEvent_t ev_aff = split_ok ? p->split_ev[2 * nl] : nullptr;        // A: affine done
+  hipEvent_t ev_emb = split_ok ? p->split_ev[2 * nl + 1] : nullptr;    // B: embed done
+  hipEvent_t ev_fork = split_ok ? p->split_ev[2 * nl + 2] : nullptr;
+  hipEvent_t ev_join = split_ok ? p->split_ev[2 * nl + 3] : nullptr;
+  bool b_busy = false;   // half B has work enqueued since the last join
+  auto join_b = [&]() -> hipError_t {
+    if (!b_busy) return hipSuccess;
+    b_busy = false;
+    hipError_t e = hipEventRecord(ev_join, sb);
+    return e != hipSuccess ? e : hipStreamWaitEvent(st, ev_join, 0);
+  };
   float* xtmp = (float*)(ws + w.xtmp);
   float* res = (float*)(ws + w.res);
   // counter word of the affine kernel, the sticky non-finite tag after it,
@@ -681,8 +790,12 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   unsigned* bad = (unsigned*)(ws + w.counter) + 1;
   unsigned* seq_dev = (unsigned*)(ws + w.counter) + 2;
   AF_HIP(clear_counters(w, ws, st));
-  *(volatile unsigned*)seq_word(p, false) = 0u;   // no update of this plan is in flight
+  if (split_ok) AF_HIP(clear_counters(wb, ws, st));
+  volatile unsigned* seq_host_words = seq_word(p, false);
+  seq_host_words[0] = 0u;   // no update of this plan is in flight
+  seq_host_words[1] = 0u;
   unsigned n_updates = 0;
+  unsigned n_split = 0;   // updates that ran as a row split (half B's publications)
 
   const float* zin = z;
   for (int t = p->T - 1; t >= 0; --t) {
@@ -712,11 +825,63 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         if (!g && kmax >= 2)
           if (af_status e = graph_capture(p, key, p->blocks[t], ps, aa, ws, w, st, &g)) return e;
       }
+      // Row split: half A (rows [s, s + ra)) on st, half B on sb.  Every
+      // update is enqueued as A's prefix, B's prefix, A's rest, B's rest, so
+      // that each wait below finds the record it needs already enqueued: B's
+      // attention(l) waits for A's QKV(l) (its keys include A's rows); A's
+      // QKV(l) waits for B's attention(l) of the previous update (it rewrites
+      // K/V rows B still reads); B's embed waits for A's previous affine
+      // update (B's first row reads A's last token) and A's affine update
+      // waits for B's embed (it rewrites that token).  Each half publishes its
+      // own residual pair; the stop test adds them.
+      const int ra = split_ok ? split_rows_a(p, N, R, prefix_len + s) : 0;
+      const bool split = ra > 0;
+      Pass psa = ps, psb = ps;
+      af::AffineArgs aaa = aa, aab = aa;
+      XSync xa, xb;
+      if (split) {
+        psa.R = ra;
+        psb.s = s + ra;
+        psb.R = R - ra;
+        aaa.R = ra;
+        aab.R = R - ra;
+        aab.s = s + ra;
+        aab.partials = (float*)(ws + wb.partials);
+        aab.res = (float*)(ws + wb.res);
+        aab.counter = (unsigned*)(ws + wb.counter);
+        aab.res_host = p->host_res_dev + 2 * (size_t)N;
+        aab.seq_dev = (unsigned*)(ws + wb.counter) + 2;
+        aab.seq_host = seq_word(p, true) + 1;
+        xa.wait_qkv = ev_att;
+        xa.rec_qkv = ev_qkv;
+        xa.wait_affine = ev_emb;
+        xa.rec_affine = ev_aff;
+        xb.wait_embed = ev_aff;
+        xb.rec_embed = ev_emb;
+        xb.wait_attn = ev_qkv;
+        xb.rec_attn = ev_att;
+        // half B starts after this block's initial iterate and all earlier work
+        AF_HIP(hipEventRecord(ev_fork, st));
+        AF_HIP(hipStreamWaitEvent(sb, ev_fork, 0));
+        b_busy = true;
+      }
+      auto split_part = [&](int part) -> af_status {
+        Pass pa = psa, pb = psb;
+        pa.part = part;
+        pb.part = part;
+        if (af_status e = run_net(p, p->blocks[t], pa, ws, w, st, &aaa, 0, &xa)) return e;
+        return run_net(p, p->blocks[t], pb, ws, wb, sb, &aab, 0, &xb);
+      };
       int k = 0;
       bool nonfinite = false;
       bool prefixed = false;   // the next update's first kernels are already enqueued
       for (k = 1; k <= kmax; ++k) {
-        if (prefixed) {
+        if (split) {
+          if (!prefixed)
+            if (af_status e = split_part(PASS_PREFIX)) return e;
+          if (af_status e = split_part(PASS_REST)) return e;
+          prefixed = false;
+        } else if (prefixed) {
           Pass pr = ps;
           pr.part = PASS_REST;
           if (af_status e = jacobi_update(p, p->blocks[t], pr, aa, ws, w, st)) return e;
@@ -735,6 +900,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
           return e;
         }
         ++n_updates;
+        if (split) ++n_split;
         // the residual is read only for the stop test; at the cap (and in
         // forced-count mode) a non-finite residual is caught through the
         // sticky tag read once at the end
@@ -745,17 +911,24 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         // layer-0 K/V rows, which the next update would write identically and
         // which the refresh after an early stop recomputes, so a stop leaves
         // the result unchanged.  (Graph replay keeps whole updates.)
-        if (!g) {
+        if (split) {
+          if (af_status e = split_part(PASS_PREFIX)) return e;
+          prefixed = true;
+        } else if (!g) {
           Pass pp = ps;
           pp.part = PASS_PREFIX;
           if (af_status e = run_net(p, p->blocks[t], pp, ws, w, st)) return e;
           prefixed = true;
         }
-        if (af_status e = wait_update(p, n_updates, st)) return e;
+        if (af_status e = wait_update(p, n_updates, st, split ? sb : nullptr, n_split)) return e;
         const volatile float* hr = p->host_res;
         bool all_below = true;
         for (int n = 0; n < N; ++n) {
-          const float num = hr[2 * n], den = hr[2 * n + 1];
+          float num = hr[2 * n], den = hr[2 * n + 1];
+          if (split) {
+            num += hr[2 * (N + n)];
+            den += hr[2 * (N + n) + 1];
+          }
           if (!std::isfinite(num) || !std::isfinite(den)) nonfinite = true;
           const float r = den > 0.f ? num / den : (num == 0.f ? 0.f : INFINITY);
           if (!(r < tau)) all_below = false;
@@ -763,6 +936,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         if (nonfinite) break;
         if (tau > 0.f && all_below) break;
       }
+      AF_HIP(join_b());   // later work on st sees all of half B's writes
       if (nonfinite) {
         iters[t * nb + b] = k;
         return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +
@@ -783,6 +957,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     }
     zin = xo;
   }
+  AF_HIP(join_b());
   AF_HIP(hipMemcpyAsync(p->host_res, bad, sizeof(unsigned), hipMemcpyDeviceToHost, st));
   AF_HIP(hipStreamSynchronize(st));
   unsigned tag;
@@ -836,6 +1011,12 @@ af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
 af_status af_plan_set_fused_refresh(af_plan* p, int enable) {
   if (!p) return fail(AF_ERR_ARG, "NULL argument");
   p->fuse_refresh = enable != 0;
+  return AF_OK;
+}
+
+af_status af_plan_set_row_split(af_plan* p, int enable) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->row_split = enable != 0;
   return AF_OK;
 }
 

@@ -242,7 +242,8 @@ def schedule_sweep(torch, binding, synth, reps):
             "asymmetric_video21": asym_row}
 
 
-def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=False):
+def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=False,
+                   row_split=True):
     """End-to-end inverse of the deep o shallow flow over 21 frames (deep:
     the video21 block, shallow: the shallow_stack stack), three schedules:
     stages (the deep block over all frames in one call, then the shallow
@@ -258,6 +259,7 @@ def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=Fals
     for plan in (deep, shallow):
         plan.set_graphs(graphs)
         plan.set_fused_refresh(fused_refresh)
+        plan.set_row_split(row_split)
     flow = DeepShallowFlow(deep, shallow, F)
     z = dev(synth.normal((1, v.length, v.block.C), 1))
     nf = v.length // F
@@ -296,6 +298,8 @@ def main():
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-row-split", action="store_true",
+                    help="run every Jacobi update as one pass (no two-stream row split)")
     ap.add_argument("--fused-refresh", action="store_true",
                     help="recompute an early-stopped block's K/V in the next block's "
                          "first update instead of in a pass of its own")
@@ -332,7 +336,8 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     if args.pipeline:
         print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1),
-                                        args.graphs, args.fused_refresh)), flush=True)
+                                        args.graphs, args.fused_refresh,
+                                        not args.no_row_split)), flush=True)
         return
     if args.schedule_sweep:
         print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
@@ -342,6 +347,7 @@ def main():
     cfg, w = r.cfg, r.w
     r.plan.set_graphs(args.graphs)
     r.plan.set_fused_refresh(args.fused_refresh)
+    r.plan.set_row_split(not args.no_row_split)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -429,6 +435,7 @@ def main():
                            else {"fused_into": "gemm_head"}),
         "graphs": args.graphs,
         "fused_refresh": args.fused_refresh,
+        "row_split": not args.no_row_split,
         "kernel_ms_per_step": breakdown,
         "forward_ms": round(fwd_ms, 3),
     }

@@ -228,6 +228,24 @@ af_status af_plan_set_graphs(af_plan *p, int enable);
 af_status af_plan_set_fused_refresh(af_plan *p, int enable);
 af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *replays);
 
+/* Row split of a Jacobi update (STARFlow-V notes, 关键设计 3: the update is
+ * one parallel pass over the block's rows).  On the bf16 path, for blocks of
+ * R >= 1024 rows with N * R <= 4096 and at least 8 R cached keys before the
+ * block (prefix_len + block start >= 8 R: attention over the prefix then
+ * dominates the update), af_inverse_jacobi runs each update
+ * as two passes over the first and second half of the block's rows, on
+ * `stream` and on a second stream of the plan, ordered by events (the second
+ * half's attention waits for the first half's K/V of the same update).  The
+ * two passes overlap where one leaves the GPU idle; the stop test adds their
+ * residuals.  Results equal those of the single pass up to floating-point
+ * summation order.  Used only with direct launches (not with graphs or the
+ * fused refresh) and when ws_bytes >= af_workspace_bytes(p, N, min(B, L)),
+ * which includes the second half's scratch whenever the shape allows a split.
+ * The call returns with `stream` ordered after all of the second stream's
+ * work.  enable != 0 (the default) allows the split, 0 keeps one pass;
+ * AF_ERR_ARG if p is NULL. */
+af_status af_plan_set_row_split(af_plan *p, int enable);
+
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
  * The fused affine kernel on its own, over N samples of rows_per_sample
  * contiguous rows of C channels (token tensors [N, rows_per_sample, C]).

@@ -208,4 +208,24 @@ def test_graph_controls(lib):
     assert lib.af_plan_set_graphs(None, 1) == B.AF_ERR_ARG
     assert lib.af_plan_set_fused_refresh(h, 0) == B.AF_OK
     assert lib.af_plan_set_fused_refresh(None, 1) == B.AF_ERR_ARG
+    assert lib.af_plan_set_row_split(h, 0) == B.AF_OK
+    assert lib.af_plan_set_row_split(h, 1) == B.AF_OK
+    assert lib.af_plan_set_row_split(None, 1) == B.AF_ERR_ARG
+    lib.af_plan_destroy(h)
+
+
+def test_workspace_has_room_for_the_row_split(lib):
+    # blocks of 1024 to 4096 rows of one sample may be split over two
+    # streams: from 1024 rows the workspace holds a second half's scratch
+    # (tens of MB at d = 1024, against about 0.2 MB per extra row), and past
+    # N * R = 4096 it no longer does
+    st, h = make_plan(lib, C=48, d=1024, H=16, layers=8, max_len=4680, dtype=B.AF_BF16)
+    assert st == B.AF_OK
+    ws = lambda n, r: lib.af_workspace_bytes(h, n, r)
+    assert ws(1, 1024) - ws(1, 1023) > 20e6
+    assert ws(1, 4097) < ws(1, 4096)
+    assert ws(2, 2049) < ws(2, 2048)
+    st, h32 = make_plan(lib, C=16, d=64, H=2, layers=1, max_len=2048)   # fp32: never split
+    assert lib.af_workspace_bytes(h32, 1, 1024) - lib.af_workspace_bytes(h32, 1, 1023) < 1e6
+    lib.af_plan_destroy(h32)
     lib.af_plan_destroy(h)

@@ -82,6 +82,47 @@ def test_bf16_long_prefix_many_chunks(B, H):
     assert np.array_equal(itg2, itg) and torch.equal(xg2, xg)
 
 
+def test_row_split_matches_single_pass_and_oracle(B):
+    """Row split of the Jacobi update (two streams: a 1024-row block after an
+    8192-token prefix, so the split applies): a forced count of 3 updates
+    against the oracle and against the single pass, and the tau stop against
+    the single pass (same count within one update)."""
+    say("row split")
+    P, R = 8192, 1024
+    cfg, params, p64 = problem(C=48, d=256, H=4, layers=1, max_len=P + R, dtype="bf16",
+                               seed=70)
+    plan = B.AFPlan(cfg, params)
+    xp = synth.normal((1, P, 48), 71)
+    z = synth.normal((1, R, 48), 72)
+    out = {}
+    for split in (True, False):
+        plan.set_row_split(split)
+        plan.prefill(to_dev(xp), rows=R)
+        plan.profile_enable("affine")
+        xf, itf = plan.inverse_jacobi(to_dev(z), R, 0.0, 3, prefix_len=P,
+                                      x_last=to_dev(xp[:, -1]))
+        n_aff, _ = plan.profile_read()
+        plan.profile_disable()
+        assert n_aff == (6 if split else 3)   # one affine update per half and update
+        plan.prefill(to_dev(xp), rows=R)
+        xt, itt = plan.inverse_jacobi(to_dev(z), R, 1e-3, prefix_len=P,
+                                      x_last=to_dev(xp[:, -1]))
+        out[split] = (to_np(xf), itf, to_np(xt), itt)
+    (fa, ia, ta, ja), (fb, ib, tb, jb) = out[True], out[False]
+    cache, x_last = O.prefill(p64[0], xp, 4)
+    xo, _ = O.inverse_jacobi_block(p64[0], z, 4, R, 0.0, forced_iters=[3], pos0=P,
+                                   cache=cache, x_last=x_last)
+    e_or, e_ss = rel_l2(fa, xo), rel_l2(fa, fb)
+    print(f"forced 3: split vs oracle {e_or:.2e}, split vs single pass {e_ss:.2e}; "
+          f"tau: iters {ja.tolist()} / {jb.tolist()}")
+    assert ia[0][0] == 3 and ib[0][0] == 3
+    assert e_or < TOL_BF16 and rel_l2(fb, xo) < TOL_BF16
+    assert e_ss < 2e-3
+    assert abs(int(ja[0][0]) - int(jb[0][0])) <= 1
+    if ja[0][0] == jb[0][0]:
+        assert rel_l2(ta, tb) < 2e-3
+
+
 def test_frame480p_fullsize(B):
     """One 1560-token frame, 8 layers d=1024, B=1560, zero init, tau=1e-3."""
     w = synth.WORKLOADS["frame480p"]
