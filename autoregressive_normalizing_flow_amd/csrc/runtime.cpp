@@ -783,6 +783,11 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     hipError_t e = hipEventRecord(ev_join, sb);
     return e != hipSuccess ? e : hipStreamWaitEvent(st, ev_join, 0);
   };
+  // every return, errors included, leaves `stream` ordered after half B's work
+  struct JoinAtExit {
+    decltype(join_b)& j;
+    ~JoinAtExit() { (void)j(); }
+  } join_at_exit{join_b};
   float* xtmp = (float*)(ws + w.xtmp);
   float* res = (float*)(ws + w.res);
   // counter word of the affine kernel, the sticky non-finite tag after it,

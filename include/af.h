@@ -241,9 +241,11 @@ af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *
  * summation order.  Used only with direct launches (not with graphs or the
  * fused refresh) and when ws_bytes >= af_workspace_bytes(p, N, min(B, L)),
  * which includes the second half's scratch whenever the shape allows a split.
- * The call returns with `stream` ordered after all of the second stream's
- * work.  enable != 0 (the default) allows the split, 0 keeps one pass;
- * AF_ERR_ARG if p is NULL. */
+ * The call returns (also on an error) with `stream` ordered after all of the
+ * second stream's work.  Like the graph cache, the second stream and its
+ * events belong to the plan: a plan must not be used by two calls at once.
+ * enable != 0 (the default) allows the split, 0 keeps one pass; AF_ERR_ARG if
+ * p is NULL. */
 af_status af_plan_set_row_split(af_plan *p, int enable);
 
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
