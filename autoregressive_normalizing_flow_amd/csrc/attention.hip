@@ -559,8 +559,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   attn_bf16_body<DH, SPLIT>(a);
 }
 
-// Key chunk length: the smallest multiple of 512 keys that keeps the number
-// of units at most 1024 (four per CU); whole ranges when that is already enough.
+// Key chunk length.  For the two-blocks-per-CU kernel (d_h <= 64, not split)
+// the smallest chunk of 448..1024 keys (a multiple of the 64-key tile) that
+// keeps every unit in one round of two blocks per CU, when there is one (448
+// keys at 1560 tokens: 512 units of at most 7 tiles, against 448 units of 8
+// tiles with 512-key chunks).  Otherwise the smallest multiple of 512 keys
+// that keeps the number of units at most 1024 (four per CU); whole ranges when
+// that is already enough.
 static int att_units(int R, int pos_base, int KC, int n_qt) {
   int s = 0;
   for (int qt = 0; qt < n_qt; ++qt) {
@@ -570,9 +575,12 @@ static int att_units(int R, int pos_base, int KC, int n_qt) {
   return s;
 }
 
-int attention_chunk(int N, int R, int H, int pos_base) {
+int attention_chunk(int N, int R, int H, int dh, bool split, int pos_base) {
   const int n_qt = (R + ATT_QT - 1) / ATT_QT;
   const int nk_max = pos_base + R;
+  if (dh <= 64 && !split)
+    for (int kc = 448; kc <= 1024 && kc < nk_max; kc += ATT_KT)
+      if ((long)N * H * att_units(R, pos_base, kc, n_qt) <= 512) return kc;
   int KC = 512;
   while (KC < nk_max && (long)N * H * att_units(R, pos_base, KC, n_qt) > 1024) KC *= 2;
   return KC;
@@ -580,7 +588,9 @@ int attention_chunk(int N, int R, int H, int pos_base) {
 
 size_t attention_partial_floats(int N, int R, int H, int dh, int pos_base) {
   const int n_qt = (R + ATT_QT - 1) / ATT_QT;
-  const int KC = attention_chunk(N, R, H, pos_base);
+  // the larger of the two chunk rules' unit counts
+  const int KC = std::min(attention_chunk(N, R, H, dh, false, pos_base),
+                          attention_chunk(N, R, H, dh, true, pos_base));
   return (size_t)N * H * att_units(R, pos_base, KC, n_qt) * ATT_QT * (dh + 2);
 }
 
@@ -641,7 +651,7 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf) {
     const int n_qt = (R + ATT_QT - 1) / ATT_QT;
-    const int KC = attention_chunk(N, R, H, pos_base);
+    const int KC = attention_chunk(N, R, H, dh, split != nullptr, pos_base);
     const int U_nh = att_units(R, pos_base, KC, n_qt);
     AttnArgs a{(const bf16*)q, (const bf16*)kc, (const bf16*)vt, (bf16*)out,
                split ? (const bf16*)split->q_lo : nullptr,
