@@ -513,7 +513,11 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], const bf16*
   if (issue) dma_issue<G>(A, W, va, vb, lds_address(nxt), k_issue, wave);
   Frags<G> f;
   frag_load<G>(f, cur, grp, wm, wn, lane);
+  // raised wave priority while this wave multiplies: its MFMAs issue ahead
+X
+  __builtin_amdgcn_s_setprio(1);
   frag_mma<G>(acc, f);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int TM, int TN, class Epi>
