@@ -514,7 +514,8 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[G::TN][G::TM], const bf16*
   Frags<G> f;
   frag_load<G>(f, cur, grp, wm, wn, lane);
   // raised wave priority while this wave multiplies: its MFMAs issue ahead
-X
+  // of the other waves' loads and fragment reads (the QKV GEMM alone at 1560
+  // rows: 18.7 -> 17.9 us)
   __builtin_amdgcn_s_setprio(1);
   frag_mma<G>(acc, f);
   __builtin_amdgcn_s_setprio(0);
