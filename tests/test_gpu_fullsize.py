@@ -123,6 +123,38 @@ def test_row_split_matches_single_pass_and_oracle(B):
         assert rel_l2(ta, tb) < 2e-3
 
 
+def test_row_split_batch_of_two(B):
+    """The row split with two samples (each sample's rows halved, residual
+    pairs per sample and half): the same as the single pass, forced count and
+    tau stop, the two samples' counts shared."""
+    say("row split, batch 2")
+    P, R, N = 8192, 1024, 2
+    cfg, params, _ = problem(C=48, d=256, H=4, layers=1, max_len=P + R, dtype="bf16", seed=73)
+    plan = B.AFPlan(cfg, params)
+    xp = to_dev(synth.normal((N, P, 48), 74))
+    z = to_dev(synth.normal((N, R, 48), 75))
+    out = {}
+    for split in (True, False):
+        plan.set_row_split(split)
+        plan.prefill(xp, rows=R)
+        plan.profile_enable("affine")
+        xf, itf = plan.inverse_jacobi(z, R, 0.0, 2, prefix_len=P, x_last=xp[:, -1].contiguous())
+        n_aff, _ = plan.profile_read()
+        plan.profile_disable()
+        assert n_aff == (4 if split else 2)
+        plan.prefill(xp, rows=R)
+        xt, itt = plan.inverse_jacobi(z, R, 1e-3, prefix_len=P, x_last=xp[:, -1].contiguous())
+        out[split] = (to_np(xf), itf, to_np(xt), itt)
+    (fa, ia, ta, ja), (fb, ib, tb, jb) = out[True], out[False]
+    print(f"forced: rel {rel_l2(fa, fb):.2e}; tau: iters {ja.tolist()} / {jb.tolist()}, "
+          f"rel {rel_l2(ta, tb):.2e}")
+    assert ia[0][0] == 2 and ib[0][0] == 2 and rel_l2(fa, fb) < 2e-3
+    assert abs(int(ja[0][0]) - int(jb[0][0])) <= 1
+    if ja[0][0] == jb[0][0]:
+        assert rel_l2(ta, tb) < 2e-3
+    assert np.isfinite(ta).all()
+
+
 def test_frame480p_fullsize(B):
     """One 1560-token frame, 8 layers d=1024, B=1560, zero init, tau=1e-3."""
     w = synth.WORKLOADS["frame480p"]
