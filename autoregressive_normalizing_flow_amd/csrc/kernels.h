@@ -53,6 +53,8 @@ struct AffineArgs {
   unsigned* seq_dev;   // inverse: device counter of finished updates, or NULL
   unsigned* seq_host;  // inverse: host-mapped word that receives the counter after
                        // res_host is written (the host polls it), or NULL
+  unsigned* bad_host;  // inverse: host-mapped word that receives the sticky `bad`
+                       // value with every publication, or NULL
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

@@ -524,7 +524,10 @@ __device__ void finish_sums(const AffineArgs& a, const float* partials, int G, f
   }
   if (threadIdx.x == 0) {
     if (MODE == 0 && a.seq_host) {
-      // publish the update's number once its residuals have reached the host
+      // publish the update's number once its residuals (and the sticky
+      // non-finite tag) have reached the host
+      if (a.bad_host && a.bad)
+        system_store(a.bad_host, __hip_atomic_load(a.bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       wait_stores();
       system_store(a.seq_host, atomicAdd(a.seq_dev, 1u) + 1u);
     }

@@ -796,9 +796,10 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   unsigned* seq_dev = (unsigned*)(ws + w.counter) + 2;
   AF_HIP(clear_counters(w, ws, st));
   if (split_ok) AF_HIP(clear_counters(wb, ws, st));
+  // host-mapped words behind the residual pairs: the sequence numbers of
+  // halves A and B, then the sticky non-finite tags they publish
   volatile unsigned* seq_host_words = seq_word(p, false);
-  seq_host_words[0] = 0u;   // no update of this plan is in flight
-  seq_host_words[1] = 0u;
+  for (int i = 0; i < 4; ++i) seq_host_words[i] = 0u;   // no update of this plan is in flight
   unsigned n_updates = 0;
   unsigned n_split = 0;   // updates that ran as a row split (half B's publications)
 
@@ -817,7 +818,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                         dir, (float*)(ws + w.partials), res,
                         (unsigned*)(ws + w.counter), nullptr, bad,
                         (unsigned)(1 + t * nb + b), p->host_res_dev, seq_dev,
-                        seq_word(p, true)};
+                        seq_word(p, true), seq_word(p, true) + 2};
       // the update is the same launch sequence on every iteration of the
       // block: replay it as one graph when there are several to run (or it is
       // cached from an earlier call).  Profiled calls launch directly, as
@@ -857,6 +858,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         aab.res_host = p->host_res_dev + 2 * (size_t)N;
         aab.seq_dev = (unsigned*)(ws + wb.counter) + 2;
         aab.seq_host = seq_word(p, true) + 1;
+        aab.bad_host = seq_word(p, true) + 3;
         xa.wait_qkv = ev_att;
         xa.rec_qkv = ev_qkv;
         xa.wait_affine = ev_emb;
@@ -963,10 +965,13 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     zin = xo;
   }
   AF_HIP(join_b());
-  AF_HIP(hipMemcpyAsync(p->host_res, bad, sizeof(unsigned), hipMemcpyDeviceToHost, st));
-  AF_HIP(hipStreamSynchronize(st));
-  unsigned tag;
-  std::memcpy(&tag, p->host_res, sizeof(unsigned));
+  // The sticky non-finite tag comes with the last update's publication: wait
+  // for that (the stop test may have seen it already) instead of draining the
+  // stream, so work enqueued behind it (a speculative prefix) keeps running
+  // while the call returns.
+  if (af_status e = wait_update(p, n_updates, st, n_split ? sb : nullptr, n_split)) return e;
+  unsigned tag = seq_host_words[2];
+  if (tag == 0) tag = seq_host_words[3];
   if (tag != 0) {
     const int t = (int)(tag - 1) / nb, b = (int)(tag - 1) % nb;
     return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +

@@ -30,8 +30,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  af_forward and
  *     af_prefill are stream-ordered and return without waiting.
  *     af_inverse_jacobi blocks: the affine kernel writes each update's
- *     residual into pinned host memory of the plan for the stop test, and the
- *     call returns once x and iters are final.
+ *     residual (and a sticky non-finite tag) into pinned host memory of the
+ *     plan for the stop test, and the call returns once the last update has
+ *     published them, so iters and the status are final; x is stream-ordered
+ *     (kernels the call enqueued may still be running when it returns).
  */
 #ifndef AF_H
 #define AF_H
