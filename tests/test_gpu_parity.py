@@ -107,6 +107,32 @@ def test_inverse_flags_nonfinite(B, tau):
         plan.inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
     assert ei.value.status == B.AF_ERR_NONFINITE
     assert "Jacobi block 1" in str(ei.value)
+    # the plan stays usable: a clean call after the failure equals a fresh plan's
+    z[0, 20, 5] = 0.0
+    xa, ia = plan.inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
+    xb, ib = B.AFPlan(w.block, params).inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(ia, ib) and torch.equal(xa, xb)
+
+
+def test_back_to_back_calls_without_sync(B):
+    """An inverse call returns once its last update has published its
+    residual, possibly with kernels still queued: three calls in a row on one
+    plan and stream, with no synchronisation between them, equal the same
+    calls made one at a time."""
+    say("back-to-back inverse calls")
+    cfg, params, _ = problem(C=48, d=256, H=4, layers=2, max_len=96, dtype="bf16", seed=21)
+    plan = B.AFPlan(cfg, params)
+    zs = [to_dev(synth.normal((2, 96, 48), 22 + i)) for i in range(3)]
+    ref = []
+    for z in zs:
+        x, it = plan.inverse_jacobi(z, 32, 1e-3)
+        torch.cuda.synchronize()
+        ref.append((x.clone(), it.copy()))
+    out = [plan.inverse_jacobi(z, 32, 1e-3) for z in zs]
+    torch.cuda.synchronize()
+    for (x, it), (xr, itr) in zip(out, ref):
+        assert np.array_equal(it, itr) and torch.equal(x, xr)
 
 
 # ---------------------------------------------------------------------------
