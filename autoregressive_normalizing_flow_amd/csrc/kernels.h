@@ -54,7 +54,7 @@ struct AffineArgs {
   unsigned* seq_host;  // inverse: host-mapped word that receives the counter after
                        // res_host is written (the host polls it), or NULL
   unsigned* bad_host;  // inverse: host-mapped word that receives the sticky `bad`
-                       // value with every publication, or NULL
+                       // value when this update finds a non-finite sum, or NULL
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

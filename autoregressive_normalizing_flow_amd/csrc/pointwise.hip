@@ -514,7 +514,11 @@ __device__ void finish_sums(const AffineArgs& a, const float* partials, int G, f
           system_store(&a.res_host[2 * nn], p0);
           system_store(&a.res_host[2 * nn + 1], p1);
         }
-        if (a.bad && !(isfinite(p0) && isfinite(p1))) atomicCAS(a.bad, 0u, a.tag);
+        if (a.bad && !(isfinite(p0) && isfinite(p1))) {
+          // the first tag set stays; the host reads it beside the sequence word
+          const unsigned first = atomicCAS(a.bad, 0u, a.tag);
+          if (a.bad_host) system_store(a.bad_host, first ? first : a.tag);
+        }
       } else {
         a.res[2 * nn] = -p0;
         a.res[2 * nn + 1] = p1;
@@ -524,10 +528,8 @@ __device__ void finish_sums(const AffineArgs& a, const float* partials, int G, f
   }
   if (threadIdx.x == 0) {
     if (MODE == 0 && a.seq_host) {
-      // publish the update's number once its residuals (and the sticky
-      // non-finite tag) have reached the host
-      if (a.bad_host && a.bad)
-        system_store(a.bad_host, __hip_atomic_load(a.bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      // publish the update's number once its residuals (and a non-finite
+      // tag) have reached the host
       wait_stores();
       system_store(a.seq_host, atomicAdd(a.seq_dev, 1u) + 1u);
     }

@@ -797,7 +797,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   AF_HIP(clear_counters(w, ws, st));
   if (split_ok) AF_HIP(clear_counters(wb, ws, st));
   // host-mapped words behind the residual pairs: the sequence numbers of
-  // halves A and B, then the sticky non-finite tags they publish
+  // halves A and B, then the non-finite tags they report
   volatile unsigned* seq_host_words = seq_word(p, false);
   for (int i = 0; i < 4; ++i) seq_host_words[i] = 0u;   // no update of this plan is in flight
   unsigned n_updates = 0;
@@ -965,10 +965,11 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     zin = xo;
   }
   AF_HIP(join_b());
-  // The sticky non-finite tag comes with the last update's publication: wait
-  // for that (the stop test may have seen it already) instead of draining the
-  // stream, so work enqueued behind it (a speculative prefix) keeps running
-  // while the call returns.
+  // An update that finds a non-finite sum writes the first such tag to its
+  // half's pinned word before it publishes its number: waiting for the last
+  // update's publication (the stop test may have seen it already) replaces
+  // draining the stream, so work enqueued behind it (a speculative prefix)
+  // keeps running while the call returns.
   if (af_status e = wait_update(p, n_updates, st, n_split ? sb : nullptr, n_split)) return e;
   unsigned tag = seq_host_words[2];
   if (tag == 0) tag = seq_host_words[3];
