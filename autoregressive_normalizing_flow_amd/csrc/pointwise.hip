@@ -469,7 +469,7 @@ hipError_t launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t st) {
 int affine_groups(int N, int R, int C) {
   const long quads = ((long)R * C + 3) / 4;
   long g = (quads + 255) / 256;             // one quad per thread per pass
-  const long cap = std::max(1, 2048 / std::max(N, 1));
+  const long cap = std::max(1, 8192 / std::max(N, 1));
   if (g > cap) g = cap;
   return (int)std::max(1L, g);
 }

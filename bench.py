@@ -316,9 +316,8 @@ def main():
                          "(B = 1 is the GPU sequential baseline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the per-GPU kernel is measured at its real shape; see the sharding "
-              "design in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path; the "
+              "per-GPU kernels are measured at their real shape.", file=sys.stderr)
         sys.exit(2)
 
     import torch
