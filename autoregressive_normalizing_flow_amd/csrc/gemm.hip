@@ -8,6 +8,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 namespace af {
@@ -737,19 +739,33 @@ TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = fal
   return best;
 }
 
+namespace {
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+}
+
+void set_gemm_events(hipEvent_t start, hipEvent_t stop) {
+  g_ev_start = start;
+  g_ev_stop = stop;
+}
+
+bool gemm_events_pending() { return g_ev_start != nullptr; }
+
 template <int TM, int TN, bool SPLIT, class Epi>
 static void launch_cfg(const void* A, const void* Alo, const void* W, int M, int N,
                        int K, int splits, const Epi& epi, hipStream_t st) {
   using G = GemmCfg<TM, TN>;
   const int tiles = ((M + G::BM - 1) / G::BM) * (N / G::BN);
+  // events bracketing this kernel alone, when the profiler asked for them
+  const hipEvent_t e0 = g_ev_start, e1 = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
   if (SPLIT)
-    hipLaunchKernelGGL((gemm_bf16_kernel<TM, TN, SPLIT, Epi>), dim3(tiles * splits),
-                       dim3(256), 0, st, (const bf16*)A, (const bf16*)Alo, (const bf16*)W,
-                       M, N, K, K / splits, epi);
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<TM, TN, SPLIT, Epi>), dim3(tiles * splits),
+                          dim3(256), 0, st, e0, e1, 0, (const bf16*)A, (const bf16*)Alo,
+                          (const bf16*)W, M, N, K, K / splits, epi);
   else
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<TM, TN, Epi>), dim3(tiles * splits),
-                       dim3(512), 0, st, (const bf16*)A, (const bf16*)W, M, N, K,
-                       K / splits, epi);
+    hipExtLaunchKernelGGL((gemm_bf16_dma_kernel<TM, TN, Epi>), dim3(tiles * splits),
+                          dim3(512), 0, st, e0, e1, 0, (const bf16*)A, (const bf16*)W, M,
+                          N, K, K / splits, epi);
 }
 
 // Alo != NULL selects the split (hi + lo) activation kernel.

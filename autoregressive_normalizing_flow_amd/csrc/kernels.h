@@ -83,6 +83,12 @@ struct QKVDst {
   void* kc_lo;
   void* vt_lo;
 };
+// Timing of one bf16 GEMM kernel (profiling only): after set_gemm_events(a, b)
+// the next bf16 GEMM launch of this thread records a at the kernel's start and
+// b at its end (hipExtLaunchKernelGGL) and clears the pair; gemm_events_pending()
+// tells whether it is still unused.
+void set_gemm_events(hipEvent_t start, hipEvent_t stop);
+bool gemm_events_pending();
 // The bf16 path stores Q times log2(e) / sqrt(dh), the base-2 softmax units
 // the bf16 attention takes (scaled in fp32 before the one rounding to bf16).
 hipError_t launch_gemm_qkv(bool bf16, const void* A, const void* A_lo, const void* W,

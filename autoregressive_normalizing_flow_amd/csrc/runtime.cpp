@@ -225,19 +225,34 @@ WsLayout layout_b(const af_plan* p, int N, int rows, const WsLayout& w) {
 }
 
 // Launch helper with optional per-class event timing (direct launches only:
-// nothing is captured into a graph while a class is profiled).
+// nothing is captured into a graph while a class is profiled).  The bf16
+// projection GEMMs are one kernel per launch call, and their events are taken
+// by the kernel launch itself, so they time the kernel alone; the other
+// classes are bracketed by event records on the stream, which also count the
+// gaps before and after the kernels.
 struct Launch {
   hipStream_t st;
-  hipEvent_t e1 = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bool ext = false;
   Launch(af_plan* p, hipStream_t s, int cls) : st(s) {
     if (p->prof_class != cls || p->prof_n >= (int)p->ev.size() / 2) return;
-    const hipEvent_t e0 = p->ev[2 * p->prof_n];
+    e0 = p->ev[2 * p->prof_n];
     e1 = p->ev[2 * p->prof_n + 1];
     ++p->prof_n;
-    (void)hipEventRecord(e0, st);
+    ext = p->bf &&
+          (cls == K_QKV || cls == K_O || cls == K_MLP1 || cls == K_MLP2);
+    if (ext) af::set_gemm_events(e0, e1);
+    else (void)hipEventRecord(e0, st);
   }
   ~Launch() {
-    if (e1) (void)hipEventRecord(e1, st);
+    if (!e1) return;
+    if (ext && !af::gemm_events_pending()) return;   // the kernel took them
+    if (ext) {
+      // no GEMM launched (an error path): leave an empty interval
+      af::set_gemm_events(nullptr, nullptr);
+      (void)hipEventRecord(e0, st);
+    }
+    (void)hipEventRecord(e1, st);
   }
 };
 
