@@ -716,7 +716,10 @@ static const int kTileCfgs[][2] = {{7, 4}, {7, 3}, {7, 2}, {4, 4}, {4, 2}};
 // 1560 rows (bf16, d = 1024): a block's time grows with its operand bytes,
 // (BM + BN) * K / S (the per-CU load path sets the pace), and with its output
 // tile, BM * BN (epilogue); blocks beyond 256 take another round; each extra
-// split plane costs its consumer one more fp32 [M, N] read.
+// split plane costs its consumer one more fp32 [M, N] read (0.82 us per plane
+// at 1560 x 1024, from the residual + LayerNorm kernel with one and with four
+// planes).  At 1560 rows this makes MLP2 (K = 4096) two planes of 128 x 128
+// tiles rather than four of 224 x 128: 2% faster per Jacobi update.
 TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = false) {
   TileChoice best{4, 2, 1};
   double best_cost = 1e300;
@@ -729,7 +732,7 @@ TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = fal
       if (K % (64 * s) || (s > 1 && K / s < 256)) break;
       const long rounds = (tiles * s + 255) / 256;
       const double per_block = 4.28e-5 * (BM + BN) * (double)(K / s) + 4.66e-4 * BM * BN;
-      const double cost = rounds * per_block + 4.0e-7 * (s - 1) * (double)M * N;
+      const double cost = rounds * per_block + 6.7e-7 * (s - 1) * (double)M * N;
       if (cost < best_cost) {
         best_cost = cost;
         best = TileChoice{c[0], c[1], s};
