@@ -635,6 +635,8 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
 
 void af_plan_destroy(af_plan* p) {
   if (!p) return;
+  // an inverse call returns with its last kernels possibly still queued
+  (void)hipDeviceSynchronize();
   for (GraphEntry& e : p->gcache) destroy_entry(e);
   if (p->cap_stream) (void)hipStreamDestroy(p->cap_stream);
   if (p->split_stream) (void)hipStreamDestroy(p->split_stream);

@@ -114,6 +114,9 @@ typedef struct af_plan af_plan;
  * the documented ranges. */
 af_status af_plan_create(const af_block_cfg *cfg, int n_blocks,
                          const af_block_weights *w, af_plan **out);
+/* Release the plan's streams, events, graphs and pinned memory.  Work that a
+ * call left queued (see af_inverse_jacobi) may still use them, so this first
+ * waits for the current device to finish all outstanding work. */
 void af_plan_destroy(af_plan *p);
 
 /* Workspace bytes for `batch` samples when at most `rows` tokens per sample

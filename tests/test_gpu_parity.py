@@ -118,8 +118,9 @@ def test_inverse_flags_nonfinite(B, tau):
 def test_back_to_back_calls_without_sync(B):
     """An inverse call returns once its last update has published its
     residual, possibly with kernels still queued: three calls in a row on one
-    plan and stream, with no synchronisation between them, equal the same
-    calls made one at a time."""
+    plan and stream, with no synchronisation between them (and the plan
+    destroyed right after the last), equal the same calls made one at a
+    time."""
     say("back-to-back inverse calls")
     cfg, params, _ = problem(C=48, d=256, H=4, layers=2, max_len=96, dtype="bf16", seed=21)
     plan = B.AFPlan(cfg, params)
@@ -130,6 +131,7 @@ def test_back_to_back_calls_without_sync(B):
         torch.cuda.synchronize()
         ref.append((x.clone(), it.copy()))
     out = [plan.inverse_jacobi(z, 32, 1e-3) for z in zs]
+    del plan   # destroyed with the last call's kernels possibly still queued
     torch.cuda.synchronize()
     for (x, it), (xr, itr) in zip(out, ref):
         assert np.array_equal(it, itr) and torch.equal(x, xr)
