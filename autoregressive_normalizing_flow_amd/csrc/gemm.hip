@@ -719,8 +719,14 @@ static const int kTileCfgs[][2] = {{7, 4}, {7, 3}, {7, 2}, {4, 4}, {4, 2}};
 // split plane costs its consumer one more fp32 [M, N] read (0.82 us per plane
 // at 1560 x 1024, from the residual + LayerNorm kernel with one and with four
 // planes).  At 1560 rows this makes MLP2 (K = 4096) two planes of 128 x 128
-// tiles rather than four of 224 x 128: 2% faster per Jacobi update.
-TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = false) {
+// tiles rather than four of 224 x 128: 2% faster per Jacobi update.  The
+// halves of a row-split update (two 780-row passes side by side) cap the
+// planes at two: MLP2 as (4, 4) split 2 rather than the model's (4, 4) split
+// 4 made the 21-frame video inverse 1.8% faster (the model, which gives each
+// launch the whole chip, also preferred (7, 4) split 4 when given half of it:
+// +0.7% only).
+TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = false,
+                       int max_splits = 8) {
   TileChoice best{4, 2, 1};
   double best_cost = 1e300;
   for (auto& c : kTileCfgs) {
@@ -728,7 +734,7 @@ TileChoice gemm_choose(int M, int N, int K, bool allow_split, bool split_a = fal
     const int BM = 32 * c[0], BN = 32 * c[1];
     if (N % BN) continue;
     const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
-    for (int s = 1; s <= (allow_split ? 8 : 1); s *= 2) {
+    for (int s = 1; s <= (allow_split ? max_splits : 1); s *= 2) {
       if (K % (64 * s) || (s > 1 && K / s < 256)) break;
       const long rounds = (tiles * s + 255) / 256;
       const double per_block = 4.28e-5 * (BM + BN) * (double)(K / s) + 4.66e-4 * BM * BN;
@@ -870,8 +876,8 @@ hipError_t launch_gemm_resid(bool bf, const void* A, const void* Alo, const void
 
 hipError_t launch_gemm_partial(const void* A, const void* Alo, const void* W,
                                float* slab, int M, int N, int K, int* splits,
-                               hipStream_t st) {
-  TileChoice c = gemm_choose(M, N, K, true, Alo != nullptr);
+                               hipStream_t st, int max_splits) {
+  TileChoice c = gemm_choose(M, N, K, true, Alo != nullptr, max_splits);
   *splits = c.splits;
   EpiSlab es{slab, M, N};
   return run_bf16_cfg(A, Alo, W, M, N, K, c, es, st);

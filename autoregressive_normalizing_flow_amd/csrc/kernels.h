@@ -103,9 +103,11 @@ hipError_t launch_gemm_resid(bool bf16, const void* A, const void* A_lo, const v
 int gemm_resid_splits(int M, int N, int K);
 // The residual GEMMs of the bf16 path write fp32 partial planes only
 // (slab [S][M][N], S = the returned split count); launch_resid_ln finishes them.
+// At most max_splits planes (a power of two; never more than
+// gemm_resid_splits(M, N, K)).
 hipError_t launch_gemm_partial(const void* A, const void* A_lo, const void* W,
                                float* slab, int M, int N, int K, int* splits,
-                               hipStream_t st);
+                               hipStream_t st, int max_splits = 8);
 hipError_t launch_gemm_gelu(bool bf16, const void* A, const void* A_lo, const void* W,
                             const float* bias, void* out, void* out_lo, int M, int N,
                             int K, hipStream_t st);
