@@ -305,9 +305,10 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   };
   const af_block_cfg& c = p->cfg;
   const int M = ps.N * ps.R, d = c.d;
-  // a row-split half runs beside the other: its residual GEMMs take at most
-  // two split planes (measured faster than the four the shape alone gets)
-  const int max_planes = xs ? 2 : 8;
+  // a row-split half runs beside the other: its residual GEMMs take fewer
+  // split planes than the shape alone gets (measured faster: the output
+  // projection one, MLP2 two)
+  const int o_planes = xs ? 1 : 8, mlp2_planes = xs ? 2 : 8;
   float* h = (float*)(ws + w.h);
   void* a = ws + w.a;
   void* q = ws + w.q;
@@ -358,12 +359,13 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       }
       if (!post) return AF_OK;
       int S = 1;
-      LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st, max_planes));
+      LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st, o_planes));
       LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_o, h, lw.ln2_g, lw.ln2_b, a, true, a_lo,
                                        M, d, st));
       LAUNCH(K_MLP1, af::launch_gemm_gelu(true, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
                                           d, st));
-      LAUNCH(K_MLP2, af::launch_gemm_partial(u, u_lo, lw.w_2, slab, M, d, p->dmlp, &S, st, max_planes));
+      LAUNCH(K_MLP2, af::launch_gemm_partial(u, u_lo, lw.w_2, slab, M, d, p->dmlp, &S, st,
+                                                     mlp2_planes));
       if (l + 1 < c.n_layers) {
         const LayerW& nx = bw.layers[l + 1];
         LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_2, h, nx.ln1_g, nx.ln1_b, a, true, a_lo,
