@@ -324,6 +324,100 @@ def test_jacobi_stop_rule_and_forced_count():
     assert k == 1 and np.allclose(r, 1.0)   # from zero init r_1 = 1 exactly
 
 
+def test_block_residual_hand_values():
+    """The residual of the stop rule is the squared ratio
+    ||x_new - x_old||^2 / ||x_new||^2 of each sample over the whole block
+    (关键设计 3).  Values worked out by hand:
+      sample 0: x_old = 0, x_new = 1 everywhere -> r = 1;
+      sample 1: x_old = 1, x_new = 2 everywhere -> r = 1/4.
+    A ratio of norms would give 1/2 for sample 1, and a residual pooled over
+    the batch would give (n + n) / (n + 4n) = 2/5 for both."""
+    Bb, C = 5, 3
+    x_old = np.stack([np.zeros((Bb, C)), np.ones((Bb, C))])
+    x_new = np.stack([np.ones((Bb, C)), 2.0 * np.ones((Bb, C))])
+    r = O.block_residual(x_new, x_old)
+    assert r.shape == (2,)
+    assert r[0] == 1.0 and r[1] == 0.25
+    # 0 / 0 is 0 (a block that is and stays zero has converged); x / 0 is inf
+    r0 = O.block_residual(np.zeros((2, Bb, C)),
+                          np.stack([np.zeros((Bb, C)), np.ones((Bb, C))]))
+    assert r0[0] == 0.0 and r0[1] == np.inf
+
+
+def constant_net(C, L, mu0, raw0, seed=0):
+    """Every weight matrix and the position table zero, head bias
+    (mu0, raw0): mu = mu0 and log sigma = 0.5 tanh(raw0) at every token, so
+    one Jacobi update from any x^(0) lands on x = mu0 + sigma0 z."""
+    _, (p,) = tiny(C=C, max_len=L, seed=seed, aux=False)
+    for k in list(p):
+        if k.startswith("w_") or k == "pos":
+            p[k] = np.zeros_like(p[k])
+    for l in p["layers"]:
+        for k in l:
+            if k.startswith("w_"):
+                l[k] = np.zeros_like(l[k])
+    p["b_head"] = np.concatenate([mu0, raw0])
+    return p
+
+
+def test_jacobi_stop_uses_squared_per_sample_residual():
+    """The stop test through the iteration counts of the constant network,
+    where x^(1) is the exact solution x* whatever x^(0) is:
+      * x^(0) = x*/2 gives r_1 = ||x*/2||^2 / ||x*||^2 = 1/4 exactly.  With
+        tau = 0.3 the block stops after one update; a ratio of norms (1/2)
+        would not.  With tau = 0.2 it takes a second update (r_2 = 0).
+      * sample 0 starts at x* (r_1 = 0), sample 1 at zeros (r_1 = 1): the
+        block does not stop after update 1 although one sample passed.
+      * sample 0 is large and starts at x*, sample 1 is tiny and starts at
+        zeros: the residual pooled over the batch, ~1e-8, is below tau, but
+        sample 1's own r_1 = 1 is not, so the block runs a second update."""
+    L, C, Bb = 8, 2, 4
+    mu0 = np.array([0.0, 0.0])
+    raw0 = np.array([0.7, -2.0])
+    p = constant_net(C, L, mu0, raw0)
+    sig0 = np.exp(0.5 * np.tanh(raw0))
+    z = np.random.default_rng(13).standard_normal((1, L, C))
+    xs = mu0 + sig0 * z
+    tr = []
+    x, it = O.inverse_jacobi_block(p, z, 2, Bb, tau=0.3, init="given", x_init=xs / 2,
+                                   trace=tr)
+    assert list(it) == [1, 1]
+    np.testing.assert_allclose([t[2][0] for t in tr], [0.25, 0.25], rtol=1e-14)
+    np.testing.assert_allclose(x, xs, rtol=1e-15, atol=1e-15)
+    _, it = O.inverse_jacobi_block(p, z, 2, Bb, tau=0.2, init="given", x_init=xs / 2)
+    assert list(it) == [2, 2]
+
+    z2 = np.concatenate([z, np.random.default_rng(14).standard_normal((1, L, C))])
+    xs2 = mu0 + sig0 * z2
+    init = np.stack([xs2[0], np.zeros((L, C))])
+    tr = []
+    _, it = O.inverse_jacobi_block(p, z2, 2, Bb, tau=1e-3, init="given", x_init=init,
+                                   trace=tr)
+    assert list(it) == [2, 2]
+    np.testing.assert_allclose(tr[0][2], [0.0, 1.0], atol=1e-15)
+    np.testing.assert_allclose(tr[1][2], [0.0, 0.0], atol=1e-15)
+
+    z3 = np.stack([1e2 * z[0], 1e-2 * z2[1]])
+    xs3 = mu0 + sig0 * z3
+    init = np.stack([xs3[0], np.zeros((L, C))])
+    pooled = (xs3[1, :Bb] ** 2).sum() / (xs3[:, :Bb] ** 2).sum()
+    assert pooled < 1e-6
+    tr = []
+    _, it = O.inverse_jacobi_block(p, z3, 2, Bb, tau=1e-3, init="given", x_init=init,
+                                   trace=tr)
+    assert list(it) == [2, 2]
+    np.testing.assert_allclose(tr[0][2], [0.0, 1.0], atol=1e-15)
+
+
+def test_jacobi_zero_block_converges_at_once():
+    """z = 0 and mu = 0: every iterate is zero, 0/0 counts as converged, so
+    each block stops after its first update."""
+    L, C = 8, 2
+    p = constant_net(C, L, np.zeros(C), np.array([0.3, -0.4]))
+    x, it = O.inverse_jacobi_block(p, np.zeros((1, L, C)), 2, 4, tau=1e-3)
+    assert list(it) == [1, 1] and np.all(x == 0.0)
+
+
 def test_jacobi_prev_frame_init():
     F, C = 4, 2
     L = 3 * F
