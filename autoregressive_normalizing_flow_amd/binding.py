@@ -26,6 +26,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "af.h")
 
 AF_OK, AF_ERR_ARG, AF_ERR_HIP, AF_ERR_WORKSPACE, AF_ERR_NONFINITE, AF_ERR_UNSUPPORTED = range(6)
 AF_F32, AF_BF16 = 0, 1
+AF_FWD_ACCUMULATE, AF_FWD_CHECK_FINITE = 1, 2
 INIT = {"zero": 0, "given": 1, "prev_frame": 2}
 KERNEL_CLASSES = ("embed", "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1",
                   "gemm_mlp2", "gemm_head", "attention", "affine")
@@ -80,7 +81,7 @@ def load_library() -> ctypes.CDLL:
     L.af_workspace_bytes.restype = sz
     L.af_cache_bytes.argtypes = [_P, i]
     L.af_cache_bytes.restype = sz
-    L.af_forward.argtypes = [_P, _P, _P, _P, i, i, _P, sz, _P]
+    L.af_forward.argtypes = [_P, _P, _P, _P, i, i, i, i, _P, sz, _P]
     L.af_forward.restype = st
     L.af_prefill.argtypes = [_P, _P, i, i, _P, sz, _P]
     L.af_prefill.restype = st
@@ -94,6 +95,7 @@ def load_library() -> ctypes.CDLL:
     L.af_profile_disable.argtypes = [_P]
     L.af_profile_disable.restype = st
     L.af_profile_read.argtypes = [_P, ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double)]
     L.af_profile_read.restype = st
     L.af_plan_set_fused_refresh.argtypes = [_P, i]
@@ -105,6 +107,8 @@ def load_library() -> ctypes.CDLL:
     L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
                                       ctypes.POINTER(ctypes.c_longlong)]
     L.af_plan_graph_stats.restype = st
+    L.af_plan_last_residual.argtypes = [_P, i, ctypes.POINTER(ctypes.c_float)]
+    L.af_plan_last_residual.restype = st
     L.afk_affine_partials_bytes.argtypes = [i, i, i]
     L.afk_affine_partials_bytes.restype = sz
     L.afk_affine.argtypes = [i, _P, _P, _P, i, i, i, _P, _P, sz, i, _P]
@@ -194,6 +198,7 @@ class AFPlan:
         self.handle = h
         self._ws = None
         self._ws_key = None
+        self._ws_stream = None
 
     def __del__(self):
         try:
@@ -213,6 +218,11 @@ class AFPlan:
         need = self.workspace_bytes(batch, rows)
         if self._ws is None or self._ws_key[0] != batch or self._ws.numel() < need:
             old, old_batch = self._ws, (self._ws_key[0] if self._ws_key else None)
+            if old is not None and self._ws_stream is not None:
+                # an inverse call may return with kernels still writing the
+                # old workspace on the stream it used: let them finish before
+                # its cache is copied and its memory handed back
+                self._ws_stream.synchronize()
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
             self._ws_key = (batch, rows)
             if old is not None and old_batch == batch:
@@ -221,20 +231,34 @@ class AFPlan:
                 self._ws[:cache].copy_(old[:cache])
         return self._ws
 
+    def _use(self, stream):
+        """Remember the stream a call runs on: later workspace growth waits
+        for it."""
+        self._ws_stream = stream if stream is not None else torch.cuda.current_stream()
+
     # entry points ----------------------------------------------------------
-    def forward(self, x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    def forward(self, x: torch.Tensor, stream=None, logdet: Optional[torch.Tensor] = None,
+                frames_per_entry: int = 1, accumulate: bool = False,
+                check_finite: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+        """z = f(x) and the log-det per entry (af_forward): one entry per
+        sample, or per group of ``frames_per_entry`` consecutive samples;
+        ``accumulate`` adds into the given ``logdet``."""
         _tok(x, "x")
         N, L, C = x.shape
         z = torch.empty_like(x)
-        logdet = torch.empty(N, dtype=torch.float32, device=x.device)
+        if logdet is None:
+            logdet = torch.empty(N // frames_per_entry, dtype=torch.float32, device=x.device)
         ws = self.workspace(N, L)
-        af_forward(self, x, z, logdet, ws, stream)
+        flags = (AF_FWD_ACCUMULATE if accumulate else 0) | \
+                (AF_FWD_CHECK_FINITE if check_finite else 0)
+        af_forward(self, x, z, logdet, ws, stream, frames_per_entry, flags)
         return z, logdet
 
     def prefill(self, x_prefix: torch.Tensor, rows: Optional[int] = None, stream=None):
         _tok(x_prefix, "x_prefix")
         N, P, C = x_prefix.shape
         ws = self.workspace(N, max(P, rows or 0))
+        self._use(stream)
         af_prefill(self, x_prefix, ws, stream)
 
     def refresh_kv(self, x: torch.Tensor, prefix_len: int = 0,
@@ -243,6 +267,7 @@ class AFPlan:
         _tok(x, "x")
         N, L, C = x.shape
         ws = self.workspace(N, max(L, self._ws_key[1] if self._ws_key else 0))
+        self._use(stream)
         af_refresh_kv(self, x, prefix_len, x_last, ws, stream)
 
     def inverse_jacobi(self, z: torch.Tensor, B: int, tau: float = 1e-3,
@@ -259,9 +284,19 @@ class AFPlan:
         # block's first pass
         rows = min(2 * B, L) if nb > 1 and getattr(self, "_fused_refresh", False) else min(B, L)
         ws = self.workspace(N, max(rows, self._ws_key[1] if self._ws_key else 0))
+        self._use(stream)
         af_inverse_jacobi(self, z, B, tau, max_iters, init, x_init, frame_len,
                           prefix_len, x_last, x, iters, ws, stream)
         return x, iters
+
+    def last_residual(self, N: int) -> np.ndarray:
+        """[N, 2] (sum of squared change, sum of squares) of the last Jacobi
+        update of the last inverse call, as its stop test saw them."""
+        out = np.zeros((N, 2), dtype=np.float32)
+        _check(self.L.af_plan_last_residual(
+            self.handle, N, out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))),
+            "af_plan_last_residual")
+        return out
 
     # profiling -------------------------------------------------------------
     def profile_enable(self, kernel_class: str):
@@ -272,11 +307,19 @@ class AFPlan:
         _check(self.L.af_profile_disable(self.handle), "af_profile_disable")
 
     def profile_read(self) -> Tuple[int, float]:
+        """(launches, summed ms) of the profiled class since profile_enable."""
+        n, ms, _ = self.profile_read_work()
+        return n, ms
+
+    def profile_read_work(self) -> Tuple[int, float, float]:
+        """(launches, summed ms, summed algorithmic work: flops, or bytes for
+        the affine class) of the profiled class since profile_enable."""
         n = ctypes.c_int()
         ms = ctypes.c_double()
-        _check(self.L.af_profile_read(self.handle, ctypes.byref(n), ctypes.byref(ms)),
-               "af_profile_read")
-        return n.value, ms.value
+        work = ctypes.c_double()
+        _check(self.L.af_profile_read(self.handle, ctypes.byref(n), ctypes.byref(ms),
+                                      ctypes.byref(work)), "af_profile_read")
+        return n.value, ms.value, work.value
 
     def set_fused_refresh(self, enable: bool):
         _check(self.L.af_plan_set_fused_refresh(self.handle, int(bool(enable))),
@@ -302,10 +345,13 @@ class AFPlan:
 # ---------------------------------------------------------------------------
 # C-named entry points (tensors in, status checked)
 # ---------------------------------------------------------------------------
-def af_forward(plan: AFPlan, x, z, logdet, ws, stream=None):
+def af_forward(plan: AFPlan, x, z, logdet, ws, stream=None, frames_per_entry: int = 1,
+               flags: int = 0):
     N, L, C = x.shape
+    plan._use(stream)
     _check(plan.L.af_forward(plan.handle, _ptr(x), _ptr(z), _ptr(logdet), N, L,
-                             _ptr(ws), ws.numel(), _stream(stream)), "af_forward")
+                             frames_per_entry, flags, _ptr(ws), ws.numel(),
+                             _stream(stream)), "af_forward")
 
 
 def af_prefill(plan: AFPlan, x_prefix, ws, stream=None):

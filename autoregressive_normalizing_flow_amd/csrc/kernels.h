@@ -47,14 +47,16 @@ struct AffineArgs {
   float* res;          // [N][2]
   unsigned* counter;   // zero before the first launch; the kernel leaves it zero
   float* logdet;       // forward: logdet[n] += -sum log sigma (may be NULL)
-  unsigned* bad;       // inverse: set to `tag` (if still 0) when a residual sum is
-  unsigned tag;        // not finite; may be NULL
+  unsigned* bad;       // set to `tag` (if still 0) when a residual sum (inverse) is
+  unsigned tag;        // not finite or a z (forward) is not finite; may be NULL
   float* res_host;     // inverse: host-mapped copy of res written at the end, or NULL
   unsigned* seq_dev;   // inverse: device counter of finished updates, or NULL
   unsigned* seq_host;  // inverse: host-mapped word that receives the counter after
                        // res_host is written (the host polls it), or NULL
   unsigned* bad_host;  // inverse: host-mapped word that receives the sticky `bad`
                        // value when this update finds a non-finite sum, or NULL
+  int ld_group;        // forward: sample nn adds into logdet[nn / ld_group] (0 or 1:
+                       // one entry per sample)
 };
 // mode 0: inverse update + residual sums; mode 1: forward + log-sigma sums.
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);

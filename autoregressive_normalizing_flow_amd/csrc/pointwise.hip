@@ -522,7 +522,9 @@ __device__ void finish_sums(const AffineArgs& a, const float* partials, int G, f
       } else {
         a.res[2 * nn] = -p0;
         a.res[2 * nn + 1] = p1;
-        if (a.logdet) a.logdet[nn] += -p0;
+        // samples in order: a group's entry adds its frames in a fixed order
+        if (a.logdet) a.logdet[a.ld_group > 1 ? nn / a.ld_group : nn] += -p0;
+        if (a.bad && p1 != 0.f) atomicCAS(a.bad, 0u, a.tag);
       }
     }
   }

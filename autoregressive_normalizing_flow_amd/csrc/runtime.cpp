@@ -112,6 +112,7 @@ struct af_plan {
   int prof_class = -1;
   std::vector<hipEvent_t> ev;  // pairs
   int prof_n = 0;
+  double prof_work = 0.0;      // algorithmic work of the recorded launches
   // a block's cache refresh merged into the next block's first update
   bool fuse_refresh = false;
   // HIP graphs of one Jacobi update, replayed once per iteration
@@ -124,6 +125,8 @@ struct af_plan {
   bool row_split = true;
   hipStream_t split_stream = nullptr;
   std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
+  // residual pairs of the last update of the last inverse call (halves added)
+  std::vector<float> last_res;
 };
 
 namespace {
@@ -234,8 +237,9 @@ struct Launch {
   hipStream_t st;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   bool ext = false;
-  Launch(af_plan* p, hipStream_t s, int cls) : st(s) {
+  Launch(af_plan* p, hipStream_t s, int cls, double work = 0.0) : st(s) {
     if (p->prof_class != cls || p->prof_n >= (int)p->ev.size() / 2) return;
+    p->prof_work += work;
     e0 = p->ev[2 * p->prof_n];
     e1 = p->ev[2 * p->prof_n + 1];
     ++p->prof_n;
@@ -255,6 +259,15 @@ struct Launch {
     (void)hipEventRecord(e1, st);
   }
 };
+
+// LAUNCHW also states the launch's algorithmic work for the profiler.
+#define LAUNCHW(cls, work, call)                          \
+  do {                                                    \
+    Launch l_(p, st, cls, (work));                        \
+    hipError_t e_ = (call);                               \
+    if (e_ != hipSuccess)                                 \
+      return fail(AF_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
 
 #define LAUNCH(cls, call)                                 \
   do {                                                    \
@@ -322,9 +335,17 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   float* slab = (float*)(ws + w.slab);
   const int pos_base = ps.P + ps.s;
   const bool pre = ps.part != PASS_REST, post = ps.part != PASS_PREFIX;
+  // algorithmic work per launch (2 flops per multiply-add; attention 4 d flops
+  // per unmasked (query, key) pair: row t attends to pos_base + t + 1 keys)
+  const double Md = (double)M * d, dd = (double)d * d;
+  const double w_qkv = 2.0 * M * 3.0 * dd, w_o = 2.0 * M * dd, w_mlp = 2.0 * M * 4.0 * dd;
+  const double w_attn = 4.0 * d * ps.N *
+                        ((double)ps.R * pos_base + 0.5 * (double)ps.R * (ps.R + 1));
+  const double w_embed = 2.0 * Md * c.C;
+  (void)Md;
   if (pre && xs && xs->wait_embed) AF_HIP(hipStreamWaitEvent(st, xs->wait_embed, 0));
   if (pre)
-    LAUNCH(K_EMBED, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
+    LAUNCHW(K_EMBED, w_embed, af::launch_embed(ps.src, ps.x_last, bw.w_in, bw.b_in, bw.pos, h,
                                      ps.N, ps.R, c.C, d, ps.L, ps.s, ps.dir,
                                      pos_base, st));
   if (pre && xs && xs->rec_embed) AF_HIP(hipEventRecord(xs->rec_embed, st));
@@ -344,14 +365,14 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       af::QKVDst dst{q, kc, vt, ps.R, d, p->dh, c.n_heads, p->Lcap, pos_base, q_lo, kc_lo, vt_lo};
       if (l > 0 || pre) {
         if (xs) AF_HIP(wait_ev(xs->wait_qkv, l));
-        LAUNCH(K_QKV, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
+        LAUNCHW(K_QKV, w_qkv, af::launch_gemm_qkv(true, a, a_lo, lw.w_qkv, lw.b_qkv, M, 3 * d, d, dst, st));
         if (xs) AF_HIP(rec_ev(xs->rec_qkv, l));
       }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
       af::AttnSplit asp{q_lo, kc_lo, vt_lo, att_lo};
       if (l > 0 || pre) {
         if (xs) AF_HIP(wait_ev(xs->wait_attn, l));
-        LAUNCH(K_ATTN, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
+        LAUNCHW(K_ATTN, w_attn, af::launch_attention(true, q, kc, vt, att, (float*)(ws + w.attn_part),
                                             (unsigned*)(ws + w.tickets), ps.N, ps.R,
                                             c.n_heads, p->dh, d, p->Lcap, pos_base,
                                             st, sp ? &asp : nullptr));
@@ -359,12 +380,12 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
       }
       if (!post) return AF_OK;
       int S = 1;
-      LAUNCH(K_O, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st, o_planes));
+      LAUNCHW(K_O, w_o, af::launch_gemm_partial(att, att_lo, lw.w_o, slab, M, d, d, &S, st, o_planes));
       LAUNCH(K_LN, af::launch_resid_ln(slab, S, lw.b_o, h, lw.ln2_g, lw.ln2_b, a, true, a_lo,
                                        M, d, st));
-      LAUNCH(K_MLP1, af::launch_gemm_gelu(true, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
+      LAUNCHW(K_MLP1, w_mlp, af::launch_gemm_gelu(true, a, a_lo, lw.w_1, lw.b_1, u, u_lo, M, p->dmlp,
                                           d, st));
-      LAUNCH(K_MLP2, af::launch_gemm_partial(u, u_lo, lw.w_2, slab, M, d, p->dmlp, &S, st,
+      LAUNCHW(K_MLP2, w_mlp, af::launch_gemm_partial(u, u_lo, lw.w_2, slab, M, d, p->dmlp, &S, st,
                                                      mlp2_planes));
       if (l + 1 < c.n_layers) {
         const LayerW& nx = bw.layers[l + 1];
@@ -384,20 +405,20 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
                      nullptr, nullptr};
       if (l > 0 || pre) {
         LAUNCH(K_LN, af::launch_layernorm(h, lw.ln1_g, lw.ln1_b, a, false, M, d, st));
-        LAUNCH(K_QKV, af::launch_gemm_qkv(false, a, nullptr, lw.w_qkv, lw.b_qkv, M, 3 * d, d,
+        LAUNCHW(K_QKV, w_qkv, af::launch_gemm_qkv(false, a, nullptr, lw.w_qkv, lw.b_qkv, M, 3 * d, d,
                                           dst, st));
       }
       if (ps.kv_only && l == c.n_layers - 1) return AF_OK;
       if (l > 0 || pre)
-        LAUNCH(K_ATTN, af::launch_attention(false, q, kc, vt, att, nullptr, nullptr, ps.N,
+        LAUNCHW(K_ATTN, w_attn, af::launch_attention(false, q, kc, vt, att, nullptr, nullptr, ps.N,
                                             ps.R, c.n_heads, p->dh, d, p->Lcap, pos_base, st));
       if (!post) return AF_OK;
-      LAUNCH(K_O, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
+      LAUNCHW(K_O, w_o, af::launch_gemm_resid(false, att, nullptr, lw.w_o, lw.b_o, h, M, d, d,
                                         nullptr, st));
       LAUNCH(K_LN, af::launch_layernorm(h, lw.ln2_g, lw.ln2_b, a, false, M, d, st));
-      LAUNCH(K_MLP1, af::launch_gemm_gelu(false, a, nullptr, lw.w_1, lw.b_1, u, nullptr, M,
+      LAUNCHW(K_MLP1, w_mlp, af::launch_gemm_gelu(false, a, nullptr, lw.w_1, lw.b_1, u, nullptr, M,
                                           p->dmlp, d, st));
-      LAUNCH(K_MLP2, af::launch_gemm_resid(false, u, nullptr, lw.w_2, lw.b_2, h, M, d,
+      LAUNCHW(K_MLP2, w_mlp, af::launch_gemm_resid(false, u, nullptr, lw.w_2, lw.b_2, h, M, d,
                                            p->dmlp, nullptr, st));
     }
     LAUNCH(K_LN, af::launch_layernorm(h, bw.ln_f_g, bw.ln_f_b, hf, false, M, d, st));
@@ -410,16 +431,19 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   if (af::head_mfma_supported(c.C, d)) {
     const int rh = ps.R - ps.hskip, mh = ps.N * rh;
     fa.head_splits = af::head_mfma_splits(mh, d);
-    LAUNCH(K_HEAD, af::launch_head_mfma(hf, bw.w_head, head, mh, c.C, d, fa.head_splits, st,
+    LAUNCHW(K_HEAD, 4.0 * mh * c.C * d, af::launch_head_mfma(hf, bw.w_head, head, mh, c.C, d, fa.head_splits, st,
                                         rh, ps.R, ps.hskip));
   } else {
     if (ps.hskip != 0) return fail(AF_ERR_UNSUPPORTED, "head row offset needs C % 8 == 0");
     fa.head_splits = af::head_splits(M, 2 * c.C, d);
-    LAUNCH(K_HEAD, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
+    LAUNCHW(K_HEAD, 4.0 * M * c.C * d, af::launch_gemm_f32_planes(hf, bw.w_head, head, M, 2 * c.C, d,
                                               fa.head_splits, st));
   }
   if (xs && xs->wait_affine) AF_HIP(hipStreamWaitEvent(st, xs->wait_affine, 0));
-  LAUNCH(K_AFFINE, af::launch_affine(mode, fa, st));
+  // bytes: mu, raw, z (or x) read and x (or z) written; the inverse also
+  // reads the previous iterate
+  LAUNCHW(K_AFFINE, (mode == 0 ? 20.0 : 16.0) * c.C * ps.N * (ps.R - ps.hskip),
+          af::launch_affine(mode, fa, st));
   if (xs && xs->rec_affine) AF_HIP(hipEventRecord(xs->rec_affine, st));
   return AF_OK;
 }
@@ -446,9 +470,19 @@ af_status check_ws(const af_plan* p, int N, int rows, void* ws, size_t ws_bytes,
 
 // Pinned, host-coherent [N][2] residual buffer that the affine kernel writes
 // directly, so the stop test needs no copy command.
+void destroy_entry(GraphEntry& e);
+
 af_status ensure_host_res(af_plan* p, int N) {
   if (p->res_cap >= N) return AF_OK;
-  if (p->host_res) (void)hipHostFree(p->host_res);
+  if (p->host_res) {
+    // Captured updates bake in the sequence and tag words at 2 * res_cap
+    // floats past the buffer, and a new buffer may land at the old address:
+    // let outstanding work finish, then drop every graph with the old buffer.
+    AF_HIP(hipDeviceSynchronize());
+    for (GraphEntry& e : p->gcache) destroy_entry(e);
+    p->gcache.clear();
+    (void)hipHostFree(p->host_res);
+  }
   p->host_res = p->host_res_dev = nullptr;
   p->res_cap = 0;
   AF_HIP(hipHostMalloc((void**)&p->host_res, ((size_t)N * 2 + 64) * sizeof(float),
@@ -665,10 +699,14 @@ size_t af_cache_bytes(const af_plan* p, int batch) {
 }
 
 af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
-                     int L, void* ws_, size_t ws_bytes, void* stream) {
+                     int L, int frames_per_entry, int flags, void* ws_, size_t ws_bytes,
+                     void* stream) {
   if (!p || !x || !z || !logdet) return fail(AF_ERR_ARG, "NULL argument");
   if (any_misaligned(x, z)) return fail(AF_ERR_ARG, "x and z must be 16-byte aligned");
   if (N < 1 || L < 1 || L > p->cfg.max_len) return fail(AF_ERR_ARG, "need N >= 1 and 1 <= L <= max_len");
+  if (frames_per_entry < 1 || N % frames_per_entry)
+    return fail(AF_ERR_ARG, "frames_per_entry must be >= 1 and divide N");
+  if (flags & ~(AF_FWD_ACCUMULATE | AF_FWD_CHECK_FINITE)) return fail(AF_ERR_ARG, "unknown flags");
   if (x == z) return fail(AF_ERR_ARG, "x and z may not alias");
   WsLayout w;
   if (af_status s = check_ws(p, N, L, ws_, ws_bytes, &w)) return s;
@@ -676,7 +714,10 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
   char* ws = (char*)ws_;
   const int C = p->cfg.C;
   AF_HIP(clear_counters(w, ws, st));
-  AF_HIP(af::launch_fill_u32(logdet, 0u, (size_t)N, st));
+  if (!(flags & AF_FWD_ACCUMULATE))
+    AF_HIP(af::launch_fill_u32(logdet, 0u, (size_t)(N / frames_per_entry), st));
+  // the affine kernel tags the first stack block that produced a non-finite z
+  unsigned* bad = (unsigned*)(ws + w.counter) + 1;
   float* xtmp = (float*)(ws + w.xtmp);
   const float* cur = x;
   for (int t = 0; t < p->T; ++t) {
@@ -688,9 +729,18 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
                       af::head_splits(N * L, 2 * C, p->cfg.d), nullptr,
                       const_cast<float*>(cur), dst,
                       N, L, C, L, 0, t & 1, (float*)(ws + w.partials),
-                      (float*)(ws + w.res), (unsigned*)(ws + w.counter), logdet};
+                      (float*)(ws + w.res), (unsigned*)(ws + w.counter), logdet,
+                      bad, (unsigned)(t + 1)};
+    aa.ld_group = frames_per_entry;
     if (af_status s = run_net(p, p->blocks[t], ps, ws, w, st, &aa, 1)) return s;
     cur = dst;
+  }
+  if (flags & AF_FWD_CHECK_FINITE) {
+    unsigned tag = 0;
+    AF_HIP(hipStreamSynchronize(st));
+    AF_HIP(hipMemcpy(&tag, bad, sizeof(tag), hipMemcpyDeviceToHost));
+    if (tag != 0)
+      return fail(AF_ERR_NONFINITE, "non-finite z in stack block " + std::to_string(tag - 1));
   }
   return AF_OK;
 }
@@ -824,6 +874,15 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   for (int i = 0; i < 4; ++i) seq_host_words[i] = 0u;   // no update of this plan is in flight
   unsigned n_updates = 0;
   unsigned n_split = 0;   // updates that ran as a row split (half B's publications)
+  bool last_split = false;
+  p->last_res.clear();
+  // keep the residual pairs the host saw last (both halves of a split added)
+  auto record_res = [&]() {
+    const volatile float* hr = p->host_res;
+    p->last_res.assign((size_t)2 * N, 0.f);
+    for (int n = 0; n < 2 * N; ++n)
+      p->last_res[n] = last_split ? hr[n] + hr[2 * N + n] : hr[n];
+  };
 
   const float* zin = z;
   for (int t = p->T - 1; t >= 0; --t) {
@@ -930,6 +989,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         }
         ++n_updates;
         if (split) ++n_split;
+        last_split = split;
         // the residual is read only for the stop test; at the cap (and in
         // forced-count mode) a non-finite residual is caught through the
         // sticky tag read once at the end
@@ -967,6 +1027,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       }
       AF_HIP(join_b());   // later work on st sees all of half B's writes
       if (nonfinite) {
+        record_res();
         iters[t * nb + b] = k;
         return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +
                                           ", Jacobi block " + std::to_string(b));
@@ -993,6 +1054,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   // draining the stream, so work enqueued behind it (a speculative prefix)
   // keeps running while the call returns.
   if (af_status e = wait_update(p, n_updates, st, n_split ? sb : nullptr, n_split)) return e;
+  record_res();
   unsigned tag = seq_host_words[2];
   if (tag == 0) tag = seq_host_words[3];
   if (tag != 0) {
@@ -1018,6 +1080,7 @@ af_status af_profile_enable(af_plan* p, const char* kernel_class) {
   }
   p->prof_class = cls;
   p->prof_n = 0;
+  p->prof_work = 0.0;
   return AF_OK;
 }
 
@@ -1027,8 +1090,9 @@ af_status af_profile_disable(af_plan* p) {
   return AF_OK;
 }
 
-af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
+af_status af_profile_read(af_plan* p, int* launches, double* total_ms, double* work) {
   if (!p || !launches || !total_ms) return fail(AF_ERR_ARG, "NULL argument");
+  if (work) *work = p->prof_work;
   double tot = 0.0;
   for (int i = 0; i < p->prof_n; ++i) {
     AF_HIP(hipEventSynchronize(p->ev[2 * i + 1]));
@@ -1038,6 +1102,15 @@ af_status af_profile_read(af_plan* p, int* launches, double* total_ms) {
   }
   *launches = p->prof_n;
   *total_ms = tot;
+  return AF_OK;
+}
+
+af_status af_plan_last_residual(const af_plan* p, int N, float* num_den) {
+  if (!p || !num_den) return fail(AF_ERR_ARG, "NULL argument");
+  if (p->last_res.empty()) return fail(AF_ERR_ARG, "no inverse call has finished on this plan");
+  if ((size_t)2 * N != p->last_res.size())
+    return fail(AF_ERR_ARG, "N differs from the batch of the last inverse call");
+  std::memcpy(num_den, p->last_res.data(), p->last_res.size() * sizeof(float));
   return AF_OK;
 }
 

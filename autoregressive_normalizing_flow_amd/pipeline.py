@@ -58,9 +58,13 @@ class DeepShallowFlow:
         plus the shallow log-dets of the sample's frames."""
         N, L, C = x.shape
         nf = self._split(x)
-        u_f, ld_s = self.shallow.forward(x.reshape(N * nf, self.F, C).contiguous())
-        z, ld_d = self.deep.forward(u_f.reshape(N, L, C).contiguous())
-        return z, ld_d + ld_s.reshape(N, nf).sum(dim=1)
+        # the shallow stack over all frames sums each sequence's frame factors
+        # into logdet[n]; the deep block's forward then adds its own term
+        u_f, ld = self.shallow.forward(x.reshape(N * nf, self.F, C).contiguous(),
+                                       frames_per_entry=nf)
+        z, ld = self.deep.forward(u_f.reshape(N, L, C).contiguous(), logdet=ld,
+                                  accumulate=True)
+        return z, ld
 
     # inverse ----------------------------------------------------------------
     def _deep_frame(self, z, u, n, tau, max_iters, stream):

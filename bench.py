@@ -2,7 +2,7 @@
 """Benchmark: latent tokens/s inverted by video-aware block-wise Jacobi on one
 MI355X, with the roofline of the dominant kernel and the CPU oracle beside it.
 
-    python bench.py [--steps K] [--warmup W] [--workload frame480p]
+    python bench.py [--steps K] [--warmup W] [--workload video21]
 
 A step is one af_inverse_jacobi call over one batch of synthetic latents
 (every kernel of the hot path: shift+embed, LayerNorm, QKV/O/MLP GEMMs,
@@ -10,15 +10,24 @@ attention over the KV cache, head, fused affine/residual kernel, host stop
 test).  Inputs are resident in HBM before timing.  Prints ONE JSON line.
 
 Workloads (autoregressive_normalizing_flow_amd.synth.WORKLOADS):
-  frame480p      one 1560-token frame, 8 layers d=1024, B=1560   (default)
-  video21        21 frames, block = frame, previous-frame warm start
+  video21        21 frames x 1560 tokens, block = frame, previous-frame warm
+                 start, 8 layers d=1024                              (default)
+  frame480p      one 1560-token frame, 8 layers d=1024, B=1560
   shallow_stack  T=4 alternating blocks, 2 layers d=512, 21 frames batched
   wide_prefix    4 layers d=4096, 2-frame prefix, batch 2
   tiny_f32       one 8x8 frame, fp32
+
+Other modes: --schedule-sweep, --pipeline, --cpu-baselines (the oracle on
+every workload), --copy-calibration, and --summarize-trace /
+--summarize-counters (turn rocprofv3 CSV output into the summaries kept under
+profiles/).
 """
 import argparse
+import csv
+import glob
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,14 +41,10 @@ PEAK_F32_TFLOPS = 157.3      # MI355X fp32 (vector / matrix)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "latent tokens/s inverted via block Jacobi (1 GPU); % MFMA/HBM peak; iters/blk"
 GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2", "gemm_head")
+FLOP_CLASSES = GEMM_CLASSES + ("attention", "embed")
 ALL_CLASSES = GEMM_CLASSES + ("attention", "layernorm", "embed", "affine")
-
-
-def gemm_flops_per_launch(cls, M, cfg):
-    d, C = cfg.d, cfg.C
-    return {"gemm_qkv": 2 * M * 3 * d * d, "gemm_o": 2 * M * d * d,
-            "gemm_mlp1": 2 * M * 4 * d * d, "gemm_mlp2": 2 * M * d * 4 * d,
-            "gemm_head": 2 * M * 2 * C * d}[cls]
+DEFAULT_WORKLOAD = "video21"
+OTHER_CONFIGS = ("tiny_f32", "frame480p", "shallow_stack", "wide_prefix")
 
 
 class Runner:
@@ -94,35 +99,126 @@ class Runner:
         return self.x
 
 
-def cpu_baseline(runner, synth, budget_tokens):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workload: block-wise Jacobi on the first `budget_tokens` tokens of sample 0
-    with the same tau (for the stack, the last block of the stack only)."""
+# ---------------------------------------------------------------------------
+# the oracle on the host cores
+# ---------------------------------------------------------------------------
+def cpu_info():
+    """CPU model, BLAS library and the threads it uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     from threadpoolctl import threadpool_info
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+    b = blas[0] if blas else {}
+    return {"cpu": model, "host_cpus": len(os.sched_getaffinity(0)),
+            "blas": f"{b.get('internal_api', '?')} {b.get('version', '')} "
+                    f"{b.get('architecture', '')}".strip(),
+            "threads": int(b.get("num_threads", 1))}
+
+
+def oracle_sample(w, params, z, synth, max_tokens):
+    """The oracle's same-schedule block-wise Jacobi on a bounded part of a
+    workload: the first Jacobi block of sample 0 (for the video, frame 0 with
+    its zero init; for a stack, the last stack block, which the inverse runs
+    first; with a prefix, the prefix encoded first, outside the timing), cut
+    to max_tokens.  Returns (seconds, tokens, iters, description)."""
     from oracle import af_oracle as O
-    w, cfg = runner.w, runner.cfg
-    S = min(budget_tokens, w.length)
-    z = runner.z[:1, :S].detach().cpu().numpy().astype(np.float64)
+    cfg = w.block
+    S = min(max_tokens, w.jacobi_block, w.length)
+    zz = np.asarray(z[:1, :S], dtype=np.float64)
     t_idx = w.n_blocks - 1
-    p64 = O.to64(runner.params[t_idx])
+    p64 = O.to64(params[t_idx])
     kw = {}
-    if w.prefix:  # keep the sample small: encode a prefix of equal length
-        xp = synth.normal((1, w.prefix, cfg.C), 2)[:, -S:].astype(np.float64)
+    desc = (f"oracle fp64 block-Jacobi, same schedule: the first Jacobi block of sample 0 "
+            f"({S} tokens, tau={w.tau}")
+    if w.prefix:
+        xp = synth.normal((1, w.prefix, cfg.C), 2).astype(np.float64)
         cache, x_last = O.prefill(p64, xp, cfg.n_heads)
-        kw = dict(pos0=S, cache=cache, x_last=x_last)
+        kw = dict(pos0=w.prefix, cache=cache, x_last=x_last, init="given",
+                  x_init=xp[:, -w.length:][:, :S])
+        desc += f", after the {w.prefix}-token prefix (encoded untimed), given init"
+    if w.n_blocks > 1:
+        desc += f", stack block {t_idx} of {w.n_blocks}"
     t0 = time.perf_counter()
-    _, it = O.inverse_jacobi_block(p64, z, cfg.n_heads, S, w.tau,
+    _, it = O.inverse_jacobi_block(p64, zz, cfg.n_heads, S, w.tau,
                                    direction=O.direction_of(t_idx), **kw)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2), "iters": it.tolist(),
-            "sample": f"oracle fp64 block-Jacobi of the first {S} tokens of sample 0 "
-                      f"(one Jacobi block of {S}, tau={w.tau}"
-                      + (", after a prefix of equal length" if w.prefix else "")
-                      + (f", stack block {t_idx} only" if w.n_blocks > 1 else "") + ")"}
+    return dt, S, it.tolist(), desc + ")"
 
 
+def cpu_baseline(w, params, z, synth, max_tokens):
+    """The fp64 oracle (as it stands) timed on the host cores on a bounded
+    sample of the same workload (oracle_sample); z is the workload's input on
+    the host."""
+    dt, S, it, desc = oracle_sample(w, params, z, synth, max_tokens)
+    info = cpu_info()
+    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": info["threads"],
+            "kind": "oracle", "seconds": round(dt, 2), "iters": it, "sample": desc,
+            "cpu": info["cpu"], "blas": info["blas"]}
+
+
+def oracle_sequential_rate(w, params, z, synth, n_tokens):
+    """Exact sequential inverse (token by token, 'standard AR decoding') of
+    the first n_tokens of sample 0 of a workload's first Jacobi block on the
+    host cores: seconds per token (after the prefix, when there is one)."""
+    from oracle import af_oracle as O
+    cfg = w.block
+    t_idx = w.n_blocks - 1
+    p64 = O.to64(params[t_idx])
+    zz = np.asarray(z[:1, :n_tokens], dtype=np.float64)
+    kw = {}
+    if w.prefix:
+        xp = synth.normal((1, w.prefix, cfg.C), 2).astype(np.float64)
+        cache, x_last = O.prefill(p64, xp, cfg.n_heads)
+        kw = dict(pos0=w.prefix, cache=cache, x_last=x_last)
+    t0 = time.perf_counter()
+    O.inverse_sequential_block(p64, zz, cfg.n_heads, O.direction_of(t_idx), **kw)
+    return (time.perf_counter() - t0) / n_tokens
+
+
+def cpu_baselines(torch, synth, jacobi_tokens, seq_tokens):
+    """The oracle on every workload, on the host cores: the same-schedule
+    Jacobi on the first Jacobi block (bounded), and the exact sequential
+    inverse timed on its first seq_tokens tokens and extrapolated linearly to
+    the workload's tokens (labelled)."""
+    out = {"host": cpu_info()}
+    for name in ("tiny_f32", "frame480p", "video21", "shallow_stack", "wide_prefix"):
+        w = synth.WORKLOADS[name]
+        params = synth.make_params(w.block, 0, n_blocks=w.n_blocks)
+        if w.x_noise is not None:
+            from oracle import af_oracle as O
+            x = synth.noisy_latents((1, w.length, w.block.C), 2, w.x_noise)
+            z, _ = O.forward_stack([O.to64(p) for p in params], x, w.block.n_heads)
+        else:
+            z = synth.normal((w.batch, w.length, w.block.C), 1)
+        dt, S, it, desc = oracle_sample(w, params, z, synth, jacobi_tokens)
+        row = {"jacobi": {"tokens_per_s": round(S / dt, 2), "seconds": round(dt, 2),
+                          "iters": it, "sample": desc}}
+        n = min(seq_tokens, w.length)
+        spt = oracle_sequential_rate(w, params, z, synth, n)
+        total = w.batch * w.length * w.n_blocks
+        row["sequential"] = {
+            "tokens_per_s": round(1.0 / spt, 3), "timed_tokens": n,
+            "seconds_per_token": round(spt, 4),
+            "workload_seconds": round(spt * total, 1),
+            "extrapolated": n < w.length or w.batch > 1 or w.n_blocks > 1,
+            "note": ("timed on the first tokens of sample 0 (one stack block), scaled "
+                     "linearly to every token, sample and stack block")}
+        out[name] = row
+        print(json.dumps({name: row}), file=sys.stderr, flush=True)
+        del params
+    return out
+
+
+# ---------------------------------------------------------------------------
+# kernel-level measurements
+# ---------------------------------------------------------------------------
 def affine_sweep(torch, binding, tokens, reps=5):
     """The fused affine kernel alone (inverse mode), HBM-cold: `tokens` rows of
     C=48, buffers far larger than the 256 MB Infinity Cache.  Algorithmic
@@ -152,7 +248,6 @@ def affine_sweep(torch, binding, tokens, reps=5):
 
 def kernel_sources_hash():
     """Short hash of the HIP kernel sources (names and contents)."""
-    import glob
     import hashlib
     csrc = os.path.join(ROOT, "autoregressive_normalizing_flow_amd", "csrc")
     h = hashlib.sha256()
@@ -194,6 +289,39 @@ def timed_call(torch, fn, reps):
     return float(np.median(ts)), out
 
 
+# ---------------------------------------------------------------------------
+# schedules
+# ---------------------------------------------------------------------------
+def asymmetric_schedule(vplan, zv, F, B0, B1, tau):
+    """Frame 0 with blocks of B0 from zeros; every later frame n with blocks
+    of B1 kept inside the frame, warm-started from frame n-1's converged
+    tokens, attending to the K/V of frames 0..n-1 (关键设计 3: first frame
+    B = 64, later frames B = 512).  Each frame is one af_inverse_jacobi call;
+    the K/V of the frame's last Jacobi block (which that call leaves
+    unrefreshed) are then recomputed from its final tokens."""
+    nf = zv.shape[1] // F
+    x = zv.new_empty(zv.shape)
+    its = []
+    for n in range(nf):
+        zn = zv[:, n * F:(n + 1) * F]
+        if n == 0:
+            xn, it = vplan.inverse_jacobi(zn, B0, tau)
+            last = (F - 1) // B0 * B0
+        else:
+            xn, it = vplan.inverse_jacobi(zn, B1, tau, init="given",
+                                          x_init=x[:, (n - 1) * F:n * F],
+                                          prefix_len=n * F,
+                                          x_last=x[:, n * F - 1].contiguous())
+            last = (F - 1) // B1 * B1
+        x[:, n * F:(n + 1) * F].copy_(xn)
+        its.append(it[0].copy())
+        if n + 1 < nf:
+            P = n * F + last
+            vplan.refresh_kv(x[:, P:(n + 1) * F].contiguous(), prefix_len=P,
+                             x_last=x[:, P - 1].contiguous() if P > 0 else None)
+    return x, its
+
+
 def schedule_sweep(torch, binding, synth, reps):
     """Jacobi block size, warm start and schedule on the deep block (the
     frame480p and video21 shapes): tokens/s and iterations per block.  B = 1
@@ -220,24 +348,17 @@ def schedule_sweep(torch, binding, synth, reps):
     T = v.length // F
     vplan = binding.AFPlan(v.block, synth.make_params(v.block, 0))
     zv = dev(synth.normal((1, v.length, v.block.C), 1))
+    vplan.workspace(1, F)
     warm = {}
     for init in ("zero", "prev_frame"):
         kw = dict(init=init, frame_len=F) if init == "prev_frame" else {}
         ms, (xv, it) = timed_call(torch, lambda: vplan.inverse_jacobi(zv, F, v.tau, **kw), 1)
         warm[init] = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1),
                       "iters": it[0].tolist()}
-    # asymmetric schedule: frame 0 with B = 64, then its K/V as the prefix of
-    # frames 1.. solved with B = 512 and the previous-frame warm start
-    def asym():
-        x0, it0 = vplan.inverse_jacobi(zv[:, :F].contiguous(), 64, v.tau)
-        vplan.prefill(x0, rows=512)
-        x1, it1 = vplan.inverse_jacobi(zv[:, F:].contiguous(), 512, v.tau, init="prev_frame",
-                                       frame_len=F, prefix_len=F, x_last=x0[:, -1].contiguous())
-        return it0, it1
-    ms, (it0, it1) = timed_call(torch, asym, 1)
+    ms, (_, its) = timed_call(torch, lambda: asymmetric_schedule(vplan, zv, F, 64, 512, v.tau), 1)
     asym_row = {"ms": round(ms, 2), "tokens_per_s": round(v.length / ms * 1e3, 1),
-                "frame0_B64_iters_total": int(it0.sum()),
-                "frames1_B512_iters_total": int(it1.sum()), "frames": T}
+                "frame0_B64_iters_total": int(its[0].sum()),
+                "frames1_B512_iters": [it.tolist() for it in its[1:]], "frames": T}
     return {"block_sweep_frame480p": rows, "warm_start_video21": warm,
             "asymmetric_video21": asym_row}
 
@@ -288,16 +409,171 @@ def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=Fals
     return out
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> the summaries kept under profiles/
+# ---------------------------------------------------------------------------
+def _read_csv(pattern):
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise SystemExit(f"no file matches {pattern}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_trace(d, top):
+    """Markdown table of a --kernel-trace --stats run: kernel, calls, total
+    ms, average us and share, from <d>/**/*kernel_stats.csv; and the busy time
+    (union of the kernels' intervals) from *kernel_trace.csv."""
+    stats = _read_csv(os.path.join(d, "**", "*kernel_stats.csv"))
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    tot = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines = ["| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats[:top]:
+        name = r["Name"][:110]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    tr = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if tr:
+        iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                    for r in _read_csv(os.path.join(d, "**", "*kernel_trace.csv")))
+        busy, cur_s, cur_e = 0, None, None
+        for s, e in iv:
+            if cur_e is None or s > cur_e:
+                if cur_e is not None:
+                    busy += cur_e - cur_s
+                cur_s, cur_e = s, e
+            else:
+                cur_e = max(cur_e, e)
+        if cur_e is not None:
+            busy += cur_e - cur_s
+        lines.append("")
+        lines.append(f"Sum of kernel durations {tot / 1e6:.1f} ms; busy (union of intervals) "
+                     f"{busy / 1e6:.1f} ms.")
+    print("\n".join(lines))
+
+
+# kernel class of a kernel name in the inverse path (the forward's split-mode
+# kernels, which carry bf16 hi + lo operands, are listed but not classed)
+CLASS_PATTERNS = {
+    "attention": ("attn_bf16_kernel", "false>"),
+    "affine": ("affine_kernel<0", ""),
+}
+
+
+def _class_of(name):
+    for cls, (a, b) in CLASS_PATTERNS.items():
+        if a in name and b in name:
+            return cls
+    return None
+
+
+def summarize_counters(d, calib_dir, workload):
+    """Per-kernel medians of the counters of one or more --pmc passes under
+    <d> (FETCH_SIZE, WRITE_SIZE: KiB per dispatch, scaled by what the same
+    counters read for a plain copy of known size under calib_dir), and the
+    'traffic-per-launch' lines bench.py reads for the roofline."""
+    rows = _read_csv(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        key = (r["Kernel_Name"], r["Counter_Name"])
+        per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+        per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    scale = {"FETCH_SIZE": 1.0, "WRITE_SIZE": 1.0}
+    if calib_dir:
+        crow = _read_csv(os.path.join(calib_dir, "**", "*counter_collection.csv"))
+        copy_kib = 262144.0   # 256 MiB read and 256 MiB written per dispatch
+        for cn in scale:
+            vals = {}
+            for r in crow:
+                if r["Counter_Name"] == cn and "copy" in r["Kernel_Name"].lower():
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(
+                        r["Counter_Value"])
+            if vals:
+                scale[cn] = copy_kib / statistics.median(vals.values())
+    counters = sorted({k[1] for k in per})
+    kernels = sorted({k[0] for k in per})
+    print(f"Scale: FETCH_SIZE x {scale['FETCH_SIZE']:.3f}, WRITE_SIZE x "
+          f"{scale['WRITE_SIZE']:.3f} (a plain 256 MiB copy)\n")
+    print("| kernel | dispatches | " + " | ".join(f"{c} (median)" for c in counters) + " |")
+    print("|---|---:|" + "---:|" * len(counters))
+    cls_bytes = {}
+    for k in kernels:
+        vals = [per.get((k, c), {}) for c in counters]
+        n = max(len(v) for v in vals)
+        cells = [f"{statistics.median(v.values()):.0f}" if v else "" for v in vals]
+        print(f"| `{k[:100]}` | {n} | " + " | ".join(cells) + " |")
+        cls = _class_of(k)
+        if cls and ("FETCH_SIZE" in counters or "WRITE_SIZE" in counters):
+            for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                v = per.get((k, cn), {})
+                if v:
+                    cls_bytes.setdefault(cls, {}).setdefault(cn, []).extend(
+                        x * 1024 * scale[cn] for x in v.values())
+    sha = kernel_sources_hash()
+    print()
+    for cls, b in cls_bytes.items():
+        rd = statistics.mean(b.get("FETCH_SIZE", [0.0]))
+        wr = statistics.mean(b.get("WRITE_SIZE", [0.0]))
+        print(f"    traffic-per-launch {cls} {int(rd + wr)} read={int(rd)} write={int(wr)} "
+              f"sources={sha}")
+
+
+# ---------------------------------------------------------------------------
+# the benchmark
+# ---------------------------------------------------------------------------
+def roofline_of(cls, n, ms, work, cfg, workload, steps):
+    """The roofline entry of one kernel class from its profiled launches."""
+    avg_ms = ms / max(n, 1)
+    per_launch = work / max(n, 1)
+    if cls == "affine":
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+        return {"kernel": cls, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": counter_traffic(workload, cls), "bytes_per_launch": per_launch,
+                "avg_ms": round(avg_ms, 5), "launches": n}
+    peak = PEAK_BF16_TFLOPS if (cfg.dtype == "bf16" and cls not in ("gemm_head", "embed")) \
+        else PEAK_F32_TFLOPS
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    return {"kernel": cls, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": counter_traffic(workload, cls), "flops_per_launch": round(per_launch),
+            "avg_ms": round(avg_ms, 5), "launches": n}
+
+
+def quick_config(name, torch, binding, synth, steps, warmup):
+    """tokens/s and iterations of another workload (a few steps)."""
+    r = Runner(name, torch, binding, synth)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    out = {"tokens_per_s": round(r.tokens_per_step / dt, 1), "ms_per_step": round(dt * 1e3, 3),
+           "iters_per_block": r.iters.tolist(), "tokens": r.tokens_per_step}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="frame480p")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
-                    help="oracle sample size for the CPU baseline")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-tokens", type=int, default=1560,
+                    help="oracle sample size for the CPU baseline (tokens of the first "
+                         "Jacobi block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the short runs of the other workloads")
     ap.add_argument("--no-row-split", action="store_true",
                     help="run every Jacobi update as one pass (no two-stream row split)")
     ap.add_argument("--fused-refresh", action="store_true",
@@ -314,11 +590,29 @@ def main():
     ap.add_argument("--schedule-sweep", action="store_true",
                     help="only run the block-size / warm-start / schedule sweep "
                          "(B = 1 is the GPU sequential baseline)")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="only time the oracle on every workload (same-schedule Jacobi "
+                         "and exact sequential inverse) on the host cores")
+    ap.add_argument("--seq-tokens", type=int, default=32,
+                    help="tokens timed per workload for the sequential oracle")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel-trace summary of a rocprofv3 output folder")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the counter summary of rocprofv3 --pmc output folder(s)")
+    ap.add_argument("--calibration", metavar="DIR", default=None,
+                    help="rocprofv3 --pmc output of --copy-calibration (counter scale)")
+    ap.add_argument("--top", type=int, default=16)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; the "
               "per-GPU kernels are measured at their real shape.", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.top)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.calibration, args.workload)
+        return
 
     import torch
     if args.copy_calibration:
@@ -330,7 +624,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}))
         return
-    from autoregressive_normalizing_flow_amd import binding, synth
+    from autoregressive_normalizing_flow_amd import synth
+    if args.cpu_baselines:
+        print(json.dumps(cpu_baselines(torch, synth, args.cpu_tokens, args.seq_tokens)),
+              flush=True)
+        return
+    from autoregressive_normalizing_flow_amd import binding
     binding.load_library()
     assert torch.cuda.is_available(), "no GPU"
     if args.pipeline:
@@ -351,20 +650,8 @@ def main():
         r.step()
     torch.cuda.synchronize()
 
-    # per-class breakdown: one untimed profiled step per class
-    breakdown = {}
-    for cls in ALL_CLASSES:
-        r.plan.profile_enable(cls)
-        r.step()
-        n, ms = r.plan.profile_read()
-        r.plan.profile_disable()
-        breakdown[cls] = {"launches": n, "ms": round(ms, 4)}
-    dominant = max(GEMM_CLASSES, key=lambda c: breakdown[c]["ms"])
-
     # timed region: K steps as a user runs them (Jacobi updates launched
     # directly, or replayed as graphs with --graphs)
-    r.step()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         r.step()
@@ -372,6 +659,19 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = r.tokens_per_step / ((t1 - t0) / args.steps)
+    iters = r.iters.tolist()
+
+    # per-class breakdown: one profiled step per class (events on the launch
+    # stream of every launch of the class; algorithmic work from the library)
+    breakdown = {}
+    for cls in ALL_CLASSES:
+        r.plan.profile_enable(cls)
+        r.step()
+        n, ms, work = r.plan.profile_read_work()
+        r.plan.profile_disable()
+        breakdown[cls] = {"launches": n, "ms": round(ms, 4), "work": work}
+    dominant = max(ALL_CLASSES, key=lambda c: breakdown[c]["ms"])
+    gemm_dom = max(GEMM_CLASSES, key=lambda c: breakdown[c]["ms"])
 
     # the dominant kernel timed live by HIP events on the stream it is launched
     # on, over K more steps of the same workload; these launch directly, as
@@ -383,32 +683,23 @@ def main():
         r.step()
     torch.cuda.synchronize()
     p1 = time.perf_counter()
-    n_launch, dom_ms = r.plan.profile_read()
+    n_launch, dom_ms, dom_work = r.plan.profile_read_work()
     r.plan.profile_disable()
-
-    flops = gemm_flops_per_launch(dominant, r.M, cfg)
-    avg_ms = dom_ms / max(n_launch, 1)
-    peak = PEAK_BF16_TFLOPS if (cfg.dtype == "bf16" and dominant != "gemm_head") else PEAK_F32_TFLOPS
-    achieved = flops / (avg_ms * 1e-3) / 1e12
-    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": counter_traffic(w.name, dominant), "flops_per_launch": flops,
-                "avg_ms": round(avg_ms, 5), "launches": n_launch,
-                "timing": f"HIP events, {args.steps} direct-launch steps after the timed region",
-                "ms_per_step_profiled": round((p1 - p0) * 1e3 / args.steps, 3)}
+    roofline = roofline_of(dominant, n_launch, dom_ms, dom_work, cfg, w.name, args.steps)
+    roofline["timing"] = (f"HIP events on the launch stream, {args.steps} direct-launch steps "
+                          "after the timed region")
+    roofline["ms_per_step_profiled"] = round((p1 - p0) * 1e3 / args.steps, 3)
+    g = breakdown[gemm_dom]
+    gemm_roof = roofline_of(gemm_dom, g["launches"], g["ms"], g["work"], cfg, w.name, 1)
 
     # all GEMMs together (algorithmic flops / summed kernel time, one step)
-    g_flops = sum(gemm_flops_per_launch(c, r.M, cfg) * breakdown[c]["launches"]
-                  for c in GEMM_CLASSES)
+    g_flops = sum(breakdown[c]["work"] for c in GEMM_CLASSES)
     g_ms = sum(breakdown[c]["ms"] for c in GEMM_CLASSES)
-    # fused affine kernel in the path: 20*C bytes per token per launch
-    # (no separate launches when the affine update is fused into the head
-    # GEMM's kernel, which the gemm_head class then times)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     aff = breakdown["affine"]
-    aff_bytes = 20 * cfg.C * r.M
-    aff_gbs = aff_bytes * aff["launches"] / (aff["ms"] * 1e-3) / 1e9 if aff["ms"] else None
+    aff_gbs = aff["work"] / (aff["ms"] * 1e-3) / 1e9 if aff["ms"] else None
 
-    # forward pass (af_forward) time, untimed by the metric
+    # forward pass (af_forward) time, outside the metric
     torch.cuda.synchronize()
     f0 = time.perf_counter()
     r.plan.forward(r.x_fwd)
@@ -422,26 +713,37 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "tokens": w.length,
                    "jacobi_block": w.jacobi_block, "tau": w.tau, "init": w.init,
-                   "stack_blocks": w.n_blocks, "layers": cfg.n_layers, "d": cfg.d,
-                   "heads": cfg.n_heads, "C": cfg.C, "prefix": w.prefix},
-        "iters_per_block": r.iters.tolist(),
+                   "frame_len": w.frame_len, "stack_blocks": w.n_blocks,
+                   "layers": cfg.n_layers, "d": cfg.d, "heads": cfg.n_heads, "C": cfg.C,
+                   "prefix": w.prefix},
+        "iters_per_block": iters,
         "roofline": roofline,
+        "gemm_dominant": gemm_roof,
         "gemm_all": {"TFLOP/s": round(g_flops / (g_ms * 1e-3) / 1e12, 2) if g_ms else None,
                      "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / peak, 4) if g_ms else None},
         "affine_in_path": ({"bound": "hbm", "GB/s": round(aff_gbs, 1),
                             "frac": round(aff_gbs / PEAK_HBM_GBS, 4),
-                            "bytes_per_launch": aff_bytes} if aff_gbs is not None
-                           else {"fused_into": "gemm_head"}),
+                            "bytes_per_launch": aff["work"] / max(aff["launches"], 1)}
+                           if aff_gbs is not None else None),
         "graphs": args.graphs,
         "fused_refresh": args.fused_refresh,
         "row_split": not args.no_row_split,
-        "kernel_ms_per_step": breakdown,
+        "kernel_ms_per_step": {c: {"launches": b["launches"], "ms": b["ms"]}
+                               for c, b in breakdown.items()},
         "forward_ms": round(fwd_ms, 3),
     }
     if not args.no_sweep:
         out["affine_hbm_sweep"] = [affine_sweep(torch, binding, t) for t in (1 << 20, 1 << 22)]
+    z_host, params = r.z.detach().cpu().numpy(), r.params
+    if not args.no_other_configs:
+        del r
+        torch.cuda.empty_cache()
+        out["other_configs"] = {}
+        for name in OTHER_CONFIGS:
+            if name != w.name:
+                out["other_configs"][name] = quick_config(name, torch, binding, synth, 3, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(r, synth, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, params, z_host, synth, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define AF_ABI_VERSION 1
+#define AF_ABI_VERSION 2
 
 typedef enum {
   AF_OK = 0,
@@ -128,13 +128,29 @@ size_t af_workspace_bytes(const af_plan *p, int batch, int rows);
 size_t af_cache_bytes(const af_plan *p, int batch);
 
 /* Forward pass of the whole stack (blocks t = 0..n_blocks-1):
- * z = f(x) and logdet[n] = log|det dz/dx| = -sum over blocks, tokens and
- * channels of log sigma (STARFlow-V notes, 关键设计 1 and 损失函数).
- * x, z: [N, L, C] (may not alias); logdet: [N] (overwritten).  Needs
- * L <= max_len and ws_bytes >= af_workspace_bytes(p, N, L).  For a single
- * block the KV cache of positions 0..L-1 is left in ws. */
+ * z = f(x) and the log-determinant log|det dz/dx| = -sum over blocks, tokens
+ * and channels of log sigma (STARFlow-V notes, 关键设计 1 and 损失函数).
+ * x, z: [N, L, C] (may not alias).  Needs L <= max_len and
+ * ws_bytes >= af_workspace_bytes(p, N, L).  For a single block the KV cache
+ * of positions 0..L-1 is left in ws.
+ *   frames_per_entry G >= 1, dividing N: the N inputs are N / G sequences of
+ *     G consecutive frames each, and logdet has N / G entries; entry j receives
+ *     the log-dets of samples jG..jG+G-1, added in sample order.  G = 1 gives
+ *     one entry per sample.  With G > 1 a shallow stack run over every frame
+ *     of a sequence yields the per-sequence sum of its frames' Jacobian
+ *     factors (关键设计 1: the deep-shallow likelihood factorises into the deep
+ *     term and one shallow factor per frame).
+ *   flags: AF_FWD_ACCUMULATE adds into logdet (which then holds the other
+ *     factors, e.g. the shallow stack's sum before the deep block's forward);
+ *     without it logdet is overwritten.  AF_FWD_CHECK_FINITE makes the call
+ *     wait for its kernels and return AF_ERR_NONFINITE if any z (or log-det
+ *     term) is not finite; without it the call is stream-ordered and does not
+ *     wait, and z then holds the non-finite values unflagged. */
+#define AF_FWD_ACCUMULATE 1
+#define AF_FWD_CHECK_FINITE 2
 af_status af_forward(af_plan *p, const float *x, float *z, float *logdet,
-                     int N, int L, void *ws, size_t ws_bytes, void *stream);
+                     int N, int L, int frames_per_entry, int flags,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* Encode observed tokens into the KV cache (STARFlow-V notes, 一个完整示例:
  * I2V / V2V conditioning): runs the single block's network on the shifted
@@ -197,12 +213,18 @@ af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
  * While enabled, every launch of the named kernel class made by this plan is
  * bracketed by HIP events on the launch stream; af_profile_read synchronises
  * on those events and returns the number of launches and their summed
- * duration in milliseconds since the last enable.  Classes: "embed",
- * "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2", "gemm_head",
- * "attention", "affine".  At most 4096 launches are recorded per enable. */
+ * duration in milliseconds since the last enable, and (work may be NULL) the
+ * summed algorithmic work of those launches: flops (2 per multiply-add) for
+ * "embed", the GEMM classes and "attention" (4 d flops per unmasked (query,
+ * key) pair, STARFlow-V notes 关键设计 3: the queries of a block attend to the
+ * cached keys up to their own position), bytes for "affine" (20 C per token
+ * in an inverse update, 16 C in the forward), 0 for "layernorm".  Classes:
+ * "embed", "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2",
+ * "gemm_head", "attention", "affine".  At most 4096 launches are recorded
+ * per enable. */
 af_status af_profile_enable(af_plan *p, const char *kernel_class);
 af_status af_profile_disable(af_plan *p);
-af_status af_profile_read(af_plan *p, int *launches, double *total_ms);
+af_status af_profile_read(af_plan *p, int *launches, double *total_ms, double *work);
 
 /* ---- graph replay of the Jacobi update (opt-in) ---------------------------
  * Every update of a Jacobi block (关键设计 3) runs the same launch sequence on
@@ -277,6 +299,15 @@ af_status afk_affine(int mode, const float *head, const float *src, float *dst,
  * otherwise).  Stream-ordered. */
 af_status afk_gemm_bf16(const void *a, const void *w, const float *bias,
                         float *y, int M, int N, int K, void *stream);
+
+/* Residual of the last Jacobi update made by the last af_inverse_jacobi call
+ * of this plan that returned AF_OK or AF_ERR_NONFINITE (STARFlow-V notes,
+ * 关键设计 3, residual stop): num_den[2n] = sum (x^(k) - x^(k-1))^2 and
+ * num_den[2n+1] = sum (x^(k))^2 of sample n over that Jacobi block, as the
+ * stop test used them (a row-split update adds its two halves).  num_den is a
+ * HOST float array [N][2]; N must be the batch of that call.  AF_ERR_ARG on a
+ * NULL argument, a different N, or before any inverse call. */
+af_status af_plan_last_residual(const af_plan *p, int N, float *num_den);
 
 const char *af_status_str(af_status s);
 const char *af_last_error(void);

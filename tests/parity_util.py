@@ -13,6 +13,13 @@ from oracle import af_oracle as O
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
 TOL_LOGDET = 1e-3
+# Per-token bound beside the whole-tensor one: no single token's relative
+# error (its error norm over the C channels against its own norm) may exceed
+# five times the tensor bar.  The tensor bar bounds the root-mean-square of
+# the tokens' errors; tokens see rounding errors of the same kind, so their
+# largest relative error exceeds the mean by a small factor, while one wrong
+# token (an error of its own size) fails at once.
+TOL_BF16_TOKEN = 5 * TOL_BF16
 
 
 def say(*a):
@@ -25,6 +32,66 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def token_rel_max(a, b) -> float:
+    """Largest per-token relative error: max over (sample, token) of
+    ||a_t - b_t|| / ||b_t|| over the channel axis (token tensors [N, L, C])."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    num = np.linalg.norm(a - b, axis=-1)
+    den = np.maximum(np.linalg.norm(b, axis=-1), 1e-300)
+    return float((num / den).max())
+
+
+class Progress(list):
+    """A trace list for the oracle's Jacobi loop that prints each update as
+    it is appended (long oracle runs stay visibly alive)."""
+
+    def __init__(self, tag):
+        super().__init__()
+        self.tag = tag
+
+    def append(self, item):
+        b, k, r = item
+        print(f"  [oracle {self.tag}] block {b} update {k} r {np.max(r):.3e}", flush=True)
+        super().append(item)
+
+
+def layer0_cache(p64, x, H, chunk=1560):
+    """K/V of positions 0..P-1 for a ONE-layer block: layer 0's K and V of a
+    row depend only on that row's shifted token and position (they are
+    computed before its attention), so the oracle's network run on row chunks
+    without a cache gives exactly those rows' cache entries."""
+    assert len(p64["layers"]) == 1
+    sh = O.shift(np.asarray(x, np.float64))
+    P = sh.shape[1]
+    ks, vs = [], []
+    for c0 in range(0, P, chunk):
+        c1 = min(P, c0 + chunk)
+        _, _, kv = O.net_rows(p64, sh[:, c0:c1], np.arange(c0, c1), H, None)
+        ks.append(kv[0][0])
+        vs.append(kv[0][1])
+    return [(np.concatenate(ks, axis=2), np.concatenate(vs, axis=2))]
+
+
+def chunked_prefill(p64, x, H, chunk=520):
+    """The oracle's prefill over row chunks, each attending to the cache of
+    the chunks before it (equal to one pass over all rows: the cache
+    equivalence the oracle's pins check), so that no chunk's score matrix
+    spans the whole prefix."""
+    x = np.asarray(x, np.float64)
+    N, P, C = x.shape
+    d = p64["w_in"].shape[0]
+    sh = O.shift(x)
+    e = np.zeros((N, H, 0, d // H))
+    cache = [(e.copy(), e.copy()) for _ in p64["layers"]]
+    for c0 in range(0, P, chunk):
+        c1 = min(P, c0 + chunk)
+        _, _, kv = O.net_rows(p64, sh[:, c0:c1], np.arange(c0, c1), H, cache)
+        cache = [(np.concatenate([kc, k], axis=2), np.concatenate([vc, v], axis=2))
+                 for (kc, vc), (k, v) in zip(cache, kv)]
+    return cache, x[:, -1].copy()
 
 
 def rel_err(a, b) -> np.ndarray:

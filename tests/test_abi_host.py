@@ -24,7 +24,9 @@ def test_exports_every_header_function(lib):
     assert "af_forward" in names and "af_inverse_jacobi" in names and "af_prefill" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.af_abi_version() == 1
+    import re
+    ver = int(re.search(r"#define AF_ABI_VERSION (\d+)", open(B.HEADER).read()).group(1))
+    assert lib.af_abi_version() == ver
     assert lib.af_status_str(0) == b"AF_OK"
     assert lib.af_status_str(4) == b"AF_ERR_NONFINITE"
 
@@ -117,17 +119,24 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     iters = (ctypes.c_int32 * 16)()
     big = lib.af_workspace_bytes(h, 1, 64)
     # NULL inputs
-    assert lib.af_forward(h, None, buf, buf, 1, 64, buf, big, None) == B.AF_ERR_ARG
+    assert lib.af_forward(h, None, buf, buf, 1, 64, 1, 0, buf, big, None) == B.AF_ERR_ARG
     # L beyond max_len
     assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 65,
-                          buf, 1 << 40, None) == B.AF_ERR_ARG
+                          1, 0, buf, 1 << 40, None) == B.AF_ERR_ARG
     # workspace too small (checked before any launch)
     aligned = ctypes.c_void_p(1 << 20)
     assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
-                          aligned, 16, None) == B.AF_ERR_WORKSPACE
+                          1, 0, aligned, 16, None) == B.AF_ERR_WORKSPACE
+    # log-det entries must group whole samples; unknown flags
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 3, 64,
+                          2, 0, aligned, 1 << 40, None) == B.AF_ERR_ARG
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
+                          0, 0, aligned, 1 << 40, None) == B.AF_ERR_ARG
+    assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
+                          1, 4, aligned, 1 << 40, None) == B.AF_ERR_ARG
     # misaligned workspace
     assert lib.af_forward(h, buf, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
-                          ctypes.c_void_p((1 << 20) + 4), big, None) == B.AF_ERR_ARG
+                          1, 0, ctypes.c_void_p((1 << 20) + 4), big, None) == B.AF_ERR_ARG
 
     def inv(**kw):
         a = dict(z=buf, N=1, L=64, B=16, tau=1e-3, max_iters=0, init=0, x_init=None,
@@ -153,7 +162,7 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     assert inv(x=odd) == B.AF_ERR_ARG
     assert inv(init=1, x_init=odd) == B.AF_ERR_ARG
     assert lib.af_forward(h, odd, ctypes.c_void_p(_FAKE.ctypes.data + 64), buf, 1, 64,
-                          aligned, big, None) == B.AF_ERR_ARG
+                          1, 0, aligned, big, None) == B.AF_ERR_ARG
     assert lib.af_prefill(h, None, 1, 8, aligned, big, None) == B.AF_ERR_ARG
     lib.af_plan_destroy(h)
 
@@ -185,6 +194,16 @@ def test_refresh_kv_validation(lib):
     assert lib.af_refresh_kv(h, buf, 1, 60, 8, buf, ws, big, None) == B.AF_ERR_ARG   # past max_len
     assert lib.af_refresh_kv(h, buf, 1, 0, 0, None, ws, big, None) == B.AF_ERR_ARG
     assert lib.af_refresh_kv(h, buf, 1, 8, 0, None, ws, 16, None) == B.AF_ERR_WORKSPACE
+    lib.af_plan_destroy(h)
+
+
+def test_last_residual_needs_a_finished_call(lib):
+    st, h = make_plan(lib)
+    assert st == B.AF_OK
+    out = (ctypes.c_float * 4)()
+    assert lib.af_plan_last_residual(h, 2, out) == B.AF_ERR_ARG
+    assert lib.af_plan_last_residual(h, 2, None) == B.AF_ERR_ARG
+    assert lib.af_plan_last_residual(None, 2, out) == B.AF_ERR_ARG
     lib.af_plan_destroy(h)
 
 

@@ -92,6 +92,40 @@ def test_affine_flags_nonfinite(B):
     assert ei.value.status == B.AF_ERR_NONFINITE
 
 
+def test_forward_flags_and_grouped_logdet(B):
+    """af_forward on a stack of two blocks over six frames: with
+    frames_per_entry = 3 the two log-det entries are the sums of the oracle's
+    per-frame log-dets (关键设计 1: one shallow factor per frame); with
+    AF_FWD_ACCUMULATE they add to what the buffer held; a NaN in frame 4 is
+    reported (AF_ERR_NONFINITE, stack block 0) only when the check is asked
+    for."""
+    say("forward flags")
+    cfg, params, ps64 = problem(C=16, d=256, H=4, layers=1, max_len=40, dtype="bf16",
+                                seed=19, n_blocks=2)
+    plan = B.AFPlan(cfg, params)
+    x = synth.normal((6, 40, 16), 20)
+    zo, ldo = O.forward_stack(ps64, x, 4)
+    zg, ldg = plan.forward(to_dev(x), frames_per_entry=3, check_finite=True)
+    assert ldg.shape == (2,)
+    assert rel_l2(to_np(zg), zo) < TOL_BF16
+    sums = ldo.reshape(2, 3).sum(axis=1)
+    assert np.all(rel_err(to_np(ldg), sums) < TOL_LOGDET)
+    base = torch.tensor([1.5, -2.0], device="cuda")
+    _, lda = plan.forward(to_dev(x), logdet=base.clone(), frames_per_entry=3,
+                          accumulate=True)
+    assert np.all(rel_err(to_np(lda), sums + np.array([1.5, -2.0])) < TOL_LOGDET)
+    xb = x.copy()
+    xb[4, 9, 2] = np.nan
+    with pytest.raises(B.AFError) as ei:
+        plan.forward(to_dev(xb), check_finite=True)
+    assert ei.value.status == B.AF_ERR_NONFINITE and "stack block 0" in str(ei.value)
+    zn, _ = plan.forward(to_dev(xb))   # stream-ordered: no check, no error
+    torch.cuda.synchronize()
+    assert not np.isfinite(to_np(zn)[4]).all() and np.isfinite(to_np(zn)[:4]).all()
+    # a clean call afterwards passes the check (the tag starts at zero per call)
+    plan.forward(to_dev(x), check_finite=True)
+
+
 @pytest.mark.parametrize("tau", [1e-3, 0.0])
 def test_inverse_flags_nonfinite(B, tau):
     """A NaN latent in the second Jacobi block: reported as AF_ERR_NONFINITE
