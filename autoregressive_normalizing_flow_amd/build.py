@@ -65,5 +65,30 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_abi_sanitize_check() -> str:
+    """Host-only AddressSanitizer / UndefinedBehaviorSanitizer build of the
+    C ABI's host runtime (csrc/runtime.cpp, compiled by g++ with the HIP
+    headers) linked with the kernel objects of the last build() and the test
+    driver tests/abi_sanitize.cpp.  Returns the executable's path."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=False)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    exe = os.path.join(BUILD, "abi_sanitize")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "abi_sanitize.cpp"), os.path.join(CSRC, "runtime.cpp"),
+           *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     build()

@@ -559,6 +559,711 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   attn_bf16_body<DH, SPLIT>(a);
 }
 
+// Merge of a query tile's key-chunk partials in chunk order, MC slots per
+// memory round trip (run by the chunk that took the tile's last ticket): lane
+// (j, hh) of wave w combines query tq = 32 w + j, dimensions db*32 + 8g + 4hh
+// .. +3, and writes row t_q of the output if it is a real row.
+template <int DH>
+__device__ __forceinline__ void attn32_merge(const AttnArgs& a, int unit0, int n_chunks,
+                                             int tq, int t_q, int n, int head, int hh) {
+  constexpr int DB = DH / 32;
+  constexpr int SLOT = ATT_QT * (DH + 2);
+  constexpr int MC = DH <= 64 ? ATT_MAXC : ATT_MAXC / 2;
+  const float* tile0 = a.part + (size_t)unit0 * SLOT;
+  float m = -1e30f, l = 0.f;
+  f32x4 o[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) o[db][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < n_chunks; c0 += MC) {
+    float mc[MC], lc[MC];
+    f32x4 oc[MC][DB][4];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      const int cc = min(c0 + c, n_chunks - 1);
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(tile0 + (size_t)cc * SLOT);
+      mc[c] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rs, (ATT_QT * DH + tq) * 4, 0, ATT_SC1));
+      lc[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, (ATT_QT * DH + ATT_QT + tq) * 4, 0, ATT_SC1));
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          oc[c][db][g] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, (tq * DH + db * 32 + 8 * g + 4 * hh) * 4, 0, ATT_SC1));
+    }
+    float mg = m;
+#pragma unroll
+    for (int c = 0; c < MC; ++c)
+      if (c0 + c < n_chunks) mg = fmaxf(mg, mc[c]);
+    const float alpha = __builtin_amdgcn_exp2f(m - mg);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) o[db][g] *= alpha;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      if (c0 + c >= n_chunks) break;
+      const float w = __builtin_amdgcn_exp2f(mc[c] - mg);
+      l = fmaf(w, lc[c], l);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][g][e] = fmaf(w, oc[c][db][g][e], o[db][g][e]);
+    }
+    m = mg;
+  }
+  if (t_q < a.R) {
+    const float inv = 1.0f / l;
+    bf16* orow = a.out + ((size_t)n * a.R + t_q) * a.d + head * DH + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (bf16)(o[db][g][e] * inv);
+        *(bf16x4*)(orow + db * 32 + 8 * g) = ob;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 attention on the 32 x 32 x 16 matrix cores (v_mfma_f32_32x32x16_bf16),
+// the path of every Jacobi update.  Same work units, chunk merge and cache
+// layouts as above; per 64-key tile and wave (32 queries) it issues 8 MFMAs
+// for the scores, 4 for the row sums and 4 DH/32 for P V, each doing twice the
+// work of a 16 x 16 x 32 step for the same operand bytes.
+//
+// Lane l of a wave holds query j = l % 32 of the wave's 32 (the two halves
+// h = l / 32 hold the same query).  Operand layouts of the 32 x 32 x 16 step:
+// A lane l gives row l % 32, k = 8h .. 8h+7; B lane l gives column l % 32,
+// the same k; the accumulator's element r of lane l is row 8 (r / 4) + 4h +
+// r % 4 of column l % 32.
+//   S^T = K Q^T:  A = 32 key rows of K (16 contiguous bytes of a row), B = Q^T
+//                 (the lane's query, held in registers); lane l gets the scores
+//                 of its query for keys 8 (r / 4) + 4h + r % 4 of the block.
+//   O^T += Vt P^T: B = P^T straight from those registers: of each 16-key step
+//                 g the lane holds keys {16g + 4h + i, 16g + 8 + 4h + i}, i < 4,
+//                 as its 8 k-slots; the Vt tile is stored in LDS with each
+//                 16-key group permuted to [0-3, 8-11, 4-7, 12-15], so that the
+//                 A fragment of those keys is one 16-byte read at 16g + 8h.
+//   row sums:     an all-ones A operand sums the same bf16 P^T over the keys.
+// ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void attn32_body(const AttnArgs& a) {
+  constexpr int KS = DH / 16;                   // k-steps of the scores
+  constexpr int DB = DH / 32;                   // 32-dimension blocks of O^T
+  constexpr int KROW = DH + 8;                  // K tile row in LDS (bf16)
+  constexpr int VROW = ATT_KT + 8;              // Vt tile row in LDS (bf16)
+  constexpr int CK = ATT_KT * DH / 8 / 256;     // 16-byte chunks per thread per tile
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][ATT_KT * KROW];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][DH * VROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, hh = lane >> 5;
+  // unit -> (sample, head, query tile, chunk), as in attn_bf16_body
+  int u = blockIdx.x;
+  if (a.xcd_map) {
+    const int xcd = u & 7, local = u >> 3;
+    const int jj = local / a.U_nh;
+    u = (jj * 8 + xcd) * a.U_nh + (local - jj * a.U_nh);
+  }
+  const int nh = u / a.U_nh;
+  int rem = u - nh * a.U_nh;
+  const int n = nh / a.H, head = nh - n * a.H;
+  int qt = 0, n_chunks = att_chunks(0, a.R, a.pos_base, a.KC);
+  while (rem >= n_chunks) {
+    rem -= n_chunks;
+    ++qt;
+    n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
+  }
+  const int chunk = rem;
+  const int R = a.R, d = a.d, Lcap = a.Lcap, pos_base = a.pos_base;
+  const int q_lo = qt * ATT_QT;
+  const int nk = pos_base + min(R, q_lo + ATT_QT);
+  const int k_begin = chunk * a.KC;
+  const int k_end = min(nk, k_begin + a.KC);
+  const int t_begin = k_begin / ATT_KT;
+  const int n_tiles = (k_end - k_begin + ATT_KT - 1) / ATT_KT;
+  const size_t hb = (size_t)n * a.H + head;
+  const bf16* kbase = a.kc + hb * Lcap * DH;
+  const bf16* vbase = a.vt + hb * DH * Lcap;
+  // a wave whose 32 queries all lie past the last row only loads and syncs
+  const bool active = q_lo + wave * 32 < R;
+  const int t_q = q_lo + wave * 32 + j;             // this lane's query row
+  const int qpos = pos_base + t_q;
+  const int wave_qmin = pos_base + q_lo + wave * 32;
+
+  bf16x8 qf[KS];
+  {
+    const size_t qo = ((size_t)n * R + min(t_q, R - 1)) * d + head * DH + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(a.q + qo + ks * 16);
+  }
+  float m_run = 0.f;
+  // accumulator seed of the scores: -m_run in every element
+  f32x16 acc_o[DB], acc_l, negm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc_l[e] = 0.f;
+    negm[e] = 0.f;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_o[db] = acc_l;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+
+  // register stages: tile kt+2 loads while kt is multiplied and kt+1 waits
+  // to be stored into the other LDS buffer
+  struct Stage {
+    u32x4 k[CK], v[CK];
+  } ra, rb;
+  uint32_t koff[CK], voff[CK];
+#pragma unroll
+  for (int i = 0; i < CK; ++i) {
+    const int c = tid + i * 256;
+    const int key = c / (DH / 8), dc = c - key * (DH / 8);
+    const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
+    koff[i] = (uint32_t)(key * DH + dc * 8);
+    voff[i] = (uint32_t)(drow * Lcap + kc8 * 8);
+  }
+  auto gload = [&](Stage& st, int kt) {
+    const int k0 = (t_begin + kt) * ATT_KT;
+    const bf16* kp = kbase + (size_t)k0 * DH;
+    const bf16* vp = vbase + k0;
+    // every address is inside the allocation (k0 + 64 <= Lcap)
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      st.k[i] = *(const u32x4*)(kp + koff[i]);
+      st.v[i] = *(const u32x4*)(vp + voff[i]);
+    }
+    if (k0 + ATT_KT > k_end) {
+      // ragged last tile: keys at or past k_end become zeros
+#pragma unroll
+      for (int i = 0; i < CK; ++i) {
+        const int c = tid + i * 256;
+        if (k0 + c / (DH / 8) >= k_end) st.k[i] = u32x4{0u, 0u, 0u, 0u};
+        const int kk0 = k0 + (c % (ATT_KT / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned lo_ok = (kk0 + 2 * e) < k_end ? 0xFFFFu : 0u;
+          const unsigned hi_ok = (kk0 + 2 * e + 1) < k_end ? 0xFFFF0000u : 0u;
+          st.v[i][e] &= (lo_ok | hi_ok);
+        }
+      }
+    }
+  };
+  auto lstore = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * 256;
+      const int key = c / (DH / 8), dc = c - key * (DH / 8);
+      *(u32x4*)(&sK[buf][key * KROW + dc * 8]) = st.k[i];
+      // keys 8 kc8 .. +7 of the tile: 16-key group g = kc8 / 2, half kc8 % 2;
+      // keys 0-3 / 4-7 of the half go to physical 4 half / 8 + 4 half
+      const int drow = c / (ATT_KT / 8), kc8 = c - drow * (ATT_KT / 8);
+      const int g = kc8 >> 1, half = kc8 & 1;
+      bf16* row = &sV[buf][drow * VROW + 16 * g + 4 * half];
+      *(uint2*)row = uint2{st.v[i][0], st.v[i][1]};
+      *(uint2*)(row + 8) = uint2{st.v[i][2], st.v[i][3]};
+    }
+  };
+
+  auto compute = [&](int kt, int cur) {
+    const int key0 = (t_begin + kt) * ATT_KT;
+    f32x16 s[2];
+    {
+      bf16x8 kf[2][KS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[kb][ks] = *(const bf16x8*)(&sK[cur][(kb * 32 + j) * KROW + ks * 16 + 8 * hh]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[0], negm, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    // the P V operands, read while the score MFMAs run (d_h <= 64; the
+    // wider head reads them at their use, within its register budget)
+    constexpr int VPRE = DH <= 64 ? 4 : 1;
+    auto vread = [&](int db, int g) {
+      return *(const bf16x8*)(&sV[cur][(db * 32 + j) * VROW + 16 * g + 8 * hh]);
+    };
+    bf16x8 vf[DB][VPRE];
+    if constexpr (DH <= 64) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vf[db][g] = vread(db, g);
+    }
+    const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
+    if (need_mask) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > qpos || key >= k_end) s[kb][r] = -INFINITY;
+        }
+    }
+    // The exponentials are taken against the current reference first and
+    // the reference check (a max tree over the tile, the two halves of the
+    // query combined by a lane swap) runs beside them; in the rare tile that
+    // moves the reference they are taken again.
+    bf16x8 pf[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i]);
+    float tm[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = s[c >> 1];
+      const int o = 8 * (c & 1);
+      tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]),
+                    fmaxf(fmaxf(v[o + 3], v[o + 4]), fmaxf(fmaxf(v[o + 5], v[o + 6]), v[o + 7])));
+    }
+    float t = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                       false, false);
+      t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool move = t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      asm volatile("" ::: "memory");
+      const float dm = move ? t : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      m_run += dm;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) negm[e] = -m_run;
+      acc_l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i] - dm);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[g], acc_l, 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            DH <= 64 ? vf[db][g % VPRE] : vread(db, g), pf[g], acc_o[db], 0, 0, 0);
+    }
+  };
+
+  gload(ra, 0);
+  if (n_tiles > 1) gload(rb, 1);
+  lstore(ra, 0);
+  __syncthreads();
+#pragma clang loop unroll(disable)
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    if (kt + 2 < n_tiles) gload(ra, kt + 2);
+    if (active) compute(kt, 0);
+    if (kt + 1 < n_tiles) lstore(rb, 1);
+    __syncthreads();
+    if (kt + 1 >= n_tiles) break;
+    if (kt + 3 < n_tiles) gload(rb, kt + 3);
+    if (active) compute(kt + 1, 1);
+    if (kt + 2 < n_tiles) lstore(ra, 0);
+    __syncthreads();
+  }
+
+  // lane (j, hh) holds dimensions db*32 + 8g + 4hh .. +3 of its query in
+  // acc_o[db][4g .. 4g+3]
+  if (n_chunks == 1) {
+    if (active && t_q < R) {
+      const float inv = 1.0f / acc_l[0];
+      bf16* orow = a.out + ((size_t)n * R + t_q) * d + head * DH + 4 * hh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc_o[db][4 * g + e] * inv);
+          *(bf16x4*)(orow + db * 32 + 8 * g) = o;
+        }
+    }
+    return;
+  }
+
+  constexpr int SLOT = ATT_QT * (DH + 2);
+  const int tq = wave * 32 + j;   // query within the tile
+  if (active) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)u * SLOT);
+    const float l = acc_l[0];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc_o[db][4 * g], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2],
+                         acc_o[db][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                               (tq * DH + db * 32 + 8 * g + 4 * hh) * 4, 0,
+                                               ATT_SC1);
+      }
+    if (hh == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l > 0.f ? m_run : -1e30f), rs,
+                                            (ATT_QT * DH + tq) * 4, 0, ATT_SC1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs,
+                                            (ATT_QT * DH + ATT_QT + tq) * 4, 0, ATT_SC1);
+    }
+  }
+  wait_stores();
+  __syncthreads();
+  __shared__ unsigned s_last;
+  if (tid == 0) {
+    unsigned* tk = a.tickets + (size_t)nh * a.n_qt + qt;
+    const unsigned last = atomicAdd(tk, 1u) + 1u == (unsigned)n_chunks;
+    if (last) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last || !active) return;
+
+  attn32_merge<DH>(a, u - chunk, n_chunks, tq, t_q, n, head, hh);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+attn32_kernel(AttnArgs a) {
+  attn32_body<DH>(a);
+}
+
+// ---------------------------------------------------------------------------
+// The same computation with the K and Vt tiles moved from global memory
+// straight into LDS (global_load_lds_dwordx4): no staging registers and no
+// LDS stores in the loop.  Tiles are kept in a ring of STAGES buffers (tile x
+// in buffer x % STAGES), each a K tile [64 keys][DH] and a Vt tile [DH][64
+// keys] in rows of whole 16-byte chunks, XOR-swizzled: chunk c of row r sits
+// at slot c ^ (r & 7) of the row, so the 16-byte fragment reads of 32 rows
+// are conflict-free.  Vt is stored in key order; the P operand is brought to
+// the same key order instead: of each 16-key step the lane pair (j, j + 32)
+// swaps the middle 8 bytes of their P fragments (v_permlane32_swap), after
+// which lane half h holds keys 16g + 8h .. +7, the keys of its Vt fragment.
+// Iteration t issues the loads of tile t + STAGES - 1 into the buffer of tile
+// t - 1 (free since the barrier that ended iteration t - 1), computes tile t,
+// then waits for its share of tile t + 1 and meets the other waves at the
+// barrier.  Keys of the last tile at or past the chunk end are zeroed in LDS
+// before use (the cache holds stale rows there).
+// ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
+  static_assert(DH == 64 || DH == 128, "head width");
+  constexpr int KS = DH / 16, DB = DH / 32;
+  constexpr int STAGES = DH <= 64 ? 3 : 2;
+  constexpr int KBYTES = ATT_KT * DH * 2;           // K tile bytes (= Vt tile bytes)
+  constexpr int NI = DH / 8;                        // K (and Vt) instructions per tile
+  constexpr int IPW = 2 * NI / 4;                   // instructions per wave per tile
+  constexpr int CPR = DH / 8;                       // K chunks per row
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES][2 * KBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (the DMA takes its LDS address in a scalar register)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hh = lane >> 5;
+  int u = blockIdx.x;
+  if (a.xcd_map) {
+    const int xcd = u & 7, local = u >> 3;
+    const int jj = local / a.U_nh;
+    u = (jj * 8 + xcd) * a.U_nh + (local - jj * a.U_nh);
+  }
+  const int nh = u / a.U_nh;
+  int rem = u - nh * a.U_nh;
+  const int n = nh / a.H, head = nh - n * a.H;
+  int qt = 0, n_chunks = att_chunks(0, a.R, a.pos_base, a.KC);
+  while (rem >= n_chunks) {
+    rem -= n_chunks;
+    ++qt;
+    n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
+  }
+  const int chunk = rem;
+  const int R = a.R, d = a.d, Lcap = a.Lcap, pos_base = a.pos_base;
+  const int q_lo = qt * ATT_QT;
+  const int nk = pos_base + min(R, q_lo + ATT_QT);
+  const int k_begin = chunk * a.KC;
+  const int k_end = min(nk, k_begin + a.KC);
+  const int t_begin = k_begin / ATT_KT;
+  const int n_tiles = (k_end - k_begin + ATT_KT - 1) / ATT_KT;
+  const size_t hb = (size_t)n * a.H + head;
+  const bf16* kbase = a.kc + hb * Lcap * DH;
+  const bf16* vbase = a.vt + hb * DH * Lcap;
+  const bool active = q_lo + wave * 32 < R;
+  const int t_q = q_lo + wave * 32 + j;
+  const int qpos = pos_base + t_q;
+  const int wave_qmin = pos_base + q_lo + wave * 32;
+
+  // this wave's DMA lanes: K instruction q = wave + 4i covers rows
+  // (64 / CPR) q .. ; Vt instruction q covers dimensions 8q .. 8q + 7
+  uint32_t koff[NI / 4], voff[NI / 4];
+#pragma unroll
+  for (int i = 0; i < NI / 4; ++i) {
+    const int q = wave + 4 * i;
+    {
+      const int r = q * (64 / CPR) + lane / CPR, s = lane % CPR, c = s ^ (r & 7);
+      koff[i] = (uint32_t)((r * DH + c * 8) * 2);
+    }
+    {
+      const int r = 8 * q + (lane >> 3), s = lane & 7, c = s ^ (r & 7);
+      voff[i] = (uint32_t)((r * Lcap + c * 8) * 2);
+    }
+  }
+  const uint32_t lds0 = lds_address(&smem[0][0]);
+  auto issue = [&](int kt) {
+    const int k0 = (t_begin + kt) * ATT_KT;
+    const uint32_t st = lds0 + (uint32_t)((kt % STAGES) * 2 * KBYTES);
+    const bf16* kp = kbase + (size_t)k0 * DH;
+    const bf16* vp = vbase + k0;
+#pragma unroll
+    for (int i = 0; i < NI / 4; ++i) {
+      const int q = wave + 4 * i;
+      dma16(kp, koff[i], st + q * 1024);
+      dma16(vp, voff[i], st + KBYTES + q * 1024);
+    }
+  };
+  // LDS byte offsets of this lane's fragments within a stage
+  auto kfrag = [&](int kb, int ks) {
+    const int r = kb * 32 + j, c = 2 * ks + hh;
+    return r * DH * 2 + 16 * (c ^ (r & 7));
+  };
+  auto vfrag = [&](int db, int g) {
+    const int r = db * 32 + j, c = 2 * g + hh;
+    return KBYTES + r * 128 + 16 * (c ^ (r & 7));
+  };
+
+  bf16x8 qf[KS];   // this lane's query fragments, read from LDS in the prologue
+  float m_run = 0.f;
+  f32x16 acc_o[DB], acc_l, negm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc_l[e] = 0.f;
+    negm[e] = 0.f;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_o[db] = acc_l;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+
+  auto compute = [&](int kt) {
+    const char* stg = &smem[kt % STAGES][0];
+    const int key0 = (t_begin + kt) * ATT_KT;
+    f32x16 s[2];
+    {
+      bf16x8 kf[2][KS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(stg + kfrag(kb, ks));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[0], negm, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
+    if (need_mask) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > qpos || key >= k_end) s[kb][r] = -INFINITY;
+        }
+    }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i]);
+    float tm[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = s[c >> 1];
+      const int o = 8 * (c & 1);
+      tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]),
+                    fmaxf(fmaxf(v[o + 3], v[o + 4]), fmaxf(fmaxf(v[o + 5], v[o + 6]), v[o + 7])));
+    }
+    float t = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                       false, false);
+      t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool move = t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      asm volatile("" ::: "memory");
+      const float dm = move ? t : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      m_run += dm;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) negm[e] = -m_run;
+      acc_l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i] - dm);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // keys {16g + 4h + i, 16g + 8 + 4h + i} -> keys 16g + 8h + i
+      u32x4 pd = __builtin_bit_cast(u32x4, pf[g]);
+      const auto s02 = __builtin_amdgcn_permlane32_swap(pd[0], pd[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(pd[1], pd[3], false, false);
+      pd = u32x4{s02[0], s13[0], s02[1], s13[1]};
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, pd);
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk, acc_l, 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)(stg + vfrag(db, g)), pk, acc_o[db], 0, 0, 0);
+    }
+  };
+  // zero the Vt columns of keys at or past k_end in tile kt's buffer
+  auto zero_tail = [&](int kt) {
+    const int kvalid = k_end - (t_begin + kt) * ATT_KT;
+    char* stg = &smem[kt % STAGES][0];
+    for (int idx = tid; idx < DH * ATT_KT; idx += 256) {
+      const int r = idx / ATT_KT, kk = idx - r * ATT_KT;
+      if (kk >= kvalid) {
+        const int c = kk >> 3, e = kk & 7;
+        *(bf16*)(stg + KBYTES + r * 128 + 16 * (c ^ (r & 7)) + 2 * e) = (bf16)0.0f;
+      }
+    }
+  };
+
+  // prologue: the query tile into the last ring buffer and tiles
+  // 0 .. STAGES-2 into the first ones, all in flight together.  The query
+  // tile is stored like a K tile (rows of DH, swizzled); its rows past the
+  // last one read that row.
+  {
+    const uint32_t qst = lds0 + (uint32_t)((STAGES - 1) * 2 * KBYTES);
+    const bf16* qb = a.q + head * DH;
+#pragma unroll
+    for (int i = 0; i < 2 * NI / 4; ++i) {
+      const int q = wave + 4 * i;   // 2 NI instructions of 64 / CPR rows
+      const int r = q * (64 / CPR) + lane / CPR, sl = lane % CPR, c = sl ^ (r & 7);
+      const int t = min(q_lo + r, R - 1);
+      dma16(qb, (uint32_t)(((size_t)n * R + t) * d * 2 + c * 16), qst + q * 1024);
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < STAGES - 1; ++kt)
+    if (kt < n_tiles) issue(kt);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  {
+    const char* qs = &smem[STAGES - 1][0];
+    const int r = wave * 32 + j;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 2 * ks + hh;
+      qf[ks] = *(const bf16x8*)(qs + r * DH * 2 + 16 * (c ^ (r & 7)));
+    }
+  }
+  // every wave has its query fragments before tile STAGES-1 reuses the buffer
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma clang loop unroll(disable)
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const bool more = kt + STAGES - 1 < n_tiles;
+    if (more) issue(kt + STAGES - 1);
+    if ((t_begin + kt) * ATT_KT + ATT_KT > k_end) {
+      zero_tail(kt);
+      __syncthreads();
+    }
+    if (active) compute(kt);
+    // tile kt + 1 has landed once at most the later tiles' loads are pending
+    if (more) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((STAGES - 2) * IPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  if (n_chunks == 1) {
+    if (active && t_q < R) {
+      const float inv = 1.0f / acc_l[0];
+      bf16* orow = a.out + ((size_t)n * R + t_q) * d + head * DH + 4 * hh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc_o[db][4 * g + e] * inv);
+          *(bf16x4*)(orow + db * 32 + 8 * g) = o;
+        }
+    }
+    return;
+  }
+
+  constexpr int SLOT = ATT_QT * (DH + 2);
+  const int tq = wave * 32 + j;
+  if (active) {
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)u * SLOT);
+    const float l = acc_l[0];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc_o[db][4 * g], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2],
+                         acc_o[db][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                               (tq * DH + db * 32 + 8 * g + 4 * hh) * 4, 0,
+                                               ATT_SC1);
+      }
+    if (hh == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l > 0.f ? m_run : -1e30f), rs,
+                                            (ATT_QT * DH + tq) * 4, 0, ATT_SC1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs,
+                                            (ATT_QT * DH + ATT_QT + tq) * 4, 0, ATT_SC1);
+    }
+  }
+  wait_stores();
+  __syncthreads();
+  __shared__ unsigned s_last;
+  if (tid == 0) {
+    unsigned* tk = a.tickets + (size_t)nh * a.n_qt + qt;
+    const unsigned last = atomicAdd(tk, 1u) + 1u == (unsigned)n_chunks;
+    if (last) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last || !active) return;
+  attn32_merge<DH>(a, u - chunk, n_chunks, tq, t_q, n, head, hh);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+attn_dma_kernel(AttnArgs a) {
+  attn_dma_body<DH>(a);
+}
+
+
 // Key chunk length.  For the two-blocks-per-CU kernel (d_h <= 64, not split)
 // the smallest chunk of 448..1024 keys (a multiple of the 64-key tile) that
 // keeps every unit in one round of two blocks per CU, when there is one (448
@@ -575,10 +1280,75 @@ static int att_units(int R, int pos_base, int KC, int n_qt) {
   return s;
 }
 
+// Key chunk of the 32 x 32 kernels: the multiple of the 64-key tile that
+// minimises the modelled time rounds x (tiles of the longest unit + a fixed
+// cost of UNIT_COST tiles per unit: its prologue, output or partial store and
+// merge share), where rounds = ceil(units / slots) and slots = 256 CUs x the
+// blocks one CU holds, plus ATT_MERGE_COST tiles per chunk of the longest
+// query tile (its merge reads them one after another); at most max(1024, N H query tiles) units (the partial
+// slots of the workspace).  Candidates are the chunk lengths that cut the
+// longest key range into c equal parts; results are memoised per shape.
+constexpr int ATT_UNIT_COST = 3;
+constexpr int ATT_MERGE_COST = 1;
+static int chunk_for_slots(int N, int R, int H, int pos_base, int slots) {
+  struct Entry { int N, R, H, pos_base, slots, kc; };
+  thread_local Entry memo[64];
+  thread_local int memo_n = 0;
+  for (int i = 0; i < memo_n; ++i) {
+    const Entry& e = memo[i];
+    if (e.N == N && e.R == R && e.H == H && e.pos_base == pos_base && e.slots == slots)
+      return e.kc;
+  }
+  const int n_qt = (R + ATT_QT - 1) / ATT_QT;
+  const int max_tiles = (pos_base + R + ATT_KT - 1) / ATT_KT;
+  const long cap = std::max<long>(1024, (long)N * H * n_qt);
+  long best_cost = -1;
+  int best = max_tiles * ATT_KT;
+  int prev_kt = -1;
+  for (int c = 1; c <= max_tiles; ++c) {
+    const int kt = (max_tiles + c - 1) / c;
+    if (kt == prev_kt) continue;
+    prev_kt = kt;
+    const long units = (long)N * H * att_units(R, pos_base, kt * ATT_KT, n_qt);
+    if (units > cap) break;
+    const long rounds = (units + slots - 1) / slots;
+    // the chunk that merges reads every chunk of its query tile in turn
+    const long cost = rounds * (kt + ATT_UNIT_COST) + ATT_MERGE_COST * c;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = kt * ATT_KT;
+    }
+  }
+  memo[memo_n % 64] = Entry{N, R, H, pos_base, slots, best};
+  ++memo_n;
+  if (memo_n >= 64) memo_n = 64;
+  return best;
+}
+
+// blocks of the 32 x 32 kernels one CU holds (registers and LDS)
+static int att_blocks_per_cu(int dh) { return dh == 128 ? 2 : 3; }
+
+// Kernel of a bf16 launch.  The split (higher-precision forward) mode runs
+// the 16 x 16 kernel; d_h = 32 the register-staged 32 x 32 kernel; a frame
+// with no cached prefix and fewer than 64 (sample, head) pairs the 16 x 16
+// kernel, measured faster there (26.7 against 35 us at 1560 tokens and 16
+// heads, where every unit is a few tiles of the causal triangle); everything
+// else the DMA-fed 32 x 32 kernel.
+enum AttKind { ATT_SPLIT16, ATT_SMALL16, ATT_REG32, ATT_DMA32 };
+static AttKind att_kind(int N, int H, int dh, bool split, int pos_base) {
+  if (split) return ATT_SPLIT16;
+  if (dh == 32) return ATT_REG32;
+  if (dh == 64 && pos_base == 0 && N * H < 64) return ATT_SMALL16;
+  return ATT_DMA32;
+}
+
 int attention_chunk(int N, int R, int H, int dh, bool split, int pos_base) {
   const int n_qt = (R + ATT_QT - 1) / ATT_QT;
   const int nk_max = pos_base + R;
-  if (dh <= 64 && !split)
+  const AttKind kind = att_kind(N, H, dh, split, pos_base);
+  if (kind == ATT_REG32 || kind == ATT_DMA32)
+    return chunk_for_slots(N, R, H, pos_base, 256 * att_blocks_per_cu(dh));
+  if (kind == ATT_SMALL16)
     for (int kc = 448; kc <= 1024 && kc < nk_max; kc += ATT_KT)
       if ((long)N * H * att_units(R, pos_base, kc, n_qt) <= 512) return kc;
   int KC = 512;
@@ -637,11 +1407,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 }
 
 template <int DH, bool SPLIT>
-static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (DH <= 64 && !SPLIT)
-    hipLaunchKernelGGL((attn_bf16_kernel_o2<DH, SPLIT>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, SPLIT>), grid, dim3(256), 0, st, a);
+static void attn_launch(const AttnArgs& a, dim3 grid, AttKind kind, hipStream_t st) {
+  if constexpr (SPLIT) {
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, true>), grid, dim3(256), 0, st, a);
+  } else if constexpr (DH == 32) {
+    hipLaunchKernelGGL((attn32_kernel<32>), grid, dim3(256), 0, st, a);
+  } else {
+    if constexpr (DH == 64)
+      if (kind == ATT_SMALL16) {
+        hipLaunchKernelGGL((attn_bf16_kernel_o2<64, false>), grid, dim3(256), 0, st, a);
+        return;
+      }
+    hipLaunchKernelGGL((attn_dma_kernel<DH>), grid, dim3(256), 0, st, a);
+  }
 }
 
 hipError_t launch_attention(bool bf, const void* q, const void* kc,
@@ -661,13 +1439,14 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
                R, H, d, Lcap, pos_base, KC, U_nh, n_qt, (N * H) % 8 == 0 ? 1 : 0};
     if (U_nh > n_qt && (!part || !tickets)) return hipErrorInvalidValue;
     const dim3 grid(N * H * U_nh);
+    const AttKind kind = att_kind(N, H, dh, split != nullptr, pos_base);
     switch (dh * 2 + (split ? 1 : 0)) {
-      case 128: attn_launch<64, false>(a, grid, st); break;
-      case 129: attn_launch<64, true>(a, grid, st); break;
-      case 256: attn_launch<128, false>(a, grid, st); break;
-      case 257: attn_launch<128, true>(a, grid, st); break;
-      case 64: attn_launch<32, false>(a, grid, st); break;
-      case 65: attn_launch<32, true>(a, grid, st); break;
+      case 128: attn_launch<64, false>(a, grid, kind, st); break;
+      case 129: attn_launch<64, true>(a, grid, kind, st); break;
+      case 256: attn_launch<128, false>(a, grid, kind, st); break;
+      case 257: attn_launch<128, true>(a, grid, kind, st); break;
+      case 64: attn_launch<32, false>(a, grid, kind, st); break;
+      case 65: attn_launch<32, true>(a, grid, kind, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

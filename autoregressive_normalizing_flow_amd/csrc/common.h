@@ -78,3 +78,24 @@ __device__ __forceinline__ void system_store(unsigned* p, unsigned v) {
 // this lane's outstanding memory operations (stores included) are complete
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4).  One
+// wave-instruction writes 64 consecutive 16-byte LDS slots (lane i -> slot i)
+// at the LDS address in m0; each lane chooses the global chunk that lands in
+// its slot.  Issued from inline asm (saddr form: 64-bit uniform base in SGPRs
+// plus a 32-bit per-lane byte offset), with every wait on it explicit: the
+// load has no result register, and completion is counted by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from base + voff into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop

@@ -393,7 +393,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // Requirements: N % BN == 0, k_len % 64 == 0, M * K * 2 and N * K * 2 below
 // 4 GiB (32-bit offsets).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int TM_, int TN_>
 struct DmaCfg {
@@ -408,18 +407,6 @@ struct DmaCfg {
   static constexpr int STAGE = (BM + BN) * BK;         // bf16 elements per stage
 };
 
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from base + voff into LDS at m0 + 16 * lane.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector-memory loads are outstanding and
 // all its LDS reads have returned, then barrier.  The asm is a compiler memory

@@ -95,6 +95,7 @@ struct GraphEntry {
 };
 
 constexpr int kGraphCacheCap = 128;
+constexpr int kProfileLaunches = 16384;   // launches recorded per af_profile_enable
 
 }  // namespace
 
@@ -122,7 +123,7 @@ struct af_plan {
   uint64_t gclock = 0;
   long long g_captures = 0, g_replays = 0;
   // row split of a Jacobi update over two streams (see af_inverse_jacobi)
-  bool row_split = true;
+  bool row_split = false;
   hipStream_t split_stream = nullptr;
   std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
   // residual pairs of the last update of the last inverse call (halves added)
@@ -608,9 +609,13 @@ af_status af_plan_create(const af_block_cfg* cfg, int n_blocks,
                          const af_block_weights* w, af_plan** out) {
   if (!cfg || !w || !out) return fail(AF_ERR_ARG, "NULL argument");
   *out = nullptr;
-  const af_block_cfg& c = *cfg;
   if (n_blocks < 1 || n_blocks > 64) return fail(AF_ERR_ARG, "n_blocks must be 1..64");
-  if (c.dtype != AF_F32 && c.dtype != AF_BF16) return fail(AF_ERR_ARG, "unknown dtype");
+  // a C caller may pass any int in the enum field: read its bytes as an int
+  // (a C++ load of an out-of-range enum value is undefined)
+  int dtype_raw;
+  std::memcpy(&dtype_raw, &cfg->dtype, sizeof(dtype_raw));
+  if (dtype_raw != AF_F32 && dtype_raw != AF_BF16) return fail(AF_ERR_ARG, "unknown dtype");
+  const af_block_cfg& c = *cfg;
   if (c.C < 1 || c.C > 256) return fail(AF_ERR_ARG, "C must be 1..256");
   if (c.n_layers < 1 || c.n_layers > 1024) return fail(AF_ERR_ARG, "n_layers must be >= 1");
   if (c.max_len < 1 || c.max_len > (1 << 24)) return fail(AF_ERR_ARG, "max_len out of range");
@@ -1072,7 +1077,7 @@ af_status af_profile_enable(af_plan* p, const char* kernel_class) {
     if (std::strcmp(kernel_class, kclass_names[i]) == 0) cls = i;
   if (cls < 0) return fail(AF_ERR_ARG, std::string("unknown kernel class ") + kernel_class);
   if (p->ev.empty()) {
-    p->ev.resize(2 * 4096);
+    p->ev.resize(2 * kProfileLaunches);
     // timing-only events: no system-scope fence (cache writeback and
     // invalidate) when recorded, which would add its own cost to the
     // bracketed launch

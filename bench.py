@@ -364,7 +364,7 @@ def schedule_sweep(torch, binding, synth, reps):
 
 
 def pipeline_bench(torch, binding, synth, reps, graphs=False, fused_refresh=False,
-                   row_split=True):
+                   row_split=False):
     """End-to-end inverse of the deep o shallow flow over 21 frames (deep:
     the video21 block, shallow: the shallow_stack stack), three schedules:
     stages (the deep block over all frames in one call, then the shallow
@@ -574,8 +574,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the short runs of the other workloads")
-    ap.add_argument("--no-row-split", action="store_true",
-                    help="run every Jacobi update as one pass (no two-stream row split)")
+    ap.add_argument("--row-split", action="store_true",
+                    help="run long-prefix Jacobi updates as two half passes on two streams "
+                         "(af_plan_set_row_split; off by default)")
     ap.add_argument("--fused-refresh", action="store_true",
                     help="recompute an early-stopped block's K/V in the next block's "
                          "first update instead of in a pass of its own")
@@ -635,7 +636,7 @@ def main():
     if args.pipeline:
         print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1),
                                         args.graphs, args.fused_refresh,
-                                        not args.no_row_split)), flush=True)
+                                        args.row_split)), flush=True)
         return
     if args.schedule_sweep:
         print(json.dumps(schedule_sweep(torch, binding, synth, max(args.steps, 1))), flush=True)
@@ -645,7 +646,7 @@ def main():
     cfg, w = r.cfg, r.w
     r.plan.set_graphs(args.graphs)
     r.plan.set_fused_refresh(args.fused_refresh)
-    r.plan.set_row_split(not args.no_row_split)
+    r.plan.set_row_split(args.row_split)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -727,7 +728,7 @@ def main():
                            if aff_gbs is not None else None),
         "graphs": args.graphs,
         "fused_refresh": args.fused_refresh,
-        "row_split": not args.no_row_split,
+        "row_split": args.row_split,
         "kernel_ms_per_step": {c: {"launches": b["launches"], "ms": b["ms"]}
                                for c, b in breakdown.items()},
         "forward_ms": round(fwd_ms, 3),

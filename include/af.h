@@ -220,7 +220,7 @@ af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
  * cached keys up to their own position), bytes for "affine" (20 C per token
  * in an inverse update, 16 C in the forward), 0 for "layernorm".  Classes:
  * "embed", "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2",
- * "gemm_head", "attention", "affine".  At most 4096 launches are recorded
+ * "gemm_head", "attention", "affine".  At most 16384 launches are recorded
  * per enable. */
 af_status af_profile_enable(af_plan *p, const char *kernel_class);
 af_status af_profile_disable(af_plan *p);
@@ -271,8 +271,8 @@ af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *
  * The call returns (also on an error) with `stream` ordered after all of the
  * second stream's work.  Like the graph cache, the second stream and its
  * events belong to the plan: a plan must not be used by two calls at once.
- * enable != 0 (the default) allows the split, 0 keeps one pass; AF_ERR_ARG if
- * p is NULL. */
+ * enable != 0 allows the split, 0 (the default) keeps one pass: with the
+ * 32 x 32 attention kernels one pass measured faster; AF_ERR_ARG if p is NULL. */
 af_status af_plan_set_row_split(af_plan *p, int enable);
 
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
