@@ -113,6 +113,8 @@ def load_library() -> ctypes.CDLL:
     L.afk_affine_partials_bytes.restype = sz
     L.afk_affine.argtypes = [i, _P, _P, _P, i, i, i, _P, _P, sz, i, _P]
     L.afk_affine.restype = st
+    L.afk_affine_noalloc.argtypes = [i, _P, _P, _P, i, i, i, _P, _P]
+    L.afk_affine_noalloc.restype = st
     L.afk_gemm_bf16.argtypes = [_P, _P, _P, _P, i, i, i, _P]
     L.afk_gemm_bf16.restype = st
     L.af_status_str.argtypes = [st]
@@ -388,6 +390,14 @@ def afk_affine(mode: int, head, src, dst, N: int, rows: int, C: int, res,
     _check(L.afk_affine(mode, _ptr(head), _ptr(src), _ptr(dst), N, rows, C,
                         _ptr(res), _ptr(partials), partials.numel(), int(check),
                         _stream(stream)), "afk_affine")
+
+
+def afk_affine_noalloc(mode: int, head, src, dst, N: int, rows: int, C: int, res,
+                       stream=None):
+    """afk_affine with its scratch in the library's static device array."""
+    L = load_library()
+    _check(L.afk_affine_noalloc(mode, _ptr(head), _ptr(src), _ptr(dst), N, rows, C, _ptr(res),
+                                _stream(stream)), "afk_affine_noalloc")
 
 
 def afk_affine_partials_bytes(N: int, rows: int, C: int) -> int:

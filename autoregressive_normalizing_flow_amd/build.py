@@ -34,7 +34,7 @@ COMMON_FLAGS = [
     "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["runtime.cpp", "pointwise.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["runtime.cpp", "pointwise.hip", "gemm.hip", "attention.hip", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

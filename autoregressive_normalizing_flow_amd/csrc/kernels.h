@@ -146,4 +146,9 @@ inline size_t attention_tickets(int N, int R, int H) {
   return (size_t)N * H * ((R + 127) / 128);
 }
 
+// Record a failure for af_last_error() from another translation unit
+// (defined with the ABI in runtime.cpp); a HIP failure also clears the
+// runtime's last-error state.  Returns status.
+int record_error(int status, const char* msg);
+
 }  // namespace af

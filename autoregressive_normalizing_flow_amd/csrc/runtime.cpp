@@ -588,6 +588,10 @@ af_status graph_capture(af_plan* p, const GraphKey& key, const BlockW& bw, const
 
 }  // namespace
 
+int af::record_error(int status, const char* msg) {
+  return (int)fail((af_status)status, msg);
+}
+
 extern "C" {
 
 const char* af_status_str(af_status s) {

@@ -293,6 +293,20 @@ af_status afk_affine(int mode, const float *head, const float *src, float *dst,
                      void *partials, size_t partials_bytes, int check,
                      void *stream);
 
+/* The fused affine kernel as afk_affine, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): its partial sums and ticket counter live in a
+ * static device array of the library, one per GPU, of AF_NOALLOC_SCRATCH_BYTES
+ * (the call needs afk_affine_partials_bytes(N, rows_per_sample, C) of it;
+ * larger requests return AF_ERR_WORKSPACE).  The call allocates nothing
+ * (no hipMalloc, no host buffer); its first call on a device looks the array
+ * up.  Same arguments and results as afk_affine with check = 0; stream-ordered.
+ * Calls that overlap on one GPU (two streams, or two threads) share the array
+ * and race: order them. */
+#define AF_NOALLOC_SCRATCH_BYTES (256 * 1024)
+af_status afk_affine_noalloc(int mode, const float *head, const float *src, float *dst,
+                             int N, int rows_per_sample, int C, float *res, void *stream);
+
 /* bf16 MFMA GEMM y[M, N] = a[M, K] * w[N, K]^T + bias[N] (bias may be NULL),
  * fp32 out, for unit parity.  a, w are bf16 bit patterns, row-major;
  * K % 64 == 0, N % 64 == 0; a and w below 4 GiB each (AF_ERR_UNSUPPORTED
