@@ -955,17 +955,25 @@ attn32_kernel(AttnArgs a) {
 // straight into LDS (global_load_lds_dwordx4): no staging registers and no
 // LDS stores in the loop.  Tiles are kept in a ring of STAGES buffers (tile x
 // in buffer x % STAGES), each a K tile [64 keys][DH] and a Vt tile [DH][64
-// keys] in rows of whole 16-byte chunks, XOR-swizzled: chunk c of row r sits
-// at slot c ^ (r & 7) of the row, so the 16-byte fragment reads of 32 rows
-// are conflict-free.  Vt is stored in key order; the P operand is brought to
-// the same key order instead: of each 16-key step the lane pair (j, j + 32)
-// swaps the middle 8 bytes of their P fragments (v_permlane32_swap), after
-// which lane half h holds keys 16g + 8h .. +7, the keys of its Vt fragment.
-// Iteration t issues the loads of tile t + STAGES - 1 into the buffer of tile
-// t - 1 (free since the barrier that ended iteration t - 1), computes tile t,
-// then waits for its share of tile t + 1 and meets the other waves at the
-// barrier.  Keys of the last tile at or past the chunk end are zeroed in LDS
-// before use (the cache holds stale rows there).
+// keys] in rows of whole 16-byte chunks, XOR-swizzled so that the 16-byte
+// fragment reads are free of bank conflicts: LDS serves a 16-byte read to 16
+// lanes per cycle over its 64 banks, and the 16 lanes of a fragment read take
+// one chunk of 16 consecutive rows.  Rows of 128 bytes (Vt, and K at d_h 64)
+// put even and odd rows on opposite bank halves, so chunk c of row r sits at
+// slot c ^ ((r >> 1) & 7); rows of 256 bytes (K at d_h 128) start on the same
+// bank, so at slot c ^ (r & 15).  (Keyed on r & 7, rows r and r + 8 collided:
+// half of the LDS cycles were conflicts, though removing them gained little at
+// d_h 64 and 7% at d_h 128.)  Vt is stored in key order; the P operand is
+// brought to the same key order instead: of each 16-key step the lane pair
+// (j, j + 32) swaps the middle 8 bytes of their P fragments
+// (v_permlane32_swap), after which lane half h holds keys 16g + 8h .. +7, the
+// keys of its Vt fragment.  Iteration t issues the loads of tile
+// t + STAGES - 1 into the buffer of tile t - 1 (free since the barrier that
+// ended iteration t - 1), computes tile t, then waits for its share of tile
+// t + 1 and meets the other waves at the barrier.  The P V MFMAs run at raised
+// wave priority, so they issue ahead of the other waves' softmax work.  Keys
+// of the last tile at or past the chunk end are zeroed in LDS before use (the
+// cache holds stale rows there).
 // ---------------------------------------------------------------------------
 template <int DH>
 __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
@@ -976,6 +984,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   constexpr int NI = DH / 8;                        // K (and Vt) instructions per tile
   constexpr int IPW = 2 * NI / 4;                   // instructions per wave per tile
   constexpr int CPR = DH / 8;                       // K chunks per row
+  // 16-byte slot of chunk c in row r of a K (or Q) tile and of a Vt tile
+  auto swzk = [](int c, int r) { return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
+  auto swzv = [](int c, int r) { return c ^ ((r >> 1) & 7); };
   typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
   __shared__ __attribute__((aligned(1024))) char smem[STAGES][2 * KBYTES];
 
@@ -1021,11 +1032,11 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   for (int i = 0; i < NI / 4; ++i) {
     const int q = wave + 4 * i;
     {
-      const int r = q * (64 / CPR) + lane / CPR, s = lane % CPR, c = s ^ (r & 7);
+      const int r = q * (64 / CPR) + lane / CPR, s = lane % CPR, c = swzk(s, r);
       koff[i] = (uint32_t)((r * DH + c * 8) * 2);
     }
     {
-      const int r = 8 * q + (lane >> 3), s = lane & 7, c = s ^ (r & 7);
+      const int r = 8 * q + (lane >> 3), s = lane & 7, c = swzv(s, r);
       voff[i] = (uint32_t)((r * Lcap + c * 8) * 2);
     }
   }
@@ -1045,11 +1056,11 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   // LDS byte offsets of this lane's fragments within a stage
   auto kfrag = [&](int kb, int ks) {
     const int r = kb * 32 + j, c = 2 * ks + hh;
-    return r * DH * 2 + 16 * (c ^ (r & 7));
+    return r * DH * 2 + 16 * swzk(c, r);
   };
   auto vfrag = [&](int db, int g) {
     const int r = db * 32 + j, c = 2 * g + hh;
-    return KBYTES + r * 128 + 16 * (c ^ (r & 7));
+    return KBYTES + r * 128 + 16 * swzv(c, r);
   };
 
   bf16x8 qf[KS];   // this lane's query fragments, read from LDS in the prologue
@@ -1066,24 +1077,27 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 
-  auto compute = [&](int kt) {
+  // scores of tile kt minus the current reference (K from its buffer)
+  auto scores = [&](f32x16 (&s)[2], int kt) {
+    const char* stg = &smem[kt % STAGES][0];
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(stg + kfrag(kb, ks));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[0], negm, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
+    }
+  };
+  // softmax of tile kt's scores and its row-sum and P V MFMAs (V from its
+  // buffer)
+  auto finish = [&](f32x16 (&s)[2], int kt) {
     const char* stg = &smem[kt % STAGES][0];
     const int key0 = (t_begin + kt) * ATT_KT;
-    f32x16 s[2];
-    {
-      bf16x8 kf[2][KS];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(stg + kfrag(kb, ks));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[0], negm, 0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
-      }
-    }
     const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
     if (need_mask) {
       asm volatile("" ::: "memory");
@@ -1132,6 +1146,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
         for (int i = 0; i < 8; ++i)
           pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i] - dm);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // keys {16g + 4h + i, 16g + 8 + 4h + i} -> keys 16g + 8h + i
@@ -1146,7 +1161,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *(const bf16x8*)(stg + vfrag(db, g)), pk, acc_o[db], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
+
   // zero the Vt columns of keys at or past k_end in tile kt's buffer
   auto zero_tail = [&](int kt) {
     const int kvalid = k_end - (t_begin + kt) * ATT_KT;
@@ -1155,7 +1172,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
       const int r = idx / ATT_KT, kk = idx - r * ATT_KT;
       if (kk >= kvalid) {
         const int c = kk >> 3, e = kk & 7;
-        *(bf16*)(stg + KBYTES + r * 128 + 16 * (c ^ (r & 7)) + 2 * e) = (bf16)0.0f;
+        *(bf16*)(stg + KBYTES + r * 128 + 16 * swzv(c, r) + 2 * e) = (bf16)0.0f;
       }
     }
   };
@@ -1170,7 +1187,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
 #pragma unroll
     for (int i = 0; i < 2 * NI / 4; ++i) {
       const int q = wave + 4 * i;   // 2 NI instructions of 64 / CPR rows
-      const int r = q * (64 / CPR) + lane / CPR, sl = lane % CPR, c = sl ^ (r & 7);
+      const int r = q * (64 / CPR) + lane / CPR, sl = lane % CPR, c = swzk(sl, r);
       const int t = min(q_lo + r, R - 1);
       dma16(qb, (uint32_t)(((size_t)n * R + t) * d * 2 + c * 16), qst + q * 1024);
     }
@@ -1185,11 +1202,12 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 2 * ks + hh;
-      qf[ks] = *(const bf16x8*)(qs + r * DH * 2 + 16 * (c ^ (r & 7)));
+      qf[ks] = *(const bf16x8*)(qs + r * DH * 2 + 16 * swzk(c, r));
     }
   }
   // every wave has its query fragments before tile STAGES-1 reuses the buffer
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  f32x16 s[2];
 #pragma clang loop unroll(disable)
   for (int kt = 0; kt < n_tiles; ++kt) {
     const bool more = kt + STAGES - 1 < n_tiles;
@@ -1198,7 +1216,10 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
       zero_tail(kt);
       __syncthreads();
     }
-    if (active) compute(kt);
+    if (active) {
+      scores(s, kt);
+      finish(s, kt);
+    }
     // tile kt + 1 has landed once at most the later tiles' loads are pending
     if (more) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((STAGES - 2) * IPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
