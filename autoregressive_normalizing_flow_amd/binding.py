@@ -115,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     L.afk_affine.restype = st
     L.afk_affine_noalloc.argtypes = [i, _P, _P, _P, i, i, i, _P, _P]
     L.afk_affine_noalloc.restype = st
+    L.afk_stream_copy.argtypes = [_P, _P, sz, _P]
+    L.afk_stream_copy.restype = st
     L.afk_gemm_bf16.argtypes = [_P, _P, _P, _P, i, i, i, _P]
     L.afk_gemm_bf16.restype = st
     L.af_status_str.argtypes = [st]
@@ -398,6 +400,14 @@ def afk_affine_noalloc(mode: int, head, src, dst, N: int, rows: int, C: int, res
     L = load_library()
     _check(L.afk_affine_noalloc(mode, _ptr(head), _ptr(src), _ptr(dst), N, rows, C, _ptr(res),
                                 _stream(stream)), "afk_affine_noalloc")
+
+
+def afk_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """dst <- src (same byte size) with the library's streaming copy kernel."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes
+    _check(load_library().afk_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "afk_stream_copy")
 
 
 def afk_affine_partials_bytes(N: int, rows: int, C: int) -> int:

@@ -62,6 +62,10 @@ struct AffineArgs {
 hipError_t launch_affine(int mode, const AffineArgs& a, hipStream_t st);
 int affine_groups(int N, int R, int C);   // G, the partial slots per sample
 
+// dst[0, bytes) = src[0, bytes) with the streaming form the affine kernel's
+// large ranges use (16-byte aligned, bytes % 16 == 0, no overlap).
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
 // Head GEMM on the fp32 matrix cores: planes[s] = hf W^T over the s-th of
 // `splits` equal K ranges, planes [splits][M][2C] as launch_affine reads them.
 // Output row m reads hf row (m / r_out) * r_in + off + m % r_out (r_out =

@@ -1185,6 +1185,19 @@ af_status afk_affine(int mode, const float* head, const float* src, float* dst,
   return AF_OK;
 }
 
+af_status afk_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return AF_OK;
+  if (!src || !dst) return fail(AF_ERR_ARG, "NULL argument");
+  if (bytes % 16 != 0) return fail(AF_ERR_ARG, "bytes must be a multiple of 16");
+  if (any_misaligned(src, dst)) return fail(AF_ERR_ARG, "src and dst must be 16-byte aligned");
+  const char* s = (const char*)src;
+  char* d = (char*)dst;
+  if (s < d + bytes && d < s + bytes) return fail(AF_ERR_ARG, "src and dst overlap");
+  hipError_t e = af::launch_stream_copy(src, dst, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AF_ERR_HIP, hipGetErrorString(e));
+  return AF_OK;
+}
+
 af_status afk_gemm_bf16(const void* a, const void* w, const float* bias, float* y,
                         int M, int N, int K, void* stream) {
   if (!a || !w || !y) return fail(AF_ERR_ARG, "NULL argument");

@@ -18,7 +18,8 @@ Workloads (autoregressive_normalizing_flow_amd.synth.WORKLOADS):
   tiny_f32       one 8x8 frame, fp32
 
 Other modes: --schedule-sweep, --pipeline, --cpu-baselines (the oracle on
-every workload), --copy-calibration, and --summarize-trace /
+every workload), --affine-sweep (the fused affine kernel HBM-cold beside the
+streaming copy), --copy-calibration, and --summarize-trace /
 --summarize-counters (turn rocprofv3 CSV output into the summaries kept under
 profiles/).
 """
@@ -219,10 +220,12 @@ def cpu_baselines(torch, synth, jacobi_tokens, seq_tokens):
 # ---------------------------------------------------------------------------
 # kernel-level measurements
 # ---------------------------------------------------------------------------
-def affine_sweep(torch, binding, tokens, reps=5):
+def affine_sweep(torch, binding, tokens, reps=7):
     """The fused affine kernel alone (inverse mode), HBM-cold: `tokens` rows of
     C=48, buffers far larger than the 256 MB Infinity Cache.  Algorithmic
-    bytes: read mu, raw, z, x_old and write x = 20*C bytes per token."""
+    bytes: read mu, raw, z, x_old and write x = 20*C bytes per token.  Beside
+    it, the library's streaming copy moving the same number of bytes (half
+    read, half written): the rate this access pattern can reach here."""
     C = 48
     head = torch.randn(tokens, 2 * C, device="cuda")
     z = torch.randn(tokens, C, device="cuda")
@@ -230,20 +233,30 @@ def affine_sweep(torch, binding, tokens, reps=5):
     part = torch.empty(binding.afk_affine_partials_bytes(1, tokens, C), dtype=torch.uint8,
                        device="cuda")
     res = torch.empty(1, 2, device="cuda")
-    binding.afk_affine(0, head, z, x, 1, tokens, C, res, part)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for a, b in ev:
-        a.record()
-        binding.afk_affine(0, head, z, x, 1, tokens, C, res, part)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
     nbytes = 20 * C * tokens
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    ms = timed(lambda: binding.afk_affine(0, head, z, x, 1, tokens, C, res, part))
     del head, z, x, part
-    return {"tokens": tokens, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
-            "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    src = torch.empty(nbytes // 2 // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: binding.afk_stream_copy(src, dst))
+    del src, dst
+    gbs, gbs_copy = nbytes / ms / 1e6, nbytes / ms_copy / 1e6
+    return {"tokens": tokens, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "copy_GB/s": round(gbs_copy, 1),
+            "vs_copy": round(gbs / gbs_copy, 3)}
 
 
 def kernel_sources_hash():
@@ -583,6 +596,9 @@ def main():
     ap.add_argument("--graphs", action="store_true",
                     help="replay the captured Jacobi update as a HIP graph instead "
                          "of launching every kernel directly")
+    ap.add_argument("--affine-sweep", action="store_true",
+                    help="print only the HBM-cold sweep of the fused affine kernel and the "
+                         "streaming copy beside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to scale HBM counters)")
     ap.add_argument("--pipeline", action="store_true",
@@ -617,11 +633,13 @@ def main():
 
     import torch
     if args.copy_calibration:
-        # a plain copy of known size: 256 MiB read + 256 MiB written per launch
+        # a plain copy of known size: 256 MiB read + 256 MiB written per
+        # launch, by the library's streaming copy kernel
+        from autoregressive_normalizing_flow_amd import binding
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            binding.afk_stream_copy(src, dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}))
         return
@@ -633,6 +651,11 @@ def main():
     from autoregressive_normalizing_flow_amd import binding
     binding.load_library()
     assert torch.cuda.is_available(), "no GPU"
+    if args.affine_sweep:
+        print(json.dumps({"affine_hbm_sweep": [affine_sweep(torch, binding, t)
+                                               for t in (1 << 20, 1 << 22, 1 << 24)]}),
+              flush=True)
+        return
     if args.pipeline:
         print(json.dumps(pipeline_bench(torch, binding, synth, max(args.steps, 1),
                                         args.graphs, args.fused_refresh,

@@ -307,6 +307,13 @@ af_status afk_affine(int mode, const float *head, const float *src, float *dst,
 af_status afk_affine_noalloc(int mode, const float *head, const float *src, float *dst,
                              int N, int rows_per_sample, int C, float *res, void *stream);
 
+/* Streaming device copy dst[0, bytes) = src[0, bytes): the bandwidth
+ * reference the fused affine kernel is measured against (contiguous range per
+ * workgroup, four 16-byte non-temporal loads in flight per thread).  src and
+ * dst are device pointers, 16-byte aligned, not overlapping; bytes is a
+ * multiple of 16 (0 is a no-op).  AF_ERR_ARG otherwise.  Stream-ordered. */
+af_status afk_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* bf16 MFMA GEMM y[M, N] = a[M, K] * w[N, K]^T + bias[N] (bias may be NULL),
  * fp32 out, for unit parity.  a, w are bf16 bit patterns, row-major;
  * K % 64 == 0, N % 64 == 0; a and w below 4 GiB each (AF_ERR_UNSUPPORTED

@@ -169,6 +169,11 @@ int main() {
   CHECK(afk_affine(0, buf, buf, buf, 1, 4, 4, buf, buf, 1024, 0, nullptr) == AF_ERR_ARG);
   CHECK(afk_affine(0, buf, buf, other, 1, 4, 4, buf, buf, 0, 0, nullptr) == AF_ERR_WORKSPACE);
   CHECK(afk_gemm_bf16(buf, buf, nullptr, other, 4, 60, 64, nullptr) == AF_ERR_ARG);
+  CHECK(afk_stream_copy(buf, other, 0, nullptr) == AF_OK);
+  CHECK(afk_stream_copy(nullptr, other, 16, nullptr) == AF_ERR_ARG);
+  CHECK(afk_stream_copy(buf, other, 24, nullptr) == AF_ERR_ARG);
+  CHECK(afk_stream_copy((char*)buf + 8, other, 16, nullptr) == AF_ERR_ARG);
+  CHECK(afk_stream_copy(buf, (char*)buf + 64, 128, nullptr) == AF_ERR_ARG);
 
   std::printf("%s: %d failed checks\n", failures ? "FAIL" : "OK", failures);
   return failures ? 1 : 0;

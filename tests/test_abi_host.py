@@ -167,6 +167,17 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     lib.af_plan_destroy(h)
 
 
+def test_stream_copy_validation(lib):
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)
+    assert lib.afk_stream_copy(a, b, 0, None) == B.AF_OK          # nothing to do
+    assert lib.afk_stream_copy(None, b, 16, None) == B.AF_ERR_ARG
+    assert lib.afk_stream_copy(a, b, 24, None) == B.AF_ERR_ARG     # not whole 16-byte words
+    assert lib.afk_stream_copy(ctypes.c_void_p((1 << 20) + 8), b, 16, None) == B.AF_ERR_ARG
+    # overlapping ranges, either order
+    assert lib.afk_stream_copy(a, ctypes.c_void_p((1 << 20) + 64), 128, None) == B.AF_ERR_ARG
+    assert lib.afk_stream_copy(ctypes.c_void_p((1 << 20) + 64), a, 128, None) == B.AF_ERR_ARG
+
+
 def test_stack_restrictions(lib):
     st, h = make_plan(lib, T=2)
     assert st == B.AF_OK

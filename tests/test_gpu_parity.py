@@ -47,7 +47,10 @@ def test_gemm_bf16_unit(B, M, N, K):
     assert rel_l2(to_np(y), ref) < 1e-6
 
 
-@pytest.mark.parametrize("N,rows,C", [(3, 77, 48), (1, 1560, 48), (2, 5, 16)])
+# (2, 349531, 48): above the size where the kernel streams (four rows in
+# flight per thread, non-temporal access), with a ragged last pass
+@pytest.mark.parametrize("N,rows,C", [(3, 77, 48), (1, 1560, 48), (2, 5, 16),
+                                      (2, 349531, 48)])
 def test_affine_unit_both_modes(B, N, rows, C):
     say("affine", N, rows, C)
     rng = np.random.default_rng(rows)
@@ -75,6 +78,16 @@ def test_affine_unit_both_modes(B, N, rows, C):
     r = to_np(res)
     assert np.all(rel_err(r[:, 0], -ls.sum(axis=(1, 2))) < 1e-4)
     assert np.all(r[:, 1] == 0)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 26) + 48])
+def test_stream_copy_exact(B, nbytes):
+    say("stream copy", nbytes)
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    B.afk_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
 
 
 def test_affine_flags_nonfinite(B):
