@@ -44,6 +44,10 @@ constexpr int ATT_KT = 64;    // keys per tile
 // largest score stays in [2^-32, 2^8] (no overflow, no underflow to zero).
 constexpr float RESCALE_LOG2 = 8.0f;
 constexpr float RESCALE_LOW = 32.0f;
+// The same window as fp32 bit patterns of p: 2^8 and 2^-32.
+constexpr unsigned F32_2P8 = 0x43800000u;
+constexpr unsigned F32_2M32 = 0x2F800000u;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Chunk slots merged per memory round trip.
 constexpr int ATT_MAXC = 4;
 // Cache-policy operand of the buffer builtins: sc1, agent-coherent access.
@@ -987,6 +991,12 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   // 16-byte slot of chunk c in row r of a K (or Q) tile and of a Vt tile
   auto swzk = [](int c, int r) { return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
   auto swzv = [](int c, int r) { return c ^ ((r >> 1) & 7); };
+  // Key held by LDS row r of a K tile: bits 2 and 3 of the row swapped.  The
+  // scores of LDS rows {16g + 4h + i, 16g + 8 + 4h + i} (i < 4) sit in lane
+  // half h, and with this order they are keys 16g + 8h .. 16g + 8h + 7, the
+  // keys of that lane half's Vt fragment: the scores feed the P V MFMAs as
+  // they are, with Vt in plain key order.
+  auto krow = [](int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); };
   typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
   __shared__ __attribute__((aligned(1024))) char smem[STAGES][2 * KBYTES];
 
@@ -1032,8 +1042,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   for (int i = 0; i < NI / 4; ++i) {
     const int q = wave + 4 * i;
     {
+      // LDS row r holds key krow(r) of the tile (see the P operand below)
       const int r = q * (64 / CPR) + lane / CPR, s = lane % CPR, c = swzk(s, r);
-      koff[i] = (uint32_t)((r * DH + c * 8) * 2);
+      koff[i] = (uint32_t)((krow(r) * DH + c * 8) * 2);
     }
     {
       const int r = 8 * q + (lane >> 3), s = lane & 7, c = swzv(s, r);
@@ -1065,17 +1076,14 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
 
   bf16x8 qf[KS];   // this lane's query fragments, read from LDS in the prologue
   float m_run = 0.f;
-  f32x16 acc_o[DB], acc_l, negm;
+  f32x16 acc_o[DB], negm;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    acc_l[e] = 0.f;
-    negm[e] = 0.f;
-  }
+  for (int e = 0; e < 16; ++e) negm[e] = 0.f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc_o[db] = acc_l;
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+  for (int db = 0; db < DB; ++db) acc_o[db] = negm;
+  // this lane's share of its row's sum of p (its lane half's keys), in two
+  // chains; the halves are added at the end
+  float lsum[2] = {0.f, 0.f};
 
   // scores of tile kt minus the current reference (K from its buffer)
   auto scores = [&](f32x16 (&s)[2], int kt) {
@@ -1085,13 +1093,14 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(stg + kfrag(kb, ks));
+    // the two 32-key halves' chains interleaved
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][0], qf[0], negm, 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][0], qf[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[0], negm, 0, 0, 0);
+    for (int ks = 1; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
+      for (int kb = 0; kb < 2; ++kb)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
-    }
   };
   // softmax of tile kt's scores and its row-sum and P V MFMAs (V from its
   // buffer)
@@ -1099,45 +1108,66 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
     const char* stg = &smem[kt % STAGES][0];
     const int key0 = (t_begin + kt) * ATT_KT;
     const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
-    if (need_mask) {
-      asm volatile("" ::: "memory");
+    auto mask = [&]() {
+      if (need_mask) {
+        asm volatile("" ::: "memory");
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > qpos || key >= k_end) s[kb][r] = -INFINITY;
-        }
-    }
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + krow(kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3));
+            if (key > qpos || key >= k_end) s[kb][r] = -INFINITY;
+          }
+      }
+    };
+    mask();
+    // p = 2^(s - m) against the current reference, and the row's largest p of
+    // the tile from the fp32 bit patterns (p >= 0, so their unsigned order is
+    // the value order: integer maxima, which run beside the exponentials)
     bf16x8 pf[4];
+    unsigned pm = 0u;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i]);
-    float tm[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x16& v = s[c >> 1];
-      const int o = 8 * (c & 1);
-      tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]),
-                    fmaxf(fmaxf(v[o + 3], v[o + 4]), fmaxf(fmaxf(v[o + 5], v[o + 6]), v[o + 7])));
-    }
-    float t = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i]);
+        pm = max(pm, __float_as_uint(e));
+        pf[g][i] = (bf16)e;
+      }
     {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
-                                                       false, false);
-      t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(pm, pm, false, false);
+      pm = max(sw[0], sw[1]);
     }
-    const bool move = t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
+    // The reference moves when the row's largest p leaves [2^-32, 2^8] (an
+    // overflow to inf included); a row whose keys of this tile are all masked
+    // (keys key0 .. key0 + 63, all above its position) keeps it.
+    const bool move = pm > F32_2P8 || (key0 <= qpos && pm < F32_2M32);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       asm volatile("" ::: "memory");
+      // the scores again (K is still in this tile's buffer) and the row maximum
+      scores(s, kt);
+      mask();
+      float tm[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& v = s[c >> 1];
+        const int o = 8 * (c & 1);
+        tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]),
+                      fmaxf(fmaxf(v[o + 3], v[o + 4]), fmaxf(fmaxf(v[o + 5], v[o + 6]), v[o + 7])));
+      }
+      float t = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                         false, false);
+        t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       const float dm = move ? t : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-dm);
       m_run += dm;
 #pragma unroll
       for (int e = 0; e < 16; ++e) negm[e] = -m_run;
-      acc_l *= alpha;
+      lsum[0] *= alpha;
+      lsum[1] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
 #pragma unroll
@@ -1149,17 +1179,21 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // keys {16g + 4h + i, 16g + 8 + 4h + i} -> keys 16g + 8h + i
-      u32x4 pd = __builtin_bit_cast(u32x4, pf[g]);
-      const auto s02 = __builtin_amdgcn_permlane32_swap(pd[0], pd[2], false, false);
-      const auto s13 = __builtin_amdgcn_permlane32_swap(pd[1], pd[3], false, false);
-      pd = u32x4{s02[0], s13[0], s02[1], s13[1]};
-      const bf16x8 pk = __builtin_bit_cast(bf16x8, pd);
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk, acc_l, 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)(stg + vfrag(db, g)), pk, acc_o[db], 0, 0, 0);
+            *(const bf16x8*)(stg + vfrag(db, g)), pf[g], acc_o[db], 0, 0, 0);
+      // row sums of the same bf16 p: 2-term dot products with (1, 1)
+      const u32x4 pw = __builtin_bit_cast(u32x4, pf[g]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // (a variable of its own: clang mis-reads __builtin_bit_cast of a
+        // vector element, taking element 0)
+        const unsigned pair = pw[w];
+        lsum[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                                      bf16x2{(bf16)1.0f, (bf16)1.0f},
+                                                      lsum[w & 1], false);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -1225,9 +1259,16 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
+  // the row sum: both chains, both lane halves
+  float l_row = lsum[0] + lsum[1];
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_row),
+                                                     __float_as_uint(l_row), false, false);
+    l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (n_chunks == 1) {
     if (active && t_q < R) {
-      const float inv = 1.0f / acc_l[0];
+      const float inv = 1.0f / l_row;
       bf16* orow = a.out + ((size_t)n * R + t_q) * d + head * DH + 4 * hh;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1246,7 +1287,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   const int tq = wave * 32 + j;
   if (active) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)u * SLOT);
-    const float l = acc_l[0];
+    const float l = l_row;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1278,8 +1319,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   attn32_merge<DH>(a, u - chunk, n_chunks, tq, t_q, n, head, hh);
 }
 
+// Three blocks per CU at d_h 64 (at most 168 registers), two at d_h 128.
 template <int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 3 : 2))) void
 attn_dma_kernel(AttnArgs a) {
   attn_dma_body<DH>(a);
 }
