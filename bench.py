@@ -471,15 +471,17 @@ def summarize_trace(d, top):
 # kernel class of a kernel name in the inverse path (the forward's split-mode
 # kernels, which carry bf16 hi + lo operands, are listed but not classed)
 CLASS_PATTERNS = {
-    "attention": ("attn_bf16_kernel", "false>"),
-    "affine": ("affine_kernel<0", ""),
+    "attention": (("attn_dma_kernel", ""), ("attn32_kernel", ""),
+                  ("attn_bf16_kernel", "false>")),
+    "affine": (("affine_kernel<0", ""),),
 }
 
 
 def _class_of(name):
-    for cls, (a, b) in CLASS_PATTERNS.items():
-        if a in name and b in name:
-            return cls
+    for cls, pats in CLASS_PATTERNS.items():
+        for a, b in pats:
+            if a in name and b in name:
+                return cls
     return None
 
 
