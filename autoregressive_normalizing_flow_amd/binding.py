@@ -117,6 +117,10 @@ def load_library() -> ctypes.CDLL:
     L.afk_affine_noalloc.restype = st
     L.afk_stream_copy.argtypes = [_P, _P, sz, _P]
     L.afk_stream_copy.restype = st
+    L.afk_attention_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.afk_attention_workspace_bytes.restype = sz
+    L.afk_attention.argtypes = [_P, _P, _P, _P, i, i, i, i, i, i, _P, sz, _P]
+    L.afk_attention.restype = st
     L.afk_gemm_bf16.argtypes = [_P, _P, _P, _P, i, i, i, _P]
     L.afk_gemm_bf16.restype = st
     L.af_status_str.argtypes = [st]
@@ -400,6 +404,24 @@ def afk_affine_noalloc(mode: int, head, src, dst, N: int, rows: int, C: int, res
     L = load_library()
     _check(L.afk_affine_noalloc(mode, _ptr(head), _ptr(src), _ptr(dst), N, rows, C, _ptr(res),
                                 _stream(stream)), "afk_affine_noalloc")
+
+
+def afk_attention(q: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, pos_base: int,
+                  stream=None) -> torch.Tensor:
+    """One layer's bf16 attention over a KV cache: q [N, R, H*dh] (times
+    log2(e)/sqrt(dh)), kc [N, H, Lcap, dh], vt [N, H, dh, Lcap]; returns out
+    [N, R, H*dh] bf16."""
+    assert q.dtype == kc.dtype == vt.dtype == torch.bfloat16
+    N, R, d = q.shape
+    _, H, Lcap, dh = kc.shape
+    assert d == H * dh and tuple(vt.shape) == (N, H, dh, Lcap)
+    L = load_library()
+    nb = int(L.afk_attention_workspace_bytes(N, R, H, dh, pos_base))
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    _check(L.afk_attention(_ptr(q), _ptr(kc), _ptr(vt), _ptr(out), N, R, H, dh, Lcap, pos_base,
+                           _ptr(ws), ws.numel(), _stream(stream)), "afk_attention")
+    return out
 
 
 def afk_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

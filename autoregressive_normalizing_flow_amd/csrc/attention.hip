@@ -39,9 +39,13 @@ namespace af {
 // ---------------------------------------------------------------------------
 constexpr int ATT_QT = 128;   // queries per unit
 constexpr int ATT_KT = 64;    // keys per tile
-// Lazy softmax reference: p = 2^(s - m) with m moved only when the tile's
-// largest score leaves [m - RESCALE_LOW, m + RESCALE_LOG2], so p of a row's
-// largest score stays in [2^-32, 2^8] (no overflow, no underflow to zero).
+// Lazy softmax reference: p = 2^(s - m) with m moved up only when a tile's
+// largest score exceeds m + RESCALE_LOG2 (p stays at most 2^8: no overflow),
+// and down, to the tile's largest score, only while the row has no mass yet
+// (its first tile with a key may lie far below the initial m = 0).  A row
+// with mass never moves down: a later tile far below it would otherwise
+// rescale O by 2^(-dm), beyond fp32 once dm < -128, and its keys' weights
+// are negligible against the mass anyway.
 constexpr float RESCALE_LOG2 = 8.0f;
 constexpr float RESCALE_LOW = 32.0f;
 // The same window as fp32 bit patterns of p: 2^8 and 2^-32.
@@ -279,9 +283,10 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 
     // online softmax (base 2; q carries log2(e) / sqrt(dh)) per query.  The
     // reference m is lazy: it moves only when some row's largest score in the
-    // tile leaves [m - RESCALE_LOW, m + RESCALE_LOG2]; until then p = 2^(s - m)
-    // is at most 2^RESCALE_LOG2 (harmless in fp32 and in bf16) and the
-    // accumulators are not touched.  The same m scales O and the row sum, so
+    // tile exceeds m + RESCALE_LOG2, or lies below m - RESCALE_LOW while the
+    // row has no mass yet; until then p = 2^(s - m) is at most 2^RESCALE_LOG2
+    // (harmless in fp32 and in bf16) and the accumulators are not touched.
+    // The same m scales O and the row sum, so
     // the result is that of the exact update.  Tiles wholly below every query
     // of the wave and inside [k_begin, k_end) skip the masking; both tests are
     // wave-uniform branches (the empty asm keeps the compiler from turning
@@ -312,15 +317,19 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
       t = fmaxf(t, __shfl_xor(t, 32, AF_WAVE));
       tmax[qb] = t;
       // (a row with every key masked, t = -inf, keeps its reference)
-      move |= t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
+      move |= t > RESCALE_LOG2 ||
+              (t < -RESCALE_LOW && t > -INFINITY && acc_l[qb][0] == 0.f);
     }
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float t = tmax[qb];
-        const float dm = (t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY)) ? t : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-dm);
+        const bool up = t > RESCALE_LOG2;
+        const bool down = t < -RESCALE_LOW && t > -INFINITY && acc_l[qb][0] == 0.f;
+        const float dm = (up || down) ? t : 0.f;
+        // a downward move finds O and l still zero: nothing to rescale
+        const float alpha = up ? __builtin_amdgcn_exp2f(-dm) : 1.0f;
         m_run[qb] += dm;
         negm[qb] = f32x4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
         acc_l[qb] *= alpha;
@@ -848,11 +857,13 @@ __device__ __forceinline__ void attn32_body(const AttnArgs& a) {
                                                        false, false);
       t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const bool move = t > RESCALE_LOG2 || (t < -RESCALE_LOW && t > -INFINITY);
+    const bool up = t > RESCALE_LOG2;
+    const bool move = up || (t < -RESCALE_LOW && t > -INFINITY && acc_l[0] == 0.f);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       asm volatile("" ::: "memory");
       const float dm = move ? t : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      // a downward move finds O and l still zero: nothing to rescale
+      const float alpha = up ? __builtin_amdgcn_exp2f(-dm) : 1.0f;
       m_run += dm;
 #pragma unroll
       for (int e = 0; e < 16; ++e) negm[e] = -m_run;
@@ -1084,6 +1095,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   // this lane's share of its row's sum of p (its lane half's keys), in two
   // chains; the halves are added at the end
   float lsum[2] = {0.f, 0.f};
+  bool row_mass = false;   // the row's running sum is no longer zero
 
   // scores of tile kt minus the current reference (K from its buffer)
   auto scores = [&](f32x16 (&s)[2], int kt) {
@@ -1138,10 +1150,12 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(pm, pm, false, false);
       pm = max(sw[0], sw[1]);
     }
-    // The reference moves when the row's largest p leaves [2^-32, 2^8] (an
-    // overflow to inf included); a row whose keys of this tile are all masked
-    // (keys key0 .. key0 + 63, all above its position) keeps it.
-    const bool move = pm > F32_2P8 || (key0 <= qpos && pm < F32_2M32);
+    // The reference moves up when the row's largest p exceeds 2^8 (an
+    // overflow to inf included), and down while the row has no mass yet when
+    // it is below 2^-32; a row whose keys of this tile are all masked (keys
+    // key0 .. key0 + 63, all above its position) keeps it.
+    const bool up = pm > F32_2P8;
+    const bool move = up || (!row_mass && key0 <= qpos && pm < F32_2M32);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       asm volatile("" ::: "memory");
       // the scores again (K is still in this tile's buffer) and the row maximum
@@ -1162,7 +1176,8 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
         t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       const float dm = move ? t : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      // a downward move finds O and l still zero: nothing to rescale
+      const float alpha = up ? __builtin_amdgcn_exp2f(-dm) : 1.0f;
       m_run += dm;
 #pragma unroll
       for (int e = 0; e < 16; ++e) negm[e] = -m_run;
@@ -1176,6 +1191,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
         for (int i = 0; i < 8; ++i)
           pf[g][i] = (bf16)__builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + i] - dm);
     }
+    // the row has mass once a tile put p >= 2^-32 into it (a moved reference
+    // makes the tile's largest p 1)
+    row_mass = row_mass || move || pm >= F32_2M32;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {

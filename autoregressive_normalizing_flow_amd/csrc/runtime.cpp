@@ -1185,6 +1185,36 @@ af_status afk_affine(int mode, const float* head, const float* src, float* dst,
   return AF_OK;
 }
 
+size_t afk_attention_workspace_bytes(int N, int R, int H, int dh, int pos_base) {
+  if (N < 1 || R < 1 || H < 1 || pos_base < 0 || (dh != 32 && dh != 64 && dh != 128))
+    return 0;
+  const size_t part = af::attention_partial_floats(N, R, H, dh, pos_base) * sizeof(float);
+  const size_t tick = af::attention_tickets(N, R, H) * sizeof(unsigned);
+  return ((part + 255) / 256) * 256 + ((tick + 255) / 256) * 256;
+}
+
+af_status afk_attention(const void* q, const void* kc, const void* vt, void* out, int N,
+                        int R, int H, int dh, int Lcap, int pos_base, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!q || !kc || !vt || !out || !ws) return fail(AF_ERR_ARG, "NULL argument");
+  if (any_misaligned(q, kc, vt, out, ws)) return fail(AF_ERR_ARG, "pointers must be 16-byte aligned");
+  if (N < 1 || R < 1 || H < 1 || pos_base < 0) return fail(AF_ERR_ARG, "bad sizes");
+  if (dh != 32 && dh != 64 && dh != 128) return fail(AF_ERR_UNSUPPORTED, "dh must be 32, 64 or 128");
+  if (Lcap < 64 || Lcap % 64 != 0 || (long)pos_base + R > Lcap)
+    return fail(AF_ERR_ARG, "need Lcap % 64 == 0 and pos_base + R <= Lcap");
+  if ((long)H * dh > (1 << 16)) return fail(AF_ERR_UNSUPPORTED, "H * dh too large");
+  const size_t need = afk_attention_workspace_bytes(N, R, H, dh, pos_base);
+  if (ws_bytes < need) return fail(AF_ERR_WORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t part = af::attention_partial_floats(N, R, H, dh, pos_base) * sizeof(float);
+  unsigned* tickets = (unsigned*)((char*)ws + ((part + 255) / 256) * 256);
+  AF_HIP(af::launch_fill_u32(tickets, 0u, af::attention_tickets(N, R, H), st));
+  hipError_t e = af::launch_attention(true, q, kc, vt, out, (float*)ws, tickets, N, R, H, dh,
+                                      H * dh, Lcap, pos_base, st);
+  if (e != hipSuccess) return fail(AF_ERR_HIP, hipGetErrorString(e));
+  return AF_OK;
+}
+
 af_status afk_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return AF_OK;
   if (!src || !dst) return fail(AF_ERR_ARG, "NULL argument");

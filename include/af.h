@@ -314,6 +314,27 @@ af_status afk_affine_noalloc(int mode, const float *head, const float *src, floa
  * multiple of 16 (0 is a no-op).  AF_ERR_ARG otherwise.  Stream-ordered. */
 af_status afk_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* One layer's bf16 causal attention over a KV cache (STARFlow-V notes,
+ * 关键设计 3: the block's queries attend to every cached key up to their own
+ * position), as the Jacobi path runs it, for unit parity at any shape:
+ *   out[n, t, h*dh + e] = sum_j softmax_j(q_t . k_j / sqrt(dh)) v_j[e]
+ * over keys j = 0 .. pos_base + t of head h.  Layouts (bf16 bit patterns,
+ * device pointers):
+ *   q    [N, R, H*dh]        holding Q * log2(e) / sqrt(dh), the QKV GEMM's
+ *                            storage (the softmax is taken in base 2)
+ *   kc   [N][H][Lcap][dh]    keys by position
+ *   vt   [N][H][dh][Lcap]    values, transposed
+ *   out  [N, R, H*dh]
+ * dh is 32, 64 or 128; Lcap % 64 == 0 and pos_base + R <= Lcap; cache rows at
+ * or past pos_base + R are not read into the result.  ws is device scratch of
+ * afk_attention_workspace_bytes(N, R, H, dh, pos_base) bytes (key-chunk
+ * partials and merge tickets, cleared by the call).  Every pointer 16-byte
+ * aligned; AF_ERR_ARG / AF_ERR_WORKSPACE otherwise.  Stream-ordered. */
+size_t afk_attention_workspace_bytes(int N, int R, int H, int dh, int pos_base);
+af_status afk_attention(const void *q, const void *kc, const void *vt, void *out,
+                        int N, int R, int H, int dh, int Lcap, int pos_base,
+                        void *ws, size_t ws_bytes, void *stream);
+
 /* bf16 MFMA GEMM y[M, N] = a[M, K] * w[N, K]^T + bias[N] (bias may be NULL),
  * fp32 out, for unit parity.  a, w are bf16 bit patterns, row-major;
  * K % 64 == 0, N % 64 == 0; a and w below 4 GiB each (AF_ERR_UNSUPPORTED

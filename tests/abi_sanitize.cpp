@@ -170,6 +170,12 @@ int main() {
   CHECK(afk_affine(0, buf, buf, other, 1, 4, 4, buf, buf, 0, 0, nullptr) == AF_ERR_WORKSPACE);
   CHECK(afk_gemm_bf16(buf, buf, nullptr, other, 4, 60, 64, nullptr) == AF_ERR_ARG);
   CHECK(afk_stream_copy(buf, other, 0, nullptr) == AF_OK);
+  CHECK(afk_attention_workspace_bytes(1, 100, 4, 64, 300) > 0);
+  CHECK(afk_attention_workspace_bytes(1, 100, 4, 48, 300) == 0);
+  CHECK(afk_attention(buf, buf, buf, other, 1, 100, 4, 48, 448, 300, buf, 1 << 20, nullptr) == AF_ERR_UNSUPPORTED);
+  CHECK(afk_attention(buf, buf, buf, other, 1, 100, 4, 64, 400, 300, buf, 1 << 20, nullptr) == AF_ERR_ARG);
+  CHECK(afk_attention(buf, buf, buf, other, 1, 100, 4, 64, 448, 400, buf, 1 << 20, nullptr) == AF_ERR_ARG);
+  CHECK(afk_attention(buf, buf, buf, other, 1, 100, 4, 64, 448, 300, buf, 16, nullptr) == AF_ERR_WORKSPACE);
   CHECK(afk_stream_copy(nullptr, other, 16, nullptr) == AF_ERR_ARG);
   CHECK(afk_stream_copy(buf, other, 24, nullptr) == AF_ERR_ARG);
   CHECK(afk_stream_copy((char*)buf + 8, other, 16, nullptr) == AF_ERR_ARG);

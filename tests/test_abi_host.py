@@ -167,6 +167,27 @@ def test_entry_points_reject_bad_arguments_before_device_work(lib):
     lib.af_plan_destroy(h)
 
 
+def test_attention_validation(lib):
+    a = ctypes.c_void_p(1 << 20)
+    ws = lib.afk_attention_workspace_bytes(1, 100, 4, 64, 300)
+    assert ws > 0 and lib.afk_attention_workspace_bytes(1, 100, 4, 48, 300) == 0
+    ok = dict(N=1, R=100, H=4, dh=64, Lcap=448, P=300, ws=ws)
+
+    def call(**kw):
+        c = dict(ok)
+        c.update(kw)
+        return lib.afk_attention(a, a, a, a, c["N"], c["R"], c["H"], c["dh"], c["Lcap"],
+                                 c["P"], a, c["ws"], None)
+    assert call(dh=48) == B.AF_ERR_UNSUPPORTED
+    assert call(Lcap=400) == B.AF_ERR_ARG            # not a multiple of 64
+    assert call(P=400) == B.AF_ERR_ARG               # pos_base + R beyond Lcap
+    assert call(R=0) == B.AF_ERR_ARG
+    assert call(ws=ws - 1) == B.AF_ERR_WORKSPACE
+    assert lib.afk_attention(None, a, a, a, 1, 100, 4, 64, 448, 300, a, ws, None) == B.AF_ERR_ARG
+    assert lib.afk_attention(ctypes.c_void_p((1 << 20) + 2), a, a, a, 1, 100, 4, 64, 448, 300,
+                             a, ws, None) == B.AF_ERR_ARG
+
+
 def test_stream_copy_validation(lib):
     a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)
     assert lib.afk_stream_copy(a, b, 0, None) == B.AF_OK          # nothing to do
