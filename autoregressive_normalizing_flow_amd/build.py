@@ -34,7 +34,8 @@ COMMON_FLAGS = [
     "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["runtime.cpp", "pointwise.hip", "gemm.hip", "attention.hip", "noalloc.hip"]
+SOURCES = ["runtime.cpp", "pointwise.hip", "gemm.hip", "attention.hip", "noalloc.hip",
+           "loop.hip"]
 
 
 def _compile(src: str) -> str:

@@ -150,6 +150,35 @@ inline size_t attention_tickets(int N, int R, int H) {
   return (size_t)N * H * ((R + 127) / 128);
 }
 
+// ---- the Jacobi loop on the device (small fp32 blocks) -----------------------
+constexpr int kLoopMaxLayers = 8;
+struct LoopLayer {
+  const float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o, *ln2_g, *ln2_b, *w_1, *b_1, *w_2, *b_2;
+};
+struct LoopArgs {
+  const float *w_in, *b_in, *pos, *ln_f_g, *ln_f_b, *w_head, *b_head;
+  LoopLayer layers[kLoopMaxLayers];
+  float* kc[kLoopMaxLayers];   // K cache of each layer  [N][H][Lcap][dh]
+  float* vt[kLoopMaxLayers];   // V cache (transposed)   [N][H][dh][Lcap]
+  int n_layers, C, d, H, dh, dmlp, Lcap;
+  const float* z;        // [N, L, C]
+  float* x;              // [N, L, C] written block by block
+  const float* x_init;   // init 1 (given)
+  const float* x_last;   // the token before the sequence, [N, C], or NULL (zeros)
+  int N, L, B, P, dir, init, F, max_iters;
+  float tau;             // <= 0: exactly min(max_iters, block) updates
+  int* iters_host;       // host-mapped: the block counts of this stack block
+  float* res_host;       // host-mapped: the last update's residual pairs [N][2]
+  unsigned* bad_host;    // host-mapped: 1 + the block that met a non-finite sum
+};
+// Rows N x min(B, L) <= 64, d 64 or 128, d_h 32 or 64, C % 4 == 0, C <= 64,
+// d_mlp % 64 == 0, at most kLoopMaxLayers layers.
+bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_layers,
+                           int Lcap);
+// One workgroup runs the whole Jacobi inverse of one AF block (every block of
+// the sequence, the stop tests and the cache refreshes).
+hipError_t launch_jacobi_loop(const LoopArgs& a, hipStream_t st);
+
 // Record a failure for af_last_error() from another translation unit
 // (defined with the ABI in runtime.cpp); a HIP failure also clears the
 // runtime's last-error state.  Returns status.

@@ -1,0 +1,445 @@
+// Jacobi inverse of one affine AF block with the whole loop on the device, for
+// small fp32 blocks (STARFlow-V notes, 关键设计 3: block-wise Jacobi with a KV
+// cache and a residual stop; 关键设计 1: the affine AF update).
+//
+// One workgroup runs every Jacobi block of the sequence in order: the
+// shifted embedding, every layer (LayerNorm, QKV with K/V into the cache,
+// causal attention over the cache, output projection, LayerNorm, GELU MLP),
+// the final LayerNorm and head, the affine update and the per-sample residual
+// sums; then it takes the stop test itself (every sample's
+// sum (x' - x)^2 / sum x'^2 below tau, or the update cap) and refreshes the
+// block's cache rows from its final tokens after an early stop.  No kernel
+// launch and no host read-back per update: the host launches once per AF
+// block and reads the iteration counts at the end.
+//
+// The block's activations live in LDS (rows M = N x B <= 64, d 64 or 128);
+// the weights are read from global memory (L2-resident at these sizes), each
+// thread loading a whole weight row into registers before it multiplies (one
+// memory round trip per output column instead of one per step), and the KV
+// cache is the workspace's, in the layout the other kernels use, so a later
+// call continues from it.  Attention runs one wave per (sample, head): the
+// lanes take 64 keys at a time for the scores of up to 16 rows, then the
+// value dimensions for P V, so each K row and V^T chunk is loaded once for
+// all the rows.  Arithmetic is fp32 throughout, sums in a fixed order
+// (results do not depend on scheduling).
+#include "common.h"
+#include "kernels.h"
+
+namespace af {
+
+namespace {
+
+constexpr int LT = 256;   // threads
+constexpr int UC = 64;    // MLP hidden columns per chunk
+constexpr int RG = 16;    // attention rows per wave pass
+constexpr int KT = 64;    // attention keys per wave pass (one per lane)
+
+// Shared-memory carve-up of one block's state (floats).
+struct LoopLds {
+  int xb, zb, prev, h, a, q, o, u, hd, ps, red;
+  int total;
+};
+
+__host__ __device__ LoopLds loop_lds(int M, int N, int C, int d) {
+  LoopLds l{};
+  int off = 0;
+  auto take = [&](int n) { const int o = off; off += (n + 3) & ~3; return o; };
+  l.xb = take(M * C);
+  l.zb = take(M * C);
+  l.prev = take(N * C);
+  l.h = take(M * d);
+  l.a = take(M * d);
+  l.q = take(M * d);
+  l.o = take(M * d);
+  l.u = take(M * UC);
+  l.hd = take(M * 2 * C);
+  l.ps = take(LT / 64 * RG * KT);   // one probability strip per wave
+  l.red = take(4 * LT + 64);
+  l.total = off;
+  return l;
+}
+
+// y[m][n] = X[m] . W[n] (+ bias[n]) for n < Nout, m < M, contraction length
+// K; X in LDS with row stride ldx, W row-major with row stride ldw (global).
+// One thread per output column: its W row goes to registers first (K / 4
+// independent 16-byte loads), then row by row against X (two partial sums,
+// added at the end); epi(m, n, value) consumes each result.
+template <int K, class Epi>
+__device__ void linear(const float* X, int ldx, int M, const float* W, int ldw,
+                       const float* bias, int Nout, Epi epi) {
+  for (int n = threadIdx.x; n < Nout; n += LT) {
+    float4 wr[K / 4];
+    const float* wp = W + (size_t)n * ldw;
+#pragma unroll
+    for (int k = 0; k < K / 4; ++k) wr[k] = *(const float4*)(wp + 4 * k);
+    const float bn = bias ? bias[n] : 0.f;
+#pragma clang loop unroll(disable)
+    for (int m = 0; m < M; ++m) {
+      const float* xr = X + m * ldx;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < K / 4; k += 2) {
+        const float4 x0 = *(const float4*)(xr + 4 * k);
+        const float4 x1 = *(const float4*)(xr + 4 * k + 4);
+        acc0 = fmaf(x0.x, wr[k].x, acc0);
+        acc0 = fmaf(x0.y, wr[k].y, acc0);
+        acc0 = fmaf(x0.z, wr[k].z, acc0);
+        acc0 = fmaf(x0.w, wr[k].w, acc0);
+        acc1 = fmaf(x1.x, wr[k + 1].x, acc1);
+        acc1 = fmaf(x1.y, wr[k + 1].y, acc1);
+        acc1 = fmaf(x1.z, wr[k + 1].z, acc1);
+        acc1 = fmaf(x1.w, wr[k + 1].w, acc1);
+      }
+      epi(m, n, (acc0 + acc1) + bn);
+    }
+  }
+}
+
+// out[m] = LayerNorm(in[m]) * g + b over rows of width d (eps 1e-5), one
+// wave per row.
+__device__ void layernorm_rows(const float* in, float* out, int M, int d, const float* g,
+                               const float* b) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int m = wave; m < M; m += LT / 64) {
+    const float* r = in + m * d;
+    float s = 0.f;
+    for (int e = lane; e < d; e += 64) s += r[e];
+    const float mean = wave_sum(s) / d;
+    float v = 0.f;
+    for (int e = lane; e < d; e += 64) {
+      const float t = r[e] - mean;
+      v += t * t;
+    }
+    const float rstd = rsqrtf(wave_sum(v) / d + 1e-5f);
+    for (int e = lane; e < d; e += 64) out[m * d + e] = (r[e] - mean) * rstd * g[e] + b[e];
+  }
+}
+
+// Causal attention of the block rows over the cache, one wave per (sample,
+// head) at a time: for RG rows and KT keys per pass, lane j scores key j0 + j
+// against each row (its K row in registers, the rows' q from LDS), the online
+// softmax per row keeps (max, sum) in registers of every lane, then lane e
+// adds sum_j p_rj V^T[e][j0 + j] for each row (its V^T chunk in registers).
+// Keys past a row's position are masked; cache rows past the last key are
+// never multiplied (their p is 0 and their V is replaced by 0).
+template <int D, int DH>
+__device__ void loop_attention(const LoopArgs& a, const float* q, float* o, float* ps,
+                               const float* kc, const float* vt, int s, int R) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int N = a.N, H = a.H;
+  const float scale = 1.0f / sqrtf((float)DH);
+  float* pw = ps + wave * RG * KT;
+  for (int pair = wave; pair < N * H; pair += LT / 64) {
+    const int nn = pair / H, head = pair - nn * H;
+    const size_t base = (size_t)nn * H + head;
+    const float* kr = kc + base * a.Lcap * DH;
+    const float* vr = vt + base * DH * a.Lcap;
+    for (int t0 = 0; t0 < R; t0 += RG) {
+      const int rows = min(RG, R - t0);
+      const int nkmax = a.P + s + t0 + rows;   // keys of the group's last row
+      float om[RG], ol[RG], oacc[RG];
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        om[r] = -INFINITY;
+        ol[r] = 0.f;
+        oacc[r] = 0.f;
+      }
+      for (int j0 = 0; j0 < nkmax; j0 += KT) {
+        const int j = j0 + lane;
+        const bool kv = j < nkmax;
+        float4 kreg[DH / 4];
+#pragma unroll
+        for (int e = 0; e < DH / 4; ++e)
+          kreg[e] = kv ? *(const float4*)(kr + (size_t)j * DH + 4 * e) : float4{0.f, 0.f, 0.f, 0.f};
+        // this lane's V^T chunk (dimension e = lane), zero past the last key
+        float vv[KT];
+        if (lane < DH) {
+          const float* vp = vr + (size_t)lane * a.Lcap + j0;
+#pragma unroll
+          for (int jj = 0; jj < KT; jj += 4) {
+            const float4 v4 = *(const float4*)(vp + jj);
+            vv[jj] = j0 + jj < nkmax ? v4.x : 0.f;
+            vv[jj + 1] = j0 + jj + 1 < nkmax ? v4.y : 0.f;
+            vv[jj + 2] = j0 + jj + 2 < nkmax ? v4.z : 0.f;
+            vv[jj + 3] = j0 + jj + 3 < nkmax ? v4.w : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          if (r >= rows) continue;
+          const float* qr = q + (nn * R + t0 + r) * D + head * DH;
+          float sv = 0.f;
+#pragma unroll
+          for (int e = 0; e < DH / 4; ++e) {
+            const float4 q4 = *(const float4*)(qr + 4 * e);
+            sv = fmaf(q4.x, kreg[e].x, sv);
+            sv = fmaf(q4.y, kreg[e].y, sv);
+            sv = fmaf(q4.z, kreg[e].z, sv);
+            sv = fmaf(q4.w, kreg[e].w, sv);
+          }
+          sv = (kv && j <= a.P + s + t0 + r) ? sv * scale : -INFINITY;
+          const float mn = fmaxf(om[r], wave_max(sv));
+          const float al = expf(om[r] - mn);
+          const float pv = expf(sv - mn);
+          ol[r] = ol[r] * al + wave_sum(pv);
+          om[r] = mn;
+          oacc[r] *= al;
+          pw[r * KT + lane] = pv;
+        }
+        // the strip is complete before any lane reads it (one wave: LDS
+        // accesses stay in order; the barrier keeps the compiler from
+        // reordering them)
+        __builtin_amdgcn_wave_barrier();
+        if (lane < DH) {
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            if (r >= rows) continue;
+            float acc = oacc[r];
+#pragma unroll
+            for (int jj = 0; jj < KT; jj += 4) {
+              const float4 p4 = *(const float4*)(pw + r * KT + jj);
+              acc = fmaf(p4.x, vv[jj], acc);
+              acc = fmaf(p4.y, vv[jj + 1], acc);
+              acc = fmaf(p4.z, vv[jj + 2], acc);
+              acc = fmaf(p4.w, vv[jj + 3], acc);
+            }
+            oacc[r] = acc;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (lane < DH) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          if (r >= rows) continue;
+          o[(nn * R + t0 + r) * D + head * DH + lane] = oacc[r] / ol[r];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// One Jacobi update (or, with kv_only, the cache refresh: every layer's K/V of
+// the block rows from the current tokens) of block [s, s + R).
+template <int D, int DH>
+__device__ void loop_pass(const LoopArgs& a, float* sm, const LoopLds& L, int s, int R,
+                          bool kv_only) {
+  const int N = a.N, C = a.C, H = a.H, M = N * R;
+  const int tid = threadIdx.x;
+  const float* xb = sm + L.xb;
+  const float* prev = sm + L.prev;
+  float* h = sm + L.h;
+  float* act = sm + L.a;
+  float* q = sm + L.q;
+  float* o = sm + L.o;
+  float* u = sm + L.u;
+  // shift + embed: row m = n R + t takes token t - 1 of the block (the token
+  // before the block at t = 0), position P + s + t
+  for (int idx = tid; idx < M * D; idx += LT) {
+    const int m = idx / D, e = idx - m * D, n = m / R, t = m - n * R;
+    const float* in = t == 0 ? prev + n * C : xb + (m - 1) * C;
+    const float* w = a.w_in + (size_t)e * C;
+    float acc = a.b_in[e] + a.pos[(size_t)(a.P + s + t) * D + e];
+    for (int c = 0; c < C; c += 4) {
+      const float4 w4 = *(const float4*)(w + c);
+      acc = fmaf(in[c], w4.x, acc);
+      acc = fmaf(in[c + 1], w4.y, acc);
+      acc = fmaf(in[c + 2], w4.z, acc);
+      acc = fmaf(in[c + 3], w4.w, acc);
+    }
+    h[idx] = acc;
+  }
+  __syncthreads();
+  for (int l = 0; l < a.n_layers; ++l) {
+    const LoopLayer& w = a.layers[l];
+    float* kc = a.kc[l];
+    float* vt = a.vt[l];
+    layernorm_rows(h, act, M, D, w.ln1_g, w.ln1_b);
+    __syncthreads();
+    // QKV: Q into LDS, K and V of the block rows into the cache
+    linear<D>(act, D, M, w.w_qkv, D, w.b_qkv, 3 * D, [&](int m, int n, float v) {
+      const int which = n / D, hd = n - which * D;
+      if (which == 0) {
+        q[m * D + hd] = v;
+        return;
+      }
+      const int nn = m / R, t = m - nn * R, p = a.P + s + t;
+      const int head = hd / DH, e = hd - head * DH;
+      const size_t base = (size_t)nn * H + head;
+      if (which == 1) kc[(base * a.Lcap + p) * DH + e] = v;
+      else vt[(base * DH + e) * a.Lcap + p] = v;
+    });
+    __syncthreads();   // the cache rows are written (workgroup scope)
+    if (kv_only && l == a.n_layers - 1) return;
+    loop_attention<D, DH>(a, q, o, sm + L.ps, kc, vt, s, R);
+    __syncthreads();
+    // output projection into the residual stream
+    linear<D>(o, D, M, w.w_o, D, w.b_o, D, [&](int m, int n, float v) { h[m * D + n] += v; });
+    __syncthreads();
+    layernorm_rows(h, act, M, D, w.ln2_g, w.ln2_b);
+    __syncthreads();
+    // MLP in hidden chunks of UC columns: u = GELU(a W1^T + b1), h += u W2^T
+    for (int c0 = 0; c0 < a.dmlp; c0 += UC) {
+      linear<D>(act, D, M, w.w_1 + (size_t)c0 * D, D, w.b_1 + c0, UC,
+                [&](int m, int n, float v) { u[m * UC + n] = gelu_erf(v); });
+      __syncthreads();
+      linear<UC>(u, UC, M, w.w_2 + c0, a.dmlp, nullptr, D,
+                 [&](int m, int n, float v) { h[m * D + n] += v; });
+      __syncthreads();
+    }
+    for (int idx = tid; idx < M * D; idx += LT) h[idx] += w.b_2[idx % D];
+    __syncthreads();
+  }
+}
+
+// The affine update of the block from the head output, with each sample's
+// residual pair in red[2 LT + 2n], red[2 LT + 2n + 1] (summed in a fixed
+// order).
+template <int D>
+__device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int R) {
+  const int N = a.N, C = a.C, M = N * R, tid = threadIdx.x;
+  float* xb = sm + L.xb;
+  const float* zb = sm + L.zb;
+  float* h = sm + L.h;
+  float* act = sm + L.a;
+  float* hd = sm + L.hd;
+  float* red = sm + L.red;
+  layernorm_rows(h, act, M, D, a.ln_f_g, a.ln_f_b);
+  __syncthreads();
+  linear<D>(act, D, M, a.w_head, D, a.b_head, 2 * C,
+            [&](int m, int n, float v) { hd[m * 2 * C + n] = v; });
+  __syncthreads();
+  // per-thread partial sums of each sample's rows, then a fixed-order tree
+  for (int n = 0; n < N; ++n) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int idx = tid; idx < R * C; idx += LT) {
+      const int m = n * R + idx / C, c = idx % C;
+      const float mu = hd[m * 2 * C + c];
+      const float ls = 0.5f * tanhf(hd[m * 2 * C + C + c]);
+      const float xn = mu + expf(ls) * zb[m * C + c];
+      const float df = xn - xb[m * C + c];
+      s0 += df * df;
+      s1 += xn * xn;
+    }
+    red[2 * tid] = s0;
+    red[2 * tid + 1] = s1;
+    __syncthreads();
+    for (int w = LT / 2; w > 0; w >>= 1) {
+      if (tid < w) {
+        red[2 * tid] += red[2 * (tid + w)];
+        red[2 * tid + 1] += red[2 * (tid + w) + 1];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      red[2 * LT + 2 * n] = red[0];
+      red[2 * LT + 2 * n + 1] = red[1];
+    }
+    __syncthreads();
+  }
+  // the new iterate (after every thread read the old one)
+  for (int idx = tid; idx < M * C; idx += LT) {
+    const int m = idx / C, c = idx % C;
+    const float mu = hd[m * 2 * C + c];
+    const float ls = 0.5f * tanhf(hd[m * 2 * C + C + c]);
+    xb[idx] = mu + expf(ls) * zb[idx];
+  }
+  __syncthreads();
+}
+
+template <int D, int DH>
+__global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int N = a.N, C = a.C, tid = threadIdx.x;
+  const int nb = (a.L + a.B - 1) / a.B;
+  const LoopLds L = loop_lds(N * min(a.B, a.L), N, C, D);
+  float* xb = sm + L.xb;
+  float* zb = sm + L.zb;
+  float* prev = sm + L.prev;
+  float* red = sm + L.red;
+  // the token before the sequence
+  for (int idx = tid; idx < N * C; idx += LT)
+    prev[idx] = a.x_last ? a.x_last[idx] : 0.f;
+  for (int b = 0; b < nb; ++b) {
+    const int s = b * a.B, R = min(a.B, a.L - s), M = N * R;
+    // z of the block and the first iterate
+    for (int idx = tid; idx < M * C; idx += LT) {
+      const int m = idx / C, c = idx - m * C, n = m / R, t = m - n * R, i = s + t;
+      const size_t g = ((size_t)n * a.L + storage_index(i, a.L, a.dir)) * C + c;
+      zb[idx] = a.z[g];
+      float x0 = 0.f;
+      if (a.init == 1) x0 = a.x_init[g];
+      else if (a.init == 2 && s >= a.F)
+        x0 = a.x[((size_t)n * a.L + storage_index(i - a.F, a.L, a.dir)) * C + c];
+      xb[idx] = x0;
+    }
+    __syncthreads();
+    const int kmax = a.max_iters <= 0 ? R : min(a.max_iters, R);
+    int k = 0;
+    bool bad = false;
+    while (k < kmax) {
+      loop_pass<D, DH>(a, sm, L, s, R, false);
+      loop_affine<D>(a, sm, L, R);
+      ++k;
+      bool all = true;
+      for (int n = 0; n < N; ++n) {
+        const float num = red[2 * LT + 2 * n], den = red[2 * LT + 2 * n + 1];
+        if (!(isfinite(num) && isfinite(den))) bad = true;
+        const float r = den > 0.f ? num / den : (num == 0.f ? 0.f : INFINITY);
+        all = all && r < a.tau;
+      }
+      if (bad || (a.tau > 0.f && all)) break;
+    }
+    // the last update's residual pairs and the block's count
+    if (tid == 0) {
+      for (int n = 0; n < 2 * N; ++n) system_store(&a.res_host[n], red[2 * LT + n]);
+      system_store((unsigned*)&a.iters_host[b], (unsigned)k);
+      if (bad) system_store(a.bad_host, (unsigned)(1 + b));
+    }
+    if (bad) return;
+    // an early stop leaves the cache rows from the previous iterate: recompute
+    // them from the final tokens
+    if (k < R) {
+      __syncthreads();
+      loop_pass<D, DH>(a, sm, L, s, R, true);
+    }
+    // the block's tokens out, and each sample's last token for the next block
+    for (int idx = tid; idx < M * C; idx += LT) {
+      const int m = idx / C, c = idx - m * C, n = m / R, t = m - n * R;
+      a.x[((size_t)n * a.L + storage_index(s + t, a.L, a.dir)) * C + c] = xb[idx];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < N * C; idx += LT) {
+      const int n = idx / C, c = idx - n * C;
+      prev[idx] = xb[((n + 1) * R - 1) * C + c];
+    }
+    __syncthreads();
+  }
+}
+
+bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_layers,
+                           int Lcap) {
+  if (N < 1 || Bc < 1 || H < 1 || (d != 64 && d != 128) || d % H != 0) return false;
+  const int dh = d / H;
+  if (dh != 32 && dh != 64) return false;
+  const int M = N * Bc;
+  if (M > 64 || C % 4 != 0 || C > 64 || Lcap % 64 != 0) return false;
+  if (dmlp % UC != 0 || n_layers < 1 || n_layers > kLoopMaxLayers) return false;
+  return loop_lds(M, N, C, d).total * sizeof(float) <= 64 * 1024;
+}
+
+hipError_t launch_jacobi_loop(const LoopArgs& a, hipStream_t st) {
+  const int Bc = a.B < a.L ? a.B : a.L;
+  const size_t lds = loop_lds(a.N * Bc, a.N, a.C, a.d).total * sizeof(float);
+  const dim3 g(1), b(LT);
+  if (a.d == 64 && a.dh == 32) hipLaunchKernelGGL((jacobi_loop_kernel<64, 32>), g, b, lds, st, a);
+  else if (a.d == 64 && a.dh == 64) hipLaunchKernelGGL((jacobi_loop_kernel<64, 64>), g, b, lds, st, a);
+  else if (a.d == 128 && a.dh == 32) hipLaunchKernelGGL((jacobi_loop_kernel<128, 32>), g, b, lds, st, a);
+  else if (a.d == 128 && a.dh == 64) hipLaunchKernelGGL((jacobi_loop_kernel<128, 64>), g, b, lds, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace af

@@ -70,10 +70,11 @@ struct WsLayout {
   size_t cache_lo, a_lo, q_lo, att_lo, u_lo, total;
 };
 
-enum KClass { K_EMBED, K_LN, K_QKV, K_O, K_MLP1, K_MLP2, K_HEAD, K_ATTN, K_AFFINE, K_NCLASS };
+enum KClass { K_EMBED, K_LN, K_QKV, K_O, K_MLP1, K_MLP2, K_HEAD, K_ATTN, K_AFFINE, K_LOOP,
+              K_NCLASS };
 const char* kclass_names[K_NCLASS] = {"embed", "layernorm", "gemm_qkv", "gemm_o",
                                       "gemm_mlp1", "gemm_mlp2", "gemm_head",
-                                      "attention", "affine"};
+                                      "attention", "affine", "device_loop"};
 
 // Key of a captured Jacobi update: every host value its launches bake in.
 struct GraphKey {
@@ -128,6 +129,12 @@ struct af_plan {
   std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
   // residual pairs of the last update of the last inverse call (halves added)
   std::vector<float> last_res;
+  // the Jacobi loop on the device for small fp32 blocks (on by default);
+  // pinned block counts and non-finite words of its launches
+  bool device_loop = true;
+  int* loop_host = nullptr;
+  int* loop_host_dev = nullptr;
+  size_t loop_cap = 0;   // ints
 };
 
 namespace {
@@ -690,6 +697,7 @@ void af_plan_destroy(af_plan* p) {
   if (p->split_stream) (void)hipStreamDestroy(p->split_stream);
   for (hipEvent_t e : p->split_ev) (void)hipEventDestroy(e);
   if (p->host_res) (void)hipHostFree(p->host_res);
+  if (p->loop_host) (void)hipHostFree(p->loop_host);
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   delete p;
 }
@@ -784,6 +792,109 @@ af_status af_refresh_kv(af_plan* p, const float* x, int N, int L, int prefix_len
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
 }
 
+// The whole Jacobi inverse of each AF block of the stack in one launch (small
+// fp32 blocks): the loop, its stop tests and the cache refreshes run on the
+// device, which writes the block counts, the last residual pairs and a
+// non-finite word to pinned memory; the host waits once at the end.
+static af_status inverse_on_device(af_plan* p, const float* z, int N, int L, int B, float tau,
+                                   int max_iters, af_init init, const float* x_init,
+                                   int frame_len, int prefix_len, const float* x_last,
+                                   float* x, int32_t* iters, char* ws, const WsLayout& w,
+                                   int nb, hipStream_t st) {
+  const af_block_cfg& c = p->cfg;
+  const size_t need = (size_t)p->T * nb + p->T;
+  if (p->loop_cap < need) {
+    if (p->loop_host) {
+      AF_HIP(hipDeviceSynchronize());
+      (void)hipHostFree(p->loop_host);
+    }
+    p->loop_host = p->loop_host_dev = nullptr;
+    p->loop_cap = 0;
+    AF_HIP(hipHostMalloc((void**)&p->loop_host, need * sizeof(int),
+                         hipHostMallocMapped | hipHostMallocCoherent));
+    AF_HIP(hipHostGetDevicePointer((void**)&p->loop_host_dev, p->loop_host, 0));
+    p->loop_cap = need;
+  }
+  volatile int* lh = p->loop_host;
+  for (size_t i = 0; i < need; ++i) lh[i] = 0;
+  float* xtmp = (float*)(ws + w.xtmp);
+  const float* zin = z;
+  for (int t = p->T - 1; t >= 0; --t) {
+    const BlockW& bw = p->blocks[t];
+    af::LoopArgs a{};
+    a.w_in = bw.w_in;
+    a.b_in = bw.b_in;
+    a.pos = bw.pos;
+    a.ln_f_g = bw.ln_f_g;
+    a.ln_f_b = bw.ln_f_b;
+    a.w_head = bw.w_head;
+    a.b_head = bw.b_head;
+    for (int l = 0; l < c.n_layers; ++l) {
+      const LayerW& lw = bw.layers[l];
+      a.layers[l] = af::LoopLayer{lw.ln1_g, lw.ln1_b, (const float*)lw.w_qkv, lw.b_qkv,
+                                  (const float*)lw.w_o, lw.b_o, lw.ln2_g, lw.ln2_b,
+                                  (const float*)lw.w_1, lw.b_1, (const float*)lw.w_2, lw.b_2};
+      a.kc[l] = (float*)(ws + w.cache + (size_t)(2 * l) * w.cache_layer);
+      a.vt[l] = (float*)(ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer);
+    }
+    a.n_layers = c.n_layers;
+    a.C = c.C;
+    a.d = c.d;
+    a.H = c.n_heads;
+    a.dh = p->dh;
+    a.dmlp = p->dmlp;
+    a.Lcap = p->Lcap;
+    a.z = zin;
+    a.x = (t % 2 == 0) ? x : xtmp;
+    a.x_init = x_init;
+    a.x_last = x_last;
+    a.N = N;
+    a.L = L;
+    a.B = B;
+    a.P = prefix_len;
+    a.dir = t & 1;
+    a.init = (int)init;
+    a.F = frame_len;
+    a.max_iters = max_iters;
+    a.tau = tau;
+    a.iters_host = p->loop_host_dev + (size_t)t * nb;
+    a.res_host = p->host_res_dev;
+    a.bad_host = (unsigned*)(p->loop_host_dev + (size_t)p->T * nb + t);
+    LAUNCH(K_LOOP, af::launch_jacobi_loop(a, st));
+    zin = a.x;
+  }
+  AF_HIP(hipStreamSynchronize(st));
+  for (int t = 0; t < p->T; ++t)
+    for (int b = 0; b < nb; ++b) iters[t * nb + b] = lh[(size_t)t * nb + b];
+  if (p->prof_class == K_LOOP) {
+    // the launches' algorithmic flops, known once the counts are: per update
+    // of a block of R rows, embed 2CdM, per layer QKV 6d^2 M + O 2d^2 M + MLP
+    // 4 d dmlp M + attention 4d per (query, key) pair, head 4CdM; a refresh
+    // (early stop) is the layers' QKV and attention but the last layer's
+    const double d = c.d, C = c.C, dm = p->dmlp;
+    for (int t = 0; t < p->T; ++t)
+      for (int b = 0; b < nb; ++b) {
+        const int s = b * B, R = std::min(B, L - s), k = iters[t * nb + b];
+        const double M = (double)N * R;
+        const double pairs = (double)N * R * (prefix_len + s + (R + 1) / 2.0);
+        const double layer = M * (6 * d * d + 2 * d * d + 4 * d * dm) + 4 * d * pairs;
+        const double upd = 2 * C * d * M + c.n_layers * layer + 4 * C * d * M;
+        double work = k * upd;
+        if (k < R) work += 2 * C * d * M + c.n_layers * layer - (layer - 6 * d * d * M);
+        p->prof_work += work;
+      }
+  }
+  p->last_res.assign((size_t)2 * N, 0.f);
+  for (int n = 0; n < 2 * N; ++n) p->last_res[n] = p->host_res[n];
+  for (int t = p->T - 1; t >= 0; --t) {
+    const int tag = lh[(size_t)p->T * nb + t];
+    if (tag != 0)
+      return fail(AF_ERR_NONFINITE, "non-finite x in stack block " + std::to_string(t) +
+                                        ", Jacobi block " + std::to_string(tag - 1));
+  }
+  return AF_OK;
+}
+
 af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
                             float tau, int max_iters, af_init init,
                             const float* x_init, int frame_len, int prefix_len,
@@ -811,6 +922,11 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   if (af_status s = ensure_host_res(p, N)) return s;
   const int C = p->cfg.C;
   const int nb = (L + B - 1) / B;
+  if (!p->bf && p->device_loop && !p->graphs && !p->row_split && !p->fuse_refresh &&
+      af::jacobi_loop_supported(N, Bc, C, p->cfg.d, p->cfg.n_heads, p->dmlp, p->cfg.n_layers,
+                                p->Lcap))
+    return inverse_on_device(p, z, N, L, B, tau, max_iters, init, x_init, frame_len, prefix_len,
+                             x_last, x, iters, (char*)ws_, w, nb, (hipStream_t)stream);
   // A block that stops early has its cache rows recomputed from its final
   // tokens.  With a workspace for two blocks of rows, that pass is merged into
   // the next block's first update (one pass over both blocks' rows; the head
@@ -1126,6 +1242,12 @@ af_status af_plan_last_residual(const af_plan* p, int N, float* num_den) {
 af_status af_plan_set_fused_refresh(af_plan* p, int enable) {
   if (!p) return fail(AF_ERR_ARG, "NULL argument");
   p->fuse_refresh = enable != 0;
+  return AF_OK;
+}
+
+af_status af_plan_set_device_loop(af_plan* p, int enable) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->device_loop = enable != 0;
   return AF_OK;
 }
 

@@ -43,7 +43,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "latent tokens/s inverted via block Jacobi (1 GPU); % MFMA/HBM peak; iters/blk"
 GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2", "gemm_head")
 FLOP_CLASSES = GEMM_CLASSES + ("attention", "embed")
-ALL_CLASSES = GEMM_CLASSES + ("attention", "layernorm", "embed", "affine")
+ALL_CLASSES = GEMM_CLASSES + ("attention", "layernorm", "embed", "affine", "device_loop")
 DEFAULT_WORKLOAD = "video21"
 OTHER_CONFIGS = ("tiny_f32", "frame480p", "shallow_stack", "wide_prefix")
 
@@ -541,8 +541,19 @@ def summarize_counters(d, calib_dir, workload):
 # ---------------------------------------------------------------------------
 def roofline_of(cls, n, ms, work, cfg, workload, steps):
     """The roofline entry of one kernel class from its profiled launches."""
+    if n == 0 or ms <= 0:
+        return {"kernel": cls, "launches": n, "achieved": None}
     avg_ms = ms / max(n, 1)
     per_launch = work / max(n, 1)
+    if cls == "device_loop":
+        # the whole Jacobi loop of a small fp32 block in one workgroup: vector
+        # fp32 arithmetic on one CU, against the chip's fp32 vector peak
+        achieved = per_launch / (avg_ms * 1e-3) / 1e12
+        return {"kernel": cls, "bound": "alu", "achieved": round(achieved, 4),
+                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_F32_TFLOPS, 6), "traffic": None,
+                "flops_per_launch": round(per_launch), "avg_ms": round(avg_ms, 5),
+                "launches": n}
     if cls == "affine":
         achieved = per_launch / (avg_ms * 1e-3) / 1e9
         return {"kernel": cls, "bound": "hbm", "achieved": round(achieved, 1),

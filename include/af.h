@@ -275,6 +275,23 @@ af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *
  * 32 x 32 attention kernels one pass measured faster; AF_ERR_ARG if p is NULL. */
 af_status af_plan_set_row_split(af_plan *p, int enable);
 
+/* The Jacobi loop on the device (STARFlow-V notes, 关键设计 3: the update is
+ * repeated until the residual falls below tau).  For fp32 plans whose block
+ * fits one workgroup (N * min(B, L) <= 64 rows, d 64 or 128, d / n_heads 32
+ * or 64, C % 4 == 0, C <= 64, d_mlp % 64 == 0, at most 8 layers) and no
+ * graph replay, row split or fused refresh is asked for, af_inverse_jacobi
+ * runs the whole
+ * inverse of each AF block of the stack as one launch: every Jacobi block in
+ * order, every update, the stop test and the cache refresh after an early
+ * stop happen on the device, with no host read-back per update; the call
+ * waits for the stream once at the end and reads the block counts, the last
+ * residual pairs and a non-finite flag from pinned memory.  Results and
+ * counts follow the same rules as the launch-per-kernel path (its fp32
+ * arithmetic differs only in summation order); the KV cache in the workspace
+ * is left in the same state.  enable != 0 (the default) uses it where the
+ * shape allows, 0 keeps the launch-per-kernel path; AF_ERR_ARG if p is NULL. */
+af_status af_plan_set_device_loop(af_plan *p, int enable);
+
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
  * The fused affine kernel on its own, over N samples of rows_per_sample
  * contiguous rows of C channels (token tensors [N, rows_per_sample, C]).

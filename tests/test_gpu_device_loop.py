@@ -1,0 +1,163 @@
+"""GPU parity of the Jacobi loop on the device (af_plan_set_device_loop: one
+launch per AF block runs every update, the stop test and the cache refresh
+for small fp32 blocks) against the CPU fp64 oracle, and against the
+launch-per-kernel path on the same inputs.  Bars: iteration counts equal the
+oracle's; relative L2 <= 1e-4 (fp32); the two GPU paths agree to 1e-5 with
+the same counts.
+
+Method: STARFlow-V notes (papernotes.org), 关键设计 3 (block-wise Jacobi,
+residual stop, KV cache, previous-frame warm start), 关键设计 1 (affine AF
+block, alternating directions), 一个完整示例 (prefix encoding into the KV
+cache)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from autoregressive_normalizing_flow_amd import synth  # noqa: E402
+from oracle import af_oracle as O  # noqa: E402
+from parity_util import TOL_F32, problem, rel_l2, say, to_dev, to_np  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from autoregressive_normalizing_flow_amd import binding
+    binding.load_library()
+    return binding
+
+
+def both_paths(plan, fn):
+    """fn() with the device loop, then with it off (the plan is left with
+    the device loop on)."""
+    plan.set_device_loop(True)
+    dev = fn()
+    plan.set_device_loop(False)
+    try:
+        ref = fn()
+    finally:
+        plan.set_device_loop(True)
+    return dev, ref
+
+
+def check_pair(dev, ref, xo, ito):
+    (xd, itd), (xr, itr) = dev, ref
+    print("iters device", itd.tolist(), "launches", itr.tolist(), "oracle", np.asarray(ito).tolist())
+    assert np.array_equal(itd, itr)
+    assert np.array_equal(itd.reshape(np.asarray(ito).shape), ito)
+    assert rel_l2(to_np(xd), to_np(xr)) < 1e-5
+    assert rel_l2(to_np(xd), xo) < TOL_F32
+
+
+@pytest.mark.parametrize("C,d,H,layers,L,N,Bj,tau", [
+    (16, 64, 2, 1, 64, 1, 16, 1e-3),    # the tiny_f32 workload's block
+    (8, 64, 2, 2, 45, 3, 16, 1e-4),     # batch 3, ragged last block, 2 layers
+    (4, 64, 1, 1, 20, 2, 8, 1e-3),      # one head of 64
+    (12, 128, 4, 1, 32, 1, 32, 1e-3),   # a whole 32-row block, d 128
+])
+def test_device_loop_matches_oracle(B, C, d, H, layers, L, N, Bj, tau):
+    say("device loop", C, d, H, layers, L, N, Bj, tau)
+    cfg, params, (p64,) = problem(C=C, d=d, H=H, layers=layers, max_len=L, dtype="f32",
+                                  seed=C + d + L)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((N, L, C), 1)
+    dev, ref = both_paths(plan, lambda: plan.inverse_jacobi(to_dev(z), Bj, tau))
+    xo, ito = O.inverse_jacobi_block(p64, z, H, Bj, tau)
+    check_pair(dev, ref, xo, ito)
+    # the stop test saw the last update's residual pair (when the last block
+    # stopped before its cap)
+    last_len = L - (L - 1) // Bj * Bj
+    if dev[1][0, -1] < last_len:
+        num, den = plan.last_residual(N).T
+        assert np.all(num / np.maximum(den, 1e-30) < tau)
+
+
+def test_device_loop_forced_counts_and_sequential(B):
+    say("device loop forced")
+    cfg, params, (p64,) = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((2, 20, 4), 6)
+    dev, ref = both_paths(plan, lambda: plan.inverse_jacobi(to_dev(z), 8, 0.0, max_iters=3))
+    xo, _ = O.inverse_jacobi_block(p64, z, 1, 8, 0.0, max_iters=3)
+    check_pair(dev, ref, xo, [3, 3, 3])
+    # B = 1: sequential decoding; tau <= 0 without a cap: Bb updates, exact
+    x1, it1 = plan.inverse_jacobi(to_dev(z), 1, 1e-3)
+    assert np.all(it1 == 1)
+    assert rel_l2(to_np(x1), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
+    xf, itf = plan.inverse_jacobi(to_dev(z), 8, 0.0)
+    assert itf.tolist() == [[8, 8, 4]]
+    assert rel_l2(to_np(xf), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
+
+
+def test_device_loop_stack_alternating(B):
+    """T = 3 blocks (L->R, R->L, L->R), batch 2, ragged last Jacobi block."""
+    say("device loop stack")
+    cfg, params, p64 = problem(C=4, d=64, H=2, layers=1, max_len=27, dtype="f32", seed=21,
+                               n_blocks=3)
+    plan = B.AFPlan(cfg, params)
+    x_in = synth.normal((2, 27, 4), 22)
+    z, _ = O.forward_stack(p64, x_in, 2)
+    dev, ref = both_paths(plan, lambda: plan.inverse_jacobi(to_dev(z), 8, 1e-4))
+    xo, ito = O.inverse_jacobi_stack(p64, z, 2, 8, 1e-4)
+    check_pair(dev, ref, xo, ito)
+
+
+def test_device_loop_prefix_given_and_prev_frame(B):
+    say("device loop prefix")
+    cfg, params, (p64,) = problem(C=8, d=64, H=2, layers=2, max_len=60, dtype="f32", seed=31)
+    plan = B.AFPlan(cfg, params)
+    xp = synth.normal((2, 12, 8), 32)
+    z = synth.normal((2, 36, 8), 33)
+    xinit = synth.normal((2, 36, 8), 34)
+    cache, x_last = O.prefill(p64, xp, 2)
+    xo, ito = O.inverse_jacobi_block(p64, z, 2, 12, 1e-3, init="given", x_init=xinit,
+                                     pos0=12, cache=cache, x_last=x_last)
+
+    def run():
+        plan.prefill(to_dev(xp), rows=36)
+        return plan.inverse_jacobi(to_dev(z), 12, 1e-3, init="given", x_init=to_dev(xinit),
+                                   prefix_len=12, x_last=to_dev(xp[:, -1]))
+    check_pair(*both_paths(plan, run), xo, ito)
+    # previous-frame warm start, frames of 12 tokens = one block each
+    z2 = synth.normal((1, 48, 8), 35)
+    dev, ref = both_paths(plan, lambda: plan.inverse_jacobi(to_dev(z2), 12, 1e-3,
+                                                            init="prev_frame", frame_len=12))
+    xo2, ito2 = O.inverse_jacobi_block(p64, z2, 2, 12, 1e-3, init="prev_frame", frame_len=12)
+    check_pair(dev, ref, xo2, ito2)
+
+
+def test_device_loop_reports_nonfinite(B):
+    say("device loop nonfinite")
+    cfg, params, _ = problem(C=8, d=64, H=2, layers=1, max_len=40, dtype="f32", seed=41)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((1, 40, 8), 42)
+    z[0, 25, 3] = np.nan
+    with pytest.raises(B.AFError) as ei:
+        plan.inverse_jacobi(to_dev(z), 10, 1e-3)
+    assert ei.value.status == B.AF_ERR_NONFINITE and "Jacobi block 2" in str(ei.value)
+    # the plan works again afterwards
+    z[0, 25, 3] = 0.5
+    x, it = plan.inverse_jacobi(to_dev(z), 10, 1e-3)
+    assert np.isfinite(to_np(x)).all() and it.shape == (1, 4)
+
+
+def test_device_loop_leaves_the_cache_as_the_launch_path(B):
+    """After an inverse, continuing the sequence from the cache (a second call
+    with the first call's tokens as prefix) gives the same result whichever
+    path filled the cache."""
+    say("device loop cache")
+    cfg, params, (p64,) = problem(C=8, d=64, H=2, layers=1, max_len=64, dtype="f32", seed=51)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((1, 32, 8), 52)
+    z2 = synth.normal((1, 32, 8), 53)
+
+    def run():
+        x, _ = plan.inverse_jacobi(to_dev(z), 16, 1e-4)
+        return plan.inverse_jacobi(to_dev(z2), 16, 1e-4, prefix_len=32,
+                                   x_last=x[:, -1].contiguous())
+    (xd, itd), (xr, itr) = both_paths(plan, run)
+    assert np.array_equal(itd, itr)
+    assert rel_l2(to_np(xd), to_np(xr)) < 1e-5

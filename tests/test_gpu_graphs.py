@@ -55,6 +55,10 @@ def test_graph_replays_match_direct_launches(B, case):
     cfg, params, _ = problem(C=C, d=d, H=H, layers=layers, max_len=L, dtype=dtype,
                              seed=40 + L, n_blocks=T)
     plan = B.AFPlan(cfg, params)
+    # graph replay against direct launches of the same kernels (small fp32
+    # blocks would otherwise run the Jacobi loop on the device when graphs
+    # are off)
+    plan.set_device_loop(False)
     z = to_dev(synth.normal((N, L, C), 41 + L))
     ws = plan.workspace(N, min(Bj, L))
     x_d = torch.empty_like(z)
