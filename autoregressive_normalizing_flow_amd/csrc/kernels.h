@@ -163,7 +163,8 @@ struct LoopArgs {
   int n_layers, C, d, H, dh, dmlp, Lcap;
   const float* z;        // [N, L, C]
   float* x;              // [N, L, C] written block by block
-  const float* x_init;   // init 1 (given)
+  const float* x_init;   // init 1 (given); with refresh, the final tokens
+  int refresh;           // 1: only recompute the cache rows of x_init's tokens
   const float* x_last;   // the token before the sequence, [N, C], or NULL (zeros)
   int N, L, B, P, dir, init, F, max_iters;
   float tau;             // <= 0: exactly min(max_iters, block) updates
@@ -176,7 +177,9 @@ struct LoopArgs {
 bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_layers,
                            int Lcap);
 // One workgroup runs the whole Jacobi inverse of one AF block (every block of
-// the sequence, the stop tests and the cache refreshes).
+// the sequence, the stop tests and the cache refreshes), or with a.refresh the
+// cache rows of given tokens in blocks of B rows, by the same pass as the
+// refresh after an early stop.
 hipError_t launch_jacobi_loop(const LoopArgs& a, hipStream_t st);
 
 // Record a failure for af_last_error() from another translation unit

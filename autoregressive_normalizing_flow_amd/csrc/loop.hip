@@ -8,19 +8,22 @@
 // the final LayerNorm and head, the affine update and the per-sample residual
 // sums; then it takes the stop test itself (every sample's
 // sum (x' - x)^2 / sum x'^2 below tau, or the update cap) and refreshes the
-// block's cache rows from its final tokens after an early stop.  No kernel
-// launch and no host read-back per update: the host launches once per AF
-// block and reads the iteration counts at the end.
+// block's cache rows from its final tokens after an early stop (but the last
+// block's, which nothing in the launch reads).  No kernel launch and no host
+// read-back per update: the host launches once per AF block and reads the
+// iteration counts at the end.  In refresh mode a launch runs only that
+// refresh pass, over given tokens (the rows a later call needs of an earlier
+// call's last block), so both come from the same arithmetic.
 //
 // The block's activations live in LDS (rows M = N x B <= 64, d 64 or 128);
 // the weights are read from global memory (L2-resident at these sizes), each
 // thread loading a whole weight row into registers before it multiplies (one
 // memory round trip per output column instead of one per step), and the KV
 // cache is the workspace's, in the layout the other kernels use, so a later
-// call continues from it.  Attention runs one wave per (sample, head): the
-// lanes take 64 keys at a time for the scores of up to 16 rows, then the
-// value dimensions for P V, so each K row and V^T chunk is loaded once for
-// all the rows.  Arithmetic is fp32 throughout, sums in a fixed order
+// call continues from it.  Attention runs one wave per (sample, head, four
+// rows): the lanes take 64 keys at a time for the scores of the rows, then
+// the value dimensions for P V, so each K row and V^T chunk is loaded once
+// for the four rows.  Arithmetic is fp32 throughout, sums in a fixed order
 // (results do not depend on scheduling).
 #include "common.h"
 #include "kernels.h"
@@ -31,7 +34,7 @@ namespace {
 
 constexpr int LT = 256;   // threads
 constexpr int UC = 64;    // MLP hidden columns per chunk
-constexpr int RG = 16;    // attention rows per wave pass
+constexpr int RG = 4;     // attention rows per wave pass
 constexpr int KT = 64;    // attention keys per wave pass (one per lane)
 
 // Shared-memory carve-up of one block's state (floats).
@@ -67,14 +70,17 @@ __host__ __device__ LoopLds loop_lds(int M, int N, int C, int d) {
 template <int K, class Epi>
 __device__ void linear(const float* X, int ldx, int M, const float* W, int ldw,
                        const float* bias, int Nout, Epi epi) {
-  for (int n = threadIdx.x; n < Nout; n += LT) {
+  // with fewer columns than threads, the rows are dealt over G thread groups
+  const int G = Nout < LT ? LT / Nout : 1;
+  const int grp = threadIdx.x / (LT / G >= Nout ? Nout : LT);
+  for (int n = threadIdx.x % (G > 1 ? Nout : LT); n < Nout && grp < G; n += LT) {
     float4 wr[K / 4];
     const float* wp = W + (size_t)n * ldw;
 #pragma unroll
     for (int k = 0; k < K / 4; ++k) wr[k] = *(const float4*)(wp + 4 * k);
     const float bn = bias ? bias[n] : 0.f;
 #pragma clang loop unroll(disable)
-    for (int m = 0; m < M; ++m) {
+    for (int m = grp; m < M; m += G) {
       const float* xr = X + m * ldx;
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
@@ -116,7 +122,7 @@ __device__ void layernorm_rows(const float* in, float* out, int M, int d, const 
 }
 
 // Causal attention of the block rows over the cache, one wave per (sample,
-// head) at a time: for RG rows and KT keys per pass, lane j scores key j0 + j
+// head, group of RG rows) at a time: for KT keys per pass, lane j scores key j0 + j
 // against each row (its K row in registers, the rows' q from LDS), the online
 // softmax per row keeps (max, sum) in registers of every lane, then lane e
 // adds sum_j p_rj V^T[e][j0 + j] for each row (its V^T chunk in registers).
@@ -129,12 +135,14 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
   const int N = a.N, H = a.H;
   const float scale = 1.0f / sqrtf((float)DH);
   float* pw = ps + wave * RG * KT;
-  for (int pair = wave; pair < N * H; pair += LT / 64) {
+  const int ngrp = (R + RG - 1) / RG;
+  for (int item = wave; item < N * H * ngrp; item += LT / 64) {
+    const int pair = item / ngrp, t0 = (item - pair * ngrp) * RG;
     const int nn = pair / H, head = pair - nn * H;
     const size_t base = (size_t)nn * H + head;
     const float* kr = kc + base * a.Lcap * DH;
     const float* vr = vt + base * DH * a.Lcap;
-    for (int t0 = 0; t0 < R; t0 += RG) {
+    {
       const int rows = min(RG, R - t0);
       const int nkmax = a.P + s + t0 + rows;   // keys of the group's last row
       float om[RG], ol[RG], oacc[RG];
@@ -364,6 +372,21 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
     prev[idx] = a.x_last ? a.x_last[idx] : 0.f;
   for (int b = 0; b < nb; ++b) {
     const int s = b * a.B, R = min(a.B, a.L - s), M = N * R;
+    if (a.refresh) {
+      // the block's tokens, then the pass that writes their cache rows
+      for (int idx = tid; idx < M * C; idx += LT) {
+        const int m = idx / C, c = idx - m * C, n = m / R, t = m - n * R;
+        xb[idx] = a.x_init[((size_t)n * a.L + storage_index(s + t, a.L, a.dir)) * C + c];
+      }
+      __syncthreads();
+      loop_pass<D, DH>(a, sm, L, s, R, true);
+      for (int idx = tid; idx < N * C; idx += LT) {
+        const int n = idx / C, c = idx - n * C;
+        prev[idx] = xb[((n + 1) * R - 1) * C + c];
+      }
+      __syncthreads();
+      continue;
+    }
     // z of the block and the first iterate
     for (int idx = tid; idx < M * C; idx += LT) {
       const int m = idx / C, c = idx - m * C, n = m / R, t = m - n * R, i = s + t;
@@ -400,8 +423,9 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
     }
     if (bad) return;
     // an early stop leaves the cache rows from the previous iterate: recompute
-    // them from the final tokens
-    if (k < R) {
+    // them from the final tokens (not for the last block, which nothing in
+    // this launch reads; a later call refreshes it with the same pass)
+    if (k < R && b + 1 < nb) {
       __syncthreads();
       loop_pass<D, DH>(a, sm, L, s, R, true);
     }

@@ -762,6 +762,9 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
   return AF_OK;
 }
 
+static af::LoopArgs loop_args(const af_plan* p, const BlockW& bw, char* ws, const WsLayout& w);
+static int loop_refresh_rows(const af_plan* p, int N, int L);
+
 af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
                      size_t ws_bytes, void* stream) {
   if (!p || !x_prefix) return fail(AF_ERR_ARG, "NULL argument");
@@ -787,9 +790,72 @@ af_status af_refresh_kv(af_plan* p, const float* x, int N, int L, int prefix_len
   WsLayout w;
   if (af_status s = check_ws(p, N, L, ws_, ws_bytes, &w)) return s;
   hipStream_t st = (hipStream_t)stream;
+  // the plan's device loop refreshes the rows of a call's blocks: the rows
+  // of its last block come from the same pass here
+  if (const int R = loop_refresh_rows(p, N, L)) {
+    af::LoopArgs a = loop_args(p, p->blocks[0], (char*)ws_, w);
+    a.x_init = x;
+    a.refresh = 1;
+    a.x_last = x_last;
+    a.N = N;
+    a.L = L;
+    a.B = R;
+    a.P = prefix_len;
+    // algorithmic flops: embed, every layer but the last, the last one's QKV
+    const af_block_cfg& c = p->cfg;
+    const double d = c.d, C = c.C, dm = p->dmlp;
+    double work = 0.0;
+    for (int s0 = 0; s0 < L; s0 += R) {
+      const int r = std::min(R, L - s0);
+      const double M = (double)N * r;
+      const double pairs = (double)N * r * (prefix_len + s0 + (r + 1) / 2.0);
+      const double layer = M * (6 * d * d + 2 * d * d + 4 * d * dm) + 4 * d * pairs;
+      work += 2 * C * d * M + (c.n_layers - 1) * layer + 6 * d * d * M;
+    }
+    LAUNCHW(K_LOOP, work, af::launch_jacobi_loop(a, st));
+    return AF_OK;
+  }
   Pass ps{x, x_last, N, L, 0, L, prefix_len, 0, true, false};
   AF_HIP(clear_counters(w, (char*)ws_, st));
   return run_net(p, p->blocks[0], ps, (char*)ws_, w, st);
+}
+
+// The arguments of the device loop that describe AF block bw and its cache.
+static af::LoopArgs loop_args(const af_plan* p, const BlockW& bw, char* ws, const WsLayout& w) {
+  const af_block_cfg& c = p->cfg;
+  af::LoopArgs a{};
+  a.w_in = bw.w_in;
+  a.b_in = bw.b_in;
+  a.pos = bw.pos;
+  a.ln_f_g = bw.ln_f_g;
+  a.ln_f_b = bw.ln_f_b;
+  a.w_head = bw.w_head;
+  a.b_head = bw.b_head;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& lw = bw.layers[l];
+    a.layers[l] = af::LoopLayer{lw.ln1_g, lw.ln1_b, (const float*)lw.w_qkv, lw.b_qkv,
+                                (const float*)lw.w_o, lw.b_o, lw.ln2_g, lw.ln2_b,
+                                (const float*)lw.w_1, lw.b_1, (const float*)lw.w_2, lw.b_2};
+    a.kc[l] = (float*)(ws + w.cache + (size_t)(2 * l) * w.cache_layer);
+    a.vt[l] = (float*)(ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer);
+  }
+  a.n_layers = c.n_layers;
+  a.C = c.C;
+  a.d = c.d;
+  a.H = c.n_heads;
+  a.dh = p->dh;
+  a.dmlp = p->dmlp;
+  a.Lcap = p->Lcap;
+  return a;
+}
+
+// Rows per device-loop block for a refresh of N samples (0: not supported).
+static int loop_refresh_rows(const af_plan* p, int N, int L) {
+  if (p->bf || !p->device_loop || p->graphs || p->row_split || p->fuse_refresh || N > 64)
+    return 0;
+  const int R = std::min(L, 64 / N);
+  return af::jacobi_loop_supported(N, R, p->cfg.C, p->cfg.d, p->cfg.n_heads, p->dmlp,
+                                   p->cfg.n_layers, p->Lcap) ? R : 0;
 }
 
 // The whole Jacobi inverse of each AF block of the stack in one launch (small
@@ -820,30 +886,7 @@ static af_status inverse_on_device(af_plan* p, const float* z, int N, int L, int
   float* xtmp = (float*)(ws + w.xtmp);
   const float* zin = z;
   for (int t = p->T - 1; t >= 0; --t) {
-    const BlockW& bw = p->blocks[t];
-    af::LoopArgs a{};
-    a.w_in = bw.w_in;
-    a.b_in = bw.b_in;
-    a.pos = bw.pos;
-    a.ln_f_g = bw.ln_f_g;
-    a.ln_f_b = bw.ln_f_b;
-    a.w_head = bw.w_head;
-    a.b_head = bw.b_head;
-    for (int l = 0; l < c.n_layers; ++l) {
-      const LayerW& lw = bw.layers[l];
-      a.layers[l] = af::LoopLayer{lw.ln1_g, lw.ln1_b, (const float*)lw.w_qkv, lw.b_qkv,
-                                  (const float*)lw.w_o, lw.b_o, lw.ln2_g, lw.ln2_b,
-                                  (const float*)lw.w_1, lw.b_1, (const float*)lw.w_2, lw.b_2};
-      a.kc[l] = (float*)(ws + w.cache + (size_t)(2 * l) * w.cache_layer);
-      a.vt[l] = (float*)(ws + w.cache + (size_t)(2 * l + 1) * w.cache_layer);
-    }
-    a.n_layers = c.n_layers;
-    a.C = c.C;
-    a.d = c.d;
-    a.H = c.n_heads;
-    a.dh = p->dh;
-    a.dmlp = p->dmlp;
-    a.Lcap = p->Lcap;
+    af::LoopArgs a = loop_args(p, p->blocks[t], ws, w);
     a.z = zin;
     a.x = (t % 2 == 0) ? x : xtmp;
     a.x_init = x_init;
@@ -880,7 +923,7 @@ static af_status inverse_on_device(af_plan* p, const float* z, int N, int L, int
         const double layer = M * (6 * d * d + 2 * d * d + 4 * d * dm) + 4 * d * pairs;
         const double upd = 2 * C * d * M + c.n_layers * layer + 4 * C * d * M;
         double work = k * upd;
-        if (k < R) work += 2 * C * d * M + c.n_layers * layer - (layer - 6 * d * d * M);
+        if (k < R && b + 1 < nb) work += 2 * C * d * M + c.n_layers * layer - (layer - 6 * d * d * M);
         p->prof_work += work;
       }
   }

@@ -145,19 +145,28 @@ def test_device_loop_reports_nonfinite(B):
 
 
 def test_device_loop_leaves_the_cache_as_the_launch_path(B):
-    """After an inverse, continuing the sequence from the cache (a second call
-    with the first call's tokens as prefix) gives the same result whichever
-    path filled the cache."""
+    """After an inverse, continuing the sequence from the cache (the call's
+    last block refreshed with af_refresh_kv, then a second call with the first
+    call's tokens as prefix) gives the same result whichever path filled the
+    cache, and the oracle's continuation of the first call's tokens."""
     say("device loop cache")
-    cfg, params, (p64,) = problem(C=8, d=64, H=2, layers=1, max_len=64, dtype="f32", seed=51)
+    cfg, params, (p64,) = problem(C=8, d=64, H=2, layers=2, max_len=64, dtype="f32", seed=51)
     plan = B.AFPlan(cfg, params)
     z = synth.normal((1, 32, 8), 52)
     z2 = synth.normal((1, 32, 8), 53)
+    first = []   # the first call's tokens, device loop first
 
     def run():
-        x, _ = plan.inverse_jacobi(to_dev(z), 16, 1e-4)
+        x, it = plan.inverse_jacobi(to_dev(z), 16, 1e-4)
+        first.append(to_np(x))
+        assert it[0, -1] < 16   # the last block stopped early: its rows are stale
+        plan.refresh_kv(x[:, 16:].contiguous(), prefix_len=16, x_last=x[:, 15].contiguous())
         return plan.inverse_jacobi(to_dev(z2), 16, 1e-4, prefix_len=32,
                                    x_last=x[:, -1].contiguous())
     (xd, itd), (xr, itr) = both_paths(plan, run)
     assert np.array_equal(itd, itr)
     assert rel_l2(to_np(xd), to_np(xr)) < 1e-5
+    cache, x_last = O.prefill(p64, first[0], 2)
+    xo, _ = O.inverse_jacobi_block(p64, z2, 2, 16, 1e-4, pos0=32, cache=cache, x_last=x_last,
+                                   forced_iters=itd[0].tolist())
+    assert rel_l2(to_np(xd), xo) < TOL_F32

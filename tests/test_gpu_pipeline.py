@@ -66,12 +66,16 @@ def test_deep_shallow_forward_and_pipelined_inverse(B, dtype):
     assert torch.equal(xs, xg)
 
 
-def test_deep_frames_equal_one_video_call(B):
+@pytest.mark.parametrize("device_loop", [True, False])
+def test_deep_frames_equal_one_video_call(B, device_loop):
     """Frame-by-frame deep calls (given init + prefix + refresh) reproduce the
     single af_inverse_jacobi call over the whole sequence with the
-    previous-frame warm start, bit for bit."""
-    say("deep per-frame vs one call")
+    previous-frame warm start, bit for bit, on the device loop (whose refresh
+    of a call's last block comes from af_refresh_kv, by the same pass) and on
+    the launch-per-kernel path."""
+    say("deep per-frame vs one call, device loop", device_loop)
     flow, pd, ps, deep = flows(B, "f32", 16, 64, 2, 1, 16, 4)
+    deep.set_device_loop(device_loop)
     z = to_dev(synth.normal((1, 64, 16), 3))
     u_one, it_one = deep.inverse_jacobi(z, 16, 1e-3, init="prev_frame", frame_len=16)
     u = torch.empty_like(z)
