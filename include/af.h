@@ -167,7 +167,11 @@ af_status af_prefill(af_plan *p, const float *x_prefix, int N, int P,
  * Positions 0..P-1 must already be in ws; x_last [N, C] is the token at
  * position P-1 (required when P > 0, NULL for zeros when P == 0).  With
  * P == 0 this is af_prefill.  Only for n_blocks == 1.  Needs P + L <= max_len
- * and ws_bytes >= af_workspace_bytes(p, N, L).  Stream-ordered. */
+ * and ws_bytes >= af_workspace_bytes(p, N, L).  Where af_inverse_jacobi runs
+ * on the device loop (af_plan_set_device_loop), so does this call, with the
+ * pass that refreshes a block after an early stop, so rows refreshed here
+ * equal the ones a single call over the longer sequence leaves, bit for bit.
+ * Stream-ordered. */
 af_status af_refresh_kv(af_plan *p, const float *x, int N, int L, int prefix_len,
                         const float *x_last, void *ws, size_t ws_bytes, void *stream);
 
@@ -280,16 +284,19 @@ af_status af_plan_set_row_split(af_plan *p, int enable);
  * fits one workgroup (N * min(B, L) <= 64 rows, d 64 or 128, d / n_heads 32
  * or 64, C % 4 == 0, C <= 64, d_mlp % 64 == 0, at most 8 layers) and no
  * graph replay, row split or fused refresh is asked for, af_inverse_jacobi
- * runs the whole
- * inverse of each AF block of the stack as one launch: every Jacobi block in
- * order, every update, the stop test and the cache refresh after an early
- * stop happen on the device, with no host read-back per update; the call
- * waits for the stream once at the end and reads the block counts, the last
- * residual pairs and a non-finite flag from pinned memory.  Results and
- * counts follow the same rules as the launch-per-kernel path (its fp32
- * arithmetic differs only in summation order); the KV cache in the workspace
- * is left in the same state.  enable != 0 (the default) uses it where the
- * shape allows, 0 keeps the launch-per-kernel path; AF_ERR_ARG if p is NULL. */
+ * runs the whole inverse of each AF block of the stack as one launch: every
+ * Jacobi block in order, every update, the stop test and the cache refresh
+ * after an early stop happen on the device, with no host read-back per
+ * update; the call waits for the stream once at the end and reads the block
+ * counts, the last residual pairs and a non-finite flag from pinned memory.
+ * Results and counts follow the same rules as the launch-per-kernel path (its
+ * fp32 arithmetic differs only in summation order), and so does the KV cache
+ * left in the workspace, but for the rows of the call's last Jacobi block,
+ * which neither path refreshes (here every layer's rows hold the K/V of the
+ * last update's inputs; af_refresh_kv, which takes the same route for the
+ * same shapes, brings them up to date).  enable != 0 (the default) uses it
+ * where the shape allows, 0 keeps the launch-per-kernel path; AF_ERR_ARG if p
+ * is NULL. */
 af_status af_plan_set_device_loop(af_plan *p, int enable);
 
 /* ---- kernel-level entry points (unit parity and bandwidth measurement) ---
