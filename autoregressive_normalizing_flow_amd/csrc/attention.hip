@@ -990,8 +990,16 @@ attn32_kernel(AttnArgs a) {
 // of the last tile at or past the chunk end are zeroed in LDS before use (the
 // cache holds stale rows there).
 // ---------------------------------------------------------------------------
+// One unit of the DMA kernel: keys [k_begin, k_end) of query tile qt of
+// (sample, head) pair nh.  With n_chunks == 1 the unit covers the tile's whole
+// key range and writes the normalised output; otherwise it writes its partial
+// to slot `slot`, and the last of the tile's n_chunks units to finish (slots
+// first_slot .. first_slot + n_chunks - 1, in key order) merges them.
 template <int DH>
-__device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
+__device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, const int qt,
+                                             const int k_begin, const int k_end,
+                                             const int slot, const int first_slot,
+                                             const int n_chunks) {
   static_assert(DH == 64 || DH == 128, "head width");
   constexpr int KS = DH / 16, DB = DH / 32;
   constexpr int STAGES = DH <= 64 ? 3 : 2;
@@ -1015,27 +1023,9 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   // wave-uniform (the DMA takes its LDS address in a scalar register)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hh = lane >> 5;
-  int u = blockIdx.x;
-  if (a.xcd_map) {
-    const int xcd = u & 7, local = u >> 3;
-    const int jj = local / a.U_nh;
-    u = (jj * 8 + xcd) * a.U_nh + (local - jj * a.U_nh);
-  }
-  const int nh = u / a.U_nh;
-  int rem = u - nh * a.U_nh;
   const int n = nh / a.H, head = nh - n * a.H;
-  int qt = 0, n_chunks = att_chunks(0, a.R, a.pos_base, a.KC);
-  while (rem >= n_chunks) {
-    rem -= n_chunks;
-    ++qt;
-    n_chunks = att_chunks(qt, a.R, a.pos_base, a.KC);
-  }
-  const int chunk = rem;
   const int R = a.R, d = a.d, Lcap = a.Lcap, pos_base = a.pos_base;
   const int q_lo = qt * ATT_QT;
-  const int nk = pos_base + min(R, q_lo + ATT_QT);
-  const int k_begin = chunk * a.KC;
-  const int k_end = min(nk, k_begin + a.KC);
   const int t_begin = k_begin / ATT_KT;
   const int n_tiles = (k_end - k_begin + ATT_KT - 1) / ATT_KT;
   const size_t hb = (size_t)n * a.H + head;
@@ -1304,7 +1294,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   constexpr int SLOT = ATT_QT * (DH + 2);
   const int tq = wave * 32 + j;
   if (active) {
-    const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)u * SLOT);
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)slot * SLOT);
     const float l = l_row;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -1334,7 +1324,42 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   }
   __syncthreads();
   if (!s_last || !active) return;
-  attn32_merge<DH>(a, u - chunk, n_chunks, tq, t_q, n, head, hh);
+  attn32_merge<DH>(a, first_slot, n_chunks, tq, t_q, n, head, hh);
+}
+
+template <int DH>
+__device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
+  // unit -> (sample, head, query tile, chunk).  Block ids go round-robin over
+  // the 8 XCDs; when N*H is a multiple of 8, (sample, head) pairs are dealt so
+  // that all units of one head run on one XCD and share its K/V in that L2.
+  int u = blockIdx.x;
+  if (a.xcd_map) {
+    const int xcd = u & 7, local = u >> 3;
+    const int jj = local / a.U_nh;
+    u = (jj * 8 + xcd) * a.U_nh + (local - jj * a.U_nh);
+  }
+  const int nh = u / a.U_nh;
+  int rem = u - nh * a.U_nh;
+  // Within a pair the blocks run chunk-major: chunk j of every query tile that
+  // has one, then chunk j + 1, so that the units that read one key range are
+  // dispatched together and share it in L2 (the partial slots stay numbered
+  // query tile by query tile, chunks in key order).  Against query-tile-major
+  // order, on one box: attention 132 -> 128 us per launch on average over the
+  // 21-frame video, +1.8% tokens/s.
+  int j = 0, q0 = 0;
+  for (;;) {
+    while (q0 < a.n_qt && att_chunks(q0, a.R, a.pos_base, a.KC) <= j) ++q0;
+    if (rem < a.n_qt - q0) break;
+    rem -= a.n_qt - q0;
+    ++j;
+  }
+  const int qt = q0 + rem;
+  int before = 0;
+  for (int q = 0; q < qt; ++q) before += att_chunks(q, a.R, a.pos_base, a.KC);
+  const int nk = a.pos_base + min(a.R, (qt + 1) * ATT_QT);
+  const int slot0 = nh * a.U_nh + before;
+  attn_dma_unit<DH>(a, nh, qt, j * a.KC, min(nk, (j + 1) * a.KC), slot0 + j, slot0,
+                   att_chunks(qt, a.R, a.pos_base, a.KC));
 }
 
 // Three blocks per CU at d_h 64 (at most 168 registers), two at d_h 128.

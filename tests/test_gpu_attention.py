@@ -95,3 +95,36 @@ def test_attention_layer(B, N, H, dh, R, P, extreme):
     t = token_rel_max(got, ref)
     say("   rel_l2", e, "worst token", t)
     assert e < TOL_BF16 and t < TOL_BF16_TOKEN
+
+
+def oracle_rows(qs, k, v, P, rows):
+    """The oracle's output at the given query rows only (positions P + row)."""
+    N, R, H, dh = qs.shape
+    q = qs[:, rows].astype(np.float64).transpose(0, 2, 1, 3) / (LOG2E / math.sqrt(dh))
+    o = O.attention(q, k.astype(np.float64), v.astype(np.float64),
+                    P + np.asarray(rows), np.arange(k.shape[2]))
+    return o.transpose(0, 2, 1, 3).reshape(N, len(rows), H * dh)
+
+
+@pytest.mark.parametrize("R,P", [(1560, 12480), (1000, 31000)])
+@pytest.mark.parametrize("extreme", [False, True])
+def test_attention_long_prefix_sampled(B, R, P, extreme):
+    """Long cached prefixes at 16 heads of 64 (the 9th frame of the 21-frame
+    video; 1000 queries after 31 000 keys, a ragged last query tile): several
+    key chunks per query tile, dispatched chunk-major and merged in key order.
+    Sampled query rows (both ends of every 128-row query tile and every 11th
+    row) against the oracle."""
+    N, H, dh = 1, 16, 64
+    say("attention long prefix", R, P, "extreme" if extreme else "normal")
+    qs, k, v, kc, vt, Lcap = inputs(N, H, dh, R, P, extreme, seed=R + P + 7)
+    out = B.afk_attention(bf16_dev(qs.reshape(N, R, H * dh)), bf16_dev(kc), bf16_dev(vt), P)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    rows = sorted(set(range(0, R, 11)) | {min(R - 1, t) for q in range(0, R, 128)
+                                          for t in (q, q + 127)})
+    ref = oracle_rows(qs, k, v, P, rows)
+    e = rel_l2(got[:, rows], ref)
+    t = token_rel_max(got[:, rows], ref)
+    say("   rows", len(rows), "rel_l2", e, "worst token", t)
+    assert e < TOL_BF16 and t < TOL_BF16_TOKEN
