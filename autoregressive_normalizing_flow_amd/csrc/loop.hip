@@ -32,34 +32,41 @@ namespace af {
 
 namespace {
 
-constexpr int LT = 256;   // threads
-constexpr int UC = 64;    // MLP hidden columns per chunk
+constexpr int LT = 512;   // threads
+constexpr int NW = LT / 64;   // waves
 constexpr int RG = 4;     // attention rows per wave pass
 constexpr int KT = 64;    // attention keys per wave pass (one per lane)
+constexpr int LDS_MAX = 64 * 1024;
 
-// Shared-memory carve-up of one block's state (floats).
+// Shared-memory carve-up of one block's state (floats).  uc = MLP hidden
+// columns per chunk: the whole hidden width when it fits, else the largest
+// halving of it (a multiple of 64) that does.
 struct LoopLds {
-  int xb, zb, prev, h, a, q, o, u, hd, ps, red;
-  int total;
+  int xb, zb, prev, h, a, q, o, u, hd, ps, red, fin;
+  int uc, total;
 };
 
-__host__ __device__ LoopLds loop_lds(int M, int N, int C, int d) {
+__host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp) {
   LoopLds l{};
-  int off = 0;
-  auto take = [&](int n) { const int o = off; off += (n + 3) & ~3; return o; };
-  l.xb = take(M * C);
-  l.zb = take(M * C);
-  l.prev = take(N * C);
-  l.h = take(M * d);
-  l.a = take(M * d);
-  l.q = take(M * d);
-  l.o = take(M * d);
-  l.u = take(M * UC);
-  l.hd = take(M * 2 * C);
-  l.ps = take(LT / 64 * RG * KT);   // one probability strip per wave
-  l.red = take(4 * LT + 64);
-  l.total = off;
-  return l;
+  for (int uc = dmlp;; uc /= 2) {
+    int off = 0;
+    auto take = [&](int n) { const int o = off; off += (n + 3) & ~3; return o; };
+    l.xb = take(M * C);
+    l.zb = take(M * C);
+    l.prev = take(N * C);
+    l.h = take(M * d);
+    l.a = take(M * d);
+    l.q = take(M * d);
+    l.o = take(M * d);
+    l.u = take(M * uc);
+    l.hd = take(M * 2 * C);
+    l.ps = take(NW * RG * KT);   // one probability strip per wave
+    l.red = take(NW * N * 2);    // per-wave residual partials
+    l.fin = take(N * 2);         // each sample's residual pair
+    l.uc = uc;
+    l.total = off;
+    if (off * 4 <= LDS_MAX || uc % 128 != 0) return l;
+  }
 }
 
 // y[m][n] = X[m] . W[n] (+ bias[n]) for n < Nout, m < M, contraction length
@@ -97,6 +104,51 @@ __device__ void linear(const float* X, int ldx, int M, const float* W, int ldw,
         acc1 = fmaf(x1.w, wr[k + 1].w, acc1);
       }
       epi(m, n, (acc0 + acc1) + bn);
+    }
+  }
+}
+
+// The same for a run-time contraction length K (a multiple of 64): each
+// thread takes up to RM rows at a time and walks K in slices of 64, its W
+// slice in registers; each output sums its slices in order.
+template <class Epi>
+__device__ void linear_k(const float* X, int ldx, int M, const float* W, int ldw,
+                         const float* bias, int Nout, int K, Epi epi) {
+  constexpr int RM = 4;
+  const int G = Nout < LT ? LT / Nout : 1;
+  const int grp = threadIdx.x / (LT / G >= Nout ? Nout : LT);
+  for (int n = threadIdx.x % (G > 1 ? Nout : LT); n < Nout && grp < G; n += LT) {
+    const float* wp = W + (size_t)n * ldw;
+    const float bn = bias ? bias[n] : 0.f;
+#pragma clang loop unroll(disable)
+    for (int m0 = grp; m0 < M; m0 += G * RM) {
+      float acc[RM];
+#pragma unroll
+      for (int r = 0; r < RM; ++r) acc[r] = 0.f;
+#pragma clang loop unroll(disable)
+      for (int k0 = 0; k0 < K; k0 += 64) {
+        float4 wr[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) wr[k] = *(const float4*)(wp + k0 + 4 * k);
+        // rows past M read row m0 (in bounds) and are not stored
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+#pragma unroll
+          for (int r = 0; r < RM; ++r) {
+            const int m = m0 + r * G < M ? m0 + r * G : m0;
+            const float4 x = *(const float4*)(X + m * ldx + k0 + 4 * k);
+            acc[r] = fmaf(x.x, wr[k].x, acc[r]);
+            acc[r] = fmaf(x.y, wr[k].y, acc[r]);
+            acc[r] = fmaf(x.z, wr[k].z, acc[r]);
+            acc[r] = fmaf(x.w, wr[k].w, acc[r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int m = m0 + r * G;
+        if (m < M) epi(m, n, acc[r] + bn);
+      }
     }
   }
 }
@@ -289,22 +341,22 @@ __device__ void loop_pass(const LoopArgs& a, float* sm, const LoopLds& L, int s,
     layernorm_rows(h, act, M, D, w.ln2_g, w.ln2_b);
     __syncthreads();
     // MLP in hidden chunks of UC columns: u = GELU(a W1^T + b1), h += u W2^T
+    // (+ b2 with the first chunk)
+    const int UC = L.uc;
     for (int c0 = 0; c0 < a.dmlp; c0 += UC) {
       linear<D>(act, D, M, w.w_1 + (size_t)c0 * D, D, w.b_1 + c0, UC,
                 [&](int m, int n, float v) { u[m * UC + n] = gelu_erf(v); });
       __syncthreads();
-      linear<UC>(u, UC, M, w.w_2 + c0, a.dmlp, nullptr, D,
-                 [&](int m, int n, float v) { h[m * D + n] += v; });
+      linear_k(u, UC, M, w.w_2 + c0, a.dmlp, c0 == 0 ? w.b_2 : nullptr, D, UC,
+               [&](int m, int n, float v) { h[m * D + n] += v; });
       __syncthreads();
     }
-    for (int idx = tid; idx < M * D; idx += LT) h[idx] += w.b_2[idx % D];
-    __syncthreads();
   }
 }
 
 // The affine update of the block from the head output, with each sample's
-// residual pair in red[2 LT + 2n], red[2 LT + 2n + 1] (summed in a fixed
-// order).
+// residual pair in fin[2n], fin[2n + 1] (per thread, then per wave, then over
+// the waves in order: a fixed summation order).
 template <int D>
 __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int R) {
   const int N = a.N, C = a.C, M = N * R, tid = threadIdx.x;
@@ -314,12 +366,13 @@ __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int 
   float* act = sm + L.a;
   float* hd = sm + L.hd;
   float* red = sm + L.red;
+  float* fin = sm + L.fin;
+  const int wave = tid >> 6, lane = tid & 63;
   layernorm_rows(h, act, M, D, a.ln_f_g, a.ln_f_b);
   __syncthreads();
   linear<D>(act, D, M, a.w_head, D, a.b_head, 2 * C,
             [&](int m, int n, float v) { hd[m * 2 * C + n] = v; });
   __syncthreads();
-  // per-thread partial sums of each sample's rows, then a fixed-order tree
   for (int n = 0; n < N; ++n) {
     float s0 = 0.f, s1 = 0.f;
     for (int idx = tid; idx < R * C; idx += LT) {
@@ -331,22 +384,20 @@ __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int 
       s0 += df * df;
       s1 += xn * xn;
     }
-    red[2 * tid] = s0;
-    red[2 * tid + 1] = s1;
-    __syncthreads();
-    for (int w = LT / 2; w > 0; w >>= 1) {
-      if (tid < w) {
-        red[2 * tid] += red[2 * (tid + w)];
-        red[2 * tid + 1] += red[2 * (tid + w) + 1];
-      }
-      __syncthreads();
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      red[(wave * N + n) * 2] = s0;
+      red[(wave * N + n) * 2 + 1] = s1;
     }
-    if (tid == 0) {
-      red[2 * LT + 2 * n] = red[0];
-      red[2 * LT + 2 * n + 1] = red[1];
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  if (tid < 2 * N) {
+    float t = 0.f;
+    for (int w = 0; w < NW; ++w) t += red[w * N * 2 + tid];
+    fin[tid] = t;
+  }
+  __syncthreads();
   // the new iterate (after every thread read the old one)
   for (int idx = tid; idx < M * C; idx += LT) {
     const int m = idx / C, c = idx % C;
@@ -362,11 +413,11 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int N = a.N, C = a.C, tid = threadIdx.x;
   const int nb = (a.L + a.B - 1) / a.B;
-  const LoopLds L = loop_lds(N * min(a.B, a.L), N, C, D);
+  const LoopLds L = loop_lds(N * min(a.B, a.L), N, C, D, a.dmlp);
   float* xb = sm + L.xb;
   float* zb = sm + L.zb;
   float* prev = sm + L.prev;
-  float* red = sm + L.red;
+  float* fin = sm + L.fin;
   // the token before the sequence
   for (int idx = tid; idx < N * C; idx += LT)
     prev[idx] = a.x_last ? a.x_last[idx] : 0.f;
@@ -408,7 +459,7 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
       ++k;
       bool all = true;
       for (int n = 0; n < N; ++n) {
-        const float num = red[2 * LT + 2 * n], den = red[2 * LT + 2 * n + 1];
+        const float num = fin[2 * n], den = fin[2 * n + 1];
         if (!(isfinite(num) && isfinite(den))) bad = true;
         const float r = den > 0.f ? num / den : (num == 0.f ? 0.f : INFINITY);
         all = all && r < a.tau;
@@ -417,7 +468,7 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
     }
     // the last update's residual pairs and the block's count
     if (tid == 0) {
-      for (int n = 0; n < 2 * N; ++n) system_store(&a.res_host[n], red[2 * LT + n]);
+      for (int n = 0; n < 2 * N; ++n) system_store(&a.res_host[n], fin[n]);
       system_store((unsigned*)&a.iters_host[b], (unsigned)k);
       if (bad) system_store(a.bad_host, (unsigned)(1 + b));
     }
@@ -450,13 +501,13 @@ bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_l
   if (dh != 32 && dh != 64) return false;
   const int M = N * Bc;
   if (M > 64 || C % 4 != 0 || C > 64 || Lcap % 64 != 0) return false;
-  if (dmlp % UC != 0 || n_layers < 1 || n_layers > kLoopMaxLayers) return false;
-  return loop_lds(M, N, C, d).total * sizeof(float) <= 64 * 1024;
+  if (dmlp % 64 != 0 || n_layers < 1 || n_layers > kLoopMaxLayers) return false;
+  return loop_lds(M, N, C, d, dmlp).total * sizeof(float) <= LDS_MAX;
 }
 
 hipError_t launch_jacobi_loop(const LoopArgs& a, hipStream_t st) {
   const int Bc = a.B < a.L ? a.B : a.L;
-  const size_t lds = loop_lds(a.N * Bc, a.N, a.C, a.d).total * sizeof(float);
+  const size_t lds = loop_lds(a.N * Bc, a.N, a.C, a.d, a.dmlp).total * sizeof(float);
   const dim3 g(1), b(LT);
   if (a.d == 64 && a.dh == 32) hipLaunchKernelGGL((jacobi_loop_kernel<64, 32>), g, b, lds, st, a);
   else if (a.d == 64 && a.dh == 64) hipLaunchKernelGGL((jacobi_loop_kernel<64, 64>), g, b, lds, st, a);
