@@ -165,6 +165,7 @@ struct LoopArgs {
   float* x;              // [N, L, C] written block by block
   const float* x_init;   // init 1 (given); with refresh, the final tokens
   int refresh;           // 1: only recompute the cache rows of x_init's tokens
+  int lds_max;           // LDS bytes one workgroup may take (sets the MLP chunk)
   const float* x_last;   // the token before the sequence, [N, C], or NULL (zeros)
   int N, L, B, P, dir, init, F, max_iters;
   float tau;             // <= 0: exactly min(max_iters, block) updates
@@ -173,9 +174,10 @@ struct LoopArgs {
   unsigned* bad_host;    // host-mapped: 1 + the block that met a non-finite sum
 };
 // Rows N x min(B, L) <= 64, d 64 or 128, d_h 32 or 64, C % 4 == 0, C <= 64,
-// d_mlp % 64 == 0, at most kLoopMaxLayers layers.
+// d_mlp % 64 == 0, at most kLoopMaxLayers layers, the block's state within
+// lds_max bytes of LDS.
 bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_layers,
-                           int Lcap);
+                           int Lcap, int lds_max);
 // One workgroup runs the whole Jacobi inverse of one AF block (every block of
 // the sequence, the stop tests and the cache refreshes), or with a.refresh the
 // cache rows of given tokens in blocks of B rows, by the same pass as the

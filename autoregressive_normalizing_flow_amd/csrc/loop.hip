@@ -36,17 +36,16 @@ constexpr int LT = 512;   // threads
 constexpr int NW = LT / 64;   // waves
 constexpr int RG = 4;     // attention rows per wave pass
 constexpr int KT = 64;    // attention keys per wave pass (one per lane)
-constexpr int LDS_MAX = 64 * 1024;
 
 // Shared-memory carve-up of one block's state (floats).  uc = MLP hidden
-// columns per chunk: the whole hidden width when it fits, else the largest
-// halving of it (a multiple of 64) that does.
+// columns per chunk: the whole hidden width when it fits in lds_max bytes,
+// else the largest halving of it (a multiple of 64) that does.
 struct LoopLds {
   int xb, zb, prev, h, a, q, o, u, hd, ps, red, fin;
   int uc, total;
 };
 
-__host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp) {
+__host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp, int lds_max) {
   LoopLds l{};
   for (int uc = dmlp;; uc /= 2) {
     int off = 0;
@@ -65,7 +64,7 @@ __host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp) {
     l.fin = take(N * 2);         // each sample's residual pair
     l.uc = uc;
     l.total = off;
-    if (off * 4 <= LDS_MAX || uc % 128 != 0) return l;
+    if (off * 4 <= lds_max || uc % 128 != 0) return l;
   }
 }
 
@@ -413,7 +412,7 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int N = a.N, C = a.C, tid = threadIdx.x;
   const int nb = (a.L + a.B - 1) / a.B;
-  const LoopLds L = loop_lds(N * min(a.B, a.L), N, C, D, a.dmlp);
+  const LoopLds L = loop_lds(N * min(a.B, a.L), N, C, D, a.dmlp, a.lds_max);
   float* xb = sm + L.xb;
   float* zb = sm + L.zb;
   float* prev = sm + L.prev;
@@ -495,26 +494,43 @@ __global__ __launch_bounds__(LT) void jacobi_loop_kernel(LoopArgs a) {
 }
 
 bool jacobi_loop_supported(int N, int Bc, int C, int d, int H, int dmlp, int n_layers,
-                           int Lcap) {
+                           int Lcap, int lds_max) {
   if (N < 1 || Bc < 1 || H < 1 || (d != 64 && d != 128) || d % H != 0) return false;
   const int dh = d / H;
   if (dh != 32 && dh != 64) return false;
   const int M = N * Bc;
   if (M > 64 || C % 4 != 0 || C > 64 || Lcap % 64 != 0) return false;
   if (dmlp % 64 != 0 || n_layers < 1 || n_layers > kLoopMaxLayers) return false;
-  return loop_lds(M, N, C, d, dmlp).total * sizeof(float) <= LDS_MAX;
+  return loop_lds(M, N, C, d, dmlp, lds_max).total * sizeof(float) <= (size_t)lds_max;
 }
 
 hipError_t launch_jacobi_loop(const LoopArgs& a, hipStream_t st) {
   const int Bc = a.B < a.L ? a.B : a.L;
-  const size_t lds = loop_lds(a.N * Bc, a.N, a.C, a.d, a.dmlp).total * sizeof(float);
+  const size_t lds = loop_lds(a.N * Bc, a.N, a.C, a.d, a.dmlp, a.lds_max).total * sizeof(float);
   const dim3 g(1), b(LT);
-  if (a.d == 64 && a.dh == 32) hipLaunchKernelGGL((jacobi_loop_kernel<64, 32>), g, b, lds, st, a);
-  else if (a.d == 64 && a.dh == 64) hipLaunchKernelGGL((jacobi_loop_kernel<64, 64>), g, b, lds, st, a);
-  else if (a.d == 128 && a.dh == 32) hipLaunchKernelGGL((jacobi_loop_kernel<128, 32>), g, b, lds, st, a);
-  else if (a.d == 128 && a.dh == 64) hipLaunchKernelGGL((jacobi_loop_kernel<128, 64>), g, b, lds, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  // more than 64 KB of dynamic LDS is asked for explicitly
+  auto go = [&](const void* k, auto launch) {
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    launch();
+    return hipGetLastError();
+  };
+  if (a.d == 64 && a.dh == 32)
+    return go((const void*)jacobi_loop_kernel<64, 32>,
+              [&] { hipLaunchKernelGGL((jacobi_loop_kernel<64, 32>), g, b, lds, st, a); });
+  if (a.d == 64 && a.dh == 64)
+    return go((const void*)jacobi_loop_kernel<64, 64>,
+              [&] { hipLaunchKernelGGL((jacobi_loop_kernel<64, 64>), g, b, lds, st, a); });
+  if (a.d == 128 && a.dh == 32)
+    return go((const void*)jacobi_loop_kernel<128, 32>,
+              [&] { hipLaunchKernelGGL((jacobi_loop_kernel<128, 32>), g, b, lds, st, a); });
+  if (a.d == 128 && a.dh == 64)
+    return go((const void*)jacobi_loop_kernel<128, 64>,
+              [&] { hipLaunchKernelGGL((jacobi_loop_kernel<128, 64>), g, b, lds, st, a); });
+  return hipErrorInvalidValue;
 }
 
 }  // namespace af

@@ -132,6 +132,7 @@ struct af_plan {
   // the Jacobi loop on the device for small fp32 blocks (on by default);
   // pinned block counts and non-finite words of its launches
   bool device_loop = true;
+  int loop_lds_max = 0;   // LDS bytes per workgroup for the device loop (0: not queried yet)
   int* loop_host = nullptr;
   int* loop_host_dev = nullptr;
   size_t loop_cap = 0;   // ints
@@ -763,7 +764,7 @@ af_status af_forward(af_plan* p, const float* x, float* z, float* logdet, int N,
 }
 
 static af::LoopArgs loop_args(const af_plan* p, const BlockW& bw, char* ws, const WsLayout& w);
-static int loop_refresh_rows(const af_plan* p, int N, int L);
+static int loop_refresh_rows(af_plan* p, int N, int L);
 
 af_status af_prefill(af_plan* p, const float* x_prefix, int N, int P, void* ws_,
                      size_t ws_bytes, void* stream) {
@@ -846,16 +847,37 @@ static af::LoopArgs loop_args(const af_plan* p, const BlockW& bw, char* ws, cons
   a.dh = p->dh;
   a.dmlp = p->dmlp;
   a.Lcap = p->Lcap;
+  a.lds_max = p->loop_lds_max;
   return a;
 }
 
+// LDS one workgroup of the device loop may take: the current device's limit
+// per block (160 KB on gfx950), queried once; 64 KB if the query fails.
+static int loop_lds_max(af_plan* p) {
+  if (p->loop_lds_max == 0) {
+    int dev = 0, v = 0;
+    p->loop_lds_max = 65536;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+            hipSuccess &&
+        v > 65536)
+      p->loop_lds_max = std::min(v, 160 * 1024);
+    (void)hipGetLastError();
+  }
+  return p->loop_lds_max;
+}
+
+static bool loop_supported(af_plan* p, int N, int rows) {
+  return af::jacobi_loop_supported(N, rows, p->cfg.C, p->cfg.d, p->cfg.n_heads, p->dmlp,
+                                   p->cfg.n_layers, p->Lcap, loop_lds_max(p));
+}
+
 // Rows per device-loop block for a refresh of N samples (0: not supported).
-static int loop_refresh_rows(const af_plan* p, int N, int L) {
+static int loop_refresh_rows(af_plan* p, int N, int L) {
   if (p->bf || !p->device_loop || p->graphs || p->row_split || p->fuse_refresh || N > 64)
     return 0;
   const int R = std::min(L, 64 / N);
-  return af::jacobi_loop_supported(N, R, p->cfg.C, p->cfg.d, p->cfg.n_heads, p->dmlp,
-                                   p->cfg.n_layers, p->Lcap) ? R : 0;
+  return loop_supported(p, N, R) ? R : 0;
 }
 
 // The whole Jacobi inverse of each AF block of the stack in one launch (small
@@ -966,8 +988,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   const int C = p->cfg.C;
   const int nb = (L + B - 1) / B;
   if (!p->bf && p->device_loop && !p->graphs && !p->row_split && !p->fuse_refresh &&
-      af::jacobi_loop_supported(N, Bc, C, p->cfg.d, p->cfg.n_heads, p->dmlp, p->cfg.n_layers,
-                                p->Lcap))
+      loop_supported(p, N, Bc))
     return inverse_on_device(p, z, N, L, B, tau, max_iters, init, x_init, frame_len, prefix_len,
                              x_last, x, iters, (char*)ws_, w, nb, (hipStream_t)stream);
   // A block that stops early has its cache rows recomputed from its final

@@ -224,8 +224,9 @@ af_status af_inverse_jacobi(af_plan *p, const float *z, int N, int L, int B,
  * cached keys up to their own position), bytes for "affine" (20 C per token
  * in an inverse update, 16 C in the forward), 0 for "layernorm".  Classes:
  * "embed", "layernorm", "gemm_qkv", "gemm_o", "gemm_mlp1", "gemm_mlp2",
- * "gemm_head", "attention", "affine".  At most 16384 launches are recorded
- * per enable. */
+ * "gemm_head", "attention", "affine", "device_loop" (one launch per AF block
+ * of an inverse on the device loop, its work the flops of its updates and
+ * refreshes).  At most 16384 launches are recorded per enable. */
 af_status af_profile_enable(af_plan *p, const char *kernel_class);
 af_status af_profile_disable(af_plan *p);
 af_status af_profile_read(af_plan *p, int *launches, double *total_ms, double *work);
@@ -282,7 +283,8 @@ af_status af_plan_set_row_split(af_plan *p, int enable);
 /* The Jacobi loop on the device (STARFlow-V notes, 关键设计 3: the update is
  * repeated until the residual falls below tau).  For fp32 plans whose block
  * fits one workgroup (N * min(B, L) <= 64 rows, d 64 or 128, d / n_heads 32
- * or 64, C % 4 == 0, C <= 64, d_mlp % 64 == 0, at most 8 layers) and no
+ * or 64, C % 4 == 0, C <= 64, d_mlp % 64 == 0, at most 8 layers, the block's
+ * activations within the LDS one workgroup may take: 160 KB on gfx950) and no
  * graph replay, row split or fused refresh is asked for, af_inverse_jacobi
  * runs the whole inverse of each AF block of the stack as one launch: every
  * Jacobi block in order, every update, the stop test and the cache refresh

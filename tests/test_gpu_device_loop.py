@@ -30,16 +30,30 @@ def B():
     return binding
 
 
+def loop_launches(plan, fn):
+    """(fn(), number of device-loop launches it made)."""
+    plan.profile_enable("device_loop")
+    try:
+        out = fn()
+        n, _ = plan.profile_read()
+    finally:
+        plan.profile_disable()
+    return out, n
+
+
 def both_paths(plan, fn):
     """fn() with the device loop, then with it off (the plan is left with
-    the device loop on)."""
+    the device loop on); the first must run on the device loop and the second
+    must not."""
     plan.set_device_loop(True)
-    dev = fn()
+    dev, n_dev = loop_launches(plan, fn)
+    assert n_dev > 0, "the shape did not take the device loop"
     plan.set_device_loop(False)
     try:
-        ref = fn()
+        ref, n_ref = loop_launches(plan, fn)
     finally:
         plan.set_device_loop(True)
+    assert n_ref == 0
     return dev, ref
 
 
@@ -56,7 +70,10 @@ def check_pair(dev, ref, xo, ito):
     (16, 64, 2, 1, 64, 1, 16, 1e-3),    # the tiny_f32 workload's block
     (8, 64, 2, 2, 45, 3, 16, 1e-4),     # batch 3, ragged last block, 2 layers
     (4, 64, 1, 1, 20, 2, 8, 1e-3),      # one head of 64
-    (12, 128, 4, 1, 32, 1, 32, 1e-3),   # a whole 32-row block, d 128
+    (12, 128, 4, 1, 32, 1, 32, 1e-3),   # a whole 32-row block, d 128, heads of 32
+    (16, 64, 1, 1, 40, 4, 16, 1e-3),    # 64 rows (the most), ragged last block
+    (4, 128, 2, 1, 48, 2, 32, 1e-3),    # 64 rows at d 128: the MLP in 8 chunks of 64
+    (4, 64, 2, 8, 12, 2, 4, 1e-3),      # 8 layers (the most)
 ])
 def test_device_loop_matches_oracle(B, C, d, H, layers, L, N, Bj, tau):
     say("device loop", C, d, H, layers, L, N, Bj, tau)
@@ -84,7 +101,8 @@ def test_device_loop_forced_counts_and_sequential(B):
     xo, _ = O.inverse_jacobi_block(p64, z, 1, 8, 0.0, max_iters=3)
     check_pair(dev, ref, xo, [3, 3, 3])
     # B = 1: sequential decoding; tau <= 0 without a cap: Bb updates, exact
-    x1, it1 = plan.inverse_jacobi(to_dev(z), 1, 1e-3)
+    (x1, it1), n = loop_launches(plan, lambda: plan.inverse_jacobi(to_dev(z), 1, 1e-3))
+    assert n > 0
     assert np.all(it1 == 1)
     assert rel_l2(to_np(x1), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
     xf, itf = plan.inverse_jacobi(to_dev(z), 8, 0.0)

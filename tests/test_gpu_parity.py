@@ -280,6 +280,9 @@ def test_fused_refresh_matches_separate_pass(B, dtype):
                                       seed=61)
         N, L, Bj, C, H = 2, 300, 96, 48, 4
     plan = B.AFPlan(cfg, params)
+    # both runs on the launch-per-kernel path (the fused refresh is one of
+    # its options; the device loop refreshes inside its own kernel)
+    plan.set_device_loop(False)
     z = to_dev(synth.normal((N, L, C), 62))
     ws = plan.workspace(N, min(2 * Bj, L))
     out = {}
