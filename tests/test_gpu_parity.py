@@ -19,6 +19,10 @@ from parity_util import (TOL_BF16, TOL_F32, TOL_LOGDET, oracle_jacobi_like,  # n
 
 pytestmark = pytest.mark.gpu
 
+# fp32 end-to-end cases run on both inverse paths: the device loop (the
+# default for the shapes it covers) and the launch-per-kernel path
+PATHS = pytest.mark.parametrize("dl", [True, False], ids=["device_loop", "launches"])
+
 
 @pytest.fixture(scope="module")
 def B():
@@ -139,8 +143,9 @@ def test_forward_flags_and_grouped_logdet(B):
     plan.forward(to_dev(x), check_finite=True)
 
 
+@PATHS
 @pytest.mark.parametrize("tau", [1e-3, 0.0])
-def test_inverse_flags_nonfinite(B, tau):
+def test_inverse_flags_nonfinite(B, tau, dl):
     """A NaN latent in the second Jacobi block: reported as AF_ERR_NONFINITE
     whether the residual is read back every iteration (tau > 0) or only the
     sticky tag at the end (forced count)."""
@@ -148,6 +153,7 @@ def test_inverse_flags_nonfinite(B, tau):
     w = synth.WORKLOADS["tiny_f32"]
     params = synth.make_params(w.block, 0)
     plan = B.AFPlan(w.block, params)
+    plan.set_device_loop(dl)
     z = synth.normal((1, 64, 16), 1)
     z[0, 20, 5] = np.nan
     with pytest.raises(B.AFError) as ei:
@@ -157,7 +163,9 @@ def test_inverse_flags_nonfinite(B, tau):
     # the plan stays usable: a clean call after the failure equals a fresh plan's
     z[0, 20, 5] = 0.0
     xa, ia = plan.inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
-    xb, ib = B.AFPlan(w.block, params).inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
+    fresh = B.AFPlan(w.block, params)
+    fresh.set_device_loop(dl)
+    xb, ib = fresh.inverse_jacobi(to_dev(z), 16, tau, max_iters=3)
     torch.cuda.synchronize()
     assert np.array_equal(ia, ib) and torch.equal(xa, xb)
 
@@ -187,13 +195,15 @@ def test_back_to_back_calls_without_sync(B):
 # ---------------------------------------------------------------------------
 # fp32 path, end to end
 # ---------------------------------------------------------------------------
-def test_tiny_f32_forward_and_inverse(B):
+@PATHS
+def test_tiny_f32_forward_and_inverse(B, dl):
     """One 8x8 latent frame, C=16, 1 layer d=64, 2 heads, fp32, B=16, tau=1e-3."""
     w = synth.WORKLOADS["tiny_f32"]
     say("tiny_f32")
     params = synth.make_params(w.block, 0)
     p64 = O.to64(params[0])
     plan = B.AFPlan(w.block, params)
+    plan.set_device_loop(dl)
     z = synth.normal((1, 64, 16), 1)
     x_in = synth.normal((1, 64, 16), 2)
     # forward of x
@@ -216,12 +226,14 @@ def test_tiny_f32_forward_and_inverse(B):
     assert rel_l2(to_np(xr), x_in) < 0.05
 
 
-def test_f32_stack_ragged_r2l(B):
+@PATHS
+def test_f32_stack_ragged_r2l(B, dl):
     """T=2 (L->R, R->L), ragged last Jacobi block, batch 3, dh=32."""
     say("f32 stack ragged")
     cfg, params, p64 = problem(C=5, d=64, H=2, layers=2, max_len=60, dtype="f32",
                                seed=3, n_blocks=2)
     plan = B.AFPlan(cfg, params)
+    plan.set_device_loop(dl)
     x_in = synth.normal((3, 60, 5), 4)
     zg, ldg = plan.forward(to_dev(x_in))
     zo, ldo = O.forward_stack(p64, x_in, 2)
@@ -236,7 +248,8 @@ def test_f32_stack_ragged_r2l(B):
 
 @pytest.mark.parametrize("C,d,N,L,Bj", [(24, 128, 2, 70, 32), (64, 256, 1, 50, 50),
                                          (8, 512, 3, 33, 16)])
-def test_f32_head_mfma_shapes(B, C, d, N, L, Bj):
+@PATHS
+def test_f32_head_mfma_shapes(B, C, d, N, L, Bj, dl):
     """The fp32-MFMA head at other channel counts (2C = 48, 128, 16 columns),
     K split over 1..8 ranges, ragged 16-row tiles, batch."""
     say("f32 head mfma", C, d, N, L, Bj)
@@ -244,6 +257,7 @@ def test_f32_head_mfma_shapes(B, C, d, N, L, Bj):
     cfg, params, (p64,) = problem(C=C, d=d, H=H, layers=1, max_len=L, dtype="f32",
                                   seed=C + d)
     plan = B.AFPlan(cfg, params)
+    plan.set_device_loop(dl)
     x_in = synth.normal((N, L, C), C + 1)
     zg, ldg = plan.forward(to_dev(x_in))
     zo, ldo = O.forward_block(p64, x_in, H)
@@ -307,10 +321,12 @@ def test_fused_refresh_matches_separate_pass(B, dtype):
         assert rel_l2(to_np(x1), xo) < TOL_BF16
 
 
-def test_f32_forced_count_and_sequential(B):
+@PATHS
+def test_f32_forced_count_and_sequential(B, dl):
     say("f32 forced + B=1")
     cfg, params, (p64,) = problem(C=4, d=64, H=1, layers=1, max_len=20, dtype="f32", seed=5)
     plan = B.AFPlan(cfg, params)
+    plan.set_device_loop(dl)
     z = synth.normal((2, 20, 4), 6)
     xg, itg = plan.inverse_jacobi(to_dev(z), 8, 0.0, max_iters=3)
     assert np.all(itg == 3)
@@ -326,10 +342,12 @@ def test_f32_forced_count_and_sequential(B):
     assert rel_l2(to_np(xf), O.inverse_sequential_block(p64, z, 1)) < TOL_F32
 
 
-def test_f32_prefill_given_prevframe(B):
+@PATHS
+def test_f32_prefill_given_prevframe(B, dl):
     say("f32 prefill/given/prev_frame")
     cfg, params, (p64,) = problem(C=6, d=128, H=2, layers=2, max_len=96, dtype="f32", seed=7)
     plan = B.AFPlan(cfg, params)
+    plan.set_device_loop(dl)
     xp = synth.normal((2, 32, 6), 8)
     z = synth.normal((2, 64, 6), 9)
     xinit = synth.normal((2, 64, 6), 10)
@@ -351,10 +369,12 @@ def test_f32_prefill_given_prevframe(B):
     assert rel_l2(to_np(xg2), xo2) < TOL_F32
 
 
-def test_f32_run_twice_bitwise(B):
+@PATHS
+def test_f32_run_twice_bitwise(B, dl):
     say("f32 determinism")
     cfg, params, _ = problem(C=8, d=64, H=2, layers=2, max_len=80, dtype="f32", seed=12)
     plan = B.AFPlan(cfg, params)
+    plan.set_device_loop(dl)
     z = to_dev(synth.normal((2, 80, 8), 13))
     a, ia = plan.inverse_jacobi(z, 32, 1e-3)
     b, ib = plan.inverse_jacobi(z, 32, 1e-3)
