@@ -16,11 +16,10 @@
 // call's last block), so both come from the same arithmetic.
 //
 // The block's activations live in LDS (rows M = N x B <= 64, d 64 or 128);
-// the weights are read from global memory (L2-resident at these sizes), each
-// thread loading a whole weight row into registers before it multiplies (one
-// memory round trip per output column instead of one per step), and the KV
-// cache is the workspace's, in the layout the other kernels use, so a later
-// call continues from it.  Attention runs one wave per (sample, head, four
+// the projections run on the fp32 matrix cores, one wave per 16 x 16 output
+// tile, the weights read from global memory (L2-resident at these sizes) in
+// whole float4s per lane; the KV cache is the workspace's, in the layout the
+// other kernels use, so a later call continues from it.  Attention runs one wave per (sample, head, four
 // rows): the lanes take 64 keys at a time for the scores of the rows, then
 // the value dimensions for P V, so each K row and V^T chunk is loaded once
 // for the four rows.  Arithmetic is fp32 throughout, sums in a fixed order
@@ -53,11 +52,11 @@ __host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp, int l
     l.xb = take(M * C);
     l.zb = take(M * C);
     l.prev = take(N * C);
-    l.h = take(M * d);
-    l.a = take(M * d);
-    l.q = take(M * d);
-    l.o = take(M * d);
-    l.u = take(M * uc);
+    l.h = take(M * (d + 4));   // rows padded by 4 floats: the 16 rows an MFMA
+    l.a = take(M * (d + 4));   // operand read spans fall on distinct banks
+    l.q = take(M * (d + 4));
+    l.o = take(M * (d + 4));
+    l.u = take(M * (uc + 4));
     l.hd = take(M * 2 * C);
     l.ps = take(NW * RG * KT);   // one probability strip per wave
     l.red = take(NW * N * 2);    // per-wave residual partials
@@ -68,97 +67,63 @@ __host__ __device__ LoopLds loop_lds(int M, int N, int C, int d, int dmlp, int l
   }
 }
 
-// y[m][n] = X[m] . W[n] (+ bias[n]) for n < Nout, m < M, contraction length
-// K; X in LDS with row stride ldx, W row-major with row stride ldw (global).
-// One thread per output column: its W row goes to registers first (K / 4
-// independent 16-byte loads), then row by row against X (two partial sums,
-// added at the end); epi(m, n, value) consumes each result.
-template <int K, class Epi>
+// y[m][n] = X[m] . W[n] (+ bias[n]) for m < M, n < Nout, contraction length K
+// (a multiple of 16); X in LDS with row stride ldx, W row-major with row
+// stride ldw (global).  On the fp32 matrix cores (v_mfma_f32_16x16x4f32), one
+// wave per 16-token x 16-feature tile: lane (i = l % 16, g = l / 16) feeds W
+// row f0 + i and token m0 + i at k slot g, with the k order permuted alike in
+// both operands (slot g of step 4t + e is k = 4g + 16t + e), so every lane
+// loads whole float4s, up to KG of K per load round; it receives features
+// f0 + 4g .. f0 + 4g + 3 of token m0 + i, and epi(m, n, value) consumes
+// each.  Padding rows and features past M and Nout read valid ones and are
+// not stored.
+template <int KG, class Epi>
 __device__ void linear(const float* X, int ldx, int M, const float* W, int ldw,
-                       const float* bias, int Nout, Epi epi) {
-  // with fewer columns than threads, the rows are dealt over G thread groups
-  const int G = Nout < LT ? LT / Nout : 1;
-  const int grp = threadIdx.x / (LT / G >= Nout ? Nout : LT);
-  for (int n = threadIdx.x % (G > 1 ? Nout : LT); n < Nout && grp < G; n += LT) {
-    float4 wr[K / 4];
-    const float* wp = W + (size_t)n * ldw;
-#pragma unroll
-    for (int k = 0; k < K / 4; ++k) wr[k] = *(const float4*)(wp + 4 * k);
-    const float bn = bias ? bias[n] : 0.f;
+                       const float* bias, int Nout, int K, Epi epi) {
+  static_assert(KG % 16 == 0, "k group");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int tm = (M + 15) / 16, tn = (Nout + 15) / 16;
+  for (int tile = wave; tile < tm * tn; tile += NW) {
+    const int m0 = (tile % tm) * 16, f0 = (tile / tm) * 16;
+    const float* xr = X + min(m0 + i, M - 1) * ldx + 4 * g;
+    const float* wr = W + (size_t)min(f0 + i, Nout - 1) * ldw + 4 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma clang loop unroll(disable)
-    for (int m = grp; m < M; m += G) {
-      const float* xr = X + m * ldx;
-      float acc0 = 0.f, acc1 = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KG) {
+      float4 wa[KG / 16], xb[KG / 16];
 #pragma unroll
-      for (int k = 0; k < K / 4; k += 2) {
-        const float4 x0 = *(const float4*)(xr + 4 * k);
-        const float4 x1 = *(const float4*)(xr + 4 * k + 4);
-        acc0 = fmaf(x0.x, wr[k].x, acc0);
-        acc0 = fmaf(x0.y, wr[k].y, acc0);
-        acc0 = fmaf(x0.z, wr[k].z, acc0);
-        acc0 = fmaf(x0.w, wr[k].w, acc0);
-        acc1 = fmaf(x1.x, wr[k + 1].x, acc1);
-        acc1 = fmaf(x1.y, wr[k + 1].y, acc1);
-        acc1 = fmaf(x1.z, wr[k + 1].z, acc1);
-        acc1 = fmaf(x1.w, wr[k + 1].w, acc1);
-      }
-      epi(m, n, (acc0 + acc1) + bn);
-    }
-  }
-}
-
-// The same for a run-time contraction length K (a multiple of 64): each
-// thread takes up to RM rows at a time and walks K in slices of 64, its W
-// slice in registers; each output sums its slices in order.
-template <class Epi>
-__device__ void linear_k(const float* X, int ldx, int M, const float* W, int ldw,
-                         const float* bias, int Nout, int K, Epi epi) {
-  constexpr int RM = 4;
-  const int G = Nout < LT ? LT / Nout : 1;
-  const int grp = threadIdx.x / (LT / G >= Nout ? Nout : LT);
-  for (int n = threadIdx.x % (G > 1 ? Nout : LT); n < Nout && grp < G; n += LT) {
-    const float* wp = W + (size_t)n * ldw;
-    const float bn = bias ? bias[n] : 0.f;
-#pragma clang loop unroll(disable)
-    for (int m0 = grp; m0 < M; m0 += G * RM) {
-      float acc[RM];
-#pragma unroll
-      for (int r = 0; r < RM; ++r) acc[r] = 0.f;
-#pragma clang loop unroll(disable)
-      for (int k0 = 0; k0 < K; k0 += 64) {
-        float4 wr[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) wr[k] = *(const float4*)(wp + k0 + 4 * k);
-        // rows past M read row m0 (in bounds) and are not stored
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-#pragma unroll
-          for (int r = 0; r < RM; ++r) {
-            const int m = m0 + r * G < M ? m0 + r * G : m0;
-            const float4 x = *(const float4*)(X + m * ldx + k0 + 4 * k);
-            acc[r] = fmaf(x.x, wr[k].x, acc[r]);
-            acc[r] = fmaf(x.y, wr[k].y, acc[r]);
-            acc[r] = fmaf(x.z, wr[k].z, acc[r]);
-            acc[r] = fmaf(x.w, wr[k].w, acc[r]);
-          }
+      for (int t = 0; t < KG / 16; ++t)
+        if (k0 + 16 * t < K) {
+          wa[t] = *(const float4*)(wr + k0 + 16 * t);
+          xb[t] = *(const float4*)(xr + k0 + 16 * t);
         }
-      }
 #pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        const int m = m0 + r * G;
-        if (m < M) epi(m, n, acc[r] + bn);
+      for (int t = 0; t < KG / 16; ++t)
+        if (k0 + 16 * t < K) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t].x, xb[t].x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t].y, xb[t].y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t].z, xb[t].z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t].w, xb[t].w, acc, 0, 0, 0);
+        }
+    }
+    if (m0 + i < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = f0 + 4 * g + r;
+        if (n < Nout) epi(m0 + i, n, acc[r] + (bias ? bias[n] : 0.f));
       }
     }
   }
 }
 
-// out[m] = LayerNorm(in[m]) * g + b over rows of width d (eps 1e-5), one
-// wave per row.
-__device__ void layernorm_rows(const float* in, float* out, int M, int d, const float* g,
-                               const float* b) {
+// out[m] = LayerNorm(in[m]) * g + b over rows of width d and stride ld (eps
+// 1e-5), one wave per row.
+__device__ void layernorm_rows(const float* in, float* out, int M, int d, int ld,
+                               const float* g, const float* b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int m = wave; m < M; m += LT / 64) {
-    const float* r = in + m * d;
+    const float* r = in + m * ld;
     float s = 0.f;
     for (int e = lane; e < d; e += 64) s += r[e];
     const float mean = wave_sum(s) / d;
@@ -168,7 +133,7 @@ __device__ void layernorm_rows(const float* in, float* out, int M, int d, const 
       v += t * t;
     }
     const float rstd = rsqrtf(wave_sum(v) / d + 1e-5f);
-    for (int e = lane; e < d; e += 64) out[m * d + e] = (r[e] - mean) * rstd * g[e] + b[e];
+    for (int e = lane; e < d; e += 64) out[m * ld + e] = (r[e] - mean) * rstd * g[e] + b[e];
   }
 }
 
@@ -226,7 +191,7 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
           if (r >= rows) continue;
-          const float* qr = q + (nn * R + t0 + r) * D + head * DH;
+          const float* qr = q + (nn * R + t0 + r) * (D + 4) + head * DH;
           float sv = 0.f;
 #pragma unroll
           for (int e = 0; e < DH / 4; ++e) {
@@ -271,7 +236,7 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
           if (r >= rows) continue;
-          o[(nn * R + t0 + r) * D + head * DH + lane] = oacc[r] / ol[r];
+          o[(nn * R + t0 + r) * (D + 4) + head * DH + lane] = oacc[r] / ol[r];
         }
       }
     }
@@ -294,6 +259,7 @@ __device__ void loop_pass(const LoopArgs& a, float* sm, const LoopLds& L, int s,
   float* q = sm + L.q;
   float* o = sm + L.o;
   float* u = sm + L.u;
+  constexpr int LD = D + 4;   // row stride of h, act, q, o
   // shift + embed: row m = n R + t takes token t - 1 of the block (the token
   // before the block at t = 0), position P + s + t
   for (int idx = tid; idx < M * D; idx += LT) {
@@ -308,20 +274,20 @@ __device__ void loop_pass(const LoopArgs& a, float* sm, const LoopLds& L, int s,
       acc = fmaf(in[c + 2], w4.z, acc);
       acc = fmaf(in[c + 3], w4.w, acc);
     }
-    h[idx] = acc;
+    h[m * LD + e] = acc;
   }
   __syncthreads();
   for (int l = 0; l < a.n_layers; ++l) {
     const LoopLayer& w = a.layers[l];
     float* kc = a.kc[l];
     float* vt = a.vt[l];
-    layernorm_rows(h, act, M, D, w.ln1_g, w.ln1_b);
+    layernorm_rows(h, act, M, D, LD, w.ln1_g, w.ln1_b);
     __syncthreads();
     // QKV: Q into LDS, K and V of the block rows into the cache
-    linear<D>(act, D, M, w.w_qkv, D, w.b_qkv, 3 * D, [&](int m, int n, float v) {
+    linear<D>(act, LD, M, w.w_qkv, D, w.b_qkv, 3 * D, D, [&](int m, int n, float v) {
       const int which = n / D, hd = n - which * D;
       if (which == 0) {
-        q[m * D + hd] = v;
+        q[m * LD + hd] = v;
         return;
       }
       const int nn = m / R, t = m - nn * R, p = a.P + s + t;
@@ -335,19 +301,19 @@ __device__ void loop_pass(const LoopArgs& a, float* sm, const LoopLds& L, int s,
     loop_attention<D, DH>(a, q, o, sm + L.ps, kc, vt, s, R);
     __syncthreads();
     // output projection into the residual stream
-    linear<D>(o, D, M, w.w_o, D, w.b_o, D, [&](int m, int n, float v) { h[m * D + n] += v; });
+    linear<D>(o, LD, M, w.w_o, D, w.b_o, D, D, [&](int m, int n, float v) { h[m * LD + n] += v; });
     __syncthreads();
-    layernorm_rows(h, act, M, D, w.ln2_g, w.ln2_b);
+    layernorm_rows(h, act, M, D, LD, w.ln2_g, w.ln2_b);
     __syncthreads();
     // MLP in hidden chunks of UC columns: u = GELU(a W1^T + b1), h += u W2^T
     // (+ b2 with the first chunk)
-    const int UC = L.uc;
+    const int UC = L.uc, LU = UC + 4;
     for (int c0 = 0; c0 < a.dmlp; c0 += UC) {
-      linear<D>(act, D, M, w.w_1 + (size_t)c0 * D, D, w.b_1 + c0, UC,
-                [&](int m, int n, float v) { u[m * UC + n] = gelu_erf(v); });
+      linear<D>(act, LD, M, w.w_1 + (size_t)c0 * D, D, w.b_1 + c0, UC, D,
+                [&](int m, int n, float v) { u[m * LU + n] = gelu_erf(v); });
       __syncthreads();
-      linear_k(u, UC, M, w.w_2 + c0, a.dmlp, c0 == 0 ? w.b_2 : nullptr, D, UC,
-               [&](int m, int n, float v) { h[m * D + n] += v; });
+      linear<128>(u, LU, M, w.w_2 + c0, a.dmlp, c0 == 0 ? w.b_2 : nullptr, D, UC,
+                  [&](int m, int n, float v) { h[m * LD + n] += v; });
       __syncthreads();
     }
   }
@@ -367,9 +333,10 @@ __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int 
   float* red = sm + L.red;
   float* fin = sm + L.fin;
   const int wave = tid >> 6, lane = tid & 63;
-  layernorm_rows(h, act, M, D, a.ln_f_g, a.ln_f_b);
+  constexpr int LD = D + 4;
+  layernorm_rows(h, act, M, D, LD, a.ln_f_g, a.ln_f_b);
   __syncthreads();
-  linear<D>(act, D, M, a.w_head, D, a.b_head, 2 * C,
+  linear<D>(act, LD, M, a.w_head, D, a.b_head, 2 * C, D,
             [&](int m, int n, float v) { hd[m * 2 * C + n] = v; });
   __syncthreads();
   for (int n = 0; n < N; ++n) {

@@ -72,7 +72,7 @@ def check_pair(dev, ref, xo, ito):
     (4, 64, 1, 1, 20, 2, 8, 1e-3),      # one head of 64
     (12, 128, 4, 1, 32, 1, 32, 1e-3),   # a whole 32-row block, d 128, heads of 32
     (16, 64, 1, 1, 40, 4, 16, 1e-3),    # 64 rows (the most), ragged last block
-    (4, 128, 2, 1, 48, 2, 32, 1e-3),    # 64 rows at d 128: the MLP in 8 chunks of 64
+    (4, 128, 2, 1, 48, 2, 30, 1e-3),    # 60 rows at d 128: the MLP in 8 chunks of 64
     (4, 64, 2, 8, 12, 2, 4, 1e-3),      # 8 layers (the most)
 ])
 def test_device_loop_matches_oracle(B, C, d, H, layers, L, N, Bj, tau):
