@@ -36,6 +36,32 @@ constexpr int NW = LT / 64;   // waves
 constexpr int RG = 4;     // attention rows per wave pass
 constexpr int KT = 64;    // attention keys per wave pass (one per lane)
 
+// Reductions over the 64 lanes of a wave, the result in every lane: within
+// each row of 16 lanes by DPP (quad permutes, then rotations by 4 and 8),
+// then the four row values read from lanes 0, 16, 32 and 48 and combined in
+// that order (a fixed order; no LDS round trips).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float lanes_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm 1,0,3,2
+  v += dpp_mov<0x4E>(v);    // quad_perm 2,3,0,1
+  v += dpp_mov<0x124>(v);   // row_ror 4
+  v += dpp_mov<0x128>(v);   // row_ror 8
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+__device__ __forceinline__ float lanes_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x124>(v));
+  v = fmaxf(v, dpp_mov<0x128>(v));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
+}
+
 // Shared-memory carve-up of one block's state (floats).  uc = MLP hidden
 // columns per chunk: the whole hidden width when it fits in lds_max bytes,
 // else the largest halving of it (a multiple of 64) that does.
@@ -126,13 +152,13 @@ __device__ void layernorm_rows(const float* in, float* out, int M, int d, int ld
     const float* r = in + m * ld;
     float s = 0.f;
     for (int e = lane; e < d; e += 64) s += r[e];
-    const float mean = wave_sum(s) / d;
+    const float mean = lanes_sum(s) / d;
     float v = 0.f;
     for (int e = lane; e < d; e += 64) {
       const float t = r[e] - mean;
       v += t * t;
     }
-    const float rstd = rsqrtf(wave_sum(v) / d + 1e-5f);
+    const float rstd = rsqrtf(lanes_sum(v) / d + 1e-5f);
     for (int e = lane; e < d; e += 64) out[m * ld + e] = (r[e] - mean) * rstd * g[e] + b[e];
   }
 }
@@ -140,8 +166,10 @@ __device__ void layernorm_rows(const float* in, float* out, int M, int d, int ld
 // Causal attention of the block rows over the cache, one wave per (sample,
 // head, group of RG rows) at a time: for KT keys per pass, lane j scores key j0 + j
 // against each row (its K row in registers, the rows' q from LDS), the online
-// softmax per row keeps (max, sum) in registers of every lane, then lane e
-// adds sum_j p_rj V^T[e][j0 + j] for each row (its V^T chunk in registers).
+// softmax per row keeps (max, sum) in registers of every lane, then lane l
+// adds sum_j p_rj V^T[e][j] over its share of the pass's keys for dimension
+// e = l % d_h (its V^T chunk in registers; with d_h 32 the two halves of the
+// wave take the two halves of the keys and are added at the end).
 // Keys past a row's position are masked; cache rows past the last key are
 // never multiplied (their p is 0 and their V is replaced by 0).
 template <int D, int DH>
@@ -149,7 +177,12 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
                                const float* kc, const float* vt, int s, int R) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.N, H = a.H;
-  const float scale = 1.0f / sqrtf((float)DH);
+  // scores in base-2 units: p = 2^(s log2(e) / sqrt(dh) - m)
+  const float scale = 1.4426950408889634f / sqrtf((float)DH);
+  // P V: lane l takes dimension l % DH over key part l / DH of each 64-key
+  // pass (NP parts of KP keys); the parts are added at the end
+  constexpr int NP = 64 / DH, KP = KT / NP;
+  const int ve = lane % DH, vpart = lane / DH;
   float* pw = ps + wave * RG * KT;
   const int ngrp = (R + RG - 1) / RG;
   for (int item = wave; item < N * H * ngrp; item += LT / 64) {
@@ -175,17 +208,19 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
 #pragma unroll
         for (int e = 0; e < DH / 4; ++e)
           kreg[e] = kv ? *(const float4*)(kr + (size_t)j * DH + 4 * e) : float4{0.f, 0.f, 0.f, 0.f};
-        // this lane's V^T chunk (dimension e = lane), zero past the last key
-        float vv[KT];
-        if (lane < DH) {
-          const float* vp = vr + (size_t)lane * a.Lcap + j0;
+        // this lane's V^T chunk (dimension ve, keys of part vpart), zero past
+        // the last key
+        float vv[KP];
+        {
+          const int k0 = j0 + vpart * KP;
+          const float* vp = vr + (size_t)ve * a.Lcap + k0;
 #pragma unroll
-          for (int jj = 0; jj < KT; jj += 4) {
+          for (int jj = 0; jj < KP; jj += 4) {
             const float4 v4 = *(const float4*)(vp + jj);
-            vv[jj] = j0 + jj < nkmax ? v4.x : 0.f;
-            vv[jj + 1] = j0 + jj + 1 < nkmax ? v4.y : 0.f;
-            vv[jj + 2] = j0 + jj + 2 < nkmax ? v4.z : 0.f;
-            vv[jj + 3] = j0 + jj + 3 < nkmax ? v4.w : 0.f;
+            vv[jj] = k0 + jj < nkmax ? v4.x : 0.f;
+            vv[jj + 1] = k0 + jj + 1 < nkmax ? v4.y : 0.f;
+            vv[jj + 2] = k0 + jj + 2 < nkmax ? v4.z : 0.f;
+            vv[jj + 3] = k0 + jj + 3 < nkmax ? v4.w : 0.f;
           }
         }
 #pragma unroll
@@ -202,10 +237,10 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
             sv = fmaf(q4.w, kreg[e].w, sv);
           }
           sv = (kv && j <= a.P + s + t0 + r) ? sv * scale : -INFINITY;
-          const float mn = fmaxf(om[r], wave_max(sv));
-          const float al = expf(om[r] - mn);
-          const float pv = expf(sv - mn);
-          ol[r] = ol[r] * al + wave_sum(pv);
+          const float mn = fmaxf(om[r], lanes_max(sv));
+          const float al = __builtin_amdgcn_exp2f(om[r] - mn);
+          const float pv = __builtin_amdgcn_exp2f(sv - mn);
+          ol[r] = ol[r] * al + lanes_sum(pv);
           om[r] = mn;
           oacc[r] *= al;
           pw[r * KT + lane] = pv;
@@ -214,23 +249,31 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
         // accesses stay in order; the barrier keeps the compiler from
         // reordering them)
         __builtin_amdgcn_wave_barrier();
-        if (lane < DH) {
 #pragma unroll
-          for (int r = 0; r < RG; ++r) {
-            if (r >= rows) continue;
-            float acc = oacc[r];
+        for (int r = 0; r < RG; ++r) {
+          if (r >= rows) continue;
+          float acc = oacc[r];
 #pragma unroll
-            for (int jj = 0; jj < KT; jj += 4) {
-              const float4 p4 = *(const float4*)(pw + r * KT + jj);
-              acc = fmaf(p4.x, vv[jj], acc);
-              acc = fmaf(p4.y, vv[jj + 1], acc);
-              acc = fmaf(p4.z, vv[jj + 2], acc);
-              acc = fmaf(p4.w, vv[jj + 3], acc);
-            }
-            oacc[r] = acc;
+          for (int jj = 0; jj < KP; jj += 4) {
+            const float4 p4 = *(const float4*)(pw + r * KT + vpart * KP + jj);
+            acc = fmaf(p4.x, vv[jj], acc);
+            acc = fmaf(p4.y, vv[jj + 1], acc);
+            acc = fmaf(p4.z, vv[jj + 2], acc);
+            acc = fmaf(p4.w, vv[jj + 3], acc);
           }
+          oacc[r] = acc;
         }
         __builtin_amdgcn_wave_barrier();
+      }
+      if constexpr (NP == 2) {
+        // the two key parts, lanes l and l + 32: low part first in both
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(oacc[r]),
+                                                           __float_as_uint(oacc[r]), false, false);
+          const unsigned lo = sw[0], hi = sw[1];
+          oacc[r] = __uint_as_float(lo) + __uint_as_float(hi);
+        }
       }
       if (lane < DH) {
 #pragma unroll
@@ -350,8 +393,8 @@ __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int 
       s0 += df * df;
       s1 += xn * xn;
     }
-    s0 = wave_sum(s0);
-    s1 = wave_sum(s1);
+    s0 = lanes_sum(s0);
+    s1 = lanes_sum(s1);
     if (lane == 0) {
       red[(wave * N + n) * 2] = s0;
       red[(wave * N + n) * 2 + 1] = s1;
