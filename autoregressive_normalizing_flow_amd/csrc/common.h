@@ -18,16 +18,34 @@ template <class T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 
+// Reductions over the 64 lanes of a wave, the result in every lane: within
+// each row of 16 lanes by DPP (quad permutes, then rotations by 4 and 8),
+// then the four row values read from lanes 0, 16, 32 and 48 and combined in
+// that order (a fixed order, and no LDS round trips as a permute-based
+// butterfly takes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, AF_WAVE);
-  return v;
+  v += dpp_mov<0xB1>(v);    // quad_perm 1,0,3,2
+  v += dpp_mov<0x4E>(v);    // quad_perm 2,3,0,1
+  v += dpp_mov<0x124>(v);   // row_ror 4
+  v += dpp_mov<0x128>(v);   // row_ror 8
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, AF_WAVE));
-  return v;
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x124>(v));
+  v = fmaxf(v, dpp_mov<0x128>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 // GELU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erfc from Abramowitz &

@@ -36,32 +36,6 @@ constexpr int NW = LT / 64;   // waves
 constexpr int RG = 4;     // attention rows per wave pass
 constexpr int KT = 64;    // attention keys per wave pass (one per lane)
 
-// Reductions over the 64 lanes of a wave, the result in every lane: within
-// each row of 16 lanes by DPP (quad permutes, then rotations by 4 and 8),
-// then the four row values read from lanes 0, 16, 32 and 48 and combined in
-// that order (a fixed order; no LDS round trips).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_lane(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ float lanes_sum(float v) {
-  v += dpp_mov<0xB1>(v);    // quad_perm 1,0,3,2
-  v += dpp_mov<0x4E>(v);    // quad_perm 2,3,0,1
-  v += dpp_mov<0x124>(v);   // row_ror 4
-  v += dpp_mov<0x128>(v);   // row_ror 8
-  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
-}
-__device__ __forceinline__ float lanes_max(float v) {
-  v = fmaxf(v, dpp_mov<0xB1>(v));
-  v = fmaxf(v, dpp_mov<0x4E>(v));
-  v = fmaxf(v, dpp_mov<0x124>(v));
-  v = fmaxf(v, dpp_mov<0x128>(v));
-  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
-}
-
 // Shared-memory carve-up of one block's state (floats).  uc = MLP hidden
 // columns per chunk: the whole hidden width when it fits in lds_max bytes,
 // else the largest halving of it (a multiple of 64) that does.
@@ -152,13 +126,13 @@ __device__ void layernorm_rows(const float* in, float* out, int M, int d, int ld
     const float* r = in + m * ld;
     float s = 0.f;
     for (int e = lane; e < d; e += 64) s += r[e];
-    const float mean = lanes_sum(s) / d;
+    const float mean = wave_sum(s) / d;
     float v = 0.f;
     for (int e = lane; e < d; e += 64) {
       const float t = r[e] - mean;
       v += t * t;
     }
-    const float rstd = rsqrtf(lanes_sum(v) / d + 1e-5f);
+    const float rstd = rsqrtf(wave_sum(v) / d + 1e-5f);
     for (int e = lane; e < d; e += 64) out[m * ld + e] = (r[e] - mean) * rstd * g[e] + b[e];
   }
 }
@@ -237,10 +211,10 @@ __device__ void loop_attention(const LoopArgs& a, const float* q, float* o, floa
             sv = fmaf(q4.w, kreg[e].w, sv);
           }
           sv = (kv && j <= a.P + s + t0 + r) ? sv * scale : -INFINITY;
-          const float mn = fmaxf(om[r], lanes_max(sv));
+          const float mn = fmaxf(om[r], wave_max(sv));
           const float al = __builtin_amdgcn_exp2f(om[r] - mn);
           const float pv = __builtin_amdgcn_exp2f(sv - mn);
-          ol[r] = ol[r] * al + lanes_sum(pv);
+          ol[r] = ol[r] * al + wave_sum(pv);
           om[r] = mn;
           oacc[r] *= al;
           pw[r * KT + lane] = pv;
@@ -393,8 +367,8 @@ __device__ void loop_affine(const LoopArgs& a, float* sm, const LoopLds& L, int 
       s0 += df * df;
       s1 += xn * xn;
     }
-    s0 = lanes_sum(s0);
-    s1 = lanes_sum(s1);
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
     if (lane == 0) {
       red[(wave * N + n) * 2] = s0;
       red[(wave * N + n) * 2 + 1] = s1;
