@@ -1391,11 +1391,16 @@ static int att_units(int R, int pos_base, int KC, int n_qt) {
 // cost of UNIT_COST tiles per unit: its prologue, output or partial store and
 // merge share), where rounds = ceil(units / slots) and slots = 256 CUs x the
 // blocks one CU holds, plus ATT_MERGE_COST tiles per chunk of the longest
-// query tile (its merge reads them one after another); at most max(1024, N H query tiles) units (the partial
-// slots of the workspace).  Candidates are the chunk lengths that cut the
-// longest key range into c equal parts; results are memoised per shape.
+// query tile (each chunk's partial store, ticket and share of the merge); at
+// most max(1024, N H query tiles) units (the partial slots of the workspace).
+// Candidates are the chunk lengths that cut the longest key range into c
+// equal parts; results are memoised per shape.  The merge cost was fitted to
+// a sweep of c at every frame of the 21-frame video (1560 queries, 16 heads
+// of 64, caches evicted between launches): with 16 the model picks the
+// fastest c at all 20 frames (2 chunks at frames 1 to 3, 3 from frame 4 on;
+// with 1 it took 4 at frames 1 and 2, 12% and 8% slower there).
 constexpr int ATT_UNIT_COST = 3;
-constexpr int ATT_MERGE_COST = 1;
+constexpr int ATT_MERGE_COST = 16;
 static int chunk_for_slots(int N, int R, int H, int pos_base, int slots) {
   struct Entry { int N, R, H, pos_base, slots, kc; };
   thread_local Entry memo[64];

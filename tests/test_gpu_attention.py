@@ -2,7 +2,8 @@
 the kernel the Jacobi path runs) against the oracle's exact causal softmax
 attention, at shapes that take each kernel the library routes to: the DMA
 kernel at d_h 64 (with a cached prefix, with none but 64 sample-head pairs,
-with several key chunks merged in the kernel) and at d_h 128, the 16 x 16
+with several key chunks merged in the kernel) and at d_h 128 (one chunk, and
+several merged), the 16 x 16
 kernel (no prefix, few heads) and the d_h 32 kernel; ragged query and key
 tails everywhere.  Cache rows past the last query's position hold NaN: the
 kernels must not let them into the result.
@@ -81,6 +82,7 @@ def bf16_dev(a):
     (1, 4, 64, 200, 0),        # no prefix, few heads: 16 x 16 kernel
     (1, 8, 32, 200, 700),      # d_h 32
     (2, 4, 128, 150, 600),     # d_h 128
+    (1, 4, 128, 200, 8000),    # d_h 128, key chunks merged in the kernel
 ])
 @pytest.mark.parametrize("extreme", [False, True])
 def test_attention_layer(B, N, H, dh, R, P, extreme):
