@@ -582,6 +582,23 @@ def quick_config(name, torch, binding, synth, steps, warmup):
     dt = (time.perf_counter() - t0) / steps
     out = {"tokens_per_s": round(r.tokens_per_step / dt, 1), "ms_per_step": round(dt * 1e3, 3),
            "iters_per_block": r.iters.tolist(), "tokens": r.tokens_per_step}
+    if r.w.prefix:
+        # the prefix's encoding into the KV cache, outside the metric: one
+        # af_prefill of the observed tokens (median of 3 after a warm-up)
+        N, C = r.w.batch, r.cfg.C
+        xp = torch.from_numpy(np.ascontiguousarray(
+            synth.normal((N, r.w.prefix, C), 2), np.float32)).cuda()
+        times = []
+        for i in range(4):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            r.plan.prefill(xp, rows=r.rows)
+            torch.cuda.synchronize()
+            if i:
+                times.append(time.perf_counter() - t0)
+        times.sort()
+        out["prefill_ms"] = round(times[1] * 1e3, 3)
+        out["prefill_tokens"] = N * r.w.prefix
     del r
     torch.cuda.empty_cache()
     return out
