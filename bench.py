@@ -599,6 +599,18 @@ def quick_config(name, torch, binding, synth, steps, warmup):
         times.sort()
         out["prefill_ms"] = round(times[1] * 1e3, 3)
         out["prefill_tokens"] = N * r.w.prefix
+        # the GEMMs at the prefill's shape (N x prefix rows), by event timing
+        gem = {}
+        for cls in ("gemm_qkv", "gemm_mlp1", "gemm_mlp2"):
+            r.plan.profile_enable(cls)
+            r.plan.prefill(xp, rows=r.rows)
+            n, ms, work = r.plan.profile_read_work()
+            r.plan.profile_disable()
+            if n and ms > 0:
+                tf = work / (ms * 1e-3) / 1e12
+                gem[cls] = {"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "avg_ms": round(ms / n, 4)}
+        out["prefill_gemms"] = gem
     del r
     torch.cuda.empty_cache()
     return out
