@@ -1095,7 +1095,11 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(stg + kfrag(kb, ks));
-    // the two 32-key halves' chains interleaved
+    // the two 32-key halves' chains interleaved, at raised wave priority (one
+    // below the P V MFMAs': a wave that reaches either MFMA phase issues it
+    // ahead of the other waves' softmax, which then fills the matrix pipe's
+    // busy cycles)
+    __builtin_amdgcn_s_setprio(1);
     s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][0], qf[0], negm, 0, 0, 0);
     s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][0], qf[0], negm, 0, 0, 0);
 #pragma unroll
@@ -1103,6 +1107,7 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // softmax of tile kt's scores and its row-sum and P V MFMAs (V from its
   // buffer)
@@ -1184,7 +1189,7 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
     // the row has mass once a tile put p >= 2^-32 into it (a moved reference
     // makes the tile's largest p 1)
     row_mass = row_mass || move || pm >= F32_2M32;
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
