@@ -1114,6 +1114,15 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
   auto finish = [&](f32x16 (&s)[2], int kt) {
     const char* stg = &smem[kt % STAGES][0];
     const int key0 = (t_begin + kt) * ATT_KT;
+    // the Vt fragments of the first two P V steps read before the softmax, so
+    // that the P V phase does not start on an LDS wait (at d_h 64, where the
+    // registers are there; at 128 they would spill)
+    constexpr int NPRE = DH == 64 ? 2 : 0;
+    bf16x8 vpre[NPRE > 0 ? NPRE : 1][DB];
+#pragma unroll
+    for (int g = 0; g < NPRE; ++g)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vpre[g][db] = *(const bf16x8*)(stg + vfrag(db, g));
     const bool need_mask = (key0 + ATT_KT - 1 > wave_qmin) || (key0 + ATT_KT > k_end);
     auto mask = [&]() {
       if (need_mask) {
@@ -1195,7 +1204,8 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)(stg + vfrag(db, g)), pf[g], acc_o[db], 0, 0, 0);
+            g < NPRE ? vpre[g < NPRE ? g : 0][db] : *(const bf16x8*)(stg + vfrag(db, g)), pf[g],
+            acc_o[db], 0, 0, 0);
       // row sums of the same bf16 p: 2-term dot products with (1, 1)
       const u32x4 pw = __builtin_bit_cast(u32x4, pf[g]);
 #pragma unroll
