@@ -995,11 +995,18 @@ attn32_kernel(AttnArgs a) {
 // key range and writes the normalised output; otherwise it writes its partial
 // to slot `slot`, and the last of the tile's n_chunks units to finish (slots
 // first_slot .. first_slot + n_chunks - 1, in key order) merges them.
-template <int DH>
+// G = 2: a block of 8 waves, two key groups of 4 waves with a ring each; group
+// 0 takes the first half of the unit's key tiles and group 1 the rest, both
+// over the same 128 queries, and group 1 hands its row state (reference, row
+// sum, O) to group 0 through LDS at the end, which adds it in a fixed order:
+// the unit's chain of dependent tiles is half as long, for launches with few
+// long units.
+template <int DH, int G>
 __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, const int qt,
-                                             const int k_begin, const int k_end,
+                                             const int k_begin, const int k_end_unit,
                                              const int slot, const int first_slot,
                                              const int n_chunks) {
+  static_assert(G == 1 || G == 2, "key groups");
   static_assert(DH == 64 || DH == 128, "head width");
   constexpr int KS = DH / 16, DB = DH / 32;
   constexpr int STAGES = DH <= 64 ? 3 : 2;
@@ -1017,17 +1024,33 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
   // they are, with Vt in plain key order.
   auto krow = [](int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); };
   typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES][2 * KBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_all[G][STAGES][2 * KBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (the DMA takes its LDS address in a scalar register)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = G == 1 ? 0 : wave_all >> 2;   // key group
+  const int wave = wave_all & 3;                 // wave within the group
+  char (&smem)[STAGES][2 * KBYTES] = smem_all[grp];
   const int j = lane & 31, hh = lane >> 5;
   const int n = nh / a.H, head = nh - n * a.H;
   const int R = a.R, d = a.d, Lcap = a.Lcap, pos_base = a.pos_base;
   const int q_lo = qt * ATT_QT;
-  const int t_begin = k_begin / ATT_KT;
-  const int n_tiles = (k_end - k_begin + ATT_KT - 1) / ATT_KT;
+  // the unit's key tiles, the first `half` of them to group 0; every group
+  // runs n_iter loop trips (the barriers are the block's)
+  const int t_unit = (k_end_unit - k_begin + ATT_KT - 1) / ATT_KT;
+  const int half = G == 1 ? t_unit : (t_unit + 1) / 2;
+  const int n_iter = half;
+  const int t_begin = k_begin / ATT_KT + (grp == 0 ? 0 : half);
+  const int n_tiles = grp == 0 ? half : t_unit - half;
+  const int k_end = grp == 0 ? min(k_end_unit, k_begin + half * ATT_KT) : k_end_unit;
+  // tile kt of group g ends past its key range (its Vt tail is zeroed)
+  auto tail_of = [&](int g, int kt) {
+    const int tb = k_begin / ATT_KT + (g == 0 ? 0 : half);
+    const int nt = g == 0 ? half : t_unit - half;
+    const int ke = g == 0 ? min(k_end_unit, k_begin + half * ATT_KT) : k_end_unit;
+    return kt < nt && (tb + kt) * ATT_KT + ATT_KT > ke;
+  };
   const size_t hb = (size_t)n * a.H + head;
   const bf16* kbase = a.kc + hb * Lcap * DH;
   const bf16* vbase = a.vt + hb * DH * Lcap;
@@ -1225,7 +1248,7 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
   auto zero_tail = [&](int kt) {
     const int kvalid = k_end - (t_begin + kt) * ATT_KT;
     char* stg = &smem[kt % STAGES][0];
-    for (int idx = tid; idx < DH * ATT_KT; idx += 256) {
+    for (int idx = tid & 255; idx < DH * ATT_KT; idx += 256) {   // the group's 256 threads
       const int r = idx / ATT_KT, kk = idx - r * ATT_KT;
       if (kk >= kvalid) {
         const int c = kk >> 3, e = kk & 7;
@@ -1266,14 +1289,15 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   f32x16 s[2];
 #pragma clang loop unroll(disable)
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  for (int kt = 0; kt < n_iter; ++kt) {
     const bool more = kt + STAGES - 1 < n_tiles;
     if (more) issue(kt + STAGES - 1);
-    if ((t_begin + kt) * ATT_KT + ATT_KT > k_end) {
-      zero_tail(kt);
+    const bool tail0 = tail_of(0, kt), tail1 = G == 2 && tail_of(1, kt);
+    if (tail0 || tail1) {   // block-uniform
+      if (grp == 0 ? tail0 : tail1) zero_tail(kt);
       __syncthreads();
     }
-    if (active) {
+    if (active && kt < n_tiles) {
       scores(s, kt);
       finish(s, kt);
     }
@@ -1289,8 +1313,38 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
                                                      __float_as_uint(l_row), false, false);
     l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
+  if constexpr (G == 2) {
+    // group 1's (reference, row sum, O) into the free rings, as arrays of 256
+    // lanes; group 0 adds them to its own, group 0's terms first.  A group
+    // with no key of the row (l = 0) contributes nothing.
+    float* xs = (float*)&smem_all[0][0][0];
+    const int sl = wave * 64 + lane;
+    if (grp == 1) {
+      xs[sl] = l_row > 0.f ? m_run : -1e30f;
+      xs[256 + sl] = l_row;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xs[(2 + 16 * db + e) * 256 + sl] = acc_o[db][e];
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m0 = l_row > 0.f ? m_run : -1e30f, m1 = xs[sl], l1 = xs[256 + sl];
+      const float mg = fmaxf(m0, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m0 - mg), a1 = __builtin_amdgcn_exp2f(m1 - mg);
+      l_row = l_row * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc_o[db][e] = acc_o[db][e] * a0 + xs[(2 + 16 * db + e) * 256 + sl] * a1;
+      m_run = mg;
+    }
+  }
+  // group 0 holds the block's result
+  const bool out_wave = active && grp == 0;
   if (n_chunks == 1) {
-    if (active && t_q < R) {
+    if (out_wave && t_q < R) {
       const float inv = 1.0f / l_row;
       bf16* orow = a.out + ((size_t)n * R + t_q) * d + head * DH + 4 * hh;
 #pragma unroll
@@ -1308,7 +1362,7 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
 
   constexpr int SLOT = ATT_QT * (DH + 2);
   const int tq = wave * 32 + j;
-  if (active) {
+  if (out_wave) {
     const __amdgpu_buffer_rsrc_t rs = slot_rsrc_dh<DH>(a.part + (size_t)slot * SLOT);
     const float l = l_row;
 #pragma unroll
@@ -1338,11 +1392,11 @@ __device__ __forceinline__ void attn_dma_unit(const AttnArgs& a, const int nh, c
     s_last = last;
   }
   __syncthreads();
-  if (!s_last || !active) return;
+  if (!s_last || !out_wave) return;
   attn32_merge<DH>(a, first_slot, n_chunks, tq, t_q, n, head, hh);
 }
 
-template <int DH>
+template <int DH, int G>
 __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   // unit -> (sample, head, query tile, chunk).  Block ids go round-robin over
   // the 8 XCDs; when N*H is a multiple of 8, (sample, head) pairs are dealt so
@@ -1373,7 +1427,7 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
   for (int q = 0; q < qt; ++q) before += att_chunks(q, a.R, a.pos_base, a.KC);
   const int nk = a.pos_base + min(a.R, (qt + 1) * ATT_QT);
   const int slot0 = nh * a.U_nh + before;
-  attn_dma_unit<DH>(a, nh, qt, j * a.KC, min(nk, (j + 1) * a.KC), slot0 + j, slot0,
+  attn_dma_unit<DH, G>(a, nh, qt, j * a.KC, min(nk, (j + 1) * a.KC), slot0 + j, slot0,
                    att_chunks(qt, a.R, a.pos_base, a.KC));
 }
 
@@ -1381,7 +1435,13 @@ __device__ __forceinline__ void attn_dma_body(const AttnArgs& a) {
 template <int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 3 : 2))) void
 attn_dma_kernel(AttnArgs a) {
-  attn_dma_body<DH>(a);
+  attn_dma_body<DH, 1>(a);
+}
+
+// Two key groups per block (8 waves): one block per CU (two rings).
+template <int DH>
+__global__ __launch_bounds__(512) void attn_dma2_kernel(AttnArgs a) {
+  attn_dma_body<DH, 2>(a);
 }
 
 
@@ -1455,15 +1515,23 @@ static int chunk_for_slots(int N, int R, int H, int pos_base, int slots) {
 static int att_blocks_per_cu(int dh) { return dh == 128 ? 2 : 3; }
 
 // Kernel of a bf16 launch.  The split (higher-precision forward) mode runs
-// the 16 x 16 kernel; d_h = 32 the register-staged 32 x 32 kernel; a frame
-// with no cached prefix and fewer than 64 (sample, head) pairs the 16 x 16
-// kernel, measured faster there (26.7 against 35 us at 1560 tokens and 16
-// heads, where every unit is a few tiles of the causal triangle); everything
-// else the DMA-fed 32 x 32 kernel.
-enum AttKind { ATT_SPLIT16, ATT_SMALL16, ATT_REG32, ATT_DMA32 };
-static AttKind att_kind(int N, int H, int dh, bool split, int pos_base) {
+// the 16 x 16 kernel; d_h = 32 the register-staged 32 x 32 kernel.  At d_h 64
+// a launch of at most 256 query tiles over at most 100 key tiles (the first
+// frames of a 1560-token video, or a frame with no cached prefix) runs the
+// two-key-group DMA kernel over whole key ranges, one unit per CU with the
+// chain of each unit halved (at 1560 tokens and 16 heads: 24.2 against 27.4
+// us with no prefix, 41.1 against 45.9 after one cached frame; from 5 cached
+// frames on it is slower); a frame with no cached prefix and fewer than 64
+// (sample, head) pairs otherwise the 16 x 16 kernel (26.7 against 35 us for
+// the DMA kernel at 1560 tokens and 16 heads, where every unit is a few
+// tiles of the causal triangle); everything else the DMA-fed 32 x 32 kernel.
+enum AttKind { ATT_SPLIT16, ATT_SMALL16, ATT_REG32, ATT_DMA32, ATT_DMA2 };
+static AttKind att_kind(int N, int R, int H, int dh, bool split, int pos_base) {
   if (split) return ATT_SPLIT16;
   if (dh == 32) return ATT_REG32;
+  const long n_qt = (R + ATT_QT - 1) / ATT_QT;
+  if (dh == 64 && (long)N * H * n_qt <= 256 && (long)pos_base + R <= 100 * ATT_KT)
+    return ATT_DMA2;
   if (dh == 64 && pos_base == 0 && N * H < 64) return ATT_SMALL16;
   return ATT_DMA32;
 }
@@ -1471,7 +1539,8 @@ static AttKind att_kind(int N, int H, int dh, bool split, int pos_base) {
 int attention_chunk(int N, int R, int H, int dh, bool split, int pos_base) {
   const int n_qt = (R + ATT_QT - 1) / ATT_QT;
   const int nk_max = pos_base + R;
-  const AttKind kind = att_kind(N, H, dh, split, pos_base);
+  const AttKind kind = att_kind(N, R, H, dh, split, pos_base);
+  if (kind == ATT_DMA2) return (nk_max + ATT_KT - 1) / ATT_KT * ATT_KT;   // whole ranges
   if (kind == ATT_REG32 || kind == ATT_DMA32)
     return chunk_for_slots(N, R, H, pos_base, 256 * att_blocks_per_cu(dh));
   if (kind == ATT_SMALL16)
@@ -1539,11 +1608,16 @@ static void attn_launch(const AttnArgs& a, dim3 grid, AttKind kind, hipStream_t 
   } else if constexpr (DH == 32) {
     hipLaunchKernelGGL((attn32_kernel<32>), grid, dim3(256), 0, st, a);
   } else {
-    if constexpr (DH == 64)
+    if constexpr (DH == 64) {
       if (kind == ATT_SMALL16) {
         hipLaunchKernelGGL((attn_bf16_kernel_o2<64, false>), grid, dim3(256), 0, st, a);
         return;
       }
+      if (kind == ATT_DMA2) {
+        hipLaunchKernelGGL((attn_dma2_kernel<64>), grid, dim3(512), 0, st, a);
+        return;
+      }
+    }
     hipLaunchKernelGGL((attn_dma_kernel<DH>), grid, dim3(256), 0, st, a);
   }
 }
@@ -1565,7 +1639,7 @@ hipError_t launch_attention(bool bf, const void* q, const void* kc,
                R, H, d, Lcap, pos_base, KC, U_nh, n_qt, (N * H) % 8 == 0 ? 1 : 0};
     if (U_nh > n_qt && (!part || !tickets)) return hipErrorInvalidValue;
     const dim3 grid(N * H * U_nh);
-    const AttKind kind = att_kind(N, H, dh, split != nullptr, pos_base);
+    const AttKind kind = att_kind(N, R, H, dh, split != nullptr, pos_base);
     switch (dh * 2 + (split ? 1 : 0)) {
       case 128: attn_launch<64, false>(a, grid, kind, st); break;
       case 129: attn_launch<64, true>(a, grid, kind, st); break;

@@ -1,11 +1,13 @@
 """GPU parity of one layer's bf16 attention over a KV cache (afk_attention,
 the kernel the Jacobi path runs) against the oracle's exact causal softmax
 attention, at shapes that take each kernel the library routes to: the DMA
-kernel at d_h 64 (with a cached prefix, with none but 64 sample-head pairs,
-with several key chunks merged in the kernel) and at d_h 128 (one chunk, and
-several merged), the 16 x 16
-kernel (no prefix, few heads) and the d_h 32 kernel; ragged query and key
-tails everywhere.  Cache rows past the last query's position hold NaN: the
+kernel at d_h 64 (past 256 query tiles with a short prefix, with several key
+chunks merged in the kernel) and at d_h 128 (one chunk, and several merged),
+its two-key-group form at d_h 64 (at most 256 query tiles over at most 100
+key tiles: with and without a cached prefix, one key tile per unit so that
+the second group has none, the first frames of the 1560-token video), the
+16 x 16 kernel (no prefix, under 64 sample-head pairs, past 256 query tiles)
+and the d_h 32 kernel; ragged query and key tails everywhere.  Cache rows past the last query's position hold NaN: the
 kernels must not let them into the result.
 
 "Extreme" inputs put the first 64 keys some 300 (log2 units) above the query
@@ -76,10 +78,13 @@ def bf16_dev(a):
 
 
 @pytest.mark.parametrize("N,H,dh,R,P", [
-    (1, 16, 64, 300, 2000),    # prefix: DMA kernel, ragged tails
-    (8, 8, 64, 200, 0),        # no prefix, 64 sample-head pairs: DMA kernel
-    (1, 16, 64, 130, 14000),   # long prefix: several key chunks per query tile
-    (1, 4, 64, 200, 0),        # no prefix, few heads: 16 x 16 kernel
+    (1, 16, 64, 300, 2000),    # prefix, ragged tails: two key groups
+    (8, 8, 64, 200, 0),        # no prefix, 64 sample-head pairs: two key groups
+    (1, 4, 64, 200, 0),        # no prefix, few heads: two key groups
+    (3, 5, 64, 64, 0),         # one key tile per unit: the second group idle
+    (1, 16, 64, 130, 14000),   # long prefix: DMA kernel, several key chunks per query tile
+    (2, 16, 64, 1100, 2000),   # 288 query tiles, short prefix: DMA kernel
+    (1, 32, 64, 1200, 0),      # no prefix, 32 pairs, 320 query tiles: 16 x 16 kernel
     (1, 8, 32, 200, 700),      # d_h 32
     (2, 4, 128, 150, 600),     # d_h 128
     (1, 4, 128, 200, 8000),    # d_h 128, key chunks merged in the kernel
@@ -108,14 +113,15 @@ def oracle_rows(qs, k, v, P, rows):
     return o.transpose(0, 2, 1, 3).reshape(N, len(rows), H * dh)
 
 
-@pytest.mark.parametrize("R,P", [(1560, 12480), (1000, 31000)])
+@pytest.mark.parametrize("R,P", [(1560, 0), (1560, 4680), (1560, 12480), (1000, 31000)])
 @pytest.mark.parametrize("extreme", [False, True])
 def test_attention_long_prefix_sampled(B, R, P, extreme):
-    """Long cached prefixes at 16 heads of 64 (the 9th frame of the 21-frame
-    video; 1000 queries after 31 000 keys, a ragged last query tile): several
-    key chunks per query tile, dispatched chunk-major and merged in key order.
-    Sampled query rows (both ends of every 128-row query tile and every 11th
-    row) against the oracle."""
+    """Frames of the 21-frame video at 16 heads of 64: the first and the 4th
+    (two key groups over whole key ranges, the 4th at their 98-tile limit),
+    the 9th and 1000 queries after 31 000 keys (a ragged last query tile;
+    several key chunks per query tile, dispatched chunk-major and merged in
+    key order).  Sampled query rows (both ends of every 128-row query tile and
+    every 11th row) against the oracle."""
     N, H, dh = 1, 16, 64
     say("attention long prefix", R, P, "extreme" if extreme else "normal")
     qs, k, v, kc, vt, Lcap = inputs(N, H, dh, R, P, extreme, seed=R + P + 7)
