@@ -1186,8 +1186,9 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         // While the host waits for the residual, the device runs the next
         // update's first kernels (shift + embed, first LayerNorm, layer 0's
         // QKV and attention).  They write only scratch and this block's
-        // layer-0 K/V rows, which the next update would write identically and
-        // which the refresh after an early stop recomputes, so a stop leaves
+        // layer-0 K/V rows, which the next update would write identically;
+        // after an early stop they are what the block's cache refresh needs
+        // for layer 0, and the refresh continues from them, so a stop leaves
         // the result unchanged.  (Graph replay keeps whole updates.)
         if (split) {
           if (af_status e = split_part(PASS_PREFIX)) return e;
@@ -1230,6 +1231,12 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         } else {
           Pass pr = ps;
           pr.kv_only = true;
+          // After a stop the next update's prefix has already run layer 0 on
+          // the final tokens (shift + embed into h, first LayerNorm, layer 0's
+          // K/V rows, its attention output): the refresh continues from there
+          // with the same launches it would otherwise repeat on the same
+          // inputs.  (A split prefix leaves its halves in two scratch areas.)
+          if (prefixed && !split) pr.part = PASS_REST;
           if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) return e;
         }
       }

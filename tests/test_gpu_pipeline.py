@@ -66,22 +66,34 @@ def test_deep_shallow_forward_and_pipelined_inverse(B, dtype):
     assert torch.equal(xs, xg)
 
 
-@pytest.mark.parametrize("device_loop", [True, False])
-def test_deep_frames_equal_one_video_call(B, device_loop):
+@pytest.mark.parametrize("dtype,device_loop", [("f32", True), ("f32", False),
+                                                ("bf16", False)])
+def test_deep_frames_equal_one_video_call(B, dtype, device_loop):
     """Frame-by-frame deep calls (given init + prefix + refresh) reproduce the
     single af_inverse_jacobi call over the whole sequence with the
     previous-frame warm start, bit for bit, on the device loop (whose refresh
     of a call's last block comes from af_refresh_kv, by the same pass) and on
-    the launch-per-kernel path."""
-    say("deep per-frame vs one call, device loop", device_loop)
-    flow, pd, ps, deep = flows(B, "f32", 16, 64, 2, 1, 16, 4)
+    the launch-per-kernel path, fp32 and bf16.  Inside the one call a frame
+    that stops early has its cache refreshed by continuing from the next
+    update's prefix (layer 0 already run on the final tokens); the per-frame
+    calls refresh by af_refresh_kv from the start: both must write the same
+    K/V, or the later frames would differ."""
+    say("deep per-frame vs one call", dtype, "device loop", device_loop)
+    if dtype == "f32":
+        C, F = 16, 16
+        flow, pd, ps, deep = flows(B, "f32", C, 64, 2, 1, F, 4)
+    else:
+        C, F = 48, 128
+        flow, pd, ps, deep = flows(B, "bf16", C, 256, 4, 2, F, 4, seed=7)
     deep.set_device_loop(device_loop)
-    z = to_dev(synth.normal((1, 64, 16), 3))
-    u_one, it_one = deep.inverse_jacobi(z, 16, 1e-3, init="prev_frame", frame_len=16)
+    z = to_dev(synth.normal((1, 4 * F, C), 3))
+    u_one, it_one = deep.inverse_jacobi(z, F, 1e-3, init="prev_frame", frame_len=F)
     u = torch.empty_like(z)
     its = [flow._deep_frame(z, u, n, 1e-3, 0, torch.cuda.current_stream())[0]
            for n in range(4)]
     torch.cuda.synchronize()
+    print("iters per frame", its)
+    assert all(k < F for k in its[:-1])   # early stops: every frame but the last is refreshed
     assert its == it_one[0].tolist()
     assert torch.equal(u, u_one)
 
