@@ -471,7 +471,7 @@ def summarize_trace(d, top):
 # kernel class of a kernel name in the inverse path (the forward's split-mode
 # kernels, which carry bf16 hi + lo operands, are listed but not classed)
 CLASS_PATTERNS = {
-    "attention": (("attn_dma_kernel", ""), ("attn32_kernel", ""),
+    "attention": (("attn_dma_kernel", ""), ("attn_dma2_kernel", ""), ("attn32_kernel", ""),
                   ("attn_bf16_kernel", "false>")),
     "affine": (("affine_kernel<0", ""),),
 }
