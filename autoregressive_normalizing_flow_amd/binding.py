@@ -104,6 +104,8 @@ def load_library() -> ctypes.CDLL:
     L.af_plan_set_graphs.restype = st
     L.af_plan_set_row_split.argtypes = [_P, i]
     L.af_plan_set_row_split.restype = st
+    L.af_plan_set_overlap_refresh.argtypes = [_P, i]
+    L.af_plan_set_overlap_refresh.restype = st
     L.af_plan_set_device_loop.argtypes = [_P, i]
     L.af_plan_set_device_loop.restype = st
     L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
@@ -340,6 +342,10 @@ class AFPlan:
     def set_row_split(self, enable: bool):
         _check(self.L.af_plan_set_row_split(self.handle, int(bool(enable))),
                "af_plan_set_row_split")
+
+    def set_overlap_refresh(self, enable: bool):
+        _check(self.L.af_plan_set_overlap_refresh(self.handle, int(bool(enable))),
+               "af_plan_set_overlap_refresh")
 
     def set_device_loop(self, enable: bool):
         _check(self.L.af_plan_set_device_loop(self.handle, int(bool(enable))),

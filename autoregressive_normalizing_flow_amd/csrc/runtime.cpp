@@ -125,6 +125,9 @@ struct af_plan {
   long long g_captures = 0, g_replays = 0;
   // row split of a Jacobi update over two streams (see af_inverse_jacobi)
   bool row_split = false;
+  // a block's cache refresh on the second stream beside the next block's
+  // first update (see af_inverse_jacobi; on by default)
+  bool overlap_refresh = true;
   hipStream_t split_stream = nullptr;
   std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
   // residual pairs of the last update of the last inverse call (halves added)
@@ -236,6 +239,27 @@ WsLayout layout_b(const af_plan* p, int N, int rows, const WsLayout& w) {
   return b;
 }
 
+// Scratch of a cache refresh that runs on the second stream beside the next
+// block's updates (bf16 plans): the per-pass buffers for `rows` rows placed
+// after the main layout (the refresh and the row split never run in one
+// call, so they share that space).  The refresh stops after the last layer's
+// K/V, so it never touches the head planes, the affine partials or the
+// counter words; its attention tickets are its own and are cleared with the
+// call's counters.
+bool refresh_overlap_possible(const af_plan* p) { return p->bf && p->cfg.n_layers > 1; }
+
+WsLayout layout_r(const af_plan* p, int N, int rows, const WsLayout& w) {
+  WsLayout r = layout(p, N, rows);
+  const size_t shift = w.total - r.h;
+  size_t* f[] = {&r.h, &r.a, &r.q, &r.att, &r.u, &r.hf, &r.head, &r.partials, &r.res,
+                 &r.counter, &r.tickets, &r.slab, &r.attn_part};
+  for (size_t* x : f) *x += shift;
+  r.total = r.xtmp + shift;
+  r.xtmp = w.xtmp;
+  r.cache_lo = r.a_lo = r.q_lo = r.att_lo = r.u_lo = 0;
+  return r;
+}
+
 // Launch helper with optional per-class event timing (direct launches only:
 // nothing is captured into a graph while a class is profiled).  The bf16
 // projection GEMMs are one kernel per launch call, and their events are taken
@@ -300,7 +324,8 @@ struct Pass {
 };
 constexpr int PASS_ALL = 0, PASS_PREFIX = 1, PASS_REST = 2;
 
-// Cross-stream ordering of a pass that runs beside another one (row split):
+// Cross-stream ordering of a pass that runs beside another one (the halves of
+// a row split; a cache refresh and the next block's first update):
 // events waited for or recorded on the pass's stream around its embed, its
 // QKV GEMMs, its attentions and its affine update (NULL: none).
 struct XSync {
@@ -312,6 +337,7 @@ struct XSync {
   const hipEvent_t* wait_attn = nullptr;   // [n_layers]
   const hipEvent_t* rec_attn = nullptr;    // [n_layers]
   hipEvent_t rec_affine = nullptr;
+  bool half = false;   // a row-split half (fewer split planes in its residual GEMMs)
 };
 
 // One pass of the network over chunk rows [s, s+R) of every sample:
@@ -330,7 +356,8 @@ af_status run_net(af_plan* p, const BlockW& bw, const Pass& ps, char* ws,
   // a row-split half runs beside the other: its residual GEMMs take fewer
   // split planes than the shape alone gets (measured faster: the output
   // projection one, MLP2 two)
-  const int o_planes = xs ? 1 : 8, mlp2_planes = xs ? 2 : 8;
+  const bool half = xs && xs->half;
+  const int o_planes = half ? 1 : 8, mlp2_planes = half ? 2 : 8;
   float* h = (float*)(ws + w.h);
   void* a = ws + w.a;
   void* q = ws + w.q;
@@ -706,9 +733,13 @@ void af_plan_destroy(af_plan* p) {
 size_t af_workspace_bytes(const af_plan* p, int batch, int rows) {
   if (!p || batch < 1 || rows < 1) return 0;
   const WsLayout w = layout(p, batch, rows);
-  // room for the row split's second half when a block of `rows` rows uses it
-  if (split_possible(p, batch, rows)) return layout_b(p, batch, rows, w).total;
-  return w.total;
+  // room for the row split's second half when a block of `rows` rows uses
+  // it, and for the scratch of a cache refresh beside the next block's
+  // updates (the two share the space after the main layout)
+  size_t total = w.total;
+  if (split_possible(p, batch, rows)) total = std::max(total, layout_b(p, batch, rows, w).total);
+  if (refresh_overlap_possible(p)) total = std::max(total, layout_r(p, batch, rows, w).total);
+  return total;
 }
 
 size_t af_cache_bytes(const af_plan* p, int batch) {
@@ -1020,24 +1051,42 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     wb = layout_b(p, N, Bc, w);
     split_ok = ws_bytes >= wb.total;
   }
+  // Cache refresh beside the next block (see af_plan_set_overlap_refresh):
+  // direct launches, one pass per update, room for the refresh's scratch.
+  WsLayout wr{};
+  bool overlap_ok = p->overlap_refresh && refresh_overlap_possible(p) && !p->graphs && !fuse &&
+                    !split_ok && nb > 1;
+  if (overlap_ok) {
+    wr = layout_r(p, N, Bc, w);
+    overlap_ok = ws_bytes >= wr.total;
+  }
   const int nl = p->cfg.n_layers;
-  if (split_ok) {
+  const bool two_streams = split_ok || overlap_ok;
+  if (two_streams) {
     if (!p->split_stream)
       AF_HIP(hipStreamCreateWithFlags(&p->split_stream, hipStreamNonBlocking));
     if (p->split_ev.empty()) {
       p->split_ev.resize(2 * nl + 4);
       for (auto& e : p->split_ev) AF_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     }
-    if (af_status e = ensure_host_res(p, 2 * N)) return e;
+    if (split_ok)
+      if (af_status e = ensure_host_res(p, 2 * N)) return e;
   }
   hipStream_t sb = p->split_stream;
-  const hipEvent_t* ev_qkv = split_ok ? p->split_ev.data() : nullptr;        // A: QKV(l) done
-  const hipEvent_t* ev_att = split_ok ? p->split_ev.data() + nl : nullptr;   // B: attention(l) done
-  hipEvent_t ev_aff = split_ok ? p->split_ev[2 * nl] : nullptr;        // A: affine done
-  hipEvent_t ev_emb = split_ok ? p->split_ev[2 * nl + 1] : nullptr;    // B: embed done
-  hipEvent_t ev_fork = split_ok ? p->split_ev[2 * nl + 2] : nullptr;
-  hipEvent_t ev_join = split_ok ? p->split_ev[2 * nl + 3] : nullptr;
-  bool b_busy = false;   // half B has work enqueued since the last join
+  // (with the refresh beside the next block, ev_qkv[l] marks the refresh's
+  // QKV(l), which the next block's first update waits for before its
+  // attention(l))
+  const hipEvent_t* ev_qkv = two_streams ? p->split_ev.data() : nullptr;        // A: QKV(l) done
+  const hipEvent_t* ev_att = two_streams ? p->split_ev.data() + nl : nullptr;   // B: attention(l) done
+  hipEvent_t ev_aff = two_streams ? p->split_ev[2 * nl] : nullptr;        // A: affine done
+  hipEvent_t ev_emb = two_streams ? p->split_ev[2 * nl + 1] : nullptr;    // B: embed done
+  hipEvent_t ev_fork = two_streams ? p->split_ev[2 * nl + 2] : nullptr;
+  hipEvent_t ev_join = two_streams ? p->split_ev[2 * nl + 3] : nullptr;
+  // layer 0's K/V of a refreshed block come from the prefix on `stream`
+  std::vector<hipEvent_t> ev_refresh_qkv(nl, nullptr);
+  if (overlap_ok)
+    for (int l = 1; l < nl; ++l) ev_refresh_qkv[l] = ev_qkv[l];
+  bool b_busy = false;   // the second stream has work enqueued since the last join
   auto join_b = [&]() -> hipError_t {
     if (!b_busy) return hipSuccess;
     b_busy = false;
@@ -1057,6 +1106,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
   unsigned* seq_dev = (unsigned*)(ws + w.counter) + 2;
   AF_HIP(clear_counters(w, ws, st));
   if (split_ok) AF_HIP(clear_counters(wb, ws, st));
+  if (overlap_ok) AF_HIP(clear_counters(wr, ws, st));
   // host-mapped words behind the residual pairs: the sequence numbers of
   // halves A and B, then the non-finite tags they report
   volatile unsigned* seq_host_words = seq_word(p, false);
@@ -1078,6 +1128,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
     float* xo = (t % 2 == 0) ? x : xtmp;
     const int dir = t & 1;
     int pending = 0;   // rows of the previous block whose refresh is merged here
+    bool refresh_beside = false;   // the previous block's refresh runs on the second stream
     for (int b = 0; b < nb; ++b) {
       const int s = b * B, R = (s + B < L ? s + B : L) - s;
       const int kmax = max_iters <= 0 ? R : (max_iters < R ? max_iters : R);
@@ -1129,6 +1180,7 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
         aab.seq_dev = (unsigned*)(ws + wb.counter) + 2;
         aab.seq_host = seq_word(p, true) + 1;
         aab.bad_host = seq_word(p, true) + 3;
+        xa.half = xb.half = true;
         xa.wait_qkv = ev_att;
         xa.rec_qkv = ev_qkv;
         xa.wait_affine = ev_emb;
@@ -1170,6 +1222,13 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
           pf.R = R + pending;
           pf.hskip = pending;
           if (af_status e = jacobi_update(p, p->blocks[t], pf, aa, ws, w, st)) return e;
+        } else if (k == 1 && refresh_beside) {
+          // the first update beside the previous block's refresh: its
+          // attention(l) reads that block's K/V rows of layer l
+          XSync xw;
+          xw.wait_attn = ev_refresh_qkv.data();
+          if (af_status e = run_net(p, p->blocks[t], ps, ws, w, st, &aa, 0, &xw)) return e;
+          refresh_beside = false;
         } else if (g) {
           AF_HIP(hipGraphLaunch(g->exec, st));
           ++p->g_replays;
@@ -1237,7 +1296,28 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
           // with the same launches it would otherwise repeat on the same
           // inputs.  (A split prefix leaves its halves in two scratch areas.)
           if (prefixed && !split) pr.part = PASS_REST;
-          if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) return e;
+          if (overlap_ok && pr.part == PASS_REST) {
+            // The refresh runs on the second stream, in its own scratch (the
+            // prefix's embed output and layer-0 attention output copied
+            // there), beside the next block's first update, which waits for
+            // its K/V layer by layer.  The same launches on the same inputs:
+            // results are unchanged.
+            AF_HIP(join_b());   // the previous refresh is done with that scratch
+            const size_t M = (size_t)N * R;
+            AF_HIP(hipMemcpyAsync(ws + wr.h, ws + w.h, M * p->cfg.d * 4,
+                                  hipMemcpyDeviceToDevice, st));
+            AF_HIP(hipMemcpyAsync(ws + wr.att, ws + w.att, M * p->cfg.d * p->esz,
+                                  hipMemcpyDeviceToDevice, st));
+            AF_HIP(hipEventRecord(ev_fork, st));
+            AF_HIP(hipStreamWaitEvent(sb, ev_fork, 0));
+            b_busy = true;
+            XSync xr;
+            xr.rec_qkv = ev_qkv;
+            if (af_status e = run_net(p, p->blocks[t], pr, ws, wr, sb, nullptr, 0, &xr)) return e;
+            refresh_beside = true;
+          } else if (af_status e = run_net(p, p->blocks[t], pr, ws, w, st)) {
+            return e;
+          }
         }
       }
     }
@@ -1325,6 +1405,12 @@ af_status af_plan_set_device_loop(af_plan* p, int enable) {
 af_status af_plan_set_row_split(af_plan* p, int enable) {
   if (!p) return fail(AF_ERR_ARG, "NULL argument");
   p->row_split = enable != 0;
+  return AF_OK;
+}
+
+af_status af_plan_set_overlap_refresh(af_plan* p, int enable) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->overlap_refresh = enable != 0;
   return AF_OK;
 }
 

@@ -635,6 +635,10 @@ def main():
     ap.add_argument("--fused-refresh", action="store_true",
                     help="recompute an early-stopped block's K/V in the next block's "
                          "first update instead of in a pass of its own")
+    ap.add_argument("--serial-refresh", action="store_true",
+                    help="run an early-stopped block's K/V recomputation on the call's "
+                         "stream instead of beside the next block's first update "
+                         "(af_plan_set_overlap_refresh(0))")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the captured Jacobi update as a HIP graph instead "
                          "of launching every kernel directly")
@@ -712,6 +716,7 @@ def main():
     r.plan.set_graphs(args.graphs)
     r.plan.set_fused_refresh(args.fused_refresh)
     r.plan.set_row_split(args.row_split)
+    r.plan.set_overlap_refresh(not args.serial_refresh)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -753,8 +758,29 @@ def main():
     r.plan.profile_disable()
     roofline = roofline_of(dominant, n_launch, dom_ms, dom_work, cfg, w.name, args.steps)
     roofline["timing"] = (f"HIP events on the launch stream, {args.steps} direct-launch steps "
-                          "after the timed region")
+                          "after the timed region" +
+                          ("" if args.serial_refresh or w.length <= w.jacobi_block else
+                           "; cache refreshes run beside the next block's first update, so "
+                           "some launches share the GPU with the other stream's kernels"))
     roofline["ms_per_step_profiled"] = round((p1 - p0) * 1e3 / args.steps, 3)
+    # With a block's cache refresh running beside the next block's first update
+    # (two streams), a launch's events also span the other stream's kernels
+    # that share the GPU with it: the same kernel timed over K steps with every
+    # refresh on the call's stream gives its rate alone.
+    roof_alone = None
+    if not args.serial_refresh and w.length > w.jacobi_block and cfg.dtype == "bf16":
+        r.plan.set_overlap_refresh(False)
+        r.plan.profile_enable(dominant)
+        for _ in range(args.steps):
+            r.step()
+        torch.cuda.synchronize()
+        n_a, ms_a, work_a = r.plan.profile_read_work()
+        r.plan.profile_disable()
+        r.plan.set_overlap_refresh(True)
+        roof_alone = roofline_of(dominant, n_a, ms_a, work_a, cfg, w.name, args.steps)
+        roof_alone["timing"] = (f"HIP events on the launch stream, {args.steps} steps with "
+                                "every cache refresh on the call's stream (no concurrent "
+                                "kernels)")
     g = breakdown[gemm_dom]
     gemm_roof = roofline_of(gemm_dom, g["launches"], g["ms"], g["work"], cfg, w.name, 1)
 
@@ -794,6 +820,8 @@ def main():
         "graphs": args.graphs,
         "fused_refresh": args.fused_refresh,
         "row_split": args.row_split,
+        "overlap_refresh": not args.serial_refresh,
+        "roofline_kernel_alone": roof_alone,
         "kernel_ms_per_step": {c: {"launches": b["launches"], "ms": b["ms"]}
                                for c, b in breakdown.items()},
         "forward_ms": round(fwd_ms, 3),

@@ -280,6 +280,25 @@ af_status af_plan_graph_stats(const af_plan *p, long long *captures, long long *
  * 32 x 32 attention kernels one pass measured faster; AF_ERR_ARG if p is NULL. */
 af_status af_plan_set_row_split(af_plan *p, int enable);
 
+/* Cache refresh beside the next Jacobi block (STARFlow-V notes, 关键设计 3:
+ * finished blocks feed the KV cache that later blocks attend to).  On the
+ * bf16 path with at least two layers, when a block that is not the call's
+ * last stops before e-s updates, its K/V recomputation (which continues from
+ * the layer-0 results the next update's speculative first kernels already
+ * computed from the final tokens) runs on a second stream of the plan, in
+ * scratch of its own, while the next block's first update runs on `stream`;
+ * that update's attention at layer l waits (an event) for the refresh's K/V
+ * of layer l, and everything after it on `stream` is ordered after the
+ * whole refresh.  The same kernels run on the same inputs, so results are
+ * identical to the refresh on `stream`.  Used with direct launches, one pass
+ * per update (not with graphs, the row split or the fused refresh) and when
+ * ws_bytes >= af_workspace_bytes(p, N, min(B, L)), which includes that
+ * scratch on the bf16 path.  The call returns (also on an error) with
+ * `stream` ordered after all of the second stream's work; a plan must not be
+ * used by two calls at once.  enable != 0 (the default) allows it, 0 runs
+ * every refresh on `stream`; AF_ERR_ARG if p is NULL. */
+af_status af_plan_set_overlap_refresh(af_plan *p, int enable);
+
 /* The Jacobi loop on the device (STARFlow-V notes, 关键设计 3: the update is
  * repeated until the residual falls below tau).  For fp32 plans whose block
  * fits one workgroup (N * min(B, L) <= 64 rows, d 64 or 128, d / n_heads 32

@@ -155,13 +155,22 @@ int main() {
   CHECK(af_prefill(s, buf, 1, 8, ws, sb, nullptr) == AF_ERR_UNSUPPORTED);
   af_plan_destroy(s);
 
-  // a bf16 plan at the benchmark width: workspace sizes with the row split
-  af_plan* b = make(48, 1024, 16, 8, 4680, AF_BF16, 1, &st);
+  // a one-layer bf16 plan at the benchmark width: workspace sizes with the
+  // row split (from two layers the scratch of a refresh beside the next
+  // block covers the half's at every size)
+  af_plan* b = make(48, 1024, 16, 1, 4680, AF_BF16, 1, &st);
   CHECK(st == AF_OK && b != nullptr);
   CHECK(af_workspace_bytes(b, 1, 1024) - af_workspace_bytes(b, 1, 1023) > 20000000u);
   CHECK(af_workspace_bytes(b, 1, 4097) < af_workspace_bytes(b, 1, 4096));
-  CHECK(af_cache_bytes(b, 1) == (size_t)8 * 2 * 16 * 4736 * 64 * 2);
+  CHECK(af_cache_bytes(b, 1) == (size_t)1 * 2 * 16 * 4736 * 64 * 2);
+  CHECK(af_plan_set_overlap_refresh(b, 0) == AF_OK);
+  CHECK(af_plan_set_overlap_refresh(nullptr, 1) == AF_ERR_ARG);
   af_plan_destroy(b);
+  af_plan* b8 = make(48, 1024, 16, 8, 4680, AF_BF16, 1, &st);
+  CHECK(st == AF_OK && b8 != nullptr);
+  CHECK(af_workspace_bytes(b8, 1, 4097) > af_workspace_bytes(b8, 1, 4096));
+  CHECK(af_cache_bytes(b8, 1) == (size_t)8 * 2 * 16 * 4736 * 64 * 2);
+  af_plan_destroy(b8);
 
   // kernel-level entry points: argument checks
   CHECK(afk_affine_partials_bytes(0, 4, 4) == 0);

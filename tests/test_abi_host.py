@@ -262,6 +262,9 @@ def test_graph_controls(lib):
     assert lib.af_plan_set_row_split(h, 0) == B.AF_OK
     assert lib.af_plan_set_row_split(h, 1) == B.AF_OK
     assert lib.af_plan_set_row_split(None, 1) == B.AF_ERR_ARG
+    assert lib.af_plan_set_overlap_refresh(h, 0) == B.AF_OK
+    assert lib.af_plan_set_overlap_refresh(h, 1) == B.AF_OK
+    assert lib.af_plan_set_overlap_refresh(None, 1) == B.AF_ERR_ARG
     lib.af_plan_destroy(h)
 
 
@@ -269,13 +272,27 @@ def test_workspace_has_room_for_the_row_split(lib):
     # blocks of 1024 to 4096 rows of one sample may be split over two
     # streams: from 1024 rows the workspace holds a second half's scratch
     # (tens of MB at d = 1024, against about 0.2 MB per extra row), and past
-    # N * R = 4096 it no longer does
-    st, h = make_plan(lib, C=48, d=1024, H=16, layers=8, max_len=4680, dtype=B.AF_BF16)
+    # N * R = 4096 it no longer does (one layer: no refresh runs beside the
+    # next block, whose scratch would cover the half's)
+    st, h = make_plan(lib, C=48, d=1024, H=16, layers=1, max_len=4680, dtype=B.AF_BF16)
     assert st == B.AF_OK
     ws = lambda n, r: lib.af_workspace_bytes(h, n, r)
     assert ws(1, 1024) - ws(1, 1023) > 20e6
     assert ws(1, 4097) < ws(1, 4096)
     assert ws(2, 2049) < ws(2, 2048)
+    # from two layers a block's cache refresh may run beside the next block:
+    # the workspace holds a second full set of the per-pass scratch (which does
+    # not depend on the layer count) at every block size; beside the cache the
+    # one-layer workspace holds one set plus the higher-precision forward's lo
+    # halves (a second cache among them), which are not doubled
+    st, h2 = make_plan(lib, C=48, d=1024, H=16, layers=2, max_len=4680, dtype=B.AF_BF16)
+    assert st == B.AF_OK
+    c1, c2 = lib.af_cache_bytes(h, 1), lib.af_cache_bytes(h2, 1)
+    for r in (100, 1023, 4097):
+        one = ws(1, r) - 2 * c1
+        two = lib.af_workspace_bytes(h2, 1, r) - 2 * c2
+        assert 1.6 < two / one < 2.0, (r, one, two)
+    lib.af_plan_destroy(h2)
     st, h32 = make_plan(lib, C=16, d=64, H=2, layers=1, max_len=2048)   # fp32: never split
     assert lib.af_workspace_bytes(h32, 1, 1024) - lib.af_workspace_bytes(h32, 1, 1023) < 1e6
     lib.af_plan_destroy(h32)

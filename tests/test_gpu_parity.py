@@ -14,8 +14,9 @@ torch = pytest.importorskip("torch")
 
 from autoregressive_normalizing_flow_amd import synth  # noqa: E402
 from oracle import af_oracle as O  # noqa: E402
-from parity_util import (TOL_BF16, TOL_F32, TOL_LOGDET, oracle_jacobi_like,  # noqa: E402
-                         problem, rel_err, rel_l2, say, to_dev, to_np)
+from parity_util import (TOL_BF16, TOL_BF16_TOKEN, TOL_F32, TOL_LOGDET,  # noqa: E402
+                         oracle_jacobi_like, problem, rel_err, rel_l2, say, to_dev, to_np,
+                         token_rel_max)
 
 pytestmark = pytest.mark.gpu
 
@@ -319,6 +320,46 @@ def test_fused_refresh_matches_separate_pass(B, dtype):
         assert np.all(np.abs(it0 - it1) <= 1)
         assert rel_l2(to_np(x1), to_np(x0)) < 1e-2
         assert rel_l2(to_np(x1), xo) < TOL_BF16
+
+
+@pytest.mark.parametrize("prefix", [0, 192])
+def test_refresh_beside_next_block_matches_serial(B, prefix):
+    """A block that stops early has its K/V recomputed from its final tokens;
+    run on the plan's second stream beside the next block's first update
+    (whose attention waits for it layer by layer) the result equals the
+    refresh on the call's stream bit for bit, blocks and iteration counts
+    alike, and matches the oracle.  Two samples, three layers, blocks of 96
+    rows with a ragged last block, after an encoded prefix or none."""
+    say("refresh beside the next block, prefix", prefix)
+    N, L, Bj, C, H = 2, 300, 96, 48, 4
+    cfg, params, (p64,) = problem(C=C, d=256, H=H, layers=3, max_len=prefix + L,
+                                  dtype="bf16", seed=63)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((N, L, C), 64)
+    xp = synth.normal((N, prefix, C), 65) if prefix else None
+    kw = {}
+    if prefix:
+        cache, x_last = O.prefill(p64, xp, H)
+        kw = dict(pos0=prefix, cache=cache, x_last=x_last)
+    out = {}
+    for overlap in (False, True):
+        plan.set_overlap_refresh(overlap)
+        if prefix:
+            plan.prefill(to_dev(xp))
+            x, it = plan.inverse_jacobi(to_dev(z), Bj, 1e-3, prefix_len=prefix,
+                                        x_last=to_dev(xp[:, -1]))
+        else:
+            x, it = plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+        torch.cuda.synchronize()
+        out[overlap] = (x, it)
+    (x0, it0), (x1, it1) = out[False], out[True]
+    print("iters serial", it0.tolist(), "beside", it1.tolist())
+    assert np.all(it0[0][:-1] < Bj)                 # early stops: refreshes happen
+    assert np.array_equal(it0, it1) and torch.equal(x0, x1)
+    xo, _ = oracle_jacobi_like(p64, z, H, Bj, 1e-3, it1[0], **kw)
+    e, et = rel_l2(to_np(x1), xo), token_rel_max(to_np(x1), xo)
+    print(f"beside, prefix {prefix}: rel_l2 {e:.2e}, max per-token {et:.2e}")
+    assert e < TOL_BF16 and et < TOL_BF16_TOKEN
 
 
 @PATHS
