@@ -733,7 +733,14 @@ def main():
     iters = r.iters.tolist()
 
     # per-class breakdown: one profiled step per class (events on the launch
-    # stream of every launch of the class; algorithmic work from the library)
+    # stream of every launch of the class; algorithmic work from the library).
+    # With cache refreshes beside the next block's first update, launches of
+    # the two streams overlap and each one's events also span the other's
+    # work: the breakdown runs its steps with every refresh on the call's
+    # stream, so the classes' times are the kernels' own and add up to a step.
+    overlap = not args.serial_refresh and w.length > w.jacobi_block and cfg.dtype == "bf16"
+    if overlap:
+        r.plan.set_overlap_refresh(False)
     breakdown = {}
     for cls in ALL_CLASSES:
         r.plan.profile_enable(cls)
@@ -741,46 +748,50 @@ def main():
         n, ms, work = r.plan.profile_read_work()
         r.plan.profile_disable()
         breakdown[cls] = {"launches": n, "ms": round(ms, 4), "work": work}
+    if overlap:
+        r.plan.set_overlap_refresh(True)
     dominant = max(ALL_CLASSES, key=lambda c: breakdown[c]["ms"])
     gemm_dom = max(GEMM_CLASSES, key=lambda c: breakdown[c]["ms"])
 
     # the dominant kernel timed live by HIP events on the stream it is launched
     # on, over K more steps of the same workload; these launch directly, as
-    # events recorded inside a graph carry no timing on this runtime
-    r.plan.profile_enable(dominant)
-    torch.cuda.synchronize()
-    p0 = time.perf_counter()
-    for _ in range(args.steps):
-        r.step()
-    torch.cuda.synchronize()
-    p1 = time.perf_counter()
-    n_launch, dom_ms, dom_work = r.plan.profile_read_work()
-    r.plan.profile_disable()
-    roofline = roofline_of(dominant, n_launch, dom_ms, dom_work, cfg, w.name, args.steps)
-    roofline["timing"] = (f"HIP events on the launch stream, {args.steps} direct-launch steps "
-                          "after the timed region" +
-                          ("" if args.serial_refresh or w.length <= w.jacobi_block else
-                           "; cache refreshes run beside the next block's first update, so "
-                           "some launches share the GPU with the other stream's kernels"))
-    roofline["ms_per_step_profiled"] = round((p1 - p0) * 1e3 / args.steps, 3)
-    # With a block's cache refresh running beside the next block's first update
-    # (two streams), a launch's events also span the other stream's kernels
-    # that share the GPU with it: the same kernel timed over K steps with every
-    # refresh on the call's stream gives its rate alone.
-    roof_alone = None
-    if not args.serial_refresh and w.length > w.jacobi_block and cfg.dtype == "bf16":
-        r.plan.set_overlap_refresh(False)
+    # events recorded inside a graph carry no timing on this runtime.  With
+    # cache refreshes beside the next block's first update (two streams), a
+    # launch that overlaps the other stream's kernels shares the GPU with them
+    # and its events span their work too: the roofline takes the K steps with
+    # every refresh on the call's stream (the kernels alone, as the breakdown
+    # and the counters see them), and `roofline_in_step` the same class over K
+    # steps as the timed region runs them.
+    def time_dominant(overlapped):
+        if overlap:
+            r.plan.set_overlap_refresh(overlapped)
         r.plan.profile_enable(dominant)
+        torch.cuda.synchronize()
+        p0 = time.perf_counter()
         for _ in range(args.steps):
             r.step()
         torch.cuda.synchronize()
-        n_a, ms_a, work_a = r.plan.profile_read_work()
+        p1 = time.perf_counter()
+        n_l, ms_l, work_l = r.plan.profile_read_work()
         r.plan.profile_disable()
-        r.plan.set_overlap_refresh(True)
-        roof_alone = roofline_of(dominant, n_a, ms_a, work_a, cfg, w.name, args.steps)
-        roof_alone["timing"] = (f"HIP events on the launch stream, {args.steps} steps with "
-                                "every cache refresh on the call's stream (no concurrent "
-                                "kernels)")
+        if overlap:
+            r.plan.set_overlap_refresh(True)
+        roof = roofline_of(dominant, n_l, ms_l, work_l, cfg, w.name, args.steps)
+        roof["ms_per_step_profiled"] = round((p1 - p0) * 1e3 / args.steps, 3)
+        return roof
+    roofline = time_dominant(False)
+    roofline["timing"] = (f"HIP events on the launch stream, {args.steps} direct-launch steps "
+                          "after the timed region" +
+                          (" with every cache refresh on the call's stream (the kernels alone; "
+                           "in the timed steps refreshes run beside the next block's first "
+                           "update)" if overlap else ""))
+    roof_step = None
+    if overlap:
+        roof_step = time_dominant(True)
+        roof_step["timing"] = (f"HIP events on the launch stream, {args.steps} steps as the timed "
+                               "region runs them: launches that overlap the other stream's "
+                               "kernels share the GPU with them, and their events span that "
+                               "work too")
     g = breakdown[gemm_dom]
     gemm_roof = roofline_of(gemm_dom, g["launches"], g["ms"], g["work"], cfg, w.name, 1)
 
@@ -821,9 +832,12 @@ def main():
         "fused_refresh": args.fused_refresh,
         "row_split": args.row_split,
         "overlap_refresh": not args.serial_refresh,
-        "roofline_kernel_alone": roof_alone,
+        "roofline_in_step": roof_step,
         "kernel_ms_per_step": {c: {"launches": b["launches"], "ms": b["ms"]}
                                for c, b in breakdown.items()},
+        "breakdown_timing": ("one profiled step per class" +
+                             (", every cache refresh on the call's stream (kernels alone)"
+                              if overlap else "")),
         "forward_ms": round(fwd_ms, 3),
     }
     if not args.no_sweep:
