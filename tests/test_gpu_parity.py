@@ -362,6 +362,32 @@ def test_refresh_beside_next_block_matches_serial(B, prefix):
     assert e < TOL_BF16 and et < TOL_BF16_TOKEN
 
 
+def test_refresh_beside_next_block_error_path(B):
+    """A non-finite value in a later block while an earlier block's refresh
+    may still run on the plan's second stream: the call reports
+    AF_ERR_NONFINITE for that block (with the calling stream ordered after
+    the second stream's work), and a clean call on the same plan afterwards
+    equals a fresh plan's, bit for bit."""
+    say("refresh beside the next block: error path")
+    N, L, Bj, C, H = 1, 288, 96, 48, 4
+    cfg, params, _ = problem(C=C, d=256, H=H, layers=2, max_len=L, dtype="bf16", seed=66)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((N, L, C), 67)
+    z[0, 2 * Bj + 5, 3] = np.nan                     # in the third block
+    with pytest.raises(B.AFError) as ei:
+        plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+    assert ei.value.status == B.AF_ERR_NONFINITE
+    assert "Jacobi block 2" in str(ei.value)
+    z[0, 2 * Bj + 5, 3] = 0.0
+    xa, ia = plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+    fresh = B.AFPlan(cfg, params)
+    xb, ib = fresh.inverse_jacobi(to_dev(z), Bj, 1e-3)
+    torch.cuda.synchronize()
+    print("iters", ia.tolist())
+    assert np.all(ia[0][:-1] < Bj)                  # early stops: refreshes ran beside
+    assert np.array_equal(ia, ib) and torch.equal(xa, xb)
+
+
 @PATHS
 def test_f32_forced_count_and_sequential(B, dl):
     say("f32 forced + B=1")
