@@ -362,6 +362,35 @@ def test_refresh_beside_next_block_matches_serial(B, prefix):
     assert e < TOL_BF16 and et < TOL_BF16_TOKEN
 
 
+def test_refresh_beside_next_block_in_a_stack(B):
+    """A bf16 stack of two alternating AF blocks (two layers each) with three
+    Jacobi blocks per AF block: refreshes run beside the next Jacobi block
+    inside each AF block, and the next AF block (which rewrites the same cache
+    rows with its own K/V) starts only after them.  Equal to every refresh on
+    the call's stream, bit for bit, and to the oracle's stack inverse forced to
+    the GPU's counts."""
+    say("refresh beside the next block: stack T=2")
+    N, L, Bj, C, H = 2, 240, 80, 48, 4
+    cfg, params, p64 = problem(C=C, d=256, H=H, layers=2, max_len=L, dtype="bf16",
+                               seed=68, n_blocks=2)
+    plan = B.AFPlan(cfg, params)
+    z = synth.normal((N, L, C), 69)
+    out = {}
+    for overlap in (False, True):
+        plan.set_overlap_refresh(overlap)
+        x, it = plan.inverse_jacobi(to_dev(z), Bj, 1e-3)
+        torch.cuda.synchronize()
+        out[overlap] = (x, it)
+    (x0, it0), (x1, it1) = out[False], out[True]
+    print("iters serial", it0.tolist(), "beside", it1.tolist())
+    assert np.all(it1[:, :-1] < Bj)                 # early stops in both AF blocks
+    assert np.array_equal(it0, it1) and torch.equal(x0, x1)
+    xo, _ = O.inverse_jacobi_stack(p64, z, H, Bj, 1e-3, forced_iters=it1)
+    e, et = rel_l2(to_np(x1), xo), token_rel_max(to_np(x1), xo)
+    print(f"stack beside: rel_l2 {e:.2e}, max per-token {et:.2e}")
+    assert e < TOL_BF16 and et < TOL_BF16_TOKEN
+
+
 def test_refresh_beside_next_block_error_path(B):
     """A non-finite value in a later block while an earlier block's refresh
     may still run on the plan's second stream: the call reports
