@@ -13,7 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch  # loads the HIP runtime the library then shares
@@ -106,6 +106,8 @@ def load_library() -> ctypes.CDLL:
     L.af_plan_set_row_split.restype = st
     L.af_plan_set_overlap_refresh.argtypes = [_P, i]
     L.af_plan_set_overlap_refresh.restype = st
+    L.af_plan_set_block_done.argtypes = [_P, _BLOCK_DONE_FN, _P]
+    L.af_plan_set_block_done.restype = st
     L.af_plan_set_device_loop.argtypes = [_P, i]
     L.af_plan_set_device_loop.restype = st
     L.af_plan_graph_stats.argtypes = [_P, ctypes.POINTER(ctypes.c_longlong),
@@ -135,6 +137,10 @@ def load_library() -> ctypes.CDLL:
     L.af_abi_version.restype = ctypes.c_int
     _lib = L
     return L
+
+
+# af_block_done_fn: void (*)(void *user, int stack_block, int jacobi_block)
+_BLOCK_DONE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_int)
 
 
 def header_functions() -> List[str]:
@@ -346,6 +352,31 @@ class AFPlan:
     def set_overlap_refresh(self, enable: bool):
         _check(self.L.af_plan_set_overlap_refresh(self.handle, int(bool(enable))),
                "af_plan_set_overlap_refresh")
+
+    def set_block_done(self, fn: Optional[Callable[[int, int], None]]):
+        """fn(stack_block, jacobi_block) is called on the calling thread of
+        inverse_jacobi once that block's tokens are final on the call's stream
+        (record an event there to wait for them from another stream); None
+        turns it off.  Exceptions raised by fn are kept and re-raised by the
+        next set_block_done(None)."""
+        if fn is None:
+            _check(self.L.af_plan_set_block_done(self.handle, _BLOCK_DONE_FN(), None),
+                   "af_plan_set_block_done")
+            self._done_cb = None
+            errs, self._done_errors = getattr(self, "_done_errors", []), []
+            if errs:
+                raise errs[0]
+            return
+        self._done_errors = []
+
+        def tramp(_user, t, b):
+            try:
+                fn(t, b)
+            except BaseException as e:  # no exception may cross the C ABI
+                self._done_errors.append(e)
+        self._done_cb = _BLOCK_DONE_FN(tramp)   # kept alive with the plan
+        _check(self.L.af_plan_set_block_done(self.handle, self._done_cb, None),
+               "af_plan_set_block_done")
 
     def set_device_loop(self, enable: bool):
         _check(self.L.af_plan_set_device_loop(self.handle, int(bool(enable))),

@@ -128,6 +128,10 @@ struct af_plan {
   // a block's cache refresh on the second stream beside the next block's
   // first update (see af_inverse_jacobi; on by default)
   bool overlap_refresh = true;
+  // called on the calling thread once a Jacobi block's tokens are final on
+  // the stream (af_plan_set_block_done)
+  af_block_done_fn done_fn = nullptr;
+  void* done_user = nullptr;
   hipStream_t split_stream = nullptr;
   std::vector<hipEvent_t> split_ev;   // eq[l], ea[l], then affine, fork, join
   // residual pairs of the last update of the last inverse call (halves added)
@@ -957,6 +961,9 @@ static af_status inverse_on_device(af_plan* p, const float* z, int N, int L, int
     a.res_host = p->host_res_dev;
     a.bad_host = (unsigned*)(p->loop_host_dev + (size_t)p->T * nb + t);
     LAUNCH(K_LOOP, af::launch_jacobi_loop(a, st));
+    // every Jacobi block of this AF block is final once the stream reaches here
+    if (p->done_fn)
+      for (int b = 0; b < nb; ++b) p->done_fn(p->done_user, t, b);
     zin = a.x;
   }
   AF_HIP(hipStreamSynchronize(st));
@@ -1283,6 +1290,8 @@ af_status af_inverse_jacobi(af_plan* p, const float* z, int N, int L, int B,
       }
       if (k > kmax) k = kmax;
       iters[t * nb + b] = k;
+      // the block's tokens are final once the stream reaches this point
+      if (p->done_fn) p->done_fn(p->done_user, t, b);
       pending = 0;
       if (k < R && b + 1 < nb) {
         if (fuse) {
@@ -1411,6 +1420,13 @@ af_status af_plan_set_row_split(af_plan* p, int enable) {
 af_status af_plan_set_overlap_refresh(af_plan* p, int enable) {
   if (!p) return fail(AF_ERR_ARG, "NULL argument");
   p->overlap_refresh = enable != 0;
+  return AF_OK;
+}
+
+af_status af_plan_set_block_done(af_plan* p, af_block_done_fn fn, void* user) {
+  if (!p) return fail(AF_ERR_ARG, "NULL argument");
+  p->done_fn = fn;
+  p->done_user = fn ? user : nullptr;
   return AF_OK;
 }
 

@@ -7,7 +7,9 @@ frame per block, the previous frame as the warm start, the finished frames'
 K/V in the cache) and f_S per frame.  Because f_S^-1 of frame n only needs
 u_n, it runs on a second stream, driven by a second host thread, while f_D^-1
 works on frame n+1: the deep block keeps running and the shallow stack
-consumes its output.
+consumes its output.  The pipelined inverse inverts f_D in one call over all
+frames (the same results as one call per frame) and learns from the library's
+block-done notification when each frame's tokens are final.
 
 Method: STARFlow-V notes (papernotes.org), 整体框架 (f_theta = f_D o f_S,
 u = f_S(x), z = f_D(u); f_D^-1 causal over frames, f_S^-1 per frame),
@@ -17,7 +19,8 @@ runs without pause while f_S consumes its output in parallel, so the latency
 is set by the deep block).
 
 Every step runs through the C ABI (af_forward, af_inverse_jacobi,
-af_refresh_kv); this module only schedules calls and streams.
+af_refresh_kv, af_plan_set_block_done); this module only schedules calls and
+streams.
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-from .binding import AFPlan
+from .binding import AFPlan, af_inverse_jacobi
 
 
 class DeepShallowFlow:
@@ -143,18 +146,33 @@ class DeepShallowFlow:
 
         th = threading.Thread(target=consumer, daemon=True)
         th.start()
+
+        # f_D^-1 as one call over all frames (previous-frame warm start, each
+        # finished frame's cache refreshed inside the call, beside the next
+        # frame's first update); the library reports each frame as soon as
+        # its tokens are final on the deep stream
+        def frame_done(_t, b):
+            ev = torch.cuda.Event()
+            ev.record(s_deep)
+            ready.put((b, ev))
+
+        iters = np.zeros((1, nf), dtype=np.int32)
         try:
             with torch.cuda.stream(s_deep):
-                for n in range(nf):
-                    it_d[n], ev = self._deep_frame(z, u, n, tau, max_iters, s_deep)
-                    ready.put((n, ev))
-                    if errors:
-                        break
+                ws = self.deep.workspace(1, self.F)
+                self.deep._use(s_deep)
+                self.deep.set_block_done(frame_done)
+                try:
+                    af_inverse_jacobi(self.deep, z, self.F, tau, max_iters, "prev_frame", None,
+                                      self.F, 0, None, u, iters, ws, s_deep)
+                finally:
+                    self.deep.set_block_done(None)
         finally:
             ready.put(None)
             th.join()
         if errors:
             raise errors[0]
+        it_d[:] = iters[0]
         torch.cuda.current_stream().wait_stream(s_deep)
         torch.cuda.current_stream().wait_stream(s_shallow)
         return x, it_d, it_s

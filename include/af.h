@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define AF_ABI_VERSION 2
+#define AF_ABI_VERSION 3
 
 typedef enum {
   AF_OK = 0,
@@ -298,6 +298,22 @@ af_status af_plan_set_row_split(af_plan *p, int enable);
  * used by two calls at once.  enable != 0 (the default) allows it, 0 runs
  * every refresh on `stream`; AF_ERR_ARG if p is NULL. */
 af_status af_plan_set_overlap_refresh(af_plan *p, int enable);
+
+/* Block-done notification (STARFlow-V notes, 关键设计 3: the shallow flow
+ * inverts each frame as soon as the deep block has produced it).  While
+ * af_inverse_jacobi runs, fn(user, t, b) is called on the calling thread once
+ * per Jacobi block b of stack block t, right after the work that makes that
+ * block's x final has been enqueued on `stream`: an event recorded on `stream`
+ * inside fn completes when x[:, b*B : min(L, (b+1)*B)] of stack block t is
+ * final (for t = 0, the call's output), so another stream can start on those
+ * tokens while the call goes on.  On the device loop (af_plan_set_device_loop)
+ * every Jacobi block of an AF block is reported right after that AF block's
+ * launch.  A call is not a promise that the block succeeded: the call's
+ * return status says so.  fn must not use the plan (it is inside a call) and
+ * must return promptly.  fn = NULL (the default) turns it off; AF_ERR_ARG if
+ * p is NULL. */
+typedef void (*af_block_done_fn)(void *user, int stack_block, int jacobi_block);
+af_status af_plan_set_block_done(af_plan *p, af_block_done_fn fn, void *user);
 
 /* The Jacobi loop on the device (STARFlow-V notes, 关键设计 3: the update is
  * repeated until the residual falls below tau).  For fp32 plans whose block

@@ -265,6 +265,12 @@ def test_graph_controls(lib):
     assert lib.af_plan_set_overlap_refresh(h, 0) == B.AF_OK
     assert lib.af_plan_set_overlap_refresh(h, 1) == B.AF_OK
     assert lib.af_plan_set_overlap_refresh(None, 1) == B.AF_ERR_ARG
+    calls = []
+    cb = B._BLOCK_DONE_FN(lambda user, t, b: calls.append((t, b)))
+    assert lib.af_plan_set_block_done(h, cb, None) == B.AF_OK
+    assert lib.af_plan_set_block_done(h, B._BLOCK_DONE_FN(), None) == B.AF_OK   # NULL
+    assert lib.af_plan_set_block_done(None, cb, None) == B.AF_ERR_ARG
+    assert calls == []
     lib.af_plan_destroy(h)
 
 

@@ -98,6 +98,49 @@ def test_deep_frames_equal_one_video_call(B, dtype, device_loop):
     assert torch.equal(u, u_one)
 
 
+@pytest.mark.parametrize("dtype,device_loop", [("f32", True), ("f32", False),
+                                                ("bf16", False)])
+def test_block_done_reports_final_tokens(B, dtype, device_loop):
+    """af_plan_set_block_done: one call per Jacobi block, in order, and an
+    event recorded on the call's stream inside the callback completes only
+    when that block's tokens are final (a copy of the block's rows made on
+    another stream after the event equals the call's output)."""
+    say("block done", dtype, "device loop", device_loop)
+    if dtype == "f32":
+        C, F = 16, 16
+        _, _, _, deep = flows(B, "f32", C, 64, 2, 1, F, 4)
+    else:
+        C, F = 48, 128
+        _, _, _, deep = flows(B, "bf16", C, 256, 4, 2, F, 4, seed=7)
+    deep.set_device_loop(device_loop)
+    z = to_dev(synth.normal((1, 4 * F, C), 3))
+    u = torch.empty_like(z)
+    snap = torch.full_like(z, float("nan"))
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    seen = []
+
+    def done(t, b):
+        ev = torch.cuda.Event()
+        ev.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(ev)
+            snap[:, b * F:(b + 1) * F].copy_(u[:, b * F:(b + 1) * F])
+        seen.append((t, b))
+
+    from autoregressive_normalizing_flow_amd import binding
+    it = np.zeros((1, 4), np.int32)
+    ws = deep.workspace(1, F)
+    deep.set_block_done(done)
+    binding.af_inverse_jacobi(deep, z, F, 1e-3, 0, "prev_frame", None, F, 0, None, u, it, ws)
+    deep.set_block_done(None)
+    torch.cuda.synchronize()
+    assert seen == [(0, b) for b in range(4)]
+    assert torch.equal(snap, u)
+    u2, it2 = deep.inverse_jacobi(z, F, 1e-3, init="prev_frame", frame_len=F)
+    assert np.array_equal(it, it2) and torch.equal(u, u2)
+
+
 @pytest.mark.parametrize("frame_len", [0, 16])
 def test_streaming_window_vs_oracle(B, frame_len):
     """Sliding-window generation past the block's positions: every chunk
