@@ -165,6 +165,14 @@ int main() {
   CHECK(af_cache_bytes(b, 1) == (size_t)1 * 2 * 16 * 4736 * 64 * 2);
   CHECK(af_plan_set_overlap_refresh(b, 0) == AF_OK);
   CHECK(af_plan_set_overlap_refresh(nullptr, 1) == AF_ERR_ARG);
+  {
+    static int calls = 0;
+    af_block_done_fn cb = [](void* user, int, int) { ++*(int*)user; };
+    CHECK(af_plan_set_block_done(b, cb, &calls) == AF_OK);
+    CHECK(af_plan_set_block_done(b, nullptr, nullptr) == AF_OK);
+    CHECK(af_plan_set_block_done(nullptr, cb, &calls) == AF_ERR_ARG);
+    CHECK(calls == 0);
+  }
   af_plan_destroy(b);
   af_plan* b8 = make(48, 1024, 16, 8, 4680, AF_BF16, 1, &st);
   CHECK(st == AF_OK && b8 != nullptr);
