@@ -391,6 +391,30 @@ def test_refresh_beside_next_block_in_a_stack(B):
     assert e < TOL_BF16 and et < TOL_BF16_TOKEN
 
 
+def test_refresh_beside_next_block_needs_its_workspace(B):
+    """With a workspace one byte short of af_workspace_bytes (room for the
+    main layout but not for the refresh's scratch) every refresh runs on the
+    call's stream: the same result, bit for bit, as with the full workspace."""
+    say("refresh beside the next block: small workspace")
+    N, L, Bj, C, H = 1, 288, 96, 48, 4
+    cfg, params, _ = problem(C=C, d=256, H=H, layers=2, max_len=L, dtype="bf16", seed=70)
+    plan = B.AFPlan(cfg, params)
+    z = to_dev(synth.normal((N, L, C), 71))
+    ws = plan.workspace(N, Bj)
+    assert ws.numel() == plan.workspace_bytes(N, Bj)
+    out = []
+    for w in (ws, ws[:-1]):
+        x = torch.empty_like(z)
+        it = np.zeros((1, -(-L // Bj)), np.int32)
+        B.af_inverse_jacobi(plan, z, Bj, 1e-3, 0, "zero", None, 0, 0, None, x, it, w)
+        torch.cuda.synchronize()
+        out.append((x, it))
+    (xa, ia), (xb, ib) = out
+    print("iters", ia.tolist())
+    assert np.all(ia[0][:-1] < Bj)
+    assert np.array_equal(ia, ib) and torch.equal(xa, xb)
+
+
 def test_refresh_beside_next_block_error_path(B):
     """A non-finite value in a later block while an earlier block's refresh
     may still run on the plan's second stream: the call reports
